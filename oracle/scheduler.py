@@ -1,0 +1,185 @@
+"""Iteration-level scheduling: Algorithm 1 ``Select`` and the loop around it.
+
+Sources: "连续批处理完全拆解" (Algorithm 1 and the notes after it, sections
+迭代级 FCFS / 两个约束), "CS349D Lecture 2 · 批处理与调度" (section 4.1 timeline,
+section 4.3 scheduling algorithm, exercise 1), and the ``select_batch`` of
+"Orca: The beginning of Morden LLM serving" (section Scheduling Algorithm).
+
+Readings taken where the pages are garbled or silent:
+  * every non-RUNNING request that passes the checks joins the batch, in both
+    phases; only a request in the INITIATION phase reserves slots;
+  * the reservation check breaks when ``n_rsrv + max_tokens > n_slots``, so an
+    exact fit is admitted; a failed check stops the scan (never skips);
+  * equal arrival times are ordered by submission order;
+  * a request is finished once it has generated ``out_len`` tokens; its
+    ``max_tokens`` slots return to the pool after that iteration;
+  * a request whose ``max_tokens`` exceeds ``n_slots`` can never be admitted
+    and is rejected when it is submitted;
+  * one worker (one batch in flight), so no request is RUNNING when Select runs.
+"""
+import math
+
+INITIATION = "INITIATION"
+RUNNING = "RUNNING"
+INCREMENT = "INCREMENT"
+
+
+class TooLarge(ValueError):
+    """max_tokens exceeds the K/V slot pool: the request could never be admitted."""
+
+
+class SReq:
+    """Scheduler view of a request."""
+
+    __slots__ = ("rid", "arrival", "order", "prompt_len", "out_len", "max_tokens", "state", "generated")
+
+    def __init__(self, rid, arrival, order, prompt_len, out_len, max_tokens):
+        self.rid = rid
+        self.arrival = arrival
+        self.order = order
+        self.prompt_len = prompt_len
+        self.out_len = out_len
+        self.max_tokens = max_tokens
+        self.state = INITIATION
+        self.generated = 0
+
+
+def select(pool, n_rsrv, max_bs, n_slots):
+    """Algorithm 1 ``Select``: returns (batch, n_rsrv).
+
+    Scan the requests that are not RUNNING in arrival order; stop at ``max_bs``;
+    a request that has never been scheduled must first fit its ``max_tokens``
+    into the remaining slots, otherwise the scan stops there.
+    """
+    batch = []
+    candidates = sorted((r for r in pool if r.state != RUNNING), key=lambda r: (r.arrival, r.order))
+    for r in candidates:
+        if len(batch) == max_bs:
+            break
+        if r.state == INITIATION:
+            wanted = n_rsrv + r.max_tokens
+            if wanted > n_slots:
+                break
+            n_rsrv = wanted
+        batch.append(r)
+    return batch, n_rsrv
+
+
+def work_of(r):
+    """(n_new, ctx) a batch member processes this iteration.
+
+    A request that has not run yet feeds its whole prompt with nothing cached;
+    afterwards it feeds its last generated token, with the prompt and all but
+    that token already cached.
+    """
+    if r.generated == 0:
+        return r.prompt_len, 0
+    return 1, r.prompt_len + r.generated - 1
+
+
+class Scheduler:
+    """Pool, counters and the per-iteration state transitions (one worker)."""
+
+    def __init__(self, max_bs, n_slots):
+        if max_bs <= 0:
+            raise ValueError("max_bs must be positive")
+        self.max_bs = max_bs
+        self.n_slots = n_slots
+        self.n_rsrv = 0
+        self.pool = []
+        self._order = 0
+
+    def add(self, rid, arrival, prompt_len, out_len, max_tokens):
+        if max_tokens > self.n_slots:
+            raise TooLarge(f"request {rid}: max_tokens {max_tokens} > n_slots {self.n_slots}")
+        if prompt_len < 1 or out_len < 1 or prompt_len + out_len - 1 > max_tokens:
+            raise ValueError(f"request {rid}: inconsistent lengths")
+        r = SReq(rid, arrival, self._order, prompt_len, out_len, max_tokens)
+        self._order += 1
+        self.pool.append(r)
+        return r
+
+    def select(self):
+        batch, self.n_rsrv = select(self.pool, self.n_rsrv, self.max_bs, self.n_slots)
+        for r in batch:
+            r.state = RUNNING
+        return batch
+
+    def complete(self, batch):
+        """The iteration returned one token per member: move to INCREMENT, retire finished ones."""
+        finished = []
+        for r in batch:
+            r.state = INCREMENT
+            r.generated += 1
+            if r.generated == r.out_len:
+                self.n_rsrv -= r.max_tokens
+                finished.append(r)
+        if finished:
+            gone = {id(r) for r in finished}
+            self.pool = [r for r in self.pool if id(r) not in gone]
+        return finished
+
+
+def replay(reqs, max_bs, n_slots, engine=None):
+    """Run the iteration loop on a logical clock t = 0, 1, 2, ...
+
+    ``reqs``: objects with ``rid, arrival, prompt (or prompt_len), out_len,
+    max_tokens``.  A request may join from iteration t on when its arrival is
+    ``<= t``; when the pool is empty the clock jumps to the next arrival.
+    ``engine(t, batch_work)`` -- if given -- is called with the list of
+    ``(rid, n_new, ctx)`` of the iteration, in batch order.
+
+    Returns the per-iteration log ``[(t, [(rid, n_new, ctx), ...], n_rsrv_after_select)]``.
+    """
+    s = Scheduler(max_bs, n_slots)
+    pending = sorted(reqs, key=lambda r: (r.arrival, r.rid))
+    i = 0
+    t = 0
+    log = []
+    while i < len(pending) or s.pool:
+        while i < len(pending) and pending[i].arrival <= t:
+            r = pending[i]
+            plen = len(r.prompt) if hasattr(r, "prompt") else r.prompt_len
+            s.add(r.rid, r.arrival, plen, r.out_len, r.max_tokens)
+            i += 1
+        if not s.pool:
+            t = int(math.ceil(pending[i].arrival))
+            continue
+        batch = s.select()
+        if not batch:
+            raise RuntimeError("non-empty pool produced an empty batch")
+        work = [(r.rid, *work_of(r)) for r in batch]
+        log.append((t, work, s.n_rsrv))
+        if engine is not None:
+            engine(t, work)
+        s.complete(batch)
+        t += 1
+    return log
+
+
+def timeline(log, reqs):
+    """Render a replay log as one row of P/D/wait marks per request (lecture section 4.1 style).
+
+    'P' = prefill this iteration, 'D' = decode, '·' = arrived and waiting,
+    ' ' = not arrived yet or already finished.
+    """
+    n_it = log[-1][0] + 1 if log else 0
+    rows = {r.rid: [" "] * n_it for r in reqs}
+    last = {}
+    for t, work, _ in log:
+        for rid, n_new, ctx in work:
+            rows[rid][t] = "P" if ctx == 0 and _is_first(rid, t, log) else "D"
+            last[rid] = t
+    for r in reqs:
+        for t in range(n_it):
+            if rows[r.rid][t] == " " and r.arrival <= t and t < last.get(r.rid, n_it):
+                rows[r.rid][t] = "·"
+    return {rid: "".join(v).rstrip() for rid, v in rows.items()}
+
+
+def _is_first(rid, t, log):
+    for tt, work, _ in log:
+        for w in work:
+            if w[0] == rid:
+                return tt == t
+    return False
