@@ -1,0 +1,243 @@
+/*
+ * sb.h -- C ABI of the selective-batching library (libsb.so, MI355X / gfx950).
+ *
+ * One selective-batched Transformer iteration over a ragged batch, plus the
+ * host-side K/V manager and iteration-level scheduler that feed it.
+ *
+ * Sources (web pages on Orca-style continuous batching):
+ *   [W]  "连续批处理完全拆解：Orca 的迭代级调度与选择性批处理" -- Algorithm 1,
+ *        sections 观察 (selective batching), Figure 5 (Split / Merge, K/V
+ *        manager), 迭代级 FCFS, 两个约束 (max_bs, K/V slots).
+ *   [L2] "CS349D Lecture 2 · 批处理与调度" -- sections 4.1-4.3, 5.1 (memory
+ *        manager try_admit / free), exercise 4.
+ *   [OB] "Orca: The beginning of Morden LLM serving" -- section Scheduling
+ *        Algorithm (select_batch).
+ *
+ * Conventions for every entry point:
+ *   - Return value: SB_OK (0) or a negative sb_status.  No exception crosses
+ *     the ABI.  sb_last_error() returns a thread-local message for the last
+ *     failure on the calling thread.
+ *   - "host" pointers are ordinary CPU memory; "device" pointers are GPU
+ *     memory owned by the caller (the library never allocates device memory
+ *     and never frees caller memory).  Opaque handles (sb_kv, sb_sched) are
+ *     owned by the library and released with their destroy call.
+ *   - Device work is enqueued asynchronously on the HIP stream passed as
+ *     `stream` (a hipStream_t; NULL = the default stream); the call returns
+ *     after the launches.  A launch failure returns SB_ERR_DEVICE.
+ *   - Matrices are row-major.  Weights are [out_features, in_features]
+ *     (K-contiguous).  Activations are [tokens, features].
+ */
+#ifndef SB_H
+#define SB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ------------------------------------------------------------------ status */
+typedef enum {
+    SB_OK = 0,
+    SB_ERR_INVALID = -1,    /* bad argument (null handle, non-positive size, unsupported shape) */
+    SB_ERR_NO_SLOTS = -2,   /* reservation would exceed n_slots                                  */
+    SB_ERR_NOT_FOUND = -3,  /* unknown request id, or already freed                              */
+    SB_ERR_TOO_LARGE = -4,  /* max_tokens > n_slots: the request could never be admitted         */
+    SB_ERR_DEVICE = -5,     /* HIP launch / runtime error                                        */
+    SB_ERR_WORKSPACE = -6,  /* caller-provided buffer too small                                  */
+    SB_ERR_STATE = -7,      /* call not valid in the request's current state                     */
+    SB_ERR_CAPACITY = -8    /* output array capacity too small                                   */
+} sb_status;
+
+const char* sb_last_error(void);
+
+/* ------------------------------------------------------------------ types  */
+enum { SB_F32 = 0, SB_BF16 = 1 };          /* storage dtype of weights, K/V and GEMM operands */
+enum { SB_ARCH_GPT = 0, SB_ARCH_LLAMA = 1 };
+
+/* Model shape.  GPT-style: LayerNorm (gain, shift), biases, exact-erf GeLU,
+ * learned absolute positions.  Llama-style: RMSNorm (gain), no biases,
+ * SwiGLU, rotary embedding (rotate-half, base rope_theta) on q and k.
+ * Query head h reads K/V head h / (n_heads / n_kv_heads). */
+typedef struct {
+    int32_t arch, dtype;
+    int32_t n_layers, hidden, n_heads, n_kv_heads, head_dim, ffn, vocab, max_pos;
+    float eps, rope_theta;
+} sb_model_dims;
+
+/* One layer's weights (device, model dtype).  Shapes:
+ *   ln1_g, ln1_b, ln2_g, ln2_b : [hidden]            (ln*_b NULL for Llama)
+ *   w_qkv : [(n_heads + 2 n_kv_heads) head_dim, hidden] -- Q rows, K rows, V rows
+ *   b_qkv : [(n_heads + 2 n_kv_heads) head_dim]       (NULL for Llama)
+ *   w_o   : [hidden, n_heads head_dim]; b_o : [hidden] (NULL for Llama)
+ *   w1    : [ffn, hidden] (GPT) or [2 ffn, hidden] gate rows then up rows (Llama)
+ *   b1    : [ffn] (NULL for Llama); w2 : [hidden, ffn]; b2 : [hidden] (NULL for Llama) */
+typedef struct {
+    const void *ln1_g, *ln1_b, *w_qkv, *b_qkv, *w_o, *b_o, *ln2_g, *ln2_b, *w1, *b1, *w2, *b2;
+} sb_layer_weights;
+
+/* Embedding / head weights (device, model dtype):
+ *   tok_emb [vocab, hidden]; pos_emb [max_pos, hidden] (GPT, else NULL);
+ *   lnf_g, lnf_b [hidden] (lnf_b NULL for Llama); w_lm [vocab, hidden] (not tied). */
+typedef struct {
+    const void *tok_emb, *pos_emb, *lnf_g, *lnf_b, *w_lm;
+} sb_model_weights;
+
+/* ------------------------------------------------------------------ K/V manager
+ * The Attention K/V manager of [W] Figure 5: keeps each request's keys and
+ * values until the scheduler frees the request.  Admission follows the
+ * reservation rule of [W] 两个约束 / Algorithm 1 and [L2] 4.3: a request
+ * reserves max_tokens slots (one slot = one token's K and V in every layer)
+ * when first scheduled; the reservation fails iff n_rsrv + max_tokens > n_slots.
+ * Each reservation is one contiguous slot range starting at a multiple of 8;
+ * when no hole fits, live ranges are compacted (device copies on the stream
+ * given to sb_kv_set_stream).  The counter alone decides admission.
+ *
+ * Arena layouts (caller-allocated device memory, dtype of the model):
+ *   K: [n_layers][n_kv_heads][arena_slots][head_dim]
+ *   V: [n_layers][n_kv_heads][arena_slots / 8][head_dim][8]  (8-slot blocks,
+ *      dim-major inside a block, so 8 consecutive slots of one dim are 16
+ *      contiguous bytes in bf16)                                              */
+typedef struct sb_kv sb_kv;
+
+/* Physical slots the arenas need for n_slots reservable slots and at most
+ * max_live simultaneously live requests (8-slot alignment of every range). */
+int64_t sb_kv_arena_slots(int64_t n_slots, int32_t max_live);
+/* Bytes of EACH of the K and V arenas. */
+size_t sb_kv_arena_bytes(int64_t arena_slots, int32_t n_layers, int32_t n_kv_heads, int32_t head_dim,
+                         int32_t dtype);
+/* k_arena / v_arena may both be NULL: bookkeeping only (no device copies). */
+int sb_kv_create(int64_t n_slots, int64_t arena_slots, int32_t n_layers, int32_t n_kv_heads,
+                 int32_t head_dim, int32_t dtype, void* k_arena, void* v_arena, sb_kv** out);
+int sb_kv_set_stream(sb_kv* kv, void* stream);
+/* Reserve max_tokens slots for req_id; *slot_base receives the first slot.
+ * SB_ERR_NO_SLOTS if the counter would exceed n_slots (nothing changes),
+ * SB_ERR_STATE if req_id already holds a reservation. */
+int sb_kv_reserve(sb_kv* kv, int64_t req_id, int32_t max_tokens, int64_t* slot_base);
+/* Release req_id's reservation.  SB_ERR_NOT_FOUND if it holds none. */
+int sb_kv_free(sb_kv* kv, int64_t req_id);
+int sb_kv_lookup(const sb_kv* kv, int64_t req_id, int64_t* slot_base, int32_t* max_tokens);
+int sb_kv_stats(const sb_kv* kv, int64_t* n_rsrv, int64_t* n_slots, int64_t* n_live, int64_t* n_compactions);
+/* Device pointers of layer `layer`'s K and V planes (for the kernels). */
+int sb_kv_layer_ptrs(const sb_kv* kv, int32_t layer, void** k, void** v);
+/* Scatter n rows of K and V ([n][n_kv_heads][head_dim], device, model dtype)
+ * of layer `layer` to the slots slots[0..n) (device int32). */
+int sb_kv_write(const sb_kv* kv, int32_t layer, int32_t n, const int32_t* slots, const void* k,
+                const void* v, void* stream);
+/* Gather the rows of slots[0..n) back into [n][n_kv_heads][head_dim] (device). */
+int sb_kv_read(const sb_kv* kv, int32_t layer, int32_t n, const int32_t* slots, void* k, void* v,
+               void* stream);
+void sb_kv_destroy(sb_kv* kv);
+
+/* ------------------------------------------------------------------ scheduler
+ * Iteration-level FCFS of [W] Algorithm 1 (Select) with one worker, as in
+ * [L2] 4.3 and [OB] select_batch.  Requests enter INITIATION; Select scans
+ * the pool in arrival order (ties: submission order), stops at max_bs, and
+ * stops (never skips) at the first INITIATION request whose reservation
+ * fails.  After the iteration every batch member becomes INCREMENT; a member
+ * that has generated out_len tokens is finished and its slots are freed.   */
+typedef struct sb_sched sb_sched;
+
+int sb_sched_create(int32_t max_bs, sb_kv* kv, sb_sched** out);       /* SB_ERR_INVALID if max_bs <= 0 */
+/* Submit a request.  prompt_tokens: host [prompt_len] (may be NULL: zeros).
+ * SB_ERR_TOO_LARGE if max_tokens > n_slots; SB_ERR_INVALID if
+ * prompt_len + out_len - 1 > max_tokens or a length is < 1; SB_ERR_STATE on a duplicate id. */
+int sb_sched_add(sb_sched* s, int64_t req_id, double arrival, int32_t prompt_len,
+                 const int32_t* prompt_tokens, int32_t out_len, int32_t max_tokens);
+/* Submit a request that already generated `generated` (>= 1) tokens, the last
+ * being last_token, whose K/V history (prompt_len + generated - 1 slots) the
+ * caller fills.  It reserves its slots now (SB_ERR_NO_SLOTS if they do not fit). */
+int sb_sched_add_running(sb_sched* s, int64_t req_id, double arrival, int32_t prompt_len,
+                         const int32_t* prompt_tokens, int32_t out_len, int32_t max_tokens,
+                         int32_t generated, int32_t last_token);
+/* Select the next batch (host arrays of capacity cap).  For member i:
+ * n_new[i] = tokens fed this iteration (prompt_len, or 1), ctx[i] = tokens
+ * already cached, slot_base[i] = first slot of its reservation.
+ * *n_out == 0 is legal (empty pool). */
+int sb_select_batch(sb_sched* s, int32_t cap, int64_t* ids, int32_t* n_new, int32_t* ctx,
+                    int64_t* slot_base, int32_t* n_out);
+/* Token ids fed this iteration by the n selected requests, flattened in batch
+ * order: the prompt of a first iteration, else the last generated token. */
+int sb_batch_tokens(const sb_sched* s, int32_t n, const int64_t* ids, int32_t cap, int32_t* tokens,
+                    int32_t* n_tokens);
+/* The iteration returned one token per member (new_tokens, host).  Finished
+ * requests are freed and their ids written to finished_ids (capacity n). */
+int sb_sched_complete(sb_sched* s, int32_t n, const int64_t* ids, const int32_t* new_tokens,
+                      int32_t* n_finished, int64_t* finished_ids);
+/* Generated tokens of a live or finished request (host, capacity cap). */
+int sb_sched_output(const sb_sched* s, int64_t req_id, int32_t cap, int32_t* tokens, int32_t* n);
+int sb_sched_stats(const sb_sched* s, int32_t* pool_size, int64_t* n_rsrv, int64_t* n_finished);
+void sb_sched_destroy(sb_sched* s);
+
+/* ------------------------------------------------------------------ ragged batch
+ * Split / Merge as offsets ([W] Figure 5, [L2] 4.2): request i owns rows
+ * cu_seqlens[i] .. cu_seqlens[i+1]-1 of every [T, *] activation; its j-th
+ * new token has position ctx_i + j and K/V slot slot_base_i + ctx_i + j.
+ * sb_ragged_build lays this metadata plus the attention work list out in
+ * host_staging, copies it to dev_meta (one async H2D on `stream`) and fills
+ * *out with device pointers into dev_meta.  host_staging must stay untouched
+ * until the copy is done (pinned memory recommended).                        */
+typedef struct {
+    int32_t n_req, n_tokens;       /* B and T = sum of n_new                         */
+    int32_t n_items, n_partials;   /* attention work items; split partial tiles      */
+    int32_t n_groups, max_new;     /* split-combine groups; max n_new in the batch   */
+    const int32_t* cu_seqlens;     /* device [B+1]                                   */
+    const int32_t* ctx_lens;       /* device [B]                                     */
+    const int32_t* last_row;       /* device [B]  cu_seqlens[i+1]-1                  */
+    const int32_t* tok_pos;        /* device [T]  position of each row               */
+    const int32_t* tok_slot;       /* device [T]  K/V slot of each row               */
+    const int32_t* tok_ids;        /* device [T]  token id of each row (or NULL)     */
+    const int32_t* items;          /* device [n_items][8] attention work list        */
+    const int32_t* groups;         /* device [n_groups][8] split-combine list        */
+} sb_ragged;
+
+size_t sb_ragged_bytes(const sb_model_dims* dims, int32_t max_req, int32_t max_tokens, int64_t max_keys_total);
+/* n_new, ctx: host [n_req]; slot_base: host [n_req]; token_ids: host [sum n_new] or NULL. */
+int sb_ragged_build(const sb_model_dims* dims, int32_t n_req, const int32_t* n_new, const int32_t* ctx,
+                    const int64_t* slot_base, const int32_t* token_ids, void* host_staging,
+                    void* dev_meta, size_t bytes, void* stream, sb_ragged* out);
+
+/* ------------------------------------------------------------------ device steps
+ * Residual stream x is fp32 [T, hidden] (device) for both dtypes; GEMM
+ * operands, K/V and weights are in the model dtype.                          */
+
+/* Workspace bytes of sb_layer_step / sb_lm_argmax for up to max_tokens rows,
+ * max_req requests and max_partials split-attention partial tiles. */
+size_t sb_layer_workspace_bytes(const sb_model_dims* dims, int32_t max_tokens, int32_t max_req,
+                                int32_t max_partials);
+
+/* Token embedding (+ learned position for GPT) of every row: x[t] = E[id_t] (+ P[pos_t]). */
+int sb_embed(const sb_model_dims* dims, const sb_model_weights* w, const sb_ragged* rg, float* x,
+             void* stream);
+
+/* One decoder layer over the ragged batch ([W] Figure 5 data flow), in place on x:
+ *   h = norm1(x); qkv = h W_qkv^T (+b); [RoPE q,k]; append k,v to the K/V
+ *   manager at tok_slot; o = per-request causal attention over each request's
+ *   slots [slot_base, slot_base + ctx + n_new); x += o W_o^T (+b);
+ *   h = norm2(x); x += FFN(h)  (GeLU or SwiGLU)                              */
+int sb_layer_step(const sb_model_dims* dims, const sb_layer_weights* w, const sb_ragged* rg,
+                  const sb_kv* kv, int32_t layer, float* x, void* workspace, size_t ws_bytes,
+                  void* stream);
+
+/* Final norm of each request's last row, LM head, greedy argmax (lowest index
+ * on ties).  logits: device fp32 [B, vocab] (may be NULL); out_ids: device int32 [B]. */
+int sb_lm_argmax(const sb_model_dims* dims, const sb_model_weights* w, const sb_ragged* rg,
+                 const float* x, float* logits, int32_t* out_ids, void* workspace, size_t ws_bytes,
+                 void* stream);
+
+/* ------------------------------------------------------------------ timing
+ * Per-kernel-class HIP event timing of launches made by the library (for
+ * benchmarks).  Enabling adds an event pair around every launch.            */
+enum { SB_K_GEMM_QKV = 0, SB_K_GEMM_O, SB_K_GEMM_FFN1, SB_K_GEMM_FFN2, SB_K_GEMM_LM, SB_K_ATTN,
+       SB_K_ATTN_COMBINE, SB_K_NORM, SB_K_ROPE_APPEND, SB_K_EMBED, SB_K_ARGMAX, SB_K_COUNT };
+int sb_timing_enable(int32_t on);
+/* Sum of elapsed ms and number of launches of class k since the last reset;
+ * synchronizes on the recorded events. */
+int sb_timing_read(int32_t k, double* total_ms, int64_t* count);
+int sb_timing_reset(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SB_H */

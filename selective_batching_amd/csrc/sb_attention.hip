@@ -1,0 +1,476 @@
+// Per-request attention over the ragged batch in ONE launch.
+//
+// Orca runs attention request by request -- each request's queries attend only
+// to that request's own K/V history -- and fuses the per-request attention
+// into a single kernel by concatenating the requests' thread blocks
+// ("CS349D Lecture 2", section 4.2; "连续批处理完全拆解", Figure 5).  Here the
+// host builds a work list; every workgroup takes one item (a request, a K/V
+// head, a tile of (token, query-head) rows and a key range), so prefills,
+// decodes and prefill chunks share the launch.  Split / Merge are offsets:
+// queries are read at their rows of the flattened qkv tensor and outputs are
+// written to the same rows of o.
+//
+// Math per row (token j of request i, query head h): causal softmax over the
+// request's keys 0..ctx_i + j of q.k / sqrt(d), times V.  Scores and the
+// running max / sum live in fp32 (log2 domain).
+//
+// Tiling (CDNA4, 64-wide waves): S^T = K Q^T and O^T = V^T P^T on 16x16
+// MFMA tiles, so that a query row lives in lane % 16 for both products and
+// the softmax rescale needs no cross-lane moves.  The 32-key chunk is
+// ordered so the S^T accumulators are directly the bf16 P^T operand.
+//   MODE_KEYS (<= 16 rows: decode, small chunks): the 4 waves take interleaved
+//     32-key chunks; K/V go straight from HBM into MFMA operand registers
+//     (16-byte loads); the 4 partial softmax states merge through LDS.
+//   MODE_ROWS (prefill tiles of 64 rows): each wave owns 16 rows; the
+//     workgroup stages 64-key K/V tiles through LDS (double-buffered) so the
+//     4 waves share every K/V byte.
+// Long single-tile items are split into fixed 512-key ranges; their partial
+// states are merged by attn_combine in a fixed order (deterministic and
+// independent of the rest of the batch).
+#include <cfloat>
+
+#include "sb_device.h"
+
+namespace sb {
+namespace {
+
+constexpr float kNegInf = -INFINITY;
+
+struct AttnArgs {
+    const void* qkv;
+    long long qkv_stride;     // elements per row of qkv
+    void* out;                // o [T, nq*d]
+    long long out_stride;
+    const void* K;            // layer plane base of K: [nkv][arena][d]
+    const void* V;            // layer plane base of V: [nkv][arena/8][d][8]
+    long long arena;
+    const int* cu;
+    const int* ctx;
+    const int* tok_slot;
+    const int* items;
+    float* part_o;            // [n_part][16][d]
+    float* part_ml;           // [n_part][16][2]
+    int nq, nkv, G;
+    float scale_log2;         // log2(e) / sqrt(d)
+};
+
+__device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
+
+// One wave's online-softmax state for its 16 rows (row = lane % 16).
+template <int D>
+struct WaveState {
+    f32x4 o[D / 16];          // O^T accumulators: dims 16*db + 4*(lane/16) + r
+    float m;                  // running max (log2 units), same in the 4 lanes of a row
+    float l;                  // this lane's share of the running sum
+};
+
+template <int D>
+__device__ __forceinline__ void state_init(WaveState<D>& s) {
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i) s.o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    s.m = kNegInf;
+    s.l = 0.f;
+}
+
+// Apply one chunk's scores p_raw (8 values of this lane: keys of the chunk for
+// row lane%16, already masked to -inf) to the state: returns the probabilities
+// (to feed the P.V product) and rescales the accumulators.
+__device__ __forceinline__ void softmax_chunk(float (&sc)[8], float& m, float& l, float& alpha) {
+    float mx = sc[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sc[i]);
+    mx = fmaxf(mx, shfl_xor(mx, 16));
+    mx = fmaxf(mx, shfl_xor(mx, 32));
+    const float mn = fmaxf(m, mx);
+    if (mn == kNegInf) {                 // nothing visible yet for this row
+        alpha = 1.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) sc[i] = 0.f;
+        return;
+    }
+    alpha = exp2f(m - mn);               // m == -inf -> 0
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        sc[i] = exp2f(sc[i] - mn);       // -inf -> 0
+        sum += sc[i];
+    }
+    l = l * alpha + sum;
+    m = mn;
+}
+
+// ------------------------------------------------------------------ bf16 chunk
+// Keys of a 32-key chunk starting at key cb: S^T block b covers local keys
+// 8*(m/4) + 4*b + (m%4) for MFMA row m, so that lane (g = lane/16) ends up
+// with keys 8g..8g+7 -- exactly the P^T operand layout of the 16x16x32 MFMA.
+template <int D, bool FROM_LDS>
+__device__ __forceinline__ void chunk_bf16(const AttnArgs& a, WaveState<D>& st, const bf16x8 (&qf)[D / 32],
+                                           const uint16_t* Kp, const uint16_t* Vp, long long kslot0,
+                                           int cb, int key_end, int row_limit, int lane,
+                                           const uint16_t* ldsK, const uint16_t* ldsV, int lds_key0) {
+    const int lr = lane & 15, g = lane >> 4;
+    float sc[8];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        const int kl = 8 * (lr >> 2) + 4 * b + (lr & 3);          // local key of MFMA row lr
+        const int key = cb + kl;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < D / 32; ++s) {
+            u32x4 kraw;
+            if (FROM_LDS) {
+                kraw = *(const u32x4*)(ldsK + (lds_key0 + kl) * (D + 8) + s * 32 + g * 8);
+            } else {
+                const int kk = min(key, key_end - 1);              // clamp: masked below
+                kraw = *(const u32x4*)(Kp + (kslot0 + kk) * D + s * 32 + g * 8);
+            }
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kraw), qf[s], acc, 0, 0, 0);
+        }
+        // acc[r]: key cb + 8g + 4b + r, row lr
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int k = cb + 8 * g + 4 * b + r;
+            sc[4 * b + r] = (k < key_end && k < row_limit) ? acc[r] * a.scale_log2 : kNegInf;
+        }
+    }
+    float alpha;
+    softmax_chunk(sc, st.m, st.l, alpha);
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i) st.o[i] *= alpha;
+    // P^T operand: keys 8g..8g+7 of the chunk for row lr
+    union { bf16x8 v; uint16_t h[8]; } pp;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) pp.h[i] = f2bf(sc[i]);
+    // V^T operand: V[keys cb+8g .. +8][dim 16db + lr] = 16 contiguous bytes of the blocked layout
+    const int k8 = cb + 8 * g;
+    const bool any = k8 < key_end;
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) {
+        u32x4 vraw;
+        if (FROM_LDS) {
+            vraw = *(const u32x4*)(ldsV + ((lds_key0 + 8 * g) / 8) * (D * 8 + 16) + (db * 16 + lr) * 8);
+        } else {
+            const long long blk = (kslot0 + min(k8, key_end - 1)) >> 3;
+            vraw = *(const u32x4*)(Vp + (blk * D + db * 16 + lr) * 8);
+        }
+        if (k8 + 8 > key_end) {
+            // zero the keys past the range (their memory may hold anything)
+            union { u32x4 v; uint16_t h[8]; } vv;
+            vv.v = vraw;
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                if (!any || k8 + i >= key_end) vv.h[i] = 0;
+            vraw = vv.v;
+        }
+        st.o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vraw), pp.v, st.o[db], 0, 0, 0);
+    }
+}
+
+// ------------------------------------------------------------------ fp32 chunk
+// 16x16x4 fp32 MFMA: S^T block b covers keys cb + 16b + (lane%16) as MFMA rows;
+// lane (g, r) gets keys cb + 16b + 4g + i.  P.V runs one 4-key step per (b, i).
+template <int D>
+__device__ __forceinline__ void chunk_f32(const AttnArgs& a, WaveState<D>& st, const float (&qf)[D / 4],
+                                          const float* Kp, const float* Vp, long long kslot0, int cb,
+                                          int key_end, int row_limit, int lane) {
+    const int lr = lane & 15, g = lane >> 4;
+    float sc[8];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        const int key = cb + 16 * b + lr;
+        const int kk = min(key, key_end - 1);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < D / 4; ++s)
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(Kp[(kslot0 + kk) * D + 4 * s + g], qf[s], acc, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int k = cb + 16 * b + 4 * g + r;
+            sc[4 * b + r] = (k < key_end && k < row_limit) ? acc[r] * a.scale_log2 : kNegInf;
+        }
+    }
+    float alpha;
+    softmax_chunk(sc, st.m, st.l, alpha);
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i) st.o[i] *= alpha;
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int key = cb + 16 * b + 4 * g + r;
+            const bool ok = key < key_end;
+            const long long slot = kslot0 + min(key, key_end - 1);
+#pragma unroll
+            for (int db = 0; db < D / 16; ++db) {
+                float v = Vp[((slot >> 3) * D + db * 16 + lr) * 8 + (slot & 7)];
+                v = ok ? v : 0.f;
+                st.o[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(v, sc[4 * b + r], st.o[db], 0, 0, 0);
+            }
+        }
+}
+
+template <int DT, int D>
+__global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
+    using T = typename Store<DT>::T;
+    constexpr int KT = 64;                                   // keys per LDS stage (MODE_ROWS)
+    // MODE_ROWS stages K/V tiles; MODE_KEYS merges wave states: one workgroup
+    // uses only one of the two, so they share the LDS allocation.
+    constexpr int LDS_K = (DT == SB_BF16) ? 2 * KT * (D + 8) : 0;
+    constexpr int LDS_V = (DT == SB_BF16) ? 2 * (KT / 8) * (D * 8 + 16) : 0;
+    constexpr int BYTES_ROWS = (LDS_K + LDS_V) * 2;
+    constexpr int BYTES_RED = (kWaves * 16 * (D + 1) + 2 * kWaves * 16) * 4;
+    __shared__ __attribute__((aligned(16))) char smem[BYTES_ROWS > BYTES_RED ? BYTES_ROWS : BYTES_RED];
+    uint16_t* ldsK = (uint16_t*)smem;
+    uint16_t* ldsV = ldsK + LDS_K;
+    float (*red_o)[16][D + 1] = (float (*)[16][D + 1])smem;
+    float (*red_m)[16] = (float (*)[16])(smem + kWaves * 16 * (D + 1) * 4);
+    float (*red_l)[16] = (float (*)[16])(smem + (kWaves * 16 * (D + 1) + kWaves * 16) * 4);
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int lr = lane & 15, g = lane >> 4;
+    const int* it = a.items + (long long)blockIdx.x * kItemInts;
+    const int req = it[ITEM_REQ], kvh = it[ITEM_KVH], mode = it[ITEM_MODE];
+    const int row0 = it[ITEM_ROW0], nrows = it[ITEM_NROWS];
+    const int kb = it[ITEM_KB], ke = it[ITEM_KE], part = it[ITEM_PART];
+    const int tok0 = a.cu[req], ctx = a.ctx[req];
+    const long long kslot0 = (long long)a.tok_slot[tok0] - ctx;   // slot of key 0 of this request
+    const T* Kp = (const T*)a.K + (long long)kvh * a.arena * D;
+    const T* Vp = (const T*)a.V + (long long)kvh * a.arena * D;
+
+    // rows of this wave: (token, head-in-group), token-major
+    const int wrow0 = row0 + (mode == MODE_ROWS ? wave * 16 : 0);
+    const int row = wrow0 + lr;
+    const bool row_ok = row < row0 + nrows;
+    const int tok = row_ok ? row / a.G : 0;
+    const int head = kvh * a.G + (row_ok ? row % a.G : 0);
+    const int row_limit = row_ok ? ctx + tok + 1 : 0;             // keys 0..ctx+tok are visible
+    const T* qrow = (const T*)a.qkv + (long long)(tok0 + tok) * a.qkv_stride + (long long)head * D;
+
+    WaveState<D> st;
+    state_init(st);
+
+    if constexpr (DT == SB_BF16) {
+        bf16x8 qf[D / 32];
+#pragma unroll
+        for (int s = 0; s < D / 32; ++s) {
+            u32x4 v = row_ok ? *(const u32x4*)(qrow + s * 32 + g * 8) : u32x4{0u, 0u, 0u, 0u};
+            qf[s] = __builtin_bit_cast(bf16x8, v);
+        }
+        if (mode == MODE_KEYS) {
+            for (int cb = kb + 32 * wave; cb < ke; cb += 32 * kWaves)
+                chunk_bf16<D, false>(a, st, qf, Kp, Vp, kslot0, cb, ke, row_limit, lane, nullptr, nullptr, 0);
+        } else {
+            // stage 64-key tiles of K (row-major, padded rows) and V (8-key blocks, padded) in LDS
+            const int wave_max_limit = min(ke, ctx + min(wrow0 + 15, row0 + nrows - 1) / a.G + 1);
+            const int ntiles = (ke - kb + KT - 1) / KT;
+            constexpr int KCH = KT * D / 8;                    // 16-byte chunks per K tile
+            constexpr int PER = (KCH + 255) / 256;
+            u32x4 rk[PER], rv[PER];
+            auto gload = [&](int t) {
+                const int k0 = kb + t * KT;
+#pragma unroll
+                for (int q = 0; q < PER; ++q) {
+                    const int c = tid + 256 * q;
+                    if (c < KCH) {
+                        const int kk = c / (D / 8), dc = (c % (D / 8)) * 8;
+                        const long long slot = kslot0 + min(k0 + kk, ke - 1);
+                        rk[q] = *(const u32x4*)((const uint16_t*)Kp + slot * D + dc);
+                        // V: chunk c covers blocks (c / D) of 8 keys, dim c % D
+                        const int vb = c / D, vd = c % D;
+                        const long long vslot = kslot0 + min(k0 + vb * 8, ((ke - 1) & ~7));
+                        rv[q] = *(const u32x4*)((const uint16_t*)Vp + ((vslot >> 3) * D + vd) * 8);
+                    }
+                }
+            };
+            auto lstore = [&](int buf) {
+#pragma unroll
+                for (int q = 0; q < PER; ++q) {
+                    const int c = tid + 256 * q;
+                    if (c < KCH) {
+                        const int kk = c / (D / 8), dc = (c % (D / 8)) * 8;
+                        *(u32x4*)(ldsK + buf * KT * (D + 8) + kk * (D + 8) + dc) = rk[q];
+                        const int vb = c / D, vd = c % D;
+                        *(u32x4*)(ldsV + buf * (KT / 8) * (D * 8 + 16) + vb * (D * 8 + 16) + vd * 8) = rv[q];
+                    }
+                }
+            };
+            gload(0);
+            lstore(0);
+            __syncthreads();
+            for (int t = 0; t < ntiles; ++t) {
+                const int buf = t & 1;
+                if (t + 1 < ntiles) gload(t + 1);
+                const int k0 = kb + t * KT;
+                if (k0 < wave_max_limit) {
+                    for (int c2 = 0; c2 < KT / 32; ++c2) {
+                        const int cb = k0 + 32 * c2;
+                        if (cb < wave_max_limit)
+                            chunk_bf16<D, true>(a, st, qf, Kp, Vp, kslot0, cb, ke, row_limit, lane,
+                                                ldsK + buf * KT * (D + 8), ldsV + buf * (KT / 8) * (D * 8 + 16), 32 * c2);
+                    }
+                }
+                if (t + 1 < ntiles) lstore(buf ^ 1);
+                __syncthreads();
+            }
+        }
+    } else {
+        float qf[D / 4];
+#pragma unroll
+        for (int s = 0; s < D / 4; ++s) qf[s] = row_ok ? ((const float*)qrow)[4 * s + g] : 0.f;
+        const int step = (mode == MODE_KEYS) ? 32 * kWaves : 32;
+        const int first = (mode == MODE_KEYS) ? kb + 32 * wave : kb;
+        for (int cb = first; cb < ke; cb += step)
+            chunk_f32<D>(a, st, qf, (const float*)Kp, (const float*)Vp, kslot0, cb, ke, row_limit, lane);
+    }
+
+    // total row sum over the 4 lanes of the row
+    float l = st.l;
+    l += shfl_xor(l, 16);
+    l += shfl_xor(l, 32);
+
+    if (mode == MODE_ROWS) {
+        if (!row_ok) return;
+        const float inv = 1.f / l;
+        T* orow = (T*)a.out + (long long)(tok0 + tok) * a.out_stride + (long long)head * D;
+#pragma unroll
+        for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Store<DT>::st(orow + db * 16 + 4 * g + r, st.o[db][r] * inv);
+        return;
+    }
+
+    // MODE_KEYS: merge the 4 waves' states (fixed order) through LDS
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) red_o[wave][lr][db * 16 + 4 * g + r] = st.o[db][r];
+    if (g == 0) {
+        red_m[wave][lr] = st.m;
+        red_l[wave][lr] = l;
+    }
+    __syncthreads();
+    // thread -> (row, dim range): 16 rows x D dims over 256 threads
+    constexpr int DPT = D * 16 / 256;                          // dims per thread
+    const int r = tid / (256 / 16);
+    const int d0 = (tid % (256 / 16)) * DPT;
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, red_m[w][r]);
+    float wts[kWaves], L = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        wts[w] = (red_m[w][r] == kNegInf) ? 0.f : exp2f(red_m[w][r] - M);
+        L += red_l[w][r] * wts[w];
+    }
+    const int rr = row0 + r;
+    if (rr >= row0 + nrows) return;
+    if (part < 0) {
+        const int tk = rr / a.G, hd = kvh * a.G + rr % a.G;
+        T* orow = (T*)a.out + (long long)(tok0 + tk) * a.out_stride + (long long)hd * D;
+        const float inv = 1.f / L;
+#pragma unroll
+        for (int e = 0; e < DPT; ++e) {
+            float o = 0.f;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) o += red_o[w][r][d0 + e] * wts[w];
+            Store<DT>::st(orow + d0 + e, o * inv);
+        }
+    } else {
+        float* po = a.part_o + ((long long)part * 16 + r) * D;
+#pragma unroll
+        for (int e = 0; e < DPT; ++e) {
+            float o = 0.f;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) o += red_o[w][r][d0 + e] * wts[w];
+            po[d0 + e] = o;
+        }
+        if (d0 == 0) {
+            a.part_ml[((long long)part * 16 + r) * 2 + 0] = M;
+            a.part_ml[((long long)part * 16 + r) * 2 + 1] = L;
+        }
+    }
+}
+
+// Merge the fixed-length key splits of one (request, K/V head) tile, in split order.
+template <int DT, int D>
+__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, const int* groups) {
+    using T = typename Store<DT>::T;
+    const int* gp = groups + (long long)blockIdx.x * kGroupInts;
+    const int req = gp[GRP_REQ], kvh = gp[GRP_KVH], row0 = gp[GRP_ROW0], nrows = gp[GRP_NROWS];
+    const int p0 = gp[GRP_PART0], np = gp[GRP_NPARTS];
+    const int tok0 = a.cu[req];
+    for (int idx = threadIdx.x; idx < 16 * D; idx += 256) {
+        const int r = idx / D, e = idx % D;
+        if (r >= nrows) break;
+        float M = kNegInf;
+        for (int p = 0; p < np; ++p) M = fmaxf(M, a.part_ml[((long long)(p0 + p) * 16 + r) * 2]);
+        float L = 0.f, o = 0.f;
+        for (int p = 0; p < np; ++p) {
+            const float mp = a.part_ml[((long long)(p0 + p) * 16 + r) * 2];
+            if (mp == kNegInf) continue;
+            const float w = exp2f(mp - M);
+            L += a.part_ml[((long long)(p0 + p) * 16 + r) * 2 + 1] * w;
+            o += a.part_o[((long long)(p0 + p) * 16 + r) * D + e] * w;
+        }
+        const int rr = row0 + r, tk = rr / a.G, hd = kvh * a.G + rr % a.G;
+        Store<DT>::st((T*)a.out + (long long)(tok0 + tk) * a.out_stride + (long long)hd * D + e, o / L);
+    }
+}
+
+template <int DT, int D>
+int launch_attn_d(const AttnArgs& a, int n_items, int n_groups, const int* groups, hipStream_t s) {
+    if (n_items > 0) {
+        TimedScope ts(SB_K_ATTN, s);
+        hipLaunchKernelGGL((attn_kernel<DT, D>), dim3(n_items), dim3(256), 0, s, a);
+        int st = check_launch("attention");
+        if (st) return st;
+    }
+    if (n_groups > 0) {
+        TimedScope ts(SB_K_ATTN_COMBINE, s);
+        hipLaunchKernelGGL((attn_combine_kernel<DT, D>), dim3(n_groups), dim3(256), 0, s, a, groups);
+        return check_launch("attention combine");
+    }
+    return SB_OK;
+}
+
+}  // namespace
+
+int launch_attention(const sb_model_dims* dims, const sb_ragged* rg, const void* kplane, const void* vplane,
+                     long long arena, const void* qkv, void* out, float* part_o, float* part_ml, hipStream_t s) {
+    AttnArgs a{};
+    const int D = dims->head_dim;
+    a.qkv = qkv;
+    a.qkv_stride = (long long)(dims->n_heads + 2 * dims->n_kv_heads) * D;
+    a.out = out;
+    a.out_stride = (long long)dims->n_heads * D;
+    a.K = kplane;
+    a.V = vplane;
+    a.arena = arena;
+    a.cu = rg->cu_seqlens;
+    a.ctx = rg->ctx_lens;
+    a.tok_slot = rg->tok_slot;
+    a.items = rg->items;
+    a.part_o = part_o;
+    a.part_ml = part_ml;
+    a.nq = dims->n_heads;
+    a.nkv = dims->n_kv_heads;
+    a.G = dims->n_heads / dims->n_kv_heads;
+    a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
+    if (dims->dtype == SB_BF16) {
+        switch (D) {
+            case 32: return launch_attn_d<SB_BF16, 32>(a, rg->n_items, rg->n_groups, rg->groups, s);
+            case 64: return launch_attn_d<SB_BF16, 64>(a, rg->n_items, rg->n_groups, rg->groups, s);
+            case 128: return launch_attn_d<SB_BF16, 128>(a, rg->n_items, rg->n_groups, rg->groups, s);
+        }
+    } else {
+        switch (D) {
+            case 16: return launch_attn_d<SB_F32, 16>(a, rg->n_items, rg->n_groups, rg->groups, s);
+            case 32: return launch_attn_d<SB_F32, 32>(a, rg->n_items, rg->n_groups, rg->groups, s);
+            case 64: return launch_attn_d<SB_F32, 64>(a, rg->n_items, rg->n_groups, rg->groups, s);
+            case 128: return launch_attn_d<SB_F32, 128>(a, rg->n_items, rg->n_groups, rg->groups, s);
+        }
+    }
+    return fail(SB_ERR_INVALID, "attention: unsupported head_dim %d", D);
+}
+
+}  // namespace sb

@@ -1,0 +1,52 @@
+// Internal declarations shared by the host and device halves of libsb.
+#pragma once
+#include <hip/hip_runtime_api.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <map>
+#include <string>
+#include <unordered_map>
+#include <vector>
+
+#include "sb.h"
+
+namespace sb {
+
+int fail(int status, const char* fmt, ...);   // records sb_last_error, returns status
+
+inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+
+inline size_t dtype_size(int dt) { return dt == SB_BF16 ? 2 : 4; }
+
+// Attention work decomposition (shared by the work-list builder and the kernel).
+constexpr int kRowsPerWave = 16;          // one 16x16 MFMA tile of (token, head) rows
+constexpr int kWaves = 4;                 // waves per attention workgroup
+constexpr int kRowsPerTile = kRowsPerWave * kWaves;
+constexpr int kSplitKeys = 512;           // fixed key-split length of single-tile items
+constexpr int kItemInts = 8;
+constexpr int kGroupInts = 8;
+enum { ITEM_REQ = 0, ITEM_KVH, ITEM_MODE, ITEM_ROW0, ITEM_NROWS, ITEM_KB, ITEM_KE, ITEM_PART };
+enum { MODE_ROWS = 0, MODE_KEYS = 1 };
+enum { GRP_REQ = 0, GRP_KVH, GRP_ROW0, GRP_NROWS, GRP_PART0, GRP_NPARTS };
+
+int validate_dims(const sb_model_dims* d);
+
+}  // namespace sb
+
+struct sb_kv {
+    struct Res {
+        int64_t base;
+        int64_t len;       // physical slots (max_tokens rounded up to 8)
+        int32_t max_tokens;
+    };
+    int64_t n_slots = 0, arena_slots = 0;
+    int32_t n_layers = 0, nkv = 0, d = 0, dtype = 0;
+    void* k = nullptr;
+    void* v = nullptr;
+    hipStream_t stream = nullptr;
+    int64_t n_rsrv = 0;
+    int64_t n_compactions = 0;
+    std::unordered_map<int64_t, Res> live;
+    std::map<int64_t, int64_t> by_base;    // base slot -> request id
+};

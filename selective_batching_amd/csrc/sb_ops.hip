@@ -1,0 +1,564 @@
+// Token-wise elementwise kernels and the device entry points of libsb:
+// embedding, LayerNorm / RMSNorm, RoPE + K/V append, greedy argmax, and the
+// sb_embed / sb_layer_step / sb_lm_argmax orchestration of one selective-
+// batched iteration ("连续批处理完全拆解", Figure 5 data flow; "CS349D Lecture
+// 2", section 4.2).  All of them are HBM-bound: one row per workgroup,
+// 16-byte accesses along the row where the layout allows.
+#include <cmath>
+#include <mutex>
+
+#include "sb_device.h"
+#include "sb_ops.h"
+
+namespace sb {
+
+int launch_attention(const sb_model_dims* dims, const sb_ragged* rg, const void* kplane, const void* vplane,
+                     long long arena, const void* qkv, void* out, float* part_o, float* part_ml, hipStream_t s);
+
+int check_launch(const char* what) {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(SB_ERR_DEVICE, "%s launch: %s", what, hipGetErrorString(e));
+    return SB_OK;
+}
+
+// ------------------------------------------------------------------ timing
+namespace {
+struct TimingState {
+    std::mutex mu;
+    bool on = false;
+    std::vector<std::pair<hipEvent_t, hipEvent_t>> ev[SB_K_COUNT];
+    std::vector<hipEvent_t> open[SB_K_COUNT];
+};
+TimingState& timing() {
+    static TimingState t;
+    return t;
+}
+}  // namespace
+
+void timing_begin(int kind, hipStream_t s) {
+    auto& T = timing();
+    if (!T.on) return;
+    std::lock_guard<std::mutex> g(T.mu);
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return;
+    hipEventRecord(e, s);
+    T.open[kind].push_back(e);
+}
+
+void timing_end(int kind, hipStream_t s) {
+    auto& T = timing();
+    if (!T.on) return;
+    std::lock_guard<std::mutex> g(T.mu);
+    if (T.open[kind].empty()) return;
+    hipEvent_t b = T.open[kind].back();
+    T.open[kind].pop_back();
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return;
+    hipEventRecord(e, s);
+    T.ev[kind].push_back({b, e});
+}
+
+// ------------------------------------------------------------------ kernels
+namespace {
+
+__device__ __forceinline__ float block_sum(float v, float* red) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    const int w = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[w] = v;
+    __syncthreads();
+    float t = 0.f;
+    for (int i = 0; i < (int)(blockDim.x >> 6); ++i) t += red[i];
+    return t;
+}
+
+// x[t] = E[id_t] (+ P[pos_t]) in fp32
+template <int DT>
+__global__ __launch_bounds__(256) void embed_kernel(const int* ids, const int* pos, const void* tok, const void* pe,
+                                                    float* x, int H) {
+    using T = typename Store<DT>::T;
+    const int t = blockIdx.x;
+    const T* e = (const T*)tok + (long long)ids[t] * H;
+    const T* p = pe ? (const T*)pe + (long long)pos[t] * H : nullptr;
+    float* xo = x + (long long)t * H;
+    for (int i = threadIdx.x; i < H; i += blockDim.x) {
+        float v = Store<DT>::ld(e + i);
+        if (p) v += Store<DT>::ld(p + i);
+        xo[i] = v;
+    }
+}
+
+// LayerNorm (kind 0) or RMSNorm (kind 1) of fp32 rows into dtype rows; fp32
+// statistics, two passes over registers (mean, then centred second moment).
+constexpr int kNormMaxPerThread = 12;   // float4 chunks per thread: hidden <= 12288
+template <int DT>
+__global__ __launch_bounds__(256) void norm_kernel(const float* x, const int* row_map, const void* gam, const void* bet,
+                                                   void* out, int H, int kind, float eps) {
+    using T = typename Store<DT>::T;
+    __shared__ float red[4];
+    const int r = blockIdx.x;
+    const long long src = row_map ? row_map[r] : r;
+    const float4* xr = (const float4*)(x + src * H);
+    const int n4 = H / 4;
+    float4 v[kNormMaxPerThread];
+    float s = 0.f;
+#pragma unroll
+    for (int q = 0; q < kNormMaxPerThread; ++q) {
+        const int i = threadIdx.x + 256 * q;
+        if (i < n4) {
+            v[q] = xr[i];
+            s += (v[q].x + v[q].y) + (v[q].z + v[q].w);
+        }
+    }
+    float mean = 0.f;
+    if (kind == 0) mean = block_sum(s, red) / H;
+    float s2 = 0.f;
+#pragma unroll
+    for (int q = 0; q < kNormMaxPerThread; ++q) {
+        const int i = threadIdx.x + 256 * q;
+        if (i < n4) {
+            const float a = v[q].x - mean, b = v[q].y - mean, c = v[q].z - mean, d = v[q].w - mean;
+            s2 += (a * a + b * b) + (c * c + d * d);
+        }
+    }
+    const float rstd = 1.0f / sqrtf(block_sum(s2, red) / H + eps);
+    const T* g = (const T*)gam;
+    const T* b = (const T*)bet;
+    T* o = (T*)out + (long long)r * H;
+#pragma unroll
+    for (int q = 0; q < kNormMaxPerThread; ++q) {
+        const int i = threadIdx.x + 256 * q;
+        if (i < n4) {
+            const float xs[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int e = 4 * i + c;
+                float y = (xs[c] - mean) * rstd * Store<DT>::ld(g + e);
+                if (b) y += Store<DT>::ld(b + e);
+                Store<DT>::st(o + e, y);
+            }
+        }
+    }
+}
+
+// Per token: rotate q (in place in qkv) and k by the token's position
+// (Llama-style, rotate-half pairs (i, i + d/2), angle pos * theta^(-2i/d),
+// evaluated in double precision), then append k and v to the K/V manager's
+// arenas at the token's slot.
+template <int DT>
+__global__ __launch_bounds__(128) void rope_append_kernel(void* qkv, long long stride, const int* pos, const int* slot,
+                                                          void* kplane, void* vplane, long long arena, int nq, int nkv,
+                                                          int D, int rope, double log_theta) {
+    using T = typename Store<DT>::T;
+    const int t = blockIdx.x;
+    T* row = (T*)qkv + (long long)t * stride;
+    const long long s = slot[t];
+    const int half = D / 2;
+    if (rope) {
+        for (int i = threadIdx.x; i < half; i += blockDim.x) {
+            const double inv = exp(-(2.0 * i / D) * log_theta);
+            double sn, cs;
+            sincos((double)pos[t] * inv, &sn, &cs);
+            const float c = (float)cs, sv = (float)sn;
+            for (int h = 0; h < nq + nkv; ++h) {
+                T* p = row + (long long)h * D;
+                const float x1 = Store<DT>::ld(p + i), x2 = Store<DT>::ld(p + i + half);
+                Store<DT>::st(p + i, x1 * c - x2 * sv);
+                Store<DT>::st(p + i + half, x2 * c + x1 * sv);
+            }
+        }
+        __syncthreads();
+    }
+    const T* krow = row + (long long)nq * D;
+    const T* vrow = krow + (long long)nkv * D;
+    T* K = (T*)kplane;
+    T* V = (T*)vplane;
+    for (int idx = threadIdx.x; idx < nkv * D; idx += blockDim.x) {
+        const int g = idx / D, e = idx % D;
+        K[((long long)g * arena + s) * D + e] = krow[idx];
+        V[(long long)g * arena * D + (((s >> 3) * D + e) << 3) + (s & 7)] = vrow[idx];
+    }
+}
+
+// Scatter / gather of whole K/V rows [n][nkv][d] at explicit slots.
+template <int DT>
+__global__ __launch_bounds__(256) void kv_copy_kernel(const int* slots, void* kplane, void* vplane, long long arena,
+                                                      int nkv, int D, void* k, void* v, int write) {
+    using T = typename Store<DT>::T;
+    const int t = blockIdx.x;
+    const long long s = slots[t];
+    T* K = (T*)kplane;
+    T* V = (T*)vplane;
+    T* kr = (T*)k + (long long)t * nkv * D;
+    T* vr = (T*)v + (long long)t * nkv * D;
+    for (int idx = threadIdx.x; idx < nkv * D; idx += blockDim.x) {
+        const int g = idx / D, e = idx % D;
+        T* kp = K + ((long long)g * arena + s) * D + e;
+        T* vp = V + (long long)g * arena * D + (((s >> 3) * D + e) << 3) + (s & 7);
+        if (write) {
+            *kp = kr[idx];
+            *vp = vr[idx];
+        } else {
+            kr[idx] = *kp;
+            vr[idx] = *vp;
+        }
+    }
+}
+
+// Greedy token: index of the largest logit, lowest index among equal maxima.
+__global__ __launch_bounds__(256) void argmax_kernel(const float* logits, int V, int* out) {
+    const int r = blockIdx.x;
+    const float* x = logits + (long long)r * V;
+    float bv = -INFINITY;
+    int bi = V;
+    for (int i = threadIdx.x; i < V; i += 256) {
+        const float v = x[i];
+        if (v > bv || (bi == V && v == bv)) {   // ascending scan: keep the first maximum
+            bv = v;
+            bi = i;
+        }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const float ov = __shfl_xor(bv, o, 64);
+        const int oi = __shfl_xor(bi, o, 64);
+        if (ov > bv || (ov == bv && oi < bi)) {
+            bv = ov;
+            bi = oi;
+        }
+    }
+    __shared__ float sv[4];
+    __shared__ int si[4];
+    if ((threadIdx.x & 63) == 0) {
+        sv[threadIdx.x >> 6] = bv;
+        si[threadIdx.x >> 6] = bi;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int w = 1; w < 4; ++w)
+            if (sv[w] > bv || (sv[w] == bv && si[w] < bi)) {
+                bv = sv[w];
+                bi = si[w];
+            }
+        out[r] = bi;
+    }
+}
+
+}  // namespace
+
+int launch_norm(int dtype, int kind, int rows, int H, const float* x, const int* row_map, const void* g,
+                const void* b, float eps, void* out, hipStream_t s) {
+    if (rows <= 0) return SB_OK;
+    if (H % 4 || H > 4 * 256 * kNormMaxPerThread) return fail(SB_ERR_INVALID, "norm: hidden must be a multiple of 4 and <= 12288");
+    TimedScope ts(SB_K_NORM, s);
+    if (dtype == SB_BF16)
+        hipLaunchKernelGGL(norm_kernel<SB_BF16>, dim3(rows), dim3(256), 0, s, x, row_map, g, b, out, H, kind, eps);
+    else
+        hipLaunchKernelGGL(norm_kernel<SB_F32>, dim3(rows), dim3(256), 0, s, x, row_map, g, b, out, H, kind, eps);
+    return check_launch("norm");
+}
+
+int launch_rope_append(const sb_model_dims* d, const sb_ragged* rg, void* qkv, void* kp, void* vp, long long arena,
+                       hipStream_t s) {
+    if (rg->n_tokens <= 0) return SB_OK;
+    TimedScope ts(SB_K_ROPE_APPEND, s);
+    const long long stride = (long long)(d->n_heads + 2 * d->n_kv_heads) * d->head_dim;
+    const int rope = d->arch == SB_ARCH_LLAMA;
+    const double lt = log((double)d->rope_theta);
+    if (d->dtype == SB_BF16)
+        hipLaunchKernelGGL(rope_append_kernel<SB_BF16>, dim3(rg->n_tokens), dim3(128), 0, s, qkv, stride, rg->tok_pos,
+                           rg->tok_slot, kp, vp, arena, d->n_heads, d->n_kv_heads, d->head_dim, rope, lt);
+    else
+        hipLaunchKernelGGL(rope_append_kernel<SB_F32>, dim3(rg->n_tokens), dim3(128), 0, s, qkv, stride, rg->tok_pos,
+                           rg->tok_slot, kp, vp, arena, d->n_heads, d->n_kv_heads, d->head_dim, rope, lt);
+    return check_launch("rope_append");
+}
+
+int launch_argmax(int rows, int V, const float* logits, int* out, hipStream_t s) {
+    if (rows <= 0) return SB_OK;
+    TimedScope ts(SB_K_ARGMAX, s);
+    hipLaunchKernelGGL(argmax_kernel, dim3(rows), dim3(256), 0, s, logits, V, out);
+    return check_launch("argmax");
+}
+
+// ------------------------------------------------------------------ workspace
+struct LayerWs {
+    char* h;
+    char* qkv;
+    char* o;
+    char* g;
+    float* part_o;
+    float* part_ml;
+    char* hl;
+    float* logits;
+    size_t total;
+};
+
+static size_t al(size_t v) { return (v + 255) & ~(size_t)255; }
+
+static LayerWs layer_ws(const sb_model_dims* d, char* base, int64_t T, int64_t B, int64_t P) {
+    const size_t es = dtype_size(d->dtype);
+    LayerWs w{};
+    size_t o = 0;
+    auto take = [&](size_t n) { char* p = base ? base + o : nullptr; o += al(n); return p; };
+    w.h = take((size_t)T * d->hidden * es);
+    w.qkv = take((size_t)T * (d->n_heads + 2 * d->n_kv_heads) * d->head_dim * es);
+    w.o = take((size_t)T * d->n_heads * d->head_dim * es);
+    w.g = take((size_t)T * d->ffn * es);
+    w.part_o = (float*)take((size_t)P * 16 * d->head_dim * 4);
+    w.part_ml = (float*)take((size_t)P * 16 * 2 * 4);
+    w.hl = take((size_t)B * d->hidden * es);
+    w.logits = (float*)take((size_t)B * (d->vocab > 0 ? d->vocab : 1) * 4);
+    w.total = o;
+    return w;
+}
+
+}  // namespace sb
+
+using namespace sb;
+
+extern "C" size_t sb_layer_workspace_bytes(const sb_model_dims* dims, int32_t max_tokens, int32_t max_req,
+                                           int32_t max_partials) {
+    if (validate_dims(dims) || max_tokens < 0 || max_req < 0 || max_partials < 0) return 0;
+    return layer_ws(dims, nullptr, max_tokens, max_req, max_partials).total;
+}
+
+static int check_ws(const sb_model_dims* d, const sb_ragged* rg, size_t ws_bytes) {
+    size_t need = layer_ws(d, nullptr, rg->n_tokens, rg->n_req, rg->n_partials).total;
+    if (need > ws_bytes) return fail(SB_ERR_WORKSPACE, "workspace needs %zu bytes, %zu given", need, ws_bytes);
+    return SB_OK;
+}
+
+extern "C" int sb_embed(const sb_model_dims* dims, const sb_model_weights* w, const sb_ragged* rg, float* x,
+                        void* stream) {
+    int st = validate_dims(dims);
+    if (st) return st;
+    if (!w || !rg || !x || !w->tok_emb || !rg->tok_ids) return fail(SB_ERR_INVALID, "sb_embed: NULL argument (token ids required)");
+    if (rg->n_tokens <= 0) return SB_OK;
+    const void* pe = dims->arch == SB_ARCH_GPT ? w->pos_emb : nullptr;
+    if (dims->arch == SB_ARCH_GPT && !pe) return fail(SB_ERR_INVALID, "sb_embed: GPT needs pos_emb");
+    hipStream_t s = (hipStream_t)stream;
+    TimedScope ts(SB_K_EMBED, s);
+    if (dims->dtype == SB_BF16)
+        hipLaunchKernelGGL(embed_kernel<SB_BF16>, dim3(rg->n_tokens), dim3(256), 0, s, rg->tok_ids, rg->tok_pos,
+                           w->tok_emb, pe, x, dims->hidden);
+    else
+        hipLaunchKernelGGL(embed_kernel<SB_F32>, dim3(rg->n_tokens), dim3(256), 0, s, rg->tok_ids, rg->tok_pos,
+                           w->tok_emb, pe, x, dims->hidden);
+    return check_launch("embed");
+}
+
+static int layer_gemm(const sb_model_dims* d, int epi, int kind, int M, int N, int K, const void* A, const void* W,
+                      const void* bias, void* C, long long ldc, int F, hipStream_t s) {
+    GemmArgs a{};
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.A = A;
+    a.lda = K;
+    a.W = W;
+    a.ldw = K;
+    a.bias = bias;
+    a.C = C;
+    a.ldc = ldc;
+    a.out_f32 = 0;
+    a.F = F;
+    TimedScope ts(kind, s);
+    return launch_gemm(d->dtype, epi, a, s);
+}
+
+extern "C" int sb_layer_step(const sb_model_dims* d, const sb_layer_weights* w, const sb_ragged* rg, const sb_kv* kv,
+                             int32_t layer, float* x, void* workspace, size_t ws_bytes, void* stream) {
+    int st = validate_dims(d);
+    if (st) return st;
+    if (!w || !rg || !kv || !x || !workspace) return fail(SB_ERR_INVALID, "sb_layer_step: NULL argument");
+    if (kv->d != d->head_dim || kv->nkv != d->n_kv_heads || kv->dtype != d->dtype)
+        return fail(SB_ERR_INVALID, "K/V manager shape does not match the model");
+    const bool gpt = d->arch == SB_ARCH_GPT;
+    if (!w->ln1_g || !w->w_qkv || !w->w_o || !w->ln2_g || !w->w1 || !w->w2) return fail(SB_ERR_INVALID, "missing layer weight");
+    if (gpt && (!w->ln1_b || !w->ln2_b)) return fail(SB_ERR_INVALID, "GPT layer needs LayerNorm shifts");
+    if ((st = check_ws(d, rg, ws_bytes))) return st;
+    if (rg->n_tokens <= 0) return SB_OK;
+    void *kp, *vp;
+    if ((st = sb_kv_layer_ptrs(kv, layer, &kp, &vp))) return st;
+    hipStream_t s = (hipStream_t)stream;
+    LayerWs ws = layer_ws(d, (char*)workspace, rg->n_tokens, rg->n_req, rg->n_partials);
+    const int T = rg->n_tokens, H = d->hidden, F = d->ffn;
+    const int qkv_n = (d->n_heads + 2 * d->n_kv_heads) * d->head_dim;
+    const int attn_n = d->n_heads * d->head_dim;
+    const int nk = gpt ? 0 : 1;
+    // a4: norm 1 -> a5: QKV linear (+bias)
+    if ((st = launch_norm(d->dtype, nk, T, H, x, nullptr, w->ln1_g, gpt ? w->ln1_b : nullptr, d->eps, ws.h, s))) return st;
+    if ((st = layer_gemm(d, EPI_STORE, SB_K_GEMM_QKV, T, qkv_n, H, ws.h, w->w_qkv, gpt ? w->b_qkv : nullptr, ws.qkv, qkv_n, 0, s))) return st;
+    // a5b/a6: RoPE (Llama) + append this step's k, v to the K/V manager
+    if ((st = launch_rope_append(d, rg, ws.qkv, kp, vp, kv->arena_slots, s))) return st;
+    // a7: Split -> per-request attention against K/V history -> Merge (offsets)
+    if ((st = launch_attention(d, rg, kp, vp, kv->arena_slots, ws.qkv, ws.o, ws.part_o, ws.part_ml, s))) return st;
+    // a8: attention-out linear + bias + residual into x
+    if ((st = layer_gemm(d, EPI_RESID, SB_K_GEMM_O, T, H, attn_n, ws.o, w->w_o, gpt ? w->b_o : nullptr, x, H, 0, s))) return st;
+    // a9: norm 2 -> a10: FFN1 (+bias, GeLU) or SwiGLU -> a11: FFN2 + bias + residual
+    if ((st = launch_norm(d->dtype, nk, T, H, x, nullptr, w->ln2_g, gpt ? w->ln2_b : nullptr, d->eps, ws.h, s))) return st;
+    if ((st = layer_gemm(d, gpt ? EPI_GELU : EPI_SWIGLU, SB_K_GEMM_FFN1, T, F, H, ws.h, w->w1, gpt ? w->b1 : nullptr, ws.g, F, F, s))) return st;
+    if ((st = layer_gemm(d, EPI_RESID, SB_K_GEMM_FFN2, T, H, F, ws.g, w->w2, gpt ? w->b2 : nullptr, x, H, 0, s))) return st;
+    return SB_OK;
+}
+
+extern "C" int sb_lm_argmax(const sb_model_dims* d, const sb_model_weights* w, const sb_ragged* rg, const float* x,
+                            float* logits, int32_t* out_ids, void* workspace, size_t ws_bytes, void* stream) {
+    int st = validate_dims(d);
+    if (st) return st;
+    if (!w || !rg || !x || !out_ids || !workspace || !w->lnf_g || !w->w_lm) return fail(SB_ERR_INVALID, "sb_lm_argmax: NULL argument");
+    if (d->vocab <= 0) return fail(SB_ERR_INVALID, "vocab must be positive");
+    const bool gpt = d->arch == SB_ARCH_GPT;
+    if (gpt && !w->lnf_b) return fail(SB_ERR_INVALID, "GPT final norm needs its shift");
+    if ((st = check_ws(d, rg, ws_bytes))) return st;
+    if (rg->n_req <= 0) return SB_OK;
+    hipStream_t s = (hipStream_t)stream;
+    LayerWs ws = layer_ws(d, (char*)workspace, rg->n_tokens, rg->n_req, rg->n_partials);
+    float* lg = logits ? logits : ws.logits;
+    if ((st = launch_norm(d->dtype, gpt ? 0 : 1, rg->n_req, d->hidden, x, rg->last_row, w->lnf_g, gpt ? w->lnf_b : nullptr,
+                          d->eps, ws.hl, s)))
+        return st;
+    GemmArgs a{};
+    a.M = rg->n_req;
+    a.N = d->vocab;
+    a.K = d->hidden;
+    a.A = ws.hl;
+    a.lda = d->hidden;
+    a.W = w->w_lm;
+    a.ldw = d->hidden;
+    a.bias = nullptr;
+    a.C = lg;
+    a.ldc = d->vocab;
+    a.out_f32 = 1;
+    {
+        TimedScope ts(SB_K_GEMM_LM, s);
+        if ((st = launch_gemm(d->dtype, EPI_STORE, a, s))) return st;
+    }
+    return launch_argmax(rg->n_req, d->vocab, lg, out_ids, s);
+}
+
+extern "C" int sb_kv_write(const sb_kv* kv, int32_t layer, int32_t n, const int32_t* slots, const void* k, const void* v,
+                           void* stream) {
+    if (!kv || (n > 0 && (!slots || !k || !v))) return fail(SB_ERR_INVALID, "sb_kv_write: NULL argument");
+    if (n <= 0) return SB_OK;
+    void *kp, *vp;
+    int st = sb_kv_layer_ptrs(kv, layer, &kp, &vp);
+    if (st) return st;
+    hipStream_t s = (hipStream_t)stream;
+    if (kv->dtype == SB_BF16)
+        hipLaunchKernelGGL(kv_copy_kernel<SB_BF16>, dim3(n), dim3(256), 0, s, slots, kp, vp, kv->arena_slots, kv->nkv, kv->d,
+                           (void*)k, (void*)v, 1);
+    else
+        hipLaunchKernelGGL(kv_copy_kernel<SB_F32>, dim3(n), dim3(256), 0, s, slots, kp, vp, kv->arena_slots, kv->nkv, kv->d,
+                           (void*)k, (void*)v, 1);
+    return check_launch("kv_write");
+}
+
+extern "C" int sb_kv_read(const sb_kv* kv, int32_t layer, int32_t n, const int32_t* slots, void* k, void* v, void* stream) {
+    if (!kv || (n > 0 && (!slots || !k || !v))) return fail(SB_ERR_INVALID, "sb_kv_read: NULL argument");
+    if (n <= 0) return SB_OK;
+    void *kp, *vp;
+    int st = sb_kv_layer_ptrs(kv, layer, &kp, &vp);
+    if (st) return st;
+    hipStream_t s = (hipStream_t)stream;
+    if (kv->dtype == SB_BF16)
+        hipLaunchKernelGGL(kv_copy_kernel<SB_BF16>, dim3(n), dim3(256), 0, s, slots, kp, vp, kv->arena_slots, kv->nkv, kv->d, k, v, 0);
+    else
+        hipLaunchKernelGGL(kv_copy_kernel<SB_F32>, dim3(n), dim3(256), 0, s, slots, kp, vp, kv->arena_slots, kv->nkv, kv->d, k, v, 0);
+    return check_launch("kv_read");
+}
+
+// ------------------------------------------------------------------ timing ABI
+extern "C" int sb_timing_enable(int32_t on) {
+    timing().on = on != 0;
+    return SB_OK;
+}
+
+extern "C" int sb_timing_read(int32_t k, double* total_ms, int64_t* count) {
+    if (k < 0 || k >= SB_K_COUNT) return fail(SB_ERR_INVALID, "unknown kernel class %d", k);
+    auto& T = timing();
+    std::lock_guard<std::mutex> g(T.mu);
+    double tot = 0;
+    for (auto& p : T.ev[k]) {
+        if (hipEventSynchronize(p.second) != hipSuccess) return fail(SB_ERR_DEVICE, "event sync failed");
+        float ms = 0;
+        if (hipEventElapsedTime(&ms, p.first, p.second) != hipSuccess) return fail(SB_ERR_DEVICE, "event time failed");
+        tot += ms;
+    }
+    if (total_ms) *total_ms = tot;
+    if (count) *count = (int64_t)T.ev[k].size();
+    return SB_OK;
+}
+
+extern "C" int sb_timing_reset(void) {
+    auto& T = timing();
+    std::lock_guard<std::mutex> g(T.mu);
+    for (int k = 0; k < SB_K_COUNT; ++k) {
+        for (auto& p : T.ev[k]) {
+            hipEventDestroy(p.first);
+            hipEventDestroy(p.second);
+        }
+        T.ev[k].clear();
+        for (auto e : T.open[k]) hipEventDestroy(e);
+        T.open[k].clear();
+    }
+    return SB_OK;
+}
+
+// ------------------------------------------------------------------ op-level entry points
+extern "C" int sb_op_gemm(int32_t dtype, int32_t epilogue, int32_t M, int32_t N, int32_t K, const void* A, int64_t lda,
+                          const void* W, int64_t ldw, const void* bias, void* C, int64_t ldc, int32_t out_f32, int32_t F,
+                          void* stream) {
+    if (dtype != SB_F32 && dtype != SB_BF16) return fail(SB_ERR_INVALID, "unknown dtype");
+    GemmArgs a{};
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.A = A;
+    a.lda = lda;
+    a.W = W;
+    a.ldw = ldw;
+    a.bias = bias;
+    a.C = C;
+    a.ldc = ldc;
+    a.out_f32 = out_f32;
+    a.F = F;
+    return launch_gemm(dtype, epilogue, a, (hipStream_t)stream);
+}
+
+extern "C" int sb_op_norm(int32_t dtype, int32_t kind, int32_t rows, int32_t H, const float* x, const int32_t* row_map,
+                          const void* g, const void* b, float eps, void* out, void* stream) {
+    if (dtype != SB_F32 && dtype != SB_BF16) return fail(SB_ERR_INVALID, "unknown dtype");
+    if (!x || !g || !out) return fail(SB_ERR_INVALID, "sb_op_norm: NULL argument");
+    return launch_norm(dtype, kind, rows, H, x, row_map, g, b, eps, out, (hipStream_t)stream);
+}
+
+extern "C" int sb_op_rope_append(const sb_model_dims* dims, const sb_ragged* rg, const sb_kv* kv, int32_t layer, void* qkv,
+                                 void* stream) {
+    int st = validate_dims(dims);
+    if (st) return st;
+    void *kp, *vp;
+    if ((st = sb_kv_layer_ptrs(kv, layer, &kp, &vp))) return st;
+    return launch_rope_append(dims, rg, qkv, kp, vp, kv->arena_slots, (hipStream_t)stream);
+}
+
+extern "C" int sb_op_attention(const sb_model_dims* dims, const sb_ragged* rg, const sb_kv* kv, int32_t layer,
+                               const void* qkv, void* o, void* workspace, size_t ws_bytes, void* stream) {
+    int st = validate_dims(dims);
+    if (st) return st;
+    if (!rg || !kv || !qkv || !o) return fail(SB_ERR_INVALID, "sb_op_attention: NULL argument");
+    size_t need = (size_t)rg->n_partials * 16 * (dims->head_dim + 2) * 4;
+    if (rg->n_partials > 0 && (!workspace || ws_bytes < need)) return fail(SB_ERR_WORKSPACE, "attention partials need %zu bytes", need);
+    void *kp, *vp;
+    if ((st = sb_kv_layer_ptrs(kv, layer, &kp, &vp))) return st;
+    float* po = (float*)workspace;
+    float* pm = po ? po + (size_t)rg->n_partials * 16 * dims->head_dim : nullptr;
+    return launch_attention(dims, rg, kp, vp, kv->arena_slots, qkv, o, po, pm, (hipStream_t)stream);
+}
+
+extern "C" int sb_op_argmax(int32_t rows, int32_t V, const float* logits, int32_t* out, void* stream) {
+    if (!logits || !out || V <= 0) return fail(SB_ERR_INVALID, "sb_op_argmax: bad argument");
+    return launch_argmax(rows, V, logits, out, (hipStream_t)stream);
+}

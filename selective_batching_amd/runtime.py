@@ -1,0 +1,196 @@
+"""Device memory and the iteration loop around the C ABI.
+
+PyTorch provides device memory (weights, K/V arenas, workspace, activations,
+pinned staging) and the HIP stream; every computation is a libsb call.  One
+iteration (``Engine.step``) follows the scheduling loop of Algorithm 1 with a
+single worker ("连续批处理完全拆解"; "CS349D Lecture 2", section 4.1): select a
+batch, build the ragged metadata, run embed -> layers -> LM head/argmax on the
+flattened batch, bring the B new token ids back, complete the iteration.
+"""
+import ctypes as C
+
+import numpy as np
+import torch
+
+from . import api as A
+from ._lib import (SB_ARCH_GPT, SB_ARCH_LLAMA, SB_BF16, SB_F32, sb_layer_weights, sb_model_dims,
+                   sb_model_weights)
+
+TORCH_DT = {SB_F32: torch.float32, SB_BF16: torch.bfloat16}
+DT_CODE = {"fp32": SB_F32, "bf16": SB_BF16}
+
+
+def stream_handle():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def make_dims(m, dtype: str) -> sb_model_dims:
+    """ABI model shape from any object with arch, n_layers, H, nq, nkv, d, F, V, max_pos, eps, rope_theta."""
+    return sb_model_dims(arch=SB_ARCH_GPT if m.arch == "gpt" else SB_ARCH_LLAMA, dtype=DT_CODE[dtype],
+                         n_layers=m.n_layers, hidden=m.H, n_heads=m.nq, n_kv_heads=m.nkv, head_dim=m.d, ffn=m.F,
+                         vocab=m.V, max_pos=m.max_pos, eps=m.eps, rope_theta=m.rope_theta)
+
+
+def _addr(t):
+    return None if t is None else t.data_ptr()
+
+
+LAYER_KEYS = ("ln1_g", "ln1_b", "w_qkv", "b_qkv", "w_o", "b_o", "ln2_g", "ln2_b", "w1", "b1", "w2", "b2")
+MODEL_KEYS = ("tok_emb", "pos_emb", "lnf_g", "lnf_b", "w_lm")
+
+
+class DeviceWeights:
+    """Weights resident in HBM in the model dtype, plus the ABI structs pointing at them.
+
+    ``host``: dict of numpy arrays (layout of ``synth.make_weights``), copied
+    exactly; or None with ``seed``: random init on the device (N(0, 0.02)
+    matrices and biases, gains 1 + N(0, 0.1)) for runs that do not compare
+    against the oracle.
+    """
+
+    def __init__(self, m, dtype: str, host=None, seed=0, device="cuda", layers=None, with_head=True):
+        self.m, self.dtype = m, dtype
+        tdt = TORCH_DT[DT_CODE[dtype]]
+        gen = torch.Generator(device=device)
+        gen.manual_seed(seed)
+
+        def put(arr):
+            return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).to(device=device).to(tdt)
+
+        def rnd(shape, std, mean=0.0):
+            t = torch.empty(shape, dtype=tdt, device=device)
+            t.normal_(mean, std, generator=gen)
+            return t
+
+        gpt = m.arch == "gpt"
+        n_layers = m.n_layers if layers is None else layers
+        self.layers = []
+        for l in range(n_layers):
+            if host is not None:
+                hw = host["layers"][l]
+                t = {k: (put(hw[k]) if k in hw else None) for k in LAYER_KEYS}
+            else:
+                f1 = m.F if gpt else 2 * m.F
+                t = {"ln1_g": rnd((m.H,), 0.1, 1.0), "w_qkv": rnd((m.qkv_out, m.H), 0.02),
+                     "w_o": rnd((m.H, m.nq * m.d), 0.02), "ln2_g": rnd((m.H,), 0.1, 1.0),
+                     "w1": rnd((f1, m.H), 0.02), "w2": rnd((m.H, m.F), 0.02)}
+                for k in ("ln1_b", "b_qkv", "b_o", "ln2_b", "b1", "b2"):
+                    t[k] = None
+                if gpt:
+                    t.update({"ln1_b": rnd((m.H,), 0.02), "b_qkv": rnd((m.qkv_out,), 0.02),
+                              "b_o": rnd((m.H,), 0.02), "ln2_b": rnd((m.H,), 0.02), "b1": rnd((m.F,), 0.02),
+                              "b2": rnd((m.H,), 0.02)})
+            self.layers.append(t)
+        self.model = {k: None for k in MODEL_KEYS}
+        if with_head and m.V > 0:
+            if host is not None:
+                self.model = {k: (put(host[k]) if k in host else None) for k in MODEL_KEYS}
+            else:
+                self.model = {"tok_emb": rnd((m.V, m.H), 0.02), "w_lm": rnd((m.V, m.H), 0.02),
+                              "lnf_g": rnd((m.H,), 0.1, 1.0), "lnf_b": rnd((m.H,), 0.02) if gpt else None,
+                              "pos_emb": rnd((m.max_pos, m.H), 0.02) if gpt else None}
+        self.layer_structs = [sb_layer_weights(**{k: _addr(t[k]) for k in LAYER_KEYS}) for t in self.layers]
+        self.model_struct = sb_model_weights(**{k: _addr(self.model[k]) for k in MODEL_KEYS})
+
+
+class Engine:
+    """K/V manager + scheduler + device buffers for one model on one GPU."""
+
+    def __init__(self, m, dtype: str, weights: DeviceWeights, n_slots: int, max_bs: int, max_tokens: int,
+                 max_keys_total: int = None, device="cuda", zero_arena=True):
+        self.m, self.dtype, self.w = m, dtype, weights
+        self.dims = make_dims(m, dtype)
+        self.max_bs, self.max_tokens = max_bs, max_tokens
+        self.device = device
+        L = len(weights.layers)
+        self.n_layers = L
+        L = max(L, 1)          # the K/V manager needs at least one layer plane
+        self.arena_slots = A.sb_kv_arena_slots(n_slots, max_bs)
+        nbytes = A.sb_kv_arena_bytes(self.arena_slots, L, m.nkv, m.d, self.dims.dtype)
+        alloc = torch.zeros if zero_arena else torch.empty
+        self.k_arena = alloc(nbytes, dtype=torch.uint8, device=device)
+        self.v_arena = alloc(nbytes, dtype=torch.uint8, device=device)
+        self.kv = A.sb_kv_create(n_slots, self.arena_slots, L, m.nkv, m.d, self.dims.dtype,
+                                 self.k_arena.data_ptr(), self.v_arena.data_ptr())
+        A.sb_kv_set_stream(self.kv, stream_handle())
+        self.sched = A.sb_sched_create(max_bs, self.kv)
+        self.max_keys_total = max_keys_total if max_keys_total is not None else max_bs * (n_slots + 1)
+        self.meta_bytes = A.sb_ragged_bytes(self.dims, max_bs, max_tokens, self.max_keys_total)
+        self.staging = torch.empty(self.meta_bytes, dtype=torch.uint8, pin_memory=True)
+        self.meta = torch.empty(self.meta_bytes, dtype=torch.uint8, device=device)
+        self.max_partials = m.nkv * (self.max_keys_total // 512 + 2 * max_bs)
+        self.ws_bytes = A.sb_layer_workspace_bytes(self.dims, max_tokens, max_bs, self.max_partials)
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
+        self.x = torch.empty(max_tokens * m.H, dtype=torch.float32, device=device)
+        self.ids_dev = torch.empty(max_bs, dtype=torch.int32, device=device)
+        self.ids_host = torch.empty(max_bs, dtype=torch.int32, pin_memory=True)
+        self.logits = torch.empty(max_bs * max(m.V, 1), dtype=torch.float32, device=device) if m.V > 0 else None
+
+    def close(self):
+        if self.sched:
+            A.sb_sched_destroy(self.sched)
+            self.sched = None
+        if self.kv:
+            A.sb_kv_destroy(self.kv)
+            self.kv = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # ------------------------------------------------------------ requests
+    def add(self, rid, arrival, prompt, out_len, max_tokens):
+        A.sb_sched_add(self.sched, rid, arrival, prompt, out_len, max_tokens)
+
+    def add_running(self, rid, arrival, prompt_len, out_len, max_tokens, generated, last_token):
+        A.sb_sched_add_running(self.sched, rid, arrival, prompt_len, out_len, max_tokens, generated, last_token)
+
+    # ------------------------------------------------------------ device passes
+    def build(self, n_new, ctx, slot_base, tokens):
+        return A.sb_ragged_build(self.dims, n_new, ctx, slot_base, tokens, self.staging.data_ptr(),
+                                 self.meta.data_ptr(), self.meta_bytes, stream_handle())
+
+    def forward(self, rg, layer_outputs=None, x_in=None, head=True):
+        """embed (or x_in) -> every layer -> final norm / LM head / argmax on the ragged batch ``rg``."""
+        s = stream_handle()
+        T, H = rg.n_tokens, self.m.H
+        xv = self.x[:T * H]
+        if x_in is not None:
+            xv.copy_(x_in.reshape(-1))
+        else:
+            A.sb_embed(self.dims, self.w.model_struct, rg, xv.data_ptr(), s)
+        for l in range(self.n_layers):
+            A.sb_layer_step(self.dims, self.w.layer_structs[l], rg, self.kv, l, xv.data_ptr(), self.ws.data_ptr(),
+                            self.ws_bytes, s)
+            if layer_outputs is not None:
+                layer_outputs.append(xv.view(T, H).clone())
+        if not head:
+            return None
+        A.sb_lm_argmax(self.dims, self.w.model_struct, rg, xv.data_ptr(), self.logits.data_ptr(),
+                       self.ids_dev.data_ptr(), self.ws.data_ptr(), self.ws_bytes, s)
+        return self.ids_dev[:rg.n_req]
+
+    def step(self, keep=False):
+        """One scheduler iteration; returns None for an empty pool, else a dict of the batch and its results."""
+        ids, n_new, ctx, base = A.sb_select_batch(self.sched, self.max_bs)
+        if len(ids) == 0:
+            return None
+        toks = A.sb_batch_tokens(self.sched, ids, self.max_tokens)
+        rg = self.build(n_new, ctx, base, toks)
+        outs = [] if keep else None
+        self.forward(rg, layer_outputs=outs)
+        B = len(ids)
+        self.ids_host[:B].copy_(self.ids_dev[:B], non_blocking=True)
+        torch.cuda.current_stream().synchronize()
+        new = self.ids_host[:B].numpy().copy()
+        finished = A.sb_sched_complete(self.sched, ids, new)
+        res = {"ids": ids, "n_new": n_new, "ctx": ctx, "slot_base": base, "tokens": new, "finished": finished}
+        if keep:
+            res["layer_outputs"] = [o.cpu() for o in outs]
+            res["logits"] = self.logits[:B * self.m.V].view(B, self.m.V).cpu()
+        return res
+
+    def output(self, rid):
+        return A.sb_sched_output(self.sched, rid)

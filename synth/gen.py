@@ -22,10 +22,11 @@ def bf16_round(x) -> np.ndarray:
     a = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
     if not np.all(np.isfinite(a)):
         raise ValueError("bf16_round expects finite values")
-    bits = a.view(np.uint32).astype(np.uint64)
-    lsb = (bits >> np.uint64(16)) & np.uint64(1)
-    rounded = ((bits + np.uint64(0x7FFF) + lsb) >> np.uint64(16)) << np.uint64(16)
-    return rounded.astype(np.uint32).view(np.float32).reshape(a.shape)
+    bits = a.view(np.uint32)
+    # finite inputs have bits <= 0xFF7FFFFF, so the sum below cannot wrap in uint32
+    rounded = bits + (np.uint32(0x7FFF) + ((bits >> np.uint32(16)) & np.uint32(1)))
+    rounded &= np.uint32(0xFFFF0000)
+    return rounded.view(np.float32).reshape(a.shape)
 
 
 def bf16_bits(x) -> np.ndarray:

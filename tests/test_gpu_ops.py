@@ -1,0 +1,203 @@
+"""GPU parity of each step of the iteration (op-level C entry points) against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import selective_batching_amd as sb
+from gpu_util import TOL, assert_close_rms, dev, host, print_case
+from oracle import model as M
+from synth import ModelDims, bf16_round, normal, random_ragged_batch, synthetic_kv
+from selective_batching_amd.runtime import make_dims, stream_handle
+
+pytestmark = pytest.mark.gpu
+
+DT = {"fp32": sb.SB_F32, "bf16": sb.SB_BF16}
+
+
+def _sync():
+    torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------- GEMM
+GEMM_SHAPES = [(1, 64, 64), (7, 192, 64), (100, 320, 256), (129, 256, 128), (300, 640, 512), (64, 1024, 256)]
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
+@pytest.mark.parametrize("epi", ["store", "bias", "gelu", "resid", "swiglu"])
+def test_gemm_matches_oracle(dtype, M, N, K, epi):
+    print_case("gemm", dtype, M, N, K, epi)
+    seed = M * 7 + N * 3 + K
+    A = normal(seed, "A", (M, K), dtype=dtype)
+    Wrows = 2 * N if epi == "swiglu" else N
+    W = normal(seed, "W", (Wrows, K), std=0.05, dtype=dtype)
+    b = normal(seed, "b", (N,), std=0.5, dtype=dtype) if epi in ("bias", "gelu", "resid") else None
+    x0 = normal(seed, "x0", (M, N)).astype(np.float64)
+    lin = M.linear(A, W[:N], b)
+    if epi in ("store", "bias"):
+        want, code = lin, sb.SB_EPI_STORE
+    elif epi == "gelu":
+        want, code = M.gelu(lin), sb.SB_EPI_GELU
+    elif epi == "resid":
+        want, code = x0 + lin, sb.SB_EPI_RESID
+    else:
+        want, code = M.silu(M.linear(A, W[:N])) * M.linear(A, W[N:]), sb.SB_EPI_SWIGLU
+    dA, dW = dev(A, dtype), dev(W, dtype)
+    db = dev(b, dtype) if b is not None else None
+    if epi == "resid":
+        out = torch.from_numpy(x0.astype(np.float32)).cuda()
+    else:
+        out = torch.zeros((M, N), dtype=dA.dtype, device="cuda")
+    sb.sb_op_gemm(DT[dtype], code, M, N, K, dA.data_ptr(), K, dW.data_ptr(), K, db.data_ptr() if db is not None else None,
+                  out.data_ptr(), N, 0, N if epi == "swiglu" else 0, stream_handle())
+    _sync()
+    tol = TOL[dtype] / 4 if dtype == "bf16" else TOL[dtype]
+    assert_close_rms(host(out), want, tol, f"gemm {dtype} {M}x{N}x{K} {epi}")
+
+
+def test_gemm_fp32_logits_out_and_ragged_rows():
+    """fp32 output of a bf16 GEMM (LM-head form), M not a multiple of any tile."""
+    M, N, K = 37, 4096 + 64, 256
+    A = normal(1, "A", (M, K), dtype="bf16")
+    W = normal(1, "W", (N, K), std=0.05, dtype="bf16")
+    out = torch.full((M, N), -7.0, dtype=torch.float32, device="cuda")
+    sb.sb_op_gemm(sb.SB_BF16, sb.SB_EPI_STORE, M, N, K, dev(A, "bf16").data_ptr(), K, dev(W, "bf16").data_ptr(), K, None,
+                  out.data_ptr(), N, 1, 0, stream_handle())
+    _sync()
+    assert_close_rms(host(out), M.linear(A, W), 1e-5, "bf16 gemm fp32 out")
+
+
+# ---------------------------------------------------------------- norms
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("kind", [0, 1])
+@pytest.mark.parametrize("H", [64, 256, 4096, 12288])
+def test_norm_matches_oracle(dtype, kind, H):
+    print_case("norm", dtype, kind, H)
+    rows = 5
+    x = normal(H, "x", (rows + 2, H), std=2.0, mean=0.3)
+    g = normal(H, "g", (H,), std=0.1, mean=1.0, dtype=dtype)
+    b = normal(H, "b", (H,), std=0.1, dtype=dtype) if kind == 0 else None
+    row_map = np.array([6, 0, 3, 3, 1], np.int32)
+    out = torch.zeros((rows, H), dtype={"fp32": torch.float32, "bf16": torch.bfloat16}[dtype], device="cuda")
+    dx = torch.from_numpy(x).cuda()
+    dmap = torch.from_numpy(row_map).cuda()
+    dg, dbb = dev(g, dtype), (dev(b, dtype) if b is not None else None)
+    sb.sb_op_norm(DT[dtype], kind, rows, H, dx.data_ptr(), dmap.data_ptr(), dg.data_ptr(),
+                  dbb.data_ptr() if dbb is not None else None, 1e-5, out.data_ptr(), stream_handle())
+    _sync()
+    xs = x[row_map].astype(np.float64)
+    want = M.layer_norm(xs, g, b, 1e-5) if kind == 0 else M.rms_norm(xs, g, 1e-5)
+    tol = 1e-5 if dtype == "fp32" else 8e-3
+    assert_close_rms(host(out), want, tol, f"norm {dtype} kind {kind} H {H}")
+
+
+# ---------------------------------------------------------------- argmax
+def test_argmax_ties_and_random():
+    V = 128256
+    x = normal(0, "logits", (6, V)).astype(np.float32)
+    x[1, 17] = x[1, 900] = x[1, 50000] = 100.0          # tie: lowest index wins
+    x[2, :] = 0.0
+    x[3, V - 1] = 1e9
+    d = torch.from_numpy(x).cuda()
+    out = torch.zeros(6, dtype=torch.int32, device="cuda")
+    sb.sb_op_argmax(6, V, d.data_ptr(), out.data_ptr(), stream_handle())
+    _sync()
+    got = out.cpu().numpy()
+    assert list(got) == [M.greedy(r) for r in x]
+    assert got[1] == 17 and got[2] == 0 and got[3] == V - 1
+
+
+# ---------------------------------------------------------------- attention (+ RoPE / K/V append)
+def _attention_case(m: ModelDims, dtype, batch, seed, rope_check=False):
+    """Random q/k/v for the new tokens, synthetic history in the K/V manager; GPU vs oracle."""
+    print_case("attention", m.name, dtype, batch, seed)
+    dims = make_dims(m, dtype)
+    G = m.nq // m.nkv
+    n_slots = sum(n + c for n, c in batch) + 64
+    arena = sb.sb_kv_arena_slots(n_slots, len(batch))
+    nbytes = sb.sb_kv_arena_bytes(arena, 1, m.nkv, m.d, DT[dtype])
+    ka = torch.full((nbytes,), 0x7F, dtype=torch.uint8, device="cuda")     # non-zero garbage outside writes
+    va = torch.full((nbytes,), 0x7F, dtype=torch.uint8, device="cuda")
+    kv = sb.sb_kv_create(n_slots, arena, 1, m.nkv, m.d, DT[dtype], ka.data_ptr(), va.data_ptr())
+    try:
+        bases, hist = [], []
+        for i, (n, c) in enumerate(batch):
+            base = sb.sb_kv_reserve(kv, i, n + c)
+            bases.append(base)
+            hk, hv = synthetic_kv(seed, f"h{i}", c, m.nkv, m.d, 1.0, dtype)
+            hist.append((hk, hv))
+            if c:
+                slots = torch.arange(base, base + c, dtype=torch.int32, device="cuda")
+                sb.sb_kv_write(kv, 0, c, slots.data_ptr(), dev(hk, dtype).data_ptr(), dev(hv, dtype).data_ptr(),
+                               stream_handle())
+        T = sum(n for n, _ in batch)
+        qkv = normal(seed, "qkv", (T, m.qkv_out), dtype=dtype)
+        nbytes_meta = sb.sb_ragged_bytes(dims, len(batch), T, n_slots)
+        staging = torch.empty(nbytes_meta, dtype=torch.uint8, pin_memory=True)
+        meta = torch.empty(nbytes_meta, dtype=torch.uint8, device="cuda")
+        rg = sb.sb_ragged_build(dims, [n for n, _ in batch], [c for _, c in batch], bases, None, staging.data_ptr(),
+                                meta.data_ptr(), nbytes_meta, stream_handle())
+        dqkv = dev(qkv, dtype)
+        sb.sb_op_rope_append(dims, rg, kv, 0, dqkv.data_ptr(), stream_handle())
+        o = torch.zeros((T, m.nq * m.d), dtype=dqkv.dtype, device="cuda")
+        ws = torch.empty(max(rg.n_partials, 1) * 16 * (m.d + 2) * 4, dtype=torch.uint8, device="cuda")
+        sb.sb_op_attention(dims, rg, kv, 0, dqkv.data_ptr(), o.data_ptr(), ws.data_ptr(), ws.numel(), stream_handle())
+        _sync()
+        got = host(o)
+        got_qkv = host(dqkv)
+        want = np.zeros_like(got)
+        t0 = 0
+        nq_d, nkv_d = m.nq * m.d, m.nkv * m.d
+        for i, (n, c) in enumerate(batch):
+            rows = slice(t0, t0 + n)
+            q = qkv[rows, :nq_d].reshape(n, m.nq, m.d).astype(np.float64)
+            k = qkv[rows, nq_d:nq_d + nkv_d].reshape(n, m.nkv, m.d).astype(np.float64)
+            v = qkv[rows, nq_d + nkv_d:].reshape(n, m.nkv, m.d).astype(np.float64)
+            if m.arch == "llama":
+                pos = c + np.arange(n)
+                q, k = M.rope(q, pos, m.rope_theta), M.rope(k, pos, m.rope_theta)
+                if rope_check:
+                    assert_close_rms(got_qkv[rows, :nq_d], q.reshape(n, nq_d), TOL[dtype] / 4, "rope q")
+            K = np.concatenate([hist[i][0].astype(np.float64), k], axis=0)
+            V = np.concatenate([hist[i][1].astype(np.float64), v], axis=0)
+            want[rows] = M.attention(q, K, V, c, G).reshape(n, nq_d)
+            t0 += n
+        tol = TOL[dtype] / 2 if dtype == "bf16" else TOL[dtype]
+        assert_close_rms(got, want, tol, f"attention {m.name} {dtype}")
+        # the appended rows landed in the right slots (read back through the manager)
+        if rope_check or True:
+            slots = np.concatenate([np.arange(bases[i] + c, bases[i] + c + n) for i, (n, c) in enumerate(batch)]).astype(np.int32)
+            kk = torch.zeros((T, m.nkv, m.d), dtype=dqkv.dtype, device="cuda")
+            vv = torch.zeros_like(kk)
+            sb.sb_kv_read(kv, 0, T, torch.from_numpy(slots).cuda().data_ptr(), kk.data_ptr(), vv.data_ptr(), stream_handle())
+            _sync()
+            np.testing.assert_array_equal(host(vv).reshape(T, -1), qkv[:, nq_d + nkv_d:])
+    finally:
+        sb.sb_kv_destroy(kv)
+
+
+TINY_F32 = ModelDims("attn-f32", "gpt", 1, H=64, nq=4, nkv=4, d=16, F=64, V=0)
+MINI_ATT = ModelDims("attn-mini", "gpt", 1, H=256, nq=8, nkv=8, d=32, F=64, V=0)
+GQA_BF16 = ModelDims("attn-gqa", "llama", 1, H=1024, nq=8, nkv=2, d=128, F=64, V=0, rope_theta=500000.0)
+GQA_F32 = ModelDims("attn-gqa32", "llama", 1, H=512, nq=8, nkv=2, d=64, F=64, V=0, rope_theta=10000.0)
+
+
+@pytest.mark.parametrize("m,dtype", [(TINY_F32, "fp32"), (MINI_ATT, "bf16"), (MINI_ATT, "fp32"), (GQA_BF16, "bf16"),
+                                     (GQA_F32, "fp32")])
+def test_attention_figure5_and_exercise4(m, dtype):
+    _attention_case(m, dtype, [(1, 3), (1, 1), (2, 0), (3, 0)], 1, rope_check=True)
+    _attention_case(m, dtype, [(37, 0), (9, 0), (1, 120), (1, 15), (1, 64)], 2)
+
+
+@pytest.mark.parametrize("m,dtype", [(MINI_ATT, "bf16"), (GQA_BF16, "bf16"), (GQA_F32, "fp32"), (TINY_F32, "fp32")])
+@pytest.mark.parametrize("seed", range(3))
+def test_attention_random_ragged(m, dtype, seed):
+    batch = random_ragged_batch(seed, 7, 1500, 90)     # long histories -> split items; big prefills -> row tiles
+    _attention_case(m, dtype, batch, seed + 10)
+
+
+def test_attention_edge_cases():
+    _attention_case(GQA_BF16, "bf16", [(1, 0)], 3)                  # one token, no history: o = v
+    _attention_case(GQA_BF16, "bf16", [(1, 2047)], 4)               # single long decode
+    _attention_case(GQA_BF16, "bf16", [(64, 0), (65, 0), (17, 511)], 5)   # tile boundaries
+    _attention_case(MINI_ATT, "bf16", [(16, 512), (1, 512), (1, 513)], 6)  # split boundaries

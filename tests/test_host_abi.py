@@ -1,0 +1,284 @@
+"""CPU tests of libsb's host half through the C ABI: exports, K/V manager,
+scheduler (bit-exact against the oracle) and the ragged metadata builder."""
+import ctypes
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+import selective_batching_amd as sb
+from golden import load
+from oracle import flat as FL
+from oracle import scheduler as OS
+from synth import LLAMA8B, MINI, TOY, figure5_requests, llama_mixed_batch, p4_grid_requests, poisson_trace, \
+    random_ragged_batch
+from selective_batching_amd.runtime import make_dims
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = set()
+    for h in ("sb.h", "sb_ops.h"):
+        src = open(os.path.join(ROOT, "include", h)).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        for m in re.finditer(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\**\s+\**(sb_[a-z0-9_]+)\s*\(", src, re.M):
+            names.add(m.group(1))
+    return names
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    from selective_batching_amd._lib import _PROTOS
+    assert names == set(_PROTOS), names ^ set(_PROTOS)      # header and binding agree
+    lib = ctypes.CDLL(sb.LIB_PATH)
+    missing = [n for n in sorted(names) if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+# ---------------------------------------------------------------- K/V manager
+def test_kv_reserve_free_and_errors():
+    kv = sb.sb_kv_create(100, sb.sb_kv_arena_slots(100, 4), 2, 2, 16, sb.SB_F32)
+    b0 = sb.sb_kv_reserve(kv, 1, 30)
+    b1 = sb.sb_kv_reserve(kv, 2, 70)          # exact fit: 30 + 70 == n_slots is admitted
+    assert b0 % 8 == 0 and b1 % 8 == 0
+    assert sb.sb_kv_stats(kv)["n_rsrv"] == 100
+    with pytest.raises(sb.SBError) as e:
+        sb.sb_kv_reserve(kv, 3, 1)
+    assert e.value.status == sb.SB_ERR_NO_SLOTS
+    with pytest.raises(sb.SBError) as e:
+        sb.sb_kv_reserve(kv, 1, 1)
+    assert e.value.status == sb.SB_ERR_STATE
+    sb.sb_kv_free(kv, 1)
+    with pytest.raises(sb.SBError) as e:
+        sb.sb_kv_free(kv, 1)
+    assert e.value.status == sb.SB_ERR_NOT_FOUND
+    with pytest.raises(sb.SBError) as e:
+        sb.sb_kv_reserve(kv, 9, 101)
+    assert e.value.status == sb.SB_ERR_TOO_LARGE
+    assert sb.sb_kv_stats(kv)["n_rsrv"] == 70
+    sb.sb_kv_destroy(kv)
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_kv_placement_disjoint_aligned_and_compacts(seed):
+    n_slots, max_live = 400, 12
+    arena = sb.sb_kv_arena_slots(n_slots, max_live)
+    kv = sb.sb_kv_create(n_slots, arena, 1, 1, 8, sb.SB_BF16)
+    g = np.random.default_rng(seed)
+    live = {}
+    nxt = 0
+    for _ in range(400):
+        if live and (g.random() < 0.45 or len(live) == max_live):
+            rid = list(live)[g.integers(len(live))]
+            sb.sb_kv_free(kv, rid)
+            del live[rid]
+        else:
+            mt = int(g.integers(1, 60))
+            try:
+                base = sb.sb_kv_reserve(kv, nxt, mt)
+                live[nxt] = mt
+            except sb.SBError as e:
+                assert e.status == sb.SB_ERR_NO_SLOTS
+                assert sum(live.values()) + mt > n_slots      # counter alone decides
+            nxt += 1
+        spans = sorted((sb.sb_kv_lookup(kv, r)[0], sb.sb_kv_lookup(kv, r)[1]) for r in live)
+        end = 0
+        for b, mt in spans:
+            assert b % 8 == 0 and b >= end
+            end = b + mt
+        assert end <= arena
+        assert sb.sb_kv_stats(kv)["n_rsrv"] == sum(live.values())
+    sb.sb_kv_destroy(kv)
+
+
+# ---------------------------------------------------------------- scheduler vs oracle
+def native_replay(reqs, max_bs, n_slots):
+    """The oracle's logical-clock loop, with the scheduling decisions made by libsb."""
+    kv = sb.sb_kv_create(n_slots, sb.sb_kv_arena_slots(n_slots, max_bs), 1, 1, 8, sb.SB_F32)
+    s = sb.sb_sched_create(max_bs, kv)
+    pending = sorted(reqs, key=lambda r: (r.arrival, r.rid))
+    i, t, log = 0, 0, []
+    while i < len(pending) or sb.sb_sched_stats(s)["pool"]:
+        while i < len(pending) and pending[i].arrival <= t:
+            r = pending[i]
+            sb.sb_sched_add(s, r.rid, r.arrival, r.prompt, r.out_len, r.max_tokens)
+            i += 1
+        if not sb.sb_sched_stats(s)["pool"]:
+            t = int(math.ceil(pending[i].arrival))
+            continue
+        ids, n_new, ctx, _ = sb.sb_select_batch(s, max_bs)
+        log.append((t, [(int(a), int(b), int(c)) for a, b, c in zip(ids, n_new, ctx)], sb.sb_sched_stats(s)["n_rsrv"]))
+        sb.sb_sched_complete(s, ids, np.zeros(len(ids), np.int32))
+        t += 1
+    sb.sb_sched_destroy(s)
+    sb.sb_kv_destroy(kv)
+    return log
+
+
+def test_native_scheduler_p4_timeline():
+    g = load("p4_timeline.txt")
+    reqs = p4_grid_requests(seed=0)
+    log = native_replay(reqs, 3, 10**9)
+    assert log == OS.replay(reqs, 3, 10**9)
+    assert len(log) == g["iterations"][0]
+    rows = OS.timeline(log, reqs)
+    for r in reqs:
+        assert rows[r.rid] == g[f"r{r.rid}"]
+
+
+@pytest.mark.parametrize("case", range(6))
+def test_native_scheduler_matches_oracle_random(case):
+    reqs = poisson_trace(seed=case, n=150, rate=[0.3, 1.0, 2.0, 0.6, 5.0, 0.9][case], plo=1, phi=40, olo=1, ohi=30,
+                         reserve_out=30)
+    n_slots = [200, 120, 1000, 75, 300, 10**6][case]
+    max_bs = [4, 8, 16, 3, 32, 1][case]
+    assert native_replay(reqs, max_bs, n_slots) == OS.replay(reqs, max_bs, n_slots)
+
+
+def test_native_scheduler_matches_oracle_trace_2000():
+    """The Poisson trace of the 8B-shaped serving run: 2000 requests, max_bs 64, prompt U[32,512],
+    out U[1,512], max_tokens = prompt + 512; slots tight enough that reservations bind."""
+    reqs = poisson_trace(seed=0, n=2000, rate=0.5)
+    for n_slots in (20000, 65536):
+        assert native_replay(reqs, 64, n_slots) == OS.replay(reqs, 64, n_slots)
+
+
+def test_native_scheduler_tokens_and_outputs():
+    kv = sb.sb_kv_create(64, sb.sb_kv_arena_slots(64, 4), 1, 1, 8, sb.SB_F32)
+    s = sb.sb_sched_create(4, kv)
+    reqs = figure5_requests(seed=0)
+    for r in reqs[:2]:
+        sb.sb_sched_add(s, r.rid, r.arrival, r.prompt, 8, r.max_tokens)
+    ids, n_new, ctx, base = sb.sb_select_batch(s, 4)
+    assert list(ids) == [0, 1] and list(n_new) == [3, 1] and list(ctx) == [0, 0]
+    assert list(sb.sb_batch_tokens(s, ids, 16)) == reqs[0].prompt + reqs[1].prompt
+    sb.sb_sched_complete(s, ids, [11, 12])
+    for r in reqs[2:]:
+        sb.sb_sched_add(s, r.rid, r.arrival, r.prompt, 8, r.max_tokens)
+    ids, n_new, ctx, base = sb.sb_select_batch(s, 4)
+    g = load("figure5.txt")
+    assert list(n_new) == g["n_new"] and list(ctx) == g["ctx"]
+    assert list(sb.sb_batch_tokens(s, ids, 16)) == [11, 12] + reqs[2].prompt + reqs[3].prompt
+    sb.sb_sched_complete(s, ids, [21, 22, 23, 24])
+    assert list(sb.sb_sched_output(s, 0)) == [11, 21]
+    with pytest.raises(sb.SBError) as e:
+        sb.sb_sched_complete(s, ids, [0, 0, 0, 0])         # they are not running any more
+    assert e.value.status == sb.SB_ERR_STATE
+
+
+def test_native_scheduler_errors():
+    kv = sb.sb_kv_create(10, sb.sb_kv_arena_slots(10, 2), 1, 1, 8, sb.SB_F32)
+    with pytest.raises(sb.SBError) as e:
+        sb.sb_sched_create(0, kv)
+    assert e.value.status == sb.SB_ERR_INVALID
+    s = sb.sb_sched_create(2, kv)
+    with pytest.raises(sb.SBError) as e:
+        sb.sb_sched_add(s, 0, 0.0, [1, 2, 3], 9, 11)
+    assert e.value.status == sb.SB_ERR_TOO_LARGE
+    ids, *_ = sb.sb_select_batch(s, 2)
+    assert len(ids) == 0                                    # empty pool -> empty batch
+    sb.sb_sched_add(s, 1, 0.0, [1], 1, 1)
+    with pytest.raises(sb.SBError) as e:
+        sb.sb_sched_add(s, 1, 0.0, [1], 1, 1)
+    assert e.value.status == sb.SB_ERR_STATE
+    ids, *_ = sb.sb_select_batch(s, 2)
+    fin = sb.sb_sched_complete(s, ids, [5])
+    assert list(fin) == [1] and sb.sb_kv_stats(kv)["n_rsrv"] == 0
+
+
+# ---------------------------------------------------------------- ragged metadata
+def host_ragged(m, dtype, batch, slot_base=None, tokens=None):
+    dims = make_dims(m, dtype)
+    n_new = [b[0] for b in batch]
+    ctx = [b[1] for b in batch]
+    if slot_base is None:
+        slot_base, acc = [], 0
+        for n, c in batch:
+            slot_base.append(acc)
+            acc += (n + c + 7) // 8 * 8
+    keys = sum(n + c for n, c in batch)
+    nbytes = sb.sb_ragged_bytes(dims, len(batch), sum(n_new), keys)
+    buf = np.zeros(nbytes // 4 + 1, np.int32)
+    rg = sb.sb_ragged_build(dims, n_new, ctx, slot_base, tokens, buf.ctypes.data, None, nbytes)
+    return rg, buf, slot_base
+
+
+def _arr(ptr, n):
+    return np.ctypeslib.as_array((ctypes.c_int32 * n).from_address(ptr)).copy() if n else np.zeros(0, np.int32)
+
+
+@pytest.mark.parametrize("name", ["figure5", "exercise4"])
+def test_ragged_metadata_pinned_batches(name):
+    g = load(f"{name}.txt")
+    batch = list(zip(g["n_new"], g["ctx"]))
+    rg, _, base = host_ragged(TOY, "fp32", batch)
+    B, T = len(batch), rg.n_tokens
+    assert T == g["tokens"][0]
+    assert list(_arr(rg.cu_seqlens, B + 1)) == FL.cu_seqlens(batch)
+    assert list(_arr(rg.ctx_lens, B)) == g["ctx"]
+    assert list(_arr(rg.tok_pos, T)) == FL.positions(batch)
+    assert list(_arr(rg.last_row, B)) == FL.last_rows(batch)
+    want_slots = [base[i] + c + j for i, (n, c) in enumerate(batch) for j in range(n)]
+    assert list(_arr(rg.tok_slot, T)) == want_slots
+
+
+def _coverage(m, batch, rg):
+    """Every (request, kv head, row) must see every visible key exactly once across the work items."""
+    G = m.nq // m.nkv
+    items = _arr(rg.items, rg.n_items * 8).reshape(-1, 8)
+    seen = {}
+    for req, kvh, mode, row0, nrows, kb, ke, part in items:
+        assert 0 <= kb < ke
+        assert nrows <= (64 if mode == 0 else 16)
+        n_new, ctx = batch[req]
+        for r in range(row0, row0 + nrows):
+            tok = r // G
+            assert tok < n_new
+            lim = min(ke, ctx + tok + 1)
+            for k in range(kb, lim):
+                key = (req, kvh, r, k)
+                assert key not in seen
+                seen[key] = 1
+    want = sum(m.nkv * sum(c + j + 1 for j in range(n) for _ in range(G)) for n, c in batch)
+    assert len(seen) == want
+    # split items come with a combine group naming exactly their partial tiles
+    groups = _arr(rg.groups, rg.n_groups * 8).reshape(-1, 8)
+    parts = sorted(int(p) for p in items[:, 7] if p >= 0)
+    assert parts == list(range(rg.n_partials))
+    assert sum(int(gp[5]) for gp in groups) == rg.n_partials
+
+
+@pytest.mark.parametrize("m,dtype", [(TOY, "fp32"), (MINI, "bf16"), (LLAMA8B, "bf16")])
+@pytest.mark.parametrize("seed", range(4))
+def test_attention_work_list_covers_each_pair_once(m, dtype, seed):
+    batch = random_ragged_batch(seed, 6, 1100, 40)
+    rg, _, _ = host_ragged(m, dtype, batch)
+    _coverage(m, batch, rg)
+
+
+def test_attention_work_list_llama_mixed_batch_counts():
+    batch = llama_mixed_batch(seed=0)
+    rg, _, _ = host_ragged(LLAMA8B, "bf16", batch)
+    assert rg.n_req == 256 and rg.n_tokens == sum(n for n, _ in batch)
+    items = _arr(rg.items, rg.n_items * 8).reshape(-1, 8)
+    cost = np.where(items[:, 2] == 0, 4 * items[:, 6], items[:, 6] - items[:, 5])
+    assert np.all(np.diff(cost) <= 0)                       # heaviest first
+    # pair count of the whole batch (Σ over requests of Σ_j (ctx + j + 1), per query head)
+    assert FL.useful_pairs(batch) > 0
+
+
+def test_ragged_rejects_bad_input():
+    dims = make_dims(TOY, "fp32")
+    buf = np.zeros(4096, np.int32)
+    with pytest.raises(sb.SBError) as e:
+        sb.sb_ragged_build(dims, [1], [0], [3], None, buf.ctypes.data, None, buf.nbytes)   # unaligned slot base
+    assert e.value.status == sb.SB_ERR_INVALID
+    with pytest.raises(sb.SBError) as e:
+        sb.sb_ragged_build(dims, [0], [0], [0], None, buf.ctypes.data, None, buf.nbytes)
+    assert e.value.status == sb.SB_ERR_INVALID
+    with pytest.raises(sb.SBError) as e:
+        sb.sb_ragged_build(dims, [5] * 300, [0] * 300, [0] * 300, None, buf.ctypes.data, None, 64)
+    assert e.value.status in (sb.SB_ERR_WORKSPACE, sb.SB_ERR_INVALID)
