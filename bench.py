@@ -1,0 +1,231 @@
+#!/usr/bin/env python3
+"""Throughput of one selective-batched iteration on one MI355X.
+
+Workload: the Llama-3-8B-shaped decoder (32 layers, hidden 4096, 32 query /
+8 K/V heads of 128, SwiGLU 14336, vocab 128256, bf16, random init on the
+device) over the mixed ragged batch of 240 decodes (cached context uniform in
+[128, 2048]) and 16 prefills (prompt uniform in [32, 512]), max_bs 256 --
+every request in one iteration.  Inputs are synthetic and seeded; the K/V
+history of the decodes is random bf16 already resident in HBM.
+
+A step is one pass of the whole hot path: iteration-level Select over the
+request pool (host), the ragged metadata and attention work list (host) and
+its copy to the GPU, embedding, 32 selective-batched layers, final norm + LM
+head + greedy argmax, the copy of the 256 new token ids back, and Complete
+(host).  The scheduler state is rebuilt inside the step so that every step
+re-runs the same iteration (same batch, same slots).  ``value`` is processed
+tokens per second (sum of n_new over the batch / step time).
+
+Also reported: per-kernel-class GPU time from HIP events recorded around
+every launch on the launch stream during the timed steps; the roofline of the
+dominant kernel (the FFN1 SwiGLU GEMM, MFMA-bound); decode-attention HBM
+bandwidth; and the CPU oracle timed on a bounded sample of the same workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--layers", type=int, default=32, help="decoder layers (the workload has 32)")
+    return ap.parse_args()
+
+
+def algorithmic_work(m, batch, n_layers):
+    """FLOPs and bytes the method must do per iteration (no padding; weights read once)."""
+    T = sum(n for n, _ in batch)
+    B = len(batch)
+    qkv, o, f1, f2 = m.qkv_out * m.H, m.H * m.nq * m.d, 2 * m.F * m.H, m.H * m.F
+    gemm = {"qkv": 2 * T * qkv, "o": 2 * T * o, "ffn1": 2 * T * f1, "ffn2": 2 * T * f2}
+    kv_row = 2 * m.nkv * m.d * 2                      # K and V of one token, one layer, bf16
+    dec = [(n, c) for n, c in batch if n == 1]
+    pre = [(n, c) for n, c in batch if n > 1]
+    attn_bytes_dec = sum((c + 1) * kv_row for _, c in dec)
+    attn_bytes = sum((c + n) * kv_row for n, c in batch)                     # every K/V row read once
+    attn_bytes += T * (m.nq * m.d * 2) * 2                                   # q in, o out
+    attn_flops = 4 * m.d * m.nq * sum(sum(c + j + 1 for j in range(n)) for n, c in batch)
+    return {"T": T, "B": B, "gemm_per_layer": gemm, "lm_flops": 2 * B * m.H * m.V,
+            "attn_bytes_per_layer": attn_bytes, "attn_decode_bytes_per_layer": attn_bytes_dec,
+            "attn_flops_per_layer": attn_flops, "n_dec": len(dec), "n_pre": len(pre),
+            "weight_bytes": (qkv + o + f1 + f2) * 2 * n_layers + m.V * m.H * 2}
+
+
+def cpu_baseline(m, batch, seed):
+    """The oracle (fp64 numpy, per-request plain definition) on a bounded sample of the workload."""
+    import numpy as np
+    from oracle import model as OM
+    from synth import kv_std, make_layer_weights, normal, synthetic_kv, init_std
+    cores = len(os.sched_getaffinity(0))
+    wl = make_layer_weights(m, seed, 0, "bf16")
+    dec_idx = [i for i, (n, _) in enumerate(batch) if n == 1][:6]
+    pre_idx = sorted([i for i, (n, _) in enumerate(batch) if n > 1], key=lambda i: batch[i][0])[:1]
+    sample = dec_idx + pre_idx
+    inputs = []
+    for i in sample:
+        n, c = batch[i]
+        hk, hv = synthetic_kv(seed, f"cpu{i}", c, m.nkv, m.d, kv_std(m), "bf16")
+        x = normal(seed, f"cpu.x{i}", (n, m.H))
+        inputs.append((x, c, {"k": hk.astype(np.float64), "v": hv.astype(np.float64)}))
+    t0 = time.perf_counter()
+    for x, c, cache in inputs:
+        OM.layer_forward(m, wl, x, c, cache)
+    t_layer = time.perf_counter() - t0
+    del wl
+    w_lm = normal(seed, "cpu.w_lm", (m.V, m.H), std=init_std(m.H), dtype="bf16")
+    W = {"lnf_g": np.ones(m.H, np.float32), "w_lm": w_lm}
+    t0 = time.perf_counter()
+    for x, _, _ in inputs:
+        OM.lm_logits(m, W, x[-1])
+    t_lm = time.perf_counter() - t0
+    tokens = sum(batch[i][0] for i in sample)
+    est = t_layer * m.n_layers + t_lm
+    return {"value": tokens / est, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": (f"{len(dec_idx)} decodes + {len(pre_idx)} prefill of the same batch ({tokens} tokens), "
+                       f"one decoder layer timed ({t_layer:.2f} s) x {m.n_layers} layers + LM head "
+                       f"({t_lm:.2f} s); fp64 numpy, BLAS threads = {cores}")}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path (requests shard by data "
+              "parallelism with no exchange; see the design notes).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import selective_batching_amd as sb
+    from selective_batching_amd import api as A
+    from selective_batching_amd.runtime import DeviceWeights, Engine, stream_handle
+    from synth import LLAMA8B, llama_mixed_batch, uniform_int
+
+    m = LLAMA8B.with_layers(args.layers)
+    batch = llama_mixed_batch(seed=args.seed)
+    work = algorithmic_work(m, batch, m.n_layers)
+    T, B = work["T"], work["B"]
+    torch.cuda.set_device(0)
+    print(f"[bench] {torch.cuda.get_device_name(0)}; T={T} tokens, B={B} requests, {m.n_layers} layers", file=sys.stderr,
+          flush=True)
+
+    W = DeviceWeights(m, "bf16", host=None, seed=args.seed)
+    n_slots = sum(n + c for n, c in batch) + 8 * B
+    eng = Engine(m, "bf16", W, n_slots=n_slots, max_bs=B, max_tokens=T, max_keys_total=n_slots, zero_arena=False)
+    # random bf16 K/V history already in HBM (both arenas, every slot)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(args.seed + 1)
+    for a in (eng.k_arena, eng.v_arena):
+        a.view(torch.bfloat16).normal_(0.0, 1.0, generator=g)
+    prompts = {i: uniform_int(args.seed, f"bench.prompt{i}", 0, m.V - 1, n).tolist()
+               for i, (n, c) in enumerate(batch) if n > 1}
+    last_tok = uniform_int(args.seed, "bench.last", 0, m.V - 1, B).tolist()
+
+    def load_pool():
+        """The pool of this iteration: decodes first (they arrived first), then the new prompts."""
+        for i, (n, c) in enumerate(batch):
+            if n == 1:
+                # mid-generation: prompt of c tokens, 1 generated token not fed yet -> ctx = c;
+                # max_tokens = ctx + n_new (the reservation this iteration needs)
+                eng.add_running(i, float(i), c, 2, c + 1, 1, last_tok[i])
+            else:
+                eng.add(i, float(i), prompts[i], 2, n + 1)
+
+    def reset():
+        eng.close()
+        eng.kv = A.sb_kv_create(n_slots, eng.arena_slots, m.n_layers, m.nkv, m.d, sb.SB_BF16,
+                                eng.k_arena.data_ptr(), eng.v_arena.data_ptr())
+        A.sb_kv_set_stream(eng.kv, stream_handle())
+        eng.sched = A.sb_sched_create(B, eng.kv)
+        load_pool()
+
+    def step():
+        reset()
+        res = eng.step()
+        assert res is not None and len(res["ids"]) == B and int(res["n_new"].sum()) == T
+        return res
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    A.sb_timing_reset()
+    A.sb_timing_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        res = step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    A.sb_timing_enable(False)
+    kern = {}
+    for k, name in enumerate(sb.KERNEL_CLASSES):
+        ms, n = A.sb_timing_read(k)
+        if n:
+            kern[name] = {"ms_per_step": ms / args.steps, "launches_per_step": n / args.steps, "avg_ms": ms / n}
+    A.sb_timing_reset()
+    ms_step = 1000.0 * wall / args.steps
+    gpu_ms = sum(v["ms_per_step"] for v in kern.values())
+
+    # roofline of the dominant kernel: the FFN1 (SwiGLU) GEMM, one launch per layer
+    f1 = kern["gemm_ffn1"]
+    f1_flops = work["gemm_per_layer"]["ffn1"]
+    f1_tflops = f1_flops / (f1["avg_ms"] * 1e-3) / 1e12
+    roofline = {"kernel": "gemm_bf16_kernel<128,128,SWIGLU> (FFN1 gate/up + SiLU*up)", "bound": "mfma",
+                "achieved": round(f1_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(f1_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "flops_per_launch": f1_flops, "avg_launch_ms": round(f1["avg_ms"], 4)}
+    at = kern["attention"]
+    attn_gbs = work["attn_bytes_per_layer"] / (at["avg_ms"] * 1e-3) / 1e9
+    gemm_flops = sum(work["gemm_per_layer"].values()) * m.n_layers + work["lm_flops"]
+    gemm_ms = sum(kern[k]["ms_per_step"] for k in ("gemm_qkv", "gemm_o", "gemm_ffn1", "gemm_ffn2", "gemm_lm"))
+    out = {
+        "metric": "tokens/s per selective-batched iteration; MFMA % + attention HBM GB/s",
+        "value": round(T / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": (f"Llama-3-8B-shaped decoder ({m.n_layers} layers, hidden 4096, GQA 32/8 x 128, "
+                                "SwiGLU 14336, vocab 128256), random init; one iteration over 240 decodes "
+                                "(ctx U[128,2048]) + 16 prefills (prompt U[32,512])"),
+                   "tokens_per_iteration": T, "requests": B, "decodes": work["n_dec"], "prefills": work["n_pre"],
+                   "max_bs": B, "seed": args.seed},
+        "roofline": roofline,
+        "generated_tokens_per_s": round(B / (ms_step * 1e-3), 1),
+        "gpu_kernel_ms_per_step": round(gpu_ms, 3),
+        "gemm_mfma": {"tflops": round(gemm_flops / (gemm_ms * 1e-3) / 1e12, 1),
+                      "frac": round(gemm_flops / (gemm_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)},
+        "attention": {"bound": "hbm", "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                      "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "avg_launch_ms": round(at["avg_ms"], 4),
+                      "bytes_per_launch": work["attn_bytes_per_layer"],
+                      "decode_kv_bytes_per_launch": work["attn_decode_bytes_per_layer"]},
+        "kernels_ms_per_step": {k: round(v["ms_per_step"], 3) for k, v in kern.items()},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample ...", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(m.with_layers(args.layers), batch, args.seed)
+    eng.close()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

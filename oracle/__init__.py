@@ -25,6 +25,10 @@ What it computes (fp64 numpy unless stated):
   inputs (textbook scaled-dot-product attention with a causal mask).
 * ``generate`` -- greedy generation one request at a time and under the
   continuous-batching loop.
+* ``precision`` -- optional storage-precision mode: the tensors handed from
+  one operator to the next are rounded to the model dtype (the pages fix no
+  precision; this is the reading the bf16 configurations are checked under,
+  next to the exact fp64 oracle).
 
 Pins (tests marked ``not gpu``) tie each part to facts the pages fix: the
 lecture's continuous-batching timeline, the Figure-3 and Figure-5 counts, the
@@ -34,4 +38,4 @@ invariant.  The pages' worked numbers for the lecture's mini model (max logit
 difference 1.1e-6, 4.88x fewer weight bytes) need that model's code, which the
 pages do not include: parity unpinned for those two figures.
 """
-from . import scheduler, model, flat, brute, generate  # noqa: F401
+from . import scheduler, model, flat, brute, generate, precision  # noqa: F401

@@ -14,6 +14,7 @@ round-off.
 import numpy as np
 
 from . import model as M
+from .precision import store as _store
 
 F64 = np.float64
 
@@ -52,11 +53,12 @@ def padded_pairs(batch):
     return len(batch) * max(n for n, _ in batch) * max(n + c for n, c in batch)
 
 
-def layer_forward_flat(m, w, x, batch, caches):
+def layer_forward_flat(m, w, x, batch, caches, store=None):
     """One layer over the flattened batch.
 
     x: [T, H] rows of all requests' new tokens in batch order; batch: list of
-    (n_new, ctx); caches: per-request dicts 'k','v' of this layer, extended in place.
+    (n_new, ctx); caches: per-request dicts 'k','v' of this layer, extended in place;
+    store: storage dtype of the tensors handed between operators (None: exact).
     """
     x = np.asarray(x, F64)
     T = x.shape[0]
@@ -64,7 +66,7 @@ def layer_forward_flat(m, w, x, batch, caches):
     assert cu[-1] == T
     pos = np.asarray(positions(batch))
     # token-wise: norm + QKV projection on all T rows at once
-    q, k, v = M.qkv_project(m, w, M.norm1(m, w, x), pos)
+    q, k, v = M.qkv_project(m, w, _store(M.norm1(m, w, x), store), pos, store)
     o = np.empty((T, m.nq, m.d), F64)
     # Split -> per-request attention against that request's own history -> Merge
     for i, (n_new, ctx) in enumerate(batch):
@@ -75,12 +77,12 @@ def layer_forward_flat(m, w, x, batch, caches):
         c["v"] = np.concatenate([c["v"], v[rows]], axis=0)
         o[rows] = M.attention(q[rows], c["k"], c["v"], ctx, m.group)
     # token-wise again on the merged tensor
-    x = x + M.linear(o.reshape(T, m.nq * m.d), w["w_o"], w.get("b_o"))
-    x = x + M.ffn(m, w, M.norm2(m, w, x))
+    x = x + M.linear(_store(o, store).reshape(T, m.nq * m.d), w["w_o"], w.get("b_o"))
+    x = x + M.ffn(m, w, _store(M.norm2(m, w, x), store), store)
     return x
 
 
-def forward_flat(m, W, batch_ids, batch, caches):
+def forward_flat(m, W, batch_ids, batch, caches, store=None):
     """Whole model over a flattened batch.
 
     batch_ids: per-request lists of new token ids; caches[i][layer] per request.
@@ -93,8 +95,8 @@ def forward_flat(m, W, batch_ids, batch, caches):
         x = x + np.asarray(W["pos_emb"], F64)[pos]
     outs = []
     for l, w in enumerate(W["layers"]):
-        x = layer_forward_flat(m, w, x, batch, [c[l] for c in caches])
+        x = layer_forward_flat(m, w, x, batch, [c[l] for c in caches], store)
         outs.append(x)
     lr = last_rows(batch)
-    logits = M.linear(M.final_norm(m, W, x[lr]), W["w_lm"])
+    logits = M.linear(_store(M.final_norm(m, W, x[lr]), store), W["w_lm"])
     return outs, logits

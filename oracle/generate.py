@@ -14,23 +14,23 @@ from . import flat as FL
 from .scheduler import replay
 
 
-def generate_one_at_a_time(m, W, prompt, out_len):
+def generate_one_at_a_time(m, W, prompt, out_len, store=None):
     """Returns (tokens, margins): ``out_len`` greedy tokens for one request run alone."""
     cache = M.new_cache(m)
     toks, margins = [], []
-    _, logits = M.forward_request(m, W, list(prompt), 0, cache)
+    _, logits = M.forward_request(m, W, list(prompt), 0, cache, store)
     toks.append(M.greedy(logits))
     margins.append(M.top2_margin(logits))
     ctx = len(prompt)
     while len(toks) < out_len:
-        _, logits = M.forward_request(m, W, [toks[-1]], ctx, cache)
+        _, logits = M.forward_request(m, W, [toks[-1]], ctx, cache, store)
         toks.append(M.greedy(logits))
         margins.append(M.top2_margin(logits))
         ctx += 1
     return toks, margins
 
 
-def generate_continuous(m, W, reqs, max_bs, n_slots, record=None):
+def generate_continuous(m, W, reqs, max_bs, n_slots, record=None, store=None):
     """Greedy generation of ``reqs`` under the iteration-level scheduler.
 
     Each iteration runs the flattened selective-batched forward over the
@@ -47,7 +47,7 @@ def generate_continuous(m, W, reqs, max_bs, n_slots, record=None):
         ids = []
         for rid, n_new, ctx in work:
             ids.append(list(by_id[rid].prompt) if ctx == 0 and not toks[rid] else [toks[rid][-1]])
-        outs, logits = FL.forward_flat(m, W, ids, batch, [caches[rid] for rid, _, _ in work])
+        outs, logits = FL.forward_flat(m, W, ids, batch, [caches[rid] for rid, _, _ in work], store)
         for i, (rid, _, _) in enumerate(work):
             toks[rid].append(M.greedy(logits[i]))
         if record is not None:

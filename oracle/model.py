@@ -21,6 +21,8 @@ attention) but not the model's details; the readings used here are:
 import numpy as np
 from scipy.special import erf
 
+from .precision import store as _store
+
 F64 = np.float64
 
 
@@ -119,45 +121,50 @@ def linear(x, w, b=None):
     return y
 
 
-def qkv_project(m, w, h, pos):
-    """q [L,nq,d], k [L,nkv,d], v [L,nkv,d] of the new tokens (RoPE applied for Llama)."""
+def qkv_project(m, w, h, pos, store=None):
+    """q [L,nq,d], k [L,nkv,d], v [L,nkv,d] of the new tokens (RoPE applied for Llama).
+
+    ``store``: storage dtype of the projection and of the rotated q, k (None: exact)."""
     L = h.shape[0]
-    qkv = linear(h, w["w_qkv"], w.get("b_qkv"))
+    qkv = _store(linear(h, w["w_qkv"], w.get("b_qkv")), store)
     nq_d, nkv_d = m.nq * m.d, m.nkv * m.d
     q = qkv[:, :nq_d].reshape(L, m.nq, m.d)
     k = qkv[:, nq_d:nq_d + nkv_d].reshape(L, m.nkv, m.d)
     v = qkv[:, nq_d + nkv_d:].reshape(L, m.nkv, m.d)
     if m.arch == "llama":
-        q = rope(q, pos, m.rope_theta)
-        k = rope(k, pos, m.rope_theta)
+        q = _store(rope(q, pos, m.rope_theta), store)
+        k = _store(rope(k, pos, m.rope_theta), store)
     return q, k, v
 
 
-def ffn(m, w, h):
+def ffn(m, w, h, store=None):
+    """Feed-forward block; the activation output (the second linear's input) is stored in ``store``."""
     if m.arch == "gpt":
-        return linear(gelu(linear(h, w["w1"], w["b1"])), w["w2"], w["b2"])
+        g = gelu(linear(h, w["w1"], w["b1"]))
+        return linear(_store(g, store), w["w2"], w["b2"])
     gu = linear(h, w["w1"])
     g = silu(gu[:, :m.F]) * gu[:, m.F:]
-    return linear(g, w["w2"])
+    return linear(_store(g, store), w["w2"])
 
 
-def layer_forward(m, w, x, ctx, cache):
+def layer_forward(m, w, x, ctx, cache, store=None):
     """One decoder layer for one request.
 
     x: [L, H] hidden rows of the new tokens; cache: dict with 'k', 'v' arrays
     [ctx, nkv, d] of this layer (extended in place with the new rows).
+    ``store``: storage dtype of the tensors handed between operators (None: exact).
     Returns the layer's output rows [L, H].
     """
     x = np.asarray(x, F64)
     L = x.shape[0]
     assert cache["k"].shape[0] == ctx
     pos = ctx + np.arange(L)
-    q, k, v = qkv_project(m, w, norm1(m, w, x), pos)
+    q, k, v = qkv_project(m, w, _store(norm1(m, w, x), store), pos, store)
     cache["k"] = np.concatenate([cache["k"], k], axis=0)
     cache["v"] = np.concatenate([cache["v"], v], axis=0)
-    o = attention(q, cache["k"], cache["v"], ctx, m.group)
+    o = _store(attention(q, cache["k"], cache["v"], ctx, m.group), store)
     x = x + linear(o.reshape(L, m.nq * m.d), w["w_o"], w.get("b_o"))
-    x = x + ffn(m, w, norm2(m, w, x))
+    x = x + ffn(m, w, _store(norm2(m, w, x), store), store)
     return x
 
 
@@ -173,8 +180,8 @@ def embed(m, W, ids, ctx):
     return x
 
 
-def lm_logits(m, W, x_last):
-    return linear(final_norm(m, W, np.asarray(x_last, F64)[None, :]), W["w_lm"])[0]
+def lm_logits(m, W, x_last, store=None):
+    return linear(_store(final_norm(m, W, np.asarray(x_last, F64)[None, :]), store), W["w_lm"])[0]
 
 
 def greedy(logits):
@@ -182,14 +189,14 @@ def greedy(logits):
     return int(np.argmax(logits))
 
 
-def forward_request(m, W, ids, ctx, cache):
+def forward_request(m, W, ids, ctx, cache, store=None):
     """All layers for one request's new tokens; returns (layer outputs, logits of the last token)."""
     x = embed(m, W, ids, ctx)
     outs = []
     for l, w in enumerate(W["layers"]):
-        x = layer_forward(m, w, x, ctx, cache[l])
+        x = layer_forward(m, w, x, ctx, cache[l], store)
         outs.append(x)
-    return outs, lm_logits(m, W, x[-1])
+    return outs, lm_logits(m, W, x[-1], store)
 
 
 def top2_margin(logits):

@@ -17,7 +17,9 @@
 // Tiling (CDNA4, 64-wide waves): S^T = K Q^T and O^T = V^T P^T on 16x16
 // MFMA tiles, so that a query row lives in lane % 16 for both products and
 // the softmax rescale needs no cross-lane moves.  The 32-key chunk is
-// ordered so the S^T accumulators are directly the bf16 P^T operand.
+// ordered so the S^T accumulators are directly the bf16 P^T operand; P is
+// fed as a hi + lo pair of bf16 values (two MFMAs), which keeps P.V at about
+// fp32 accuracy -- decode is HBM-bound, so the extra MFMA is free there.
 //   MODE_KEYS (<= 16 rows: decode, small chunks): the 4 waves take interleaved
 //     32-key chunks; K/V go straight from HBM into MFMA operand registers
 //     (16-byte loads); the 4 partial softmax states merge through LDS.
@@ -137,10 +139,14 @@ __device__ __forceinline__ void chunk_bf16(const AttnArgs& a, WaveState<D>& st, 
     softmax_chunk(sc, st.m, st.l, alpha);
 #pragma unroll
     for (int i = 0; i < D / 16; ++i) st.o[i] *= alpha;
-    // P^T operand: keys 8g..8g+7 of the chunk for row lr
-    union { bf16x8 v; uint16_t h[8]; } pp;
+    // P^T operand: keys 8g..8g+7 of the chunk for row lr, as hi + lo bf16 parts
+    // (p - bf16(p) is exact in fp32), so P.V keeps ~16 significant bits of p
+    union { bf16x8 v; uint16_t h[8]; } pp, pl;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) pp.h[i] = f2bf(sc[i]);
+    for (int i = 0; i < 8; ++i) {
+        pp.h[i] = f2bf(sc[i]);
+        pl.h[i] = f2bf(sc[i] - bf2f(pp.h[i]));
+    }
     // V^T operand: V[keys cb+8g .. +8][dim 16db + lr] = 16 contiguous bytes of the blocked layout
     const int k8 = cb + 8 * g;
     const bool any = k8 < key_end;
@@ -162,7 +168,9 @@ __device__ __forceinline__ void chunk_bf16(const AttnArgs& a, WaveState<D>& st, 
                 if (!any || k8 + i >= key_end) vv.h[i] = 0;
             vraw = vv.v;
         }
-        st.o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vraw), pp.v, st.o[db], 0, 0, 0);
+        const bf16x8 vv8 = __builtin_bit_cast(bf16x8, vraw);
+        st.o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv8, pp.v, st.o[db], 0, 0, 0);
+        st.o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv8, pl.v, st.o[db], 0, 0, 0);
     }
 }
 

@@ -43,9 +43,9 @@ class DeviceWeights:
     """Weights resident in HBM in the model dtype, plus the ABI structs pointing at them.
 
     ``host``: dict of numpy arrays (layout of ``synth.make_weights``), copied
-    exactly; or None with ``seed``: random init on the device (N(0, 0.02)
-    matrices and biases, gains 1 + N(0, 0.1)) for runs that do not compare
-    against the oracle.
+    exactly; or None with ``seed``: random init on the device (matrices
+    N(0, min(0.02, fan_in^-1/2)^2), embeddings and biases N(0, 0.02^2), gains
+    1 + N(0, 0.1^2)) for runs that do not compare against the oracle.
     """
 
     def __init__(self, m, dtype: str, host=None, seed=0, device="cuda", layers=None, with_head=True):
@@ -56,6 +56,9 @@ class DeviceWeights:
 
         def put(arr):
             return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).to(device=device).to(tdt)
+
+        def wstd(fan_in):
+            return min(0.02, fan_in ** -0.5)
 
         def rnd(shape, std, mean=0.0):
             t = torch.empty(shape, dtype=tdt, device=device)
@@ -71,9 +74,9 @@ class DeviceWeights:
                 t = {k: (put(hw[k]) if k in hw else None) for k in LAYER_KEYS}
             else:
                 f1 = m.F if gpt else 2 * m.F
-                t = {"ln1_g": rnd((m.H,), 0.1, 1.0), "w_qkv": rnd((m.qkv_out, m.H), 0.02),
-                     "w_o": rnd((m.H, m.nq * m.d), 0.02), "ln2_g": rnd((m.H,), 0.1, 1.0),
-                     "w1": rnd((f1, m.H), 0.02), "w2": rnd((m.H, m.F), 0.02)}
+                t = {"ln1_g": rnd((m.H,), 0.1, 1.0), "w_qkv": rnd((m.qkv_out, m.H), wstd(m.H)),
+                     "w_o": rnd((m.H, m.nq * m.d), wstd(m.nq * m.d)), "ln2_g": rnd((m.H,), 0.1, 1.0),
+                     "w1": rnd((f1, m.H), wstd(m.H)), "w2": rnd((m.H, m.F), wstd(m.F))}
                 for k in ("ln1_b", "b_qkv", "b_o", "ln2_b", "b1", "b2"):
                     t[k] = None
                 if gpt:
@@ -86,7 +89,7 @@ class DeviceWeights:
             if host is not None:
                 self.model = {k: (put(host[k]) if k in host else None) for k in MODEL_KEYS}
             else:
-                self.model = {"tok_emb": rnd((m.V, m.H), 0.02), "w_lm": rnd((m.V, m.H), 0.02),
+                self.model = {"tok_emb": rnd((m.V, m.H), 0.02), "w_lm": rnd((m.V, m.H), wstd(m.H)),
                               "lnf_g": rnd((m.H,), 0.1, 1.0), "lnf_b": rnd((m.H,), 0.02) if gpt else None,
                               "pos_emb": rnd((m.max_pos, m.H), 0.02) if gpt else None}
         self.layer_structs = [sb_layer_weights(**{k: _addr(t[k]) for k in LAYER_KEYS}) for t in self.layers]

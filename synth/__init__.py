@@ -25,6 +25,8 @@ from .configs import (  # noqa: F401
     LLAMA8B,
     GPT175B_LAYER,
     make_weights,
+    init_std,
+    kv_std,
     make_layer_weights,
     qkv_rows,
     ffn1_rows,

@@ -9,15 +9,30 @@ Weight layout (shared convention of both sides, data only):
   * GPT-style layers carry biases and LayerNorm (gamma, beta); Llama-style
     layers carry RMSNorm gamma only and no biases.
 
-Initialisation: matrices, embeddings and biases are N(0, 0.02^2); norm gains
-are 1 + N(0, 0.1^2) and LayerNorm shifts N(0, 0.02^2), so that a kernel that
-drops a gain or a shift is caught by a parity test.
+Initialisation: every matrix is N(0, s^2) with s = min(0.02, 1/sqrt(fan_in));
+embeddings and biases N(0, 0.02^2); norm gains 1 + N(0, 0.1^2) and LayerNorm
+shifts N(0, 0.02^2), so that a kernel that drops a gain or a shift is caught by
+a parity test.  s = 0.02 for the toy and mini shapes (fan_in <= 2500); for
+hidden sizes of 4096 and 12288 the 1/sqrt(fan_in) cap keeps projections near
+unit variance -- with 0.02 there, attention scores would have a standard
+deviation of ~5 (near one-hot softmax), and the layer output would jump with
+single-ulp differences of its inputs.
 """
 from dataclasses import dataclass, replace
 
 import numpy as np
 
 from .gen import normal
+
+
+def init_std(fan_in: int) -> float:
+    """Standard deviation of a random weight matrix with ``fan_in`` inputs."""
+    return min(0.02, fan_in ** -0.5)
+
+
+def kv_std(m) -> float:
+    """Scale of synthetic cached K/V rows: that of a normalised row times a projection matrix."""
+    return min(0.02 * m.H ** 0.5, 1.0)
 
 
 @dataclass(frozen=True)
@@ -73,11 +88,11 @@ def make_layer_weights(m: ModelDims, seed: int, layer: int, dtype: str) -> dict:
     H, F = m.H, m.F
     w = {}
     w["ln1_g"] = normal(seed, p + "ln1_g", (H,), std=0.1, mean=1.0, dtype=dtype)
-    w["w_qkv"] = normal(seed, p + "w_qkv", (m.qkv_out, H), std=0.02, dtype=dtype)
-    w["w_o"] = normal(seed, p + "w_o", (H, m.nq * m.d), std=0.02, dtype=dtype)
+    w["w_qkv"] = normal(seed, p + "w_qkv", (m.qkv_out, H), std=init_std(H), dtype=dtype)
+    w["w_o"] = normal(seed, p + "w_o", (H, m.nq * m.d), std=init_std(m.nq * m.d), dtype=dtype)
     w["ln2_g"] = normal(seed, p + "ln2_g", (H,), std=0.1, mean=1.0, dtype=dtype)
-    w["w1"] = normal(seed, p + "w1", (ffn1_rows(m), H), std=0.02, dtype=dtype)
-    w["w2"] = normal(seed, p + "w2", (H, F), std=0.02, dtype=dtype)
+    w["w1"] = normal(seed, p + "w1", (ffn1_rows(m), H), std=init_std(H), dtype=dtype)
+    w["w2"] = normal(seed, p + "w2", (H, F), std=init_std(F), dtype=dtype)
     if m.arch == "gpt":
         w["ln1_b"] = normal(seed, p + "ln1_b", (H,), std=0.02, dtype=dtype)
         w["b_qkv"] = normal(seed, p + "b_qkv", (m.qkv_out,), std=0.02, dtype=dtype)
@@ -93,7 +108,7 @@ def make_weights(m: ModelDims, seed: int, dtype: str, layers=None) -> dict:
     w = {"layers": []}
     if m.V > 0:
         w["tok_emb"] = normal(seed, "tok_emb", (m.V, m.H), std=0.02, dtype=dtype)
-        w["w_lm"] = normal(seed, "w_lm", (m.V, m.H), std=0.02, dtype=dtype)
+        w["w_lm"] = normal(seed, "w_lm", (m.V, m.H), std=init_std(m.H), dtype=dtype)
     if m.arch == "gpt" and m.max_pos > 0 and m.V > 0:
         w["pos_emb"] = normal(seed, "pos_emb", (m.max_pos, m.H), std=0.02, dtype=dtype)
     w["lnf_g"] = normal(seed, "lnf_g", (m.H,), std=0.1, mean=1.0, dtype=dtype)

@@ -337,3 +337,37 @@ def test_continuous_equals_one_at_a_time_timeline():
     for r in reqs:
         solo, _ = G.generate_one_at_a_time(m, W, r.prompt, r.out_len)
         assert toks[r.rid] == solo
+
+
+# ---------------------------------------------------------------- storage precision
+def test_round_to_bf16_matches_library_and_ties():
+    import torch
+    from oracle.precision import round_to_bf16, store
+    x = np.concatenate([normal(20, "r", (5000,), std=s).astype(np.float64) for s in (1e-30, 1e-3, 1.0, 1e4, 1e30)])
+    want = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(round_to_bf16(x), want)
+    # halfway cases go to the even neighbour: 1 + 2^-8 -> 1; 1 + 3*2^-8 -> 1 + 2^-6
+    np.testing.assert_array_equal(round_to_bf16([1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8)]),
+                                  [1.0, 1 + 2 ** -6, -1.0])
+    np.testing.assert_array_equal(store(x, None), x)
+    np.testing.assert_array_equal(store(x, "fp32"), x.astype(np.float32).astype(np.float64))
+
+
+@pytest.mark.parametrize("m", [TINY_GPT, TINY_LLAMA])
+def test_storage_mode_fp32_is_exact_and_bf16_is_close(m):
+    W = make_weights(m, 7, "bf16")
+    batch = [(3, 0), (1, 4)]
+    ids = [[1, 2, 3], [7]]
+    res = {}
+    for st in (None, "fp32", "bf16"):
+        caches = [M.new_cache(m), M.new_cache(m)]
+        for i, (n, c) in enumerate(batch):
+            if c:
+                M.forward_request(m, W, list(range(c)), 0, caches[i], st)
+        res[st] = FL.forward_flat(m, W, ids, batch, caches, st)
+    for l in range(m.n_layers):
+        ex = res[None][0][l]
+        scale = np.sqrt(np.mean(ex ** 2))
+        assert np.max(np.abs(res["fp32"][0][l] - ex)) <= 1e-6 * scale
+        err_bf16 = np.max(np.abs(res["bf16"][0][l] - ex))
+        assert 1e-5 * scale < err_bf16 <= 5e-2 * scale        # it does round, and only at bf16 level
