@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--layers", type=int, default=32, help="decoder layers (the workload has 32)")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="run one 1 GiB device-to-device copy before the steps (calibrates HBM counters)")
     return ap.parse_args()
 
 
@@ -158,6 +160,12 @@ def main():
         assert res is not None and len(res["ids"]) == B and int(res["n_new"].sum()) == T
         return res
 
+    if args.calib_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
