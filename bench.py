@@ -191,7 +191,8 @@ def main():
     f1 = kern["gemm_ffn1"]
     f1_flops = work["gemm_per_layer"]["ffn1"]
     f1_tflops = f1_flops / (f1["avg_ms"] * 1e-3) / 1e12
-    roofline = {"kernel": "gemm_bf16_kernel<128,128,SWIGLU> (FFN1 gate/up + SiLU*up)", "bound": "mfma",
+    kern_name = "gemm_bf16_dma_kernel<2,4,SWIGLU> (FFN1 gate/up GEMM + SiLU*up epilogue)"
+    roofline = {"kernel": kern_name, "bound": "mfma",
                 "achieved": round(f1_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(f1_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
                 "flops_per_launch": f1_flops, "avg_launch_ms": round(f1["avg_ms"], 4)}

@@ -5,12 +5,16 @@
 // ("连续批处理完全拆解", section 观察; "CS349D Lecture 2", section 4.2).  T is
 // arbitrary (ragged), so rows beyond T are masked; N and K come from the model.
 //
-// bf16: v_mfma_f32_16x16x32_bf16 tiles, 256-thread workgroups (2 x 2 waves),
-// double-buffered LDS stages fed by 16-byte global loads, padded LDS rows
-// (no bank conflicts on the 16-byte operand reads), XCD-aware tile order.
+// bf16: v_mfma_f32_16x16x32_bf16 tiles; 256 x 256 workgroup tiles of 8 waves
+// (wave tile 128 x 64, two waves per SIMD) for large GEMMs, 128 x 128 for
+// small ones; two LDS stages fed two K tiles ahead by 16-byte global loads,
+// padded LDS rows (no bank conflicts on the 16-byte operand reads), XCD-aware
+// grouped tile order.
 // fp32: a plain LDS-tiled FMA kernel with a fixed, sequential K order.
 // Epilogues fuse bias, exact GeLU, SwiGLU (SiLU(gate) * up) or the residual
 // add into the fp32 stream x.
+#include <cstdlib>
+
 #include "sb_device.h"
 
 namespace sb {
@@ -49,27 +53,33 @@ __device__ __forceinline__ void swiglu_store(const GemmArgs& a, int m, int f, fl
 }
 
 // ================================================================== bf16 MFMA
-// Workgroup tile BM x BN (BN counts W rows; for SwiGLU half are gate rows,
-// half up rows), 4 waves as 2 x 2, wave tile WM x WN of 16 x 16 MFMA blocks.
-template <int BM, int BN, int EPI>
-__global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
+// Workgroup tile BM x BN (BN counts W rows; for SwiGLU each wave's WN rows
+// are WN/2 gate rows then the matching WN/2 up rows), WAVES_M x WAVES_N waves,
+// wave tile WM x WN of 16 x 16 MFMA blocks, K in steps of 64 through two LDS
+// stages.  Each output element is one MFMA chain over K in ascending 32-wide
+// steps, whatever the tile shape: results do not depend on M or on the tile a
+// row falls in.
+template <int BM, int BN, int WAVES_M, int WAVES_N, int EPI>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_bf16_kernel(GemmArgs a) {
+    constexpr int THREADS = 64 * WAVES_M * WAVES_N;
     constexpr int BK = 64, LDSK = BK + 8;            // 144-byte rows: conflict-free 16-byte reads
-    constexpr int WM = BM / 2, WN = BN / 2;
+    constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
     constexpr int MI = WM / 16, NI = WN / 16;
     constexpr int CH = BK / 8;                       // 16-byte chunks per row
-    constexpr int A_CH = BM * CH / 256, B_CH = BN * CH / 256;
+    constexpr int A_CH = BM * CH / THREADS, B_CH = BN * CH / THREADS;
+    static_assert(A_CH * THREADS == BM * CH && B_CH * THREADS == BN * CH, "tile / thread mismatch");
     __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LDSK];
     __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * LDSK];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
     const int tiles_m = (a.M + BM - 1) / BM;
     const int out_cols = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
     const int tiles_n = (a.N + out_cols - 1) / out_cols;
     const int total = tiles_m * tiles_n;
     const int pid = xcd_remap(blockIdx.x, total);
     // grouped order: GROUP_M row tiles sweep the column tiles together (L2 reuse of both operands)
-    constexpr int GROUP_M = 8;
+    constexpr int GROUP_M = 4;
     const int per_group = GROUP_M * tiles_n;
     const int grp = pid / per_group;
     const int first_m = grp * GROUP_M;
@@ -86,15 +96,14 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
     const uint16_t* pb[B_CH];
 #pragma unroll
     for (int q = 0; q < A_CH; ++q) {
-        const int c = tid + 256 * q, row = c / CH, kc = (c % CH) * 8;
+        const int c = tid + THREADS * q, row = c / CH, kc = (c % CH) * 8;
         pa[q] = A + (long long)min(m0 + row, a.M - 1) * a.lda + kc;
     }
 #pragma unroll
     for (int q = 0; q < B_CH; ++q) {
-        const int c = tid + 256 * q, row = c / CH, kc = (c % CH) * 8;
+        const int c = tid + THREADS * q, row = c / CH, kc = (c % CH) * 8;
         int gr;
         if (EPI == EPI_SWIGLU) {
-            // LDS rows [wn*WN, wn*WN + WN/2) are gate rows, the next WN/2 the matching up rows
             const int w = row / WN, cc = row % WN;
             const int f = tn * (BN / 2) + w * (WN / 2) + (cc % (WN / 2));
             gr = min(f, a.N - 1) + (cc >= WN / 2 ? a.F : 0);
@@ -114,12 +123,12 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
     auto stash = [&](int buf) {
 #pragma unroll
         for (int q = 0; q < A_CH; ++q) {
-            const int c = tid + 256 * q;
+            const int c = tid + THREADS * q;
             *(u32x4*)&As[buf][(c / CH) * LDSK + (c % CH) * 8] = ra[q];
         }
 #pragma unroll
         for (int q = 0; q < B_CH; ++q) {
-            const int c = tid + 256 * q;
+            const int c = tid + THREADS * q;
             *(u32x4*)&Bs[buf][(c / CH) * LDSK + (c % CH) * 8] = rb[q];
         }
     };
@@ -140,18 +149,17 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
         if (kt + 1 < nk) load((kt + 1) * BK);
 #pragma unroll
         for (int ks = 0; ks < BK / 32; ++ks) {
-            bf16x8 af[MI], bfr[NI];
-#pragma unroll
-            for (int i = 0; i < MI; ++i)
-                af[i] = __builtin_bit_cast(bf16x8, *(const u32x4*)&As[buf][(wm * WM + i * 16 + lrow) * LDSK + ks * 32 + lk]);
+            bf16x8 bfr[NI];
 #pragma unroll
             for (int j = 0; j < NI; ++j)
                 bfr[j] = __builtin_bit_cast(bf16x8, *(const u32x4*)&Bs[buf][(wn * WN + j * 16 + lrow) * LDSK + ks * 32 + lk]);
 #pragma unroll
-            for (int i = 0; i < MI; ++i)
+            for (int i = 0; i < MI; ++i) {
+                const bf16x8 af = __builtin_bit_cast(bf16x8, *(const u32x4*)&As[buf][(wm * WM + i * 16 + lrow) * LDSK + ks * 32 + lk]);
 #pragma unroll
                 for (int j = 0; j < NI; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfr[j], acc[i][j], 0, 0, 0);
+            }
         }
         if (kt + 1 < nk) stash(buf ^ 1);
         __syncthreads();
@@ -172,6 +180,165 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
                 }
     } else {
         const int nbase = tn * BN + wn * WN + lrow;
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int j = 0; j < NI; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int m = rbase + i * 16 + r, n = nbase + j * 16;
+                    if (m < a.M && n < a.N) epi_store<SB_BF16, EPI>(a, m, n, acc[i][j][r]);
+                }
+    }
+}
+
+// ================================================================== bf16 MFMA, LDS-DMA pipeline
+// 256 x 256 x 32 tiles, 8 waves (2 x 4, wave tile 128 x 64), four LDS stages
+// filled three K tiles ahead by global_load_lds_dwordx4 (16 bytes per lane
+// from global memory straight into LDS, no staging registers).  The DMA puts
+// lane i's 16 bytes at stage base + 16 i, so a wave instruction fills 16 rows
+// x 4 chunks; lane i loads chunk (i % 4) ^ sw(row) of row i / 4, with
+// sw(row) = (row / 2) % 4, which makes the 16-byte operand reads of 8
+// consecutive rows hit 8 different bank groups.  Each stage is its own LDS
+// object so the compiler's wait-count tracking can tell stages apart.
+template <int WAVES_M_, int WAVES_N_>
+struct DmaCfg {
+    static constexpr int BM = 256, BN = 256, BK = 32, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
+    static constexpr int THREADS = 64 * WAVES_M * WAVES_N;
+    static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N, MI = WM / 16, NI = WN / 16;
+    static constexpr int STAGE_ELEMS = BM * BK;                 // bf16 elements of one operand tile (16 KB)
+    static constexpr int A_INSTR = BM / 16 / (THREADS / 64);    // 16-row blocks per wave per stage
+    static constexpr int B_INSTR = BN / 16 / (THREADS / 64);
+};
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef const __attribute__((address_space(1))) void gbl_void;
+
+// vmcnt <= n (other counters untouched): gfx9 encoding, vmcnt in bits 3:0 and 15:14
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+template <int WAVES_M_, int WAVES_N_, int EPI>
+__global__ __launch_bounds__(64 * WAVES_M_ * WAVES_N_) void gemm_bf16_dma_kernel(GemmArgs a) {
+    using C = DmaCfg<WAVES_M_, WAVES_N_>;
+    constexpr int BM = C::BM, BN = C::BN, BK = C::BK, WAVES_N = C::WAVES_N;
+    constexpr int WM = C::WM, WN = C::WN, MI = C::MI, NI = C::NI;
+    constexpr int STAGE_ELEMS = C::STAGE_ELEMS, A_INSTR = C::A_INSTR, B_INSTR = C::B_INSTR;
+    __shared__ __attribute__((aligned(1024))) uint16_t A0[STAGE_ELEMS], A1[STAGE_ELEMS], A2[STAGE_ELEMS], A3[STAGE_ELEMS];
+    __shared__ __attribute__((aligned(1024))) uint16_t B0[STAGE_ELEMS], B1[STAGE_ELEMS], B2[STAGE_ELEMS], B3[STAGE_ELEMS];
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+    const int tiles_m = (a.M + BM - 1) / BM;
+    const int out_cols = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
+    const int tiles_n = (a.N + out_cols - 1) / out_cols;
+    const int total = tiles_m * tiles_n;
+    const int pid = xcd_remap(blockIdx.x, total);
+    constexpr int GROUP_M = 4;
+    const int per_group = GROUP_M * tiles_n;
+    const int grp = pid / per_group;
+    const int first_m = grp * GROUP_M;
+    const int gsz = min(tiles_m - first_m, GROUP_M);
+    const int tm = first_m + (pid % per_group) % gsz;
+    const int tn = (pid % per_group) / gsz;
+    const int m0 = tm * BM;
+
+    // this lane's source chunk inside a 16-row block
+    const int brow = lane >> 2;                        // row inside the block
+    const int bchunk = (lane & 3) ^ ((brow >> 1) & 3);  // K chunk it fetches
+    const uint16_t* A = (const uint16_t*)a.A;
+    const uint16_t* W = (const uint16_t*)a.W;
+    // element offsets (32-bit: every operand here is < 2^31 elements) of this lane's source chunks
+    int srcA[A_INSTR];
+    int srcB[B_INSTR];
+#pragma unroll
+    for (int j = 0; j < A_INSTR; ++j) {
+        const int row = (wave * A_INSTR + j) * 16 + brow;
+        srcA[j] = min(m0 + row, a.M - 1) * (int)a.lda + bchunk * 8;
+    }
+#pragma unroll
+    for (int j = 0; j < B_INSTR; ++j) {
+        const int row = (wave * B_INSTR + j) * 16 + brow;
+        int gr;
+        if (EPI == EPI_SWIGLU) {
+            const int w = row / WN, cc = row % WN;
+            const int f = tn * (BN / 2) + w * (WN / 2) + (cc % (WN / 2));
+            gr = min(f, a.N - 1) + (cc >= WN / 2 ? a.F : 0);
+        } else {
+            gr = min(tn * BN + row, a.N - 1);
+        }
+        srcB[j] = gr * (int)a.ldw + bchunk * 8;
+    }
+    auto issue = [&](uint16_t* As, uint16_t* Bs, int k0) {
+#pragma unroll
+        for (int j = 0; j < A_INSTR; ++j)
+            __builtin_amdgcn_global_load_lds((gbl_void*)(A + (srcA[j] + k0)), (lds_void*)(As + (wave * A_INSTR + j) * 512), 16, 0, 0);
+#pragma unroll
+        for (int j = 0; j < B_INSTR; ++j)
+            __builtin_amdgcn_global_load_lds((gbl_void*)(W + (srcB[j] + k0)), (lds_void*)(Bs + (wave * B_INSTR + j) * 512), 16, 0, 0);
+    };
+
+    f32x4 acc[MI][NI];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NI; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int lr = lane & 15, lc = lane >> 4;
+    const int rd = lr * BK + ((lc ^ ((lr >> 1) & 3)) * 8);   // element offset of this lane's operand in a block
+    auto compute = [&](const uint16_t* As, const uint16_t* Bs) {
+        bf16x8 bfr[NI];
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
+            bfr[j] = __builtin_bit_cast(bf16x8, *(const u32x4*)(Bs + ((wn * WN) / 16 + j) * 512 + rd));
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+            const bf16x8 af = __builtin_bit_cast(bf16x8, *(const u32x4*)(As + ((wm * WM) / 16 + i) * 512 + rd));
+#pragma unroll
+            for (int j = 0; j < NI; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfr[j], acc[i][j], 0, 0, 0);
+        }
+    };
+
+    // per wave, one K tile = A_INSTR + B_INSTR DMA instructions in flight
+    constexpr int PER = A_INSTR + B_INSTR;
+    const int nk = a.K / BK;
+    issue(A0, B0, 0);
+    if (nk > 1) issue(A1, B1, BK);
+    if (nk > 2) issue(A2, B2, 2 * BK);
+    auto step = [&](int kt, uint16_t* Ac, uint16_t* Bc, uint16_t* An, uint16_t* Bn) {
+        if (kt + 2 < nk) wait_vmcnt<2 * PER>();
+        else if (kt + 1 < nk) wait_vmcnt<PER>();
+        else wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();                 // every wave's tile kt is in LDS; stage (kt+3)%4 is free
+        if (kt + 3 < nk) issue(An, Bn, (kt + 3) * BK);
+        compute(Ac, Bc);
+        __builtin_amdgcn_sched_barrier(0);            // keep each tile's operands local to its step
+    };
+    // K % 128 == 0 (checked by the launcher): whole trips of four stages, no early exits
+    for (int kt = 0; kt < nk; kt += 4) {
+        step(kt, A0, B0, A3, B3);
+        step(kt + 1, A1, B1, A0, B0);
+        step(kt + 2, A2, B2, A1, B1);
+        step(kt + 3, A3, B3, A2, B2);
+    }
+
+    const int rbase = m0 + wm * WM + (lane >> 4) * 4;
+    if (EPI == EPI_SWIGLU) {
+        const int fbase = tn * (BN / 2) + wn * (WN / 2) + lr;
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int j = 0; j < NI / 2; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int m = rbase + i * 16 + r, f = fbase + j * 16;
+                    if (m < a.M && f < a.N) swiglu_store<SB_BF16>(a, m, f, acc[i][j][r], acc[i][j + NI / 2][r]);
+                }
+    } else {
+        const int nbase = tn * BN + wn * WN + lr;
 #pragma unroll
         for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -251,13 +418,51 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
     }
 }
 
-template <int EPI>
-int launch_bf16(const GemmArgs& a, hipStream_t s) {
-    constexpr int BM = 128, BN = 128;
+// Tile configurations of the bf16 kernel: {BM, BN, waves along M, waves along N}.
+enum { CFG_128x128_4W = 0, CFG_256x256_4W, CFG_256x256_8W, CFG_256x128_4W, CFG_128x256_4W, CFG_DMA_8W, CFG_DMA_4W, CFG_COUNT };
+
+template <int BM, int BN, int WMW, int WNW, int EPI>
+int launch_bf16_cfg(const GemmArgs& a, hipStream_t s) {
     const int out_cols = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
     const long long tiles = (long long)((a.M + BM - 1) / BM) * ((a.N + out_cols - 1) / out_cols);
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, EPI>), dim3((unsigned)tiles), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WMW, WNW, EPI>), dim3((unsigned)tiles), dim3(64 * WMW * WNW), 0, s, a);
     return check_launch("gemm_bf16");
+}
+
+template <int WMW, int WNW, int EPI>
+int launch_dma(const GemmArgs& a, hipStream_t s) {
+    if (a.K % 128) return launch_bf16_cfg<256, 256, 2, 4, EPI>(a, s);   // whole four-stage trips only
+    const int out_cols = (EPI == EPI_SWIGLU) ? 128 : 256;
+    const long long tiles = (long long)((a.M + 255) / 256) * ((a.N + out_cols - 1) / out_cols);
+    hipLaunchKernelGGL((gemm_bf16_dma_kernel<WMW, WNW, EPI>), dim3((unsigned)tiles), dim3(64 * WMW * WNW), 0, s, a);
+    return check_launch("gemm_bf16_dma");
+}
+
+// Pick the tile: the largest tiles that still give every CU work; small GEMMs keep 128 x 128.
+int pick_cfg(const GemmArgs& a, int epi) {
+    const char* e = getenv("SB_GEMM_CFG");             // tuning / test override: a CFG_* index
+    if (e && *e) {
+        const int forced = atoi(e);
+        if (forced >= 0 && forced < CFG_COUNT) return forced;
+    }
+    const int ncols = (epi == EPI_SWIGLU) ? 2 * a.N : a.N;
+    const long long big = (long long)((a.M + 255) / 256) * ((ncols + 255) / 256);
+    if (big >= 128 && a.K % 128 == 0) return CFG_DMA_8W;
+    if (big >= 256) return CFG_256x256_8W;
+    return CFG_128x128_4W;
+}
+
+template <int EPI>
+int launch_bf16(const GemmArgs& a, hipStream_t s) {
+    switch (pick_cfg(a, EPI)) {
+        case CFG_256x256_4W: return launch_bf16_cfg<256, 256, 2, 2, EPI>(a, s);
+        case CFG_256x256_8W: return launch_bf16_cfg<256, 256, 2, 4, EPI>(a, s);
+        case CFG_256x128_4W: return launch_bf16_cfg<256, 128, 2, 2, EPI>(a, s);
+        case CFG_128x256_4W: return launch_bf16_cfg<128, 256, 2, 2, EPI>(a, s);
+        case CFG_DMA_8W: return launch_dma<2, 4, EPI>(a, s);
+        case CFG_DMA_4W: return launch_dma<2, 2, EPI>(a, s);
+        default: return launch_bf16_cfg<128, 128, 2, 2, EPI>(a, s);
+    }
 }
 
 template <int EPI>

@@ -216,3 +216,33 @@ def test_attention_edge_cases():
     _attention_case(GQA_BF16, "bf16", [(1, 2047)], 4)               # single long decode
     _attention_case(GQA_BF16, "bf16", [(64, 0), (65, 0), (17, 511)], 5)   # tile boundaries
     _attention_case(MINI_ATT, "bf16", [(16, 512), (1, 512), (1, 513)], 6)  # split boundaries
+
+
+@pytest.mark.parametrize("cfg", range(7))
+@pytest.mark.parametrize("epi", ["bias", "gelu", "resid", "swiglu"])
+def test_gemm_every_tile_config(cfg, epi, monkeypatch):
+    """Each bf16 tile configuration (forced) on a ragged shape: M and N not multiples of the tile, K % 128 == 0."""
+    monkeypatch.setenv("SB_GEMM_CFG", str(cfg))
+    M, N, K = 300, 640, 512
+    print_case("gemm cfg", cfg, epi, M, N, K)
+    A = normal(cfg, "A", (M, K), dtype="bf16")
+    W = normal(cfg, "W", (2 * N if epi == "swiglu" else N, K), std=0.05, dtype="bf16")
+    b = normal(cfg, "b", (N,), std=0.5, dtype="bf16")
+    x0 = normal(cfg, "x0", (M, N)).astype(np.float64)
+    code = {"bias": sb.SB_EPI_STORE, "gelu": sb.SB_EPI_GELU, "resid": sb.SB_EPI_RESID, "swiglu": sb.SB_EPI_SWIGLU}[epi]
+    dA, dW, db = dev(A, "bf16"), dev(W, "bf16"), dev(b, "bf16")
+    out = torch.from_numpy(x0.astype(np.float32)).cuda() if epi == "resid" else \
+        torch.zeros((M, N), dtype=torch.bfloat16, device="cuda")
+    bias = None if epi == "swiglu" else db.data_ptr()
+    sb.sb_op_gemm(sb.SB_BF16, code, M, N, K, dA.data_ptr(), K, dW.data_ptr(), K, bias, out.data_ptr(), N, 0,
+                  N if epi == "swiglu" else 0, stream_handle())
+    _sync()
+    lin = OM.linear(A, W[:N], None if epi == "swiglu" else b)
+    if epi == "bias":
+        assert_close_elem(host(out), lin, "bf16", f"cfg {cfg} bias")
+    elif epi == "gelu":
+        assert_close_elem(host(out), OM.gelu(lin), "bf16", f"cfg {cfg} gelu")
+    elif epi == "resid":
+        assert_close_rms(host(out), x0 + lin, TOL["fp32"], f"cfg {cfg} resid")
+    else:
+        assert_close_elem(host(out), OM.silu(OM.linear(A, W[:N])) * OM.linear(A, W[N:]), "bf16", f"cfg {cfg} swiglu")
