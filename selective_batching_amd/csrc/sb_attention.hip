@@ -22,9 +22,10 @@
 // fp32 accuracy -- decode is HBM-bound, so the extra MFMA is free there.
 //   MODE_KEYS (<= 16 rows: decode, small chunks): the 4 waves take interleaved
 //     32-key chunks; K/V go straight from HBM into MFMA operand registers
-//     (16-byte loads); the 4 partial softmax states merge through LDS.
+//     (16-byte loads, the next chunk's loads in flight while the current one
+//     computes); the 4 partial softmax states merge through LDS.
 //   MODE_ROWS (prefill tiles of 64 rows): each wave owns 16 rows; the
-//     workgroup stages 64-key K/V tiles through LDS (double-buffered) so the
+//     workgroup stages 32-key K/V tiles through LDS (double-buffered) so the
 //     4 waves share every K/V byte.
 // Long single-tile items are split into fixed 512-key ranges; their partial
 // states are merged by attn_combine in a fixed order (deterministic and
@@ -174,6 +175,76 @@ __device__ __forceinline__ void chunk_bf16(const AttnArgs& a, WaveState<D>& st, 
     }
 }
 
+// K/V registers of one 32-key chunk for the direct-from-HBM path (MODE_KEYS):
+// K operands of the two S^T blocks and V^T operands of every 16-dim block.
+template <int D>
+struct ChunkRegs {
+    u32x4 k[2][D / 32];
+    u32x4 v[D / 16];
+};
+
+template <int D>
+__device__ __forceinline__ void load_chunk_bf16(ChunkRegs<D>& r, const uint16_t* Kp, const uint16_t* Vp,
+                                                long long kslot0, int cb, int key_end, int lane) {
+    const int lr = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        const int kk = min(cb + 8 * (lr >> 2) + 4 * b + (lr & 3), key_end - 1);   // clamp: masked later
+#pragma unroll
+        for (int s = 0; s < D / 32; ++s) r.k[b][s] = *(const u32x4*)(Kp + (kslot0 + kk) * D + s * 32 + g * 8);
+    }
+    const long long blk = (kslot0 + min(cb + 8 * g, key_end - 1)) >> 3;
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) r.v[db] = *(const u32x4*)(Vp + (blk * D + db * 16 + lr) * 8);
+}
+
+template <int D>
+__device__ __forceinline__ void compute_chunk_bf16(const AttnArgs& a, WaveState<D>& st, const bf16x8 (&qf)[D / 32],
+                                                   const ChunkRegs<D>& r, int cb, int key_end, int row_limit, int lane) {
+    const int lr = lane & 15, g = lane >> 4;
+    (void)lr;
+    float sc[8];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < D / 32; ++s)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, r.k[b][s]), qf[s], acc, 0, 0, 0);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int k = cb + 8 * g + 4 * b + q;
+            sc[4 * b + q] = (k < key_end && k < row_limit) ? acc[q] * a.scale_log2 : kNegInf;
+        }
+    }
+    float alpha;
+    softmax_chunk(sc, st.m, st.l, alpha);
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i) st.o[i] *= alpha;
+    union { bf16x8 v; uint16_t h[8]; } pp, pl;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        pp.h[i] = f2bf(sc[i]);
+        pl.h[i] = f2bf(sc[i] - bf2f(pp.h[i]));
+    }
+    const int k8 = cb + 8 * g;
+    const bool tail = k8 + 8 > key_end, any = k8 < key_end;
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) {
+        u32x4 vraw = r.v[db];
+        if (tail) {
+            union { u32x4 v; uint16_t h[8]; } vv;
+            vv.v = vraw;
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                if (!any || k8 + i >= key_end) vv.h[i] = 0;
+            vraw = vv.v;
+        }
+        const bf16x8 vv8 = __builtin_bit_cast(bf16x8, vraw);
+        st.o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv8, pp.v, st.o[db], 0, 0, 0);
+        st.o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv8, pl.v, st.o[db], 0, 0, 0);
+    }
+}
+
 // ------------------------------------------------------------------ fp32 chunk
 // 16x16x4 fp32 MFMA: S^T block b covers keys cb + 16b + (lane%16) as MFMA rows;
 // lane (g, r) gets keys cb + 16b + 4g + i.  P.V runs one 4-key step per (b, i).
@@ -220,7 +291,7 @@ __device__ __forceinline__ void chunk_f32(const AttnArgs& a, WaveState<D>& st, c
 template <int DT, int D>
 __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     using T = typename Store<DT>::T;
-    constexpr int KT = 64;                                   // keys per LDS stage (MODE_ROWS)
+    constexpr int KT = 32;                                   // keys per LDS stage (MODE_ROWS)
     // MODE_ROWS stages K/V tiles; MODE_KEYS merges wave states: one workgroup
     // uses only one of the two, so they share the LDS allocation.
     constexpr int LDS_K = (DT == SB_BF16) ? 2 * KT * (D + 8) : 0;
@@ -265,8 +336,20 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
             qf[s] = __builtin_bit_cast(bf16x8, v);
         }
         if (mode == MODE_KEYS) {
-            for (int cb = kb + 32 * wave; cb < ke; cb += 32 * kWaves)
-                chunk_bf16<D, false>(a, st, qf, Kp, Vp, kslot0, cb, ke, row_limit, lane, nullptr, nullptr, 0);
+            // software pipeline: the next chunk's K/V loads are in flight while this chunk computes
+            const uint16_t* Kb = (const uint16_t*)Kp;
+            const uint16_t* Vb = (const uint16_t*)Vp;
+            int cb = kb + 32 * wave;
+            if (cb < ke) {
+                ChunkRegs<D> cur, nxt;
+                load_chunk_bf16<D>(cur, Kb, Vb, kslot0, cb, ke, lane);
+                for (; cb < ke; cb += 32 * kWaves) {
+                    const bool more = cb + 32 * kWaves < ke;
+                    if (more) load_chunk_bf16<D>(nxt, Kb, Vb, kslot0, cb + 32 * kWaves, ke, lane);
+                    compute_chunk_bf16<D>(a, st, qf, cur, cb, ke, row_limit, lane);
+                    if (more) cur = nxt;
+                }
+            }
         } else {
             // stage 64-key tiles of K (row-major, padded rows) and V (8-key blocks, padded) in LDS
             const int wave_max_limit = min(ke, ctx + min(wrow0 + 15, row0 + nrows - 1) / a.G + 1);
