@@ -220,6 +220,21 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// One 16-byte-per-lane global -> LDS transfer (global_load_lds_dwordx4): lane i
+// of the wave writes LDS bytes [lds_base + 16 i, +16).  Issued from inline
+// assembly so that the compiler's wait insertion does not see it: the caller
+// orders it with its own vmcnt waits and barriers.  lds_base is wave-uniform.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(src), "s"(lds_base)
+                 : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(lds_void*)p;
+}
+
 template <int WAVES_M_, int WAVES_N_, int EPI>
 __global__ __launch_bounds__(64 * WAVES_M_ * WAVES_N_) void gemm_bf16_dma_kernel(GemmArgs a) {
     using C = DmaCfg<WAVES_M_, WAVES_N_>;
@@ -274,10 +289,10 @@ __global__ __launch_bounds__(64 * WAVES_M_ * WAVES_N_) void gemm_bf16_dma_kernel
     auto issue = [&](uint16_t* As, uint16_t* Bs, int k0) {
 #pragma unroll
         for (int j = 0; j < A_INSTR; ++j)
-            __builtin_amdgcn_global_load_lds((gbl_void*)(A + (srcA[j] + k0)), (lds_void*)(As + (wave * A_INSTR + j) * 512), 16, 0, 0);
+            dma16(A + (srcA[j] + k0), __builtin_amdgcn_readfirstlane(lds_addr(As + (wave * A_INSTR + j) * 512)));
 #pragma unroll
         for (int j = 0; j < B_INSTR; ++j)
-            __builtin_amdgcn_global_load_lds((gbl_void*)(W + (srcB[j] + k0)), (lds_void*)(Bs + (wave * B_INSTR + j) * 512), 16, 0, 0);
+            dma16(W + (srcB[j] + k0), __builtin_amdgcn_readfirstlane(lds_addr(Bs + (wave * B_INSTR + j) * 512)));
     };
 
     f32x4 acc[MI][NI];
