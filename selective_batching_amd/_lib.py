@@ -32,7 +32,7 @@ class SBError(RuntimeError):
 
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is not built; run `python -m selective_batching_amd.build` "
+    raise ImportError(f"{LIB_PATH} is not built; run `python selective_batching_amd/build.py` "
                       "(or __graft_entry__.build()) first")
 lib = C.CDLL(LIB_PATH)
 

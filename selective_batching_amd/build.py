@@ -1,6 +1,7 @@
 """Build libsb.so (HIP for gfx950 + host C++) in-tree with hipcc.
 
-Usage: python -m selective_batching_amd.build   (or build() from Python)
+Usage: python selective_batching_amd/build.py   (or __graft_entry__.build() from Python; the file
+imports nothing from its package, so it runs before the library exists)
 """
 import os
 import shutil

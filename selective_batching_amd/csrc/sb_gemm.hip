@@ -192,27 +192,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_bf16_kernel(GemmA
     }
 }
 
-// ================================================================== bf16 MFMA, LDS-DMA pipeline
-// 256 x 256 x 32 tiles, 8 waves (2 x 4, wave tile 128 x 64), four LDS stages
-// filled three K tiles ahead by global_load_lds_dwordx4 (16 bytes per lane
-// from global memory straight into LDS, no staging registers).  The DMA puts
-// lane i's 16 bytes at stage base + 16 i, so a wave instruction fills 16 rows
-// x 4 chunks; lane i loads chunk (i % 4) ^ sw(row) of row i / 4, with
-// sw(row) = (row / 2) % 4, which makes the 16-byte operand reads of 8
-// consecutive rows hit 8 different bank groups.  Each stage is its own LDS
-// object so the compiler's wait-count tracking can tell stages apart.
-template <int WAVES_M_, int WAVES_N_>
-struct DmaCfg {
-    static constexpr int BM = 256, BN = 256, BK = 32, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
-    static constexpr int THREADS = 64 * WAVES_M * WAVES_N;
-    static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N, MI = WM / 16, NI = WN / 16;
-    static constexpr int STAGE_ELEMS = BM * BK;                 // bf16 elements of one operand tile (16 KB)
-    static constexpr int A_INSTR = BM / 16 / (THREADS / 64);    // 16-row blocks per wave per stage
-    static constexpr int B_INSTR = BN / 16 / (THREADS / 64);
-};
-
 typedef __attribute__((address_space(3))) void lds_void;
-typedef const __attribute__((address_space(1))) void gbl_void;
 
 // vmcnt <= n (other counters untouched): gfx9 encoding, vmcnt in bits 3:0 and 15:14
 template <int N>
@@ -231,18 +211,49 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
                  : "memory", "m0");
 }
 
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-    return (uint32_t)(uintptr_t)(lds_void*)p;
-}
+// Workgroup barrier that is also a compiler memory barrier (no LDS access moves across it).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-template <int WAVES_M_, int WAVES_N_, int EPI>
-__global__ __launch_bounds__(64 * WAVES_M_ * WAVES_N_) void gemm_bf16_dma_kernel(GemmArgs a) {
-    using C = DmaCfg<WAVES_M_, WAVES_N_>;
-    constexpr int BM = C::BM, BN = C::BN, BK = C::BK, WAVES_N = C::WAVES_N;
-    constexpr int WM = C::WM, WN = C::WN, MI = C::MI, NI = C::NI;
-    constexpr int STAGE_ELEMS = C::STAGE_ELEMS, A_INSTR = C::A_INSTR, B_INSTR = C::B_INSTR;
-    __shared__ __attribute__((aligned(1024))) uint16_t A0[STAGE_ELEMS], A1[STAGE_ELEMS], A2[STAGE_ELEMS], A3[STAGE_ELEMS];
-    __shared__ __attribute__((aligned(1024))) uint16_t B0[STAGE_ELEMS], B1[STAGE_ELEMS], B2[STAGE_ELEMS], B3[STAGE_ELEMS];
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(lds_void*)p; }
+
+// ================================================================== bf16 MFMA, DMA-fed
+// BM x BN tile, K in steps of BK (32 or 64) through a ring of STAGES LDS
+// stages filled by global_load_lds_dwordx4 (16 bytes per lane from global
+// memory straight into LDS, no staging registers).  A stage holds the A tile
+// then the B tile, each row-major [rows][BK]; row r keeps its BK/8 16-byte
+// k-chunks in slots permuted by sw(r) = (r >> 1) % (BK/8), so the MFMA
+// operand reads (16 rows x one chunk per lane group, 8 lanes per LDS pass)
+// hit 8 different 16-byte bank groups.  One copy instruction fills 1 KB: 64/(BK/8)
+// consecutive rows, each row's BK*2 bytes read as one contiguous run (a whole
+// 128-byte line when BK = 64).  Step kt: wait for this wave's copies of tile kt,
+// barrier (every wave's copies landed, every wave finished tile kt-1), issue
+// tile kt+STAGES-1 into the stage tile kt-1 used, then the MFMAs of tile kt.
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int BK_, int STAGES_>
+struct DmaCfg {
+    static constexpr int BM = BM_, BN = BN_, BK = BK_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, STAGES = STAGES_;
+    static constexpr int NWAVES = WAVES_M * WAVES_N, THREADS = 64 * NWAVES;
+    static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N, MI = WM / 16, NI = WN / 16;
+    static constexpr int CH = BK / 8;                            // 16-byte chunks per row
+    static constexpr int RPI = 64 / CH;                          // rows per copy instruction
+    static constexpr int STAGE_ELEMS = (BM + BN) * BK;           // A rows then B rows
+    static constexpr int A_INSTR = BM / RPI / NWAVES;            // copy instructions per wave per stage
+    static constexpr int B_INSTR = BN / RPI / NWAVES;
+    static constexpr int PER = A_INSTR + B_INSTR;
+    static_assert(BK == 32 || BK == 64, "BK");
+    static_assert(A_INSTR * RPI * NWAVES == BM && B_INSTR * RPI * NWAVES == BN, "rows must split evenly over waves");
+    static_assert(STAGES >= 2 && (STAGES - 2) * PER <= 63, "vmcnt range");
+    static_assert(STAGES * STAGE_ELEMS * 2 <= 160 * 1024, "LDS");
+};
+
+// MINW waves per SIMD at least: 2 lets two 4-wave workgroups (or one 8-wave
+// one) share a CU, so one wave's MFMAs fill the other's barrier and LDS waits.
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int BK_, int STAGES_, int MINW, bool SPREAD, int EPI>
+__global__ __launch_bounds__(64 * WAVES_M_ * WAVES_N_, MINW) void gemm_bf16_dma_kernel(GemmArgs a) {
+    using C = DmaCfg<BM_, BN_, WAVES_M_, WAVES_N_, BK_, STAGES_>;
+    constexpr int BM = C::BM, BN = C::BN, BK = C::BK, WAVES_N = C::WAVES_N, STAGES = C::STAGES;
+    constexpr int WM = C::WM, WN = C::WN, MI = C::MI, NI = C::NI, CH = C::CH, RPI = C::RPI;
+    constexpr int STAGE_ELEMS = C::STAGE_ELEMS, A_INSTR = C::A_INSTR, B_INSTR = C::B_INSTR, PER = C::PER;
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[STAGES * STAGE_ELEMS];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int wm = wave / WAVES_N, wn = wave % WAVES_N;
@@ -260,22 +271,22 @@ __global__ __launch_bounds__(64 * WAVES_M_ * WAVES_N_) void gemm_bf16_dma_kernel
     const int tn = (pid % per_group) / gsz;
     const int m0 = tm * BM;
 
-    // this lane's source chunk inside a 16-row block
-    const int brow = lane >> 2;                        // row inside the block
-    const int bchunk = (lane & 3) ^ ((brow >> 1) & 3);  // K chunk it fetches
     const uint16_t* A = (const uint16_t*)a.A;
     const uint16_t* W = (const uint16_t*)a.W;
-    // element offsets (32-bit: every operand here is < 2^31 elements) of this lane's source chunks
+    // element offsets (32-bit: every operand here is < 2^31 elements) of this lane's source chunks:
+    // lane -> row lane / CH of the instruction's rows, LDS slot lane % CH, source chunk slot ^ sw(row)
     int srcA[A_INSTR];
     int srcB[B_INSTR];
 #pragma unroll
     for (int j = 0; j < A_INSTR; ++j) {
-        const int row = (wave * A_INSTR + j) * 16 + brow;
-        srcA[j] = min(m0 + row, a.M - 1) * (int)a.lda + bchunk * 8;
+        const int row = (wave * A_INSTR + j) * RPI + lane / CH;
+        const int chunk = (lane % CH) ^ ((row >> 1) % CH);
+        srcA[j] = min(m0 + row, a.M - 1) * (int)a.lda + chunk * 8;
     }
 #pragma unroll
     for (int j = 0; j < B_INSTR; ++j) {
-        const int row = (wave * B_INSTR + j) * 16 + brow;
+        const int row = (wave * B_INSTR + j) * RPI + lane / CH;
+        const int chunk = (lane % CH) ^ ((row >> 1) % CH);
         int gr;
         if (EPI == EPI_SWIGLU) {
             const int w = row / WN, cc = row % WN;
@@ -284,15 +295,20 @@ __global__ __launch_bounds__(64 * WAVES_M_ * WAVES_N_) void gemm_bf16_dma_kernel
         } else {
             gr = min(tn * BN + row, a.N - 1);
         }
-        srcB[j] = gr * (int)a.ldw + bchunk * 8;
+        srcB[j] = gr * (int)a.ldw + chunk * 8;
     }
-    auto issue = [&](uint16_t* As, uint16_t* Bs, int k0) {
+    // LDS byte address of this wave's first A and B copy in stage 0 (wave-uniform, so scalar)
+    const uint32_t dstA = __builtin_amdgcn_readfirstlane(lds_addr(smem) + wave * A_INSTR * 1024);
+    const uint32_t dstB = __builtin_amdgcn_readfirstlane(lds_addr(smem) + BM * BK * 2 + wave * B_INSTR * 1024);
+    // copy instruction d (A copies first, then B) of the tile at k0 into `stage`
+    auto piece = [&](int stage, int k0, int d) {
+        const uint32_t so = (uint32_t)(stage * STAGE_ELEMS * 2);
+        if (d < A_INSTR) dma16(A + (srcA[d] + k0), dstA + so + d * 1024);
+        else dma16(W + (srcB[d - A_INSTR] + k0), dstB + so + (d - A_INSTR) * 1024);
+    };
+    auto issue = [&](int stage, int k0) {
 #pragma unroll
-        for (int j = 0; j < A_INSTR; ++j)
-            dma16(A + (srcA[j] + k0), __builtin_amdgcn_readfirstlane(lds_addr(As + (wave * A_INSTR + j) * 512)));
-#pragma unroll
-        for (int j = 0; j < B_INSTR; ++j)
-            dma16(W + (srcB[j] + k0), __builtin_amdgcn_readfirstlane(lds_addr(Bs + (wave * B_INSTR + j) * 512)));
+        for (int d = 0; d < PER; ++d) piece(stage, k0, d);
     };
 
     f32x4 acc[MI][NI];
@@ -302,42 +318,66 @@ __global__ __launch_bounds__(64 * WAVES_M_ * WAVES_N_) void gemm_bf16_dma_kernel
         for (int j = 0; j < NI; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int lr = lane & 15, lc = lane >> 4;
-    const int rd = lr * BK + ((lc ^ ((lr >> 1) & 3)) * 8);   // element offset of this lane's operand in a block
-    auto compute = [&](const uint16_t* As, const uint16_t* Bs) {
-        bf16x8 bfr[NI];
+    // element offset of this lane's operand (row lr of a 16-row block, chunk 4h + lc) for each 32-k half h
+    int rd[BK / 32];
 #pragma unroll
-        for (int j = 0; j < NI; ++j)
-            bfr[j] = __builtin_bit_cast(bf16x8, *(const u32x4*)(Bs + ((wn * WN) / 16 + j) * 512 + rd));
+    for (int h = 0; h < BK / 32; ++h) rd[h] = lr * BK + (((4 * h + lc) ^ ((lr >> 1) % CH)) * 8);
+    // MFMAs of the tile in `stage`, as G = (BK/32) * MI groups of NI MFMAs (one A fragment each).
+    // With SPREAD, the copies of the next tile (into nstage, at nk0) go out one per group behind
+    // the group's MFMAs, over the first PER groups, instead of all at once: a burst of copies from
+    // every wave queues in the address unit and holds the waves back from their MFMAs.
+    auto compute = [&](int stage, int nstage, int nk0, bool more) {
+        constexpr int G = (BK / 32) * MI;
+        const uint16_t* As = smem + stage * STAGE_ELEMS + (wm * WM) * BK;
+        const uint16_t* Bs = smem + stage * STAGE_ELEMS + BM * BK + (wn * WN) * BK;
 #pragma unroll
-        for (int i = 0; i < MI; ++i) {
-            const bf16x8 af = __builtin_bit_cast(bf16x8, *(const u32x4*)(As + ((wm * WM) / 16 + i) * 512 + rd));
+        for (int h = 0; h < BK / 32; ++h) {
+            bf16x8 bfr[NI];
 #pragma unroll
-            for (int j = 0; j < NI; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfr[j], acc[i][j], 0, 0, 0);
+            for (int j = 0; j < NI; ++j) bfr[j] = __builtin_bit_cast(bf16x8, *(const u32x4*)(Bs + j * 16 * BK + rd[h]));
+#pragma unroll
+            for (int i = 0; i < MI; ++i) {
+                const bf16x8 af = __builtin_bit_cast(bf16x8, *(const u32x4*)(As + i * 16 * BK + rd[h]));
+#pragma unroll
+                for (int j = 0; j < NI; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfr[j], acc[i][j], 0, 0, 0);
+                if constexpr (SPREAD) {
+                    const int g = h * MI + i;
+                    constexpr int PG = (PER + G - 1) / G;          // copies per group
+#pragma unroll
+                    for (int q = 0; q < PG; ++q) {
+                        const int d = g * PG + q;
+                        if (d < PER && more) {
+                            __builtin_amdgcn_sched_barrier(0);
+                            piece(nstage, nk0, d);
+                            __builtin_amdgcn_sched_barrier(0);
+                        }
+                    }
+                }
+            }
         }
     };
 
-    // per wave, one K tile = A_INSTR + B_INSTR DMA instructions in flight
-    constexpr int PER = A_INSTR + B_INSTR;
     const int nk = a.K / BK;
-    issue(A0, B0, 0);
-    if (nk > 1) issue(A1, B1, BK);
-    if (nk > 2) issue(A2, B2, 2 * BK);
-    auto step = [&](int kt, uint16_t* Ac, uint16_t* Bc, uint16_t* An, uint16_t* Bn) {
-        if (kt + 2 < nk) wait_vmcnt<2 * PER>();
-        else if (kt + 1 < nk) wait_vmcnt<PER>();
-        else wait_vmcnt<0>();
-        __builtin_amdgcn_s_barrier();                 // every wave's tile kt is in LDS; stage (kt+3)%4 is free
-        if (kt + 3 < nk) issue(An, Bn, (kt + 3) * BK);
-        compute(Ac, Bc);
+#pragma unroll
+    for (int t = 0; t < STAGES - 1; ++t)
+        if (t < nk) issue(t, t * BK);
+    int stage = 0;
+    for (int kt = 0; kt < nk; ++kt) {
+        // copies issued after tile kt that may stay in flight
+        const int later = min(STAGES - 2, nk - 1 - kt);
+        if (later == STAGES - 2) wait_vmcnt<(STAGES - 2) * PER>();
+        else if (later == 0) wait_vmcnt<0>();
+        else if (later == 1) wait_vmcnt<PER>();
+        else if (later == 2) wait_vmcnt<2 * PER>();
+        else wait_vmcnt<(3 * PER > 63 ? 63 : 3 * PER)>();
+        lds_barrier();
+        const int nstage = stage == 0 ? STAGES - 1 : stage - 1;
+        const bool more = kt + STAGES - 1 < nk;
+        if (!SPREAD && more) issue(nstage, (kt + STAGES - 1) * BK);
+        compute(stage, nstage, (kt + STAGES - 1) * BK, more);
         __builtin_amdgcn_sched_barrier(0);            // keep each tile's operands local to its step
-    };
-    // K % 128 == 0 (checked by the launcher): whole trips of four stages, no early exits
-    for (int kt = 0; kt < nk; kt += 4) {
-        step(kt, A0, B0, A3, B3);
-        step(kt + 1, A1, B1, A0, B0);
-        step(kt + 2, A2, B2, A1, B1);
-        step(kt + 3, A3, B3, A2, B2);
+        stage = (stage + 1 == STAGES) ? 0 : stage + 1;
     }
 
     const int rbase = m0 + wm * WM + (lane >> 4) * 4;
@@ -434,7 +474,13 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
 }
 
 // Tile configurations of the bf16 kernel: {BM, BN, waves along M, waves along N}.
-enum { CFG_128x128_4W = 0, CFG_256x256_4W, CFG_256x256_8W, CFG_256x128_4W, CFG_128x256_4W, CFG_DMA_8W, CFG_DMA_4W, CFG_COUNT };
+enum {
+    CFG_128x128_4W = 0, CFG_256x256_4W, CFG_256x256_8W, CFG_256x128_4W, CFG_128x256_4W,   // register-staged
+    CFG_DMA_256x256_8W_S4, CFG_DMA_256x128_4W_S3, CFG_DMA_128x256_4W_S3, CFG_DMA_256x256_8W_S5,  // DMA-fed, BK 32
+    CFG_DMA_256x256_8W_K64_S2, CFG_DMA_256x256_4W_K64_S2,                                     // DMA-fed, BK 64
+    CFG_DMA_256x256_8W_K64_S2_SPREAD, CFG_DMA_256x256_8W_S4_SPREAD,                           // copies spread over MFMAs
+    CFG_COUNT
+};
 
 template <int BM, int BN, int WMW, int WNW, int EPI>
 int launch_bf16_cfg(const GemmArgs& a, hipStream_t s) {
@@ -444,16 +490,20 @@ int launch_bf16_cfg(const GemmArgs& a, hipStream_t s) {
     return check_launch("gemm_bf16");
 }
 
-template <int WMW, int WNW, int EPI>
+template <int BM, int BN, int WMW, int WNW, int BK, int STAGES, int MINW, bool SPREAD, int EPI>
 int launch_dma(const GemmArgs& a, hipStream_t s) {
-    if (a.K % 128) return launch_bf16_cfg<256, 256, 2, 4, EPI>(a, s);   // whole four-stage trips only
-    const int out_cols = (EPI == EPI_SWIGLU) ? 128 : 256;
-    const long long tiles = (long long)((a.M + 255) / 256) * ((a.N + out_cols - 1) / out_cols);
-    hipLaunchKernelGGL((gemm_bf16_dma_kernel<WMW, WNW, EPI>), dim3((unsigned)tiles), dim3(64 * WMW * WNW), 0, s, a);
+    const int out_cols = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
+    const long long tiles = (long long)((a.M + BM - 1) / BM) * ((a.N + out_cols - 1) / out_cols);
+    hipLaunchKernelGGL((gemm_bf16_dma_kernel<BM, BN, WMW, WNW, BK, STAGES, MINW, SPREAD, EPI>), dim3((unsigned)tiles),
+                       dim3(64 * WMW * WNW), 0, s, a);
     return check_launch("gemm_bf16_dma");
 }
 
-// Pick the tile: the largest tiles that still give every CU work; small GEMMs keep 128 x 128.
+// Pick the tile: DMA-fed 256 x 256 x 64 tiles once there are enough of them to
+// fill most CUs (copies spread over the MFMAs when there is more than one row of
+// tiles; a single row of tiles measured faster with them in one burst); small
+// GEMMs keep 128 x 128.  Every configuration sums each output's K in the same
+// order with the same MFMA, so the choice never changes a result bit.
 int pick_cfg(const GemmArgs& a, int epi) {
     const char* e = getenv("SB_GEMM_CFG");             // tuning / test override: a CFG_* index
     if (e && *e) {
@@ -462,8 +512,7 @@ int pick_cfg(const GemmArgs& a, int epi) {
     }
     const int ncols = (epi == EPI_SWIGLU) ? 2 * a.N : a.N;
     const long long big = (long long)((a.M + 255) / 256) * ((ncols + 255) / 256);
-    if (big >= 128 && a.K % 128 == 0) return CFG_DMA_8W;
-    if (big >= 256) return CFG_256x256_8W;
+    if (big >= 128) return a.M > 256 ? CFG_DMA_256x256_8W_K64_S2_SPREAD : CFG_DMA_256x256_8W_K64_S2;
     return CFG_128x128_4W;
 }
 
@@ -474,8 +523,14 @@ int launch_bf16(const GemmArgs& a, hipStream_t s) {
         case CFG_256x256_8W: return launch_bf16_cfg<256, 256, 2, 4, EPI>(a, s);
         case CFG_256x128_4W: return launch_bf16_cfg<256, 128, 2, 2, EPI>(a, s);
         case CFG_128x256_4W: return launch_bf16_cfg<128, 256, 2, 2, EPI>(a, s);
-        case CFG_DMA_8W: return launch_dma<2, 4, EPI>(a, s);
-        case CFG_DMA_4W: return launch_dma<2, 2, EPI>(a, s);
+        case CFG_DMA_256x256_8W_S4: return launch_dma<256, 256, 2, 4, 32, 4, 2, false, EPI>(a, s);
+        case CFG_DMA_256x128_4W_S3: return launch_dma<256, 128, 2, 2, 32, 3, 2, false, EPI>(a, s);
+        case CFG_DMA_128x256_4W_S3: return launch_dma<128, 256, 2, 2, 32, 3, 2, false, EPI>(a, s);
+        case CFG_DMA_256x256_8W_S5: return launch_dma<256, 256, 2, 4, 32, 5, 2, false, EPI>(a, s);
+        case CFG_DMA_256x256_8W_K64_S2: return launch_dma<256, 256, 2, 4, 64, 2, 2, false, EPI>(a, s);
+        case CFG_DMA_256x256_4W_K64_S2: return launch_dma<256, 256, 2, 2, 64, 2, 1, false, EPI>(a, s);
+        case CFG_DMA_256x256_8W_K64_S2_SPREAD: return launch_dma<256, 256, 2, 4, 64, 2, 2, true, EPI>(a, s);
+        case CFG_DMA_256x256_8W_S4_SPREAD: return launch_dma<256, 256, 2, 4, 32, 4, 2, true, EPI>(a, s);
         default: return launch_bf16_cfg<128, 128, 2, 2, EPI>(a, s);
     }
 }

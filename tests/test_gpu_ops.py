@@ -218,12 +218,17 @@ def test_attention_edge_cases():
     _attention_case(MINI_ATT, "bf16", [(16, 512), (1, 512), (1, 513)], 6)  # split boundaries
 
 
-@pytest.mark.parametrize("cfg", range(7))
+N_GEMM_CFGS = 13  # register-staged 128x128, 256x256 (4 and 8 waves), 256x128, 128x256; DMA-fed: 4 with BK 32, 2 with BK 64, 2 spread
+
+
+@pytest.mark.parametrize("cfg", range(N_GEMM_CFGS))
 @pytest.mark.parametrize("epi", ["bias", "gelu", "resid", "swiglu"])
-def test_gemm_every_tile_config(cfg, epi, monkeypatch):
-    """Each bf16 tile configuration (forced) on a ragged shape: M and N not multiples of the tile, K % 128 == 0."""
+@pytest.mark.parametrize("K", [512, 64, 192])
+def test_gemm_every_tile_config(cfg, epi, K, monkeypatch):
+    """Each bf16 tile configuration (forced) on a ragged shape: M and N not multiples of the tile;
+    K = 64 and 192 leave fewer K tiles than LDS stages / a partial ring trip."""
     monkeypatch.setenv("SB_GEMM_CFG", str(cfg))
-    M, N, K = 300, 640, 512
+    M, N = 300, 640
     print_case("gemm cfg", cfg, epi, M, N, K)
     A = normal(cfg, "A", (M, K), dtype="bf16")
     W = normal(cfg, "W", (2 * N if epi == "swiglu" else N, K), std=0.05, dtype="bf16")
@@ -246,3 +251,27 @@ def test_gemm_every_tile_config(cfg, epi, monkeypatch):
         assert_close_rms(host(out), x0 + lin, TOL["fp32"], f"cfg {cfg} resid")
     else:
         assert_close_elem(host(out), OM.silu(OM.linear(A, W[:N])) * OM.linear(A, W[N:]), "bf16", f"cfg {cfg} swiglu")
+
+
+@pytest.mark.parametrize("epi", ["bias", "swiglu"])
+def test_gemm_configs_bitwise_identical(epi, monkeypatch):
+    """Every tile configuration gives the same bits: each output sums K in 32-wide MFMA steps in
+    ascending order whatever the tile, so the launcher's choice (which depends on M, i.e. on the
+    batch) never changes a result."""
+    M, N, K = 300, 640, 512
+    A = normal(7, "A", (M, K), dtype="bf16")
+    W = normal(7, "W", (2 * N if epi == "swiglu" else N, K), std=0.05, dtype="bf16")
+    b = normal(7, "b", (N,), std=0.5, dtype="bf16")
+    code = sb.SB_EPI_SWIGLU if epi == "swiglu" else sb.SB_EPI_STORE
+    dA, dW, db = dev(A, "bf16"), dev(W, "bf16"), dev(b, "bf16")
+    outs = []
+    for cfg in range(N_GEMM_CFGS):
+        monkeypatch.setenv("SB_GEMM_CFG", str(cfg))
+        out = torch.zeros((M, N), dtype=torch.bfloat16, device="cuda")
+        sb.sb_op_gemm(sb.SB_BF16, code, M, N, K, dA.data_ptr(), K, dW.data_ptr(), K,
+                      None if epi == "swiglu" else db.data_ptr(), out.data_ptr(), N, 0, N if epi == "swiglu" else 0,
+                      stream_handle())
+        _sync()
+        outs.append(out.view(torch.int16).cpu())
+    for cfg in range(1, N_GEMM_CFGS):
+        assert torch.equal(outs[cfg], outs[0]), f"cfg {cfg} differs from cfg 0"
