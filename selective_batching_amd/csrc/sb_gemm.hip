@@ -247,7 +247,7 @@ struct DmaCfg {
 
 // MINW waves per SIMD at least: 2 lets two 4-wave workgroups (or one 8-wave
 // one) share a CU, so one wave's MFMAs fill the other's barrier and LDS waits.
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int BK_, int STAGES_, int MINW, bool SPREAD, int EPI>
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int BK_, int STAGES_, int MINW, int FEED, int EPI>
 __global__ __launch_bounds__(64 * WAVES_M_ * WAVES_N_, MINW) void gemm_bf16_dma_kernel(GemmArgs a) {
     using C = DmaCfg<BM_, BN_, WAVES_M_, WAVES_N_, BK_, STAGES_>;
     constexpr int BM = C::BM, BN = C::BN, BK = C::BK, WAVES_N = C::WAVES_N, STAGES = C::STAGES;
@@ -323,36 +323,40 @@ __global__ __launch_bounds__(64 * WAVES_M_ * WAVES_N_, MINW) void gemm_bf16_dma_
 #pragma unroll
     for (int h = 0; h < BK / 32; ++h) rd[h] = lr * BK + (((4 * h + lc) ^ ((lr >> 1) % CH)) * 8);
     // MFMAs of the tile in `stage`, as G = (BK/32) * MI groups of NI MFMAs (one A fragment each).
-    // With SPREAD, the copies of the next tile (into nstage, at nk0) go out one per group behind
-    // the group's MFMAs, over the first PER groups, instead of all at once: a burst of copies from
-    // every wave queues in the address unit and holds the waves back from their MFMAs.
+    // FEED == 1: the copies of the next tile (into nstage, at nk0) go out one per group behind the
+    // group's MFMAs, over the first PER groups, instead of all at once: a burst of copies from every
+    // wave queues in the address unit and holds the waves back from their MFMAs.
+    constexpr int G = (BK / 32) * MI;
+    constexpr int PG = (PER + G - 1) / G;                  // copies per group
+    auto spread_copies = [&](int g, int nstage, int nk0, bool more) {
+#pragma unroll
+        for (int q = 0; q < PG; ++q) {
+            const int d = g * PG + q;
+            if (d < PER && more) {
+                __builtin_amdgcn_sched_barrier(0);
+                piece(nstage, nk0, d);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    };
     auto compute = [&](int stage, int nstage, int nk0, bool more) {
-        constexpr int G = (BK / 32) * MI;
         const uint16_t* As = smem + stage * STAGE_ELEMS + (wm * WM) * BK;
         const uint16_t* Bs = smem + stage * STAGE_ELEMS + BM * BK + (wn * WN) * BK;
+        auto ldA = [&](int h, int i) { return __builtin_bit_cast(bf16x8, *(const u32x4*)(As + i * 16 * BK + rd[h])); };
+        auto ldB = [&](int h, int j) { return __builtin_bit_cast(bf16x8, *(const u32x4*)(Bs + j * 16 * BK + rd[h])); };
+        {
 #pragma unroll
-        for (int h = 0; h < BK / 32; ++h) {
-            bf16x8 bfr[NI];
+            for (int h = 0; h < BK / 32; ++h) {
+                bf16x8 bfr[NI];
 #pragma unroll
-            for (int j = 0; j < NI; ++j) bfr[j] = __builtin_bit_cast(bf16x8, *(const u32x4*)(Bs + j * 16 * BK + rd[h]));
+                for (int j = 0; j < NI; ++j) bfr[j] = ldB(h, j);
 #pragma unroll
-            for (int i = 0; i < MI; ++i) {
-                const bf16x8 af = __builtin_bit_cast(bf16x8, *(const u32x4*)(As + i * 16 * BK + rd[h]));
+                for (int i = 0; i < MI; ++i) {
+                    const bf16x8 af = ldA(h, i);
 #pragma unroll
-                for (int j = 0; j < NI; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfr[j], acc[i][j], 0, 0, 0);
-                if constexpr (SPREAD) {
-                    const int g = h * MI + i;
-                    constexpr int PG = (PER + G - 1) / G;          // copies per group
-#pragma unroll
-                    for (int q = 0; q < PG; ++q) {
-                        const int d = g * PG + q;
-                        if (d < PER && more) {
-                            __builtin_amdgcn_sched_barrier(0);
-                            piece(nstage, nk0, d);
-                            __builtin_amdgcn_sched_barrier(0);
-                        }
-                    }
+                    for (int j = 0; j < NI; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfr[j], acc[i][j], 0, 0, 0);
+                    if constexpr (FEED == 1) spread_copies(h * MI + i, nstage, nk0, more);
                 }
             }
         }
@@ -374,7 +378,7 @@ __global__ __launch_bounds__(64 * WAVES_M_ * WAVES_N_, MINW) void gemm_bf16_dma_
         lds_barrier();
         const int nstage = stage == 0 ? STAGES - 1 : stage - 1;
         const bool more = kt + STAGES - 1 < nk;
-        if (!SPREAD && more) issue(nstage, (kt + STAGES - 1) * BK);
+        if (FEED == 0 && more) issue(nstage, (kt + STAGES - 1) * BK);
         compute(stage, nstage, (kt + STAGES - 1) * BK, more);
         __builtin_amdgcn_sched_barrier(0);            // keep each tile's operands local to its step
         stage = (stage + 1 == STAGES) ? 0 : stage + 1;
@@ -479,6 +483,7 @@ enum {
     CFG_DMA_256x256_8W_S4, CFG_DMA_256x128_4W_S3, CFG_DMA_128x256_4W_S3, CFG_DMA_256x256_8W_S5,  // DMA-fed, BK 32
     CFG_DMA_256x256_8W_K64_S2, CFG_DMA_256x256_4W_K64_S2,                                     // DMA-fed, BK 64
     CFG_DMA_256x256_8W_K64_S2_SPREAD, CFG_DMA_256x256_8W_S4_SPREAD,                           // copies spread over MFMAs
+    CFG_DMA_256x192_8W_K64_S2_SPREAD, CFG_DMA_192x256_8W_K64_S2_SPREAD,                       // fewer-tile shapes
     CFG_COUNT
 };
 
@@ -490,20 +495,42 @@ int launch_bf16_cfg(const GemmArgs& a, hipStream_t s) {
     return check_launch("gemm_bf16");
 }
 
-template <int BM, int BN, int WMW, int WNW, int BK, int STAGES, int MINW, bool SPREAD, int EPI>
+template <int BM, int BN, int WMW, int WNW, int BK, int STAGES, int MINW, int FEED, int EPI>
 int launch_dma(const GemmArgs& a, hipStream_t s) {
-    const int out_cols = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
-    const long long tiles = (long long)((a.M + BM - 1) / BM) * ((a.N + out_cols - 1) / out_cols);
-    hipLaunchKernelGGL((gemm_bf16_dma_kernel<BM, BN, WMW, WNW, BK, STAGES, MINW, SPREAD, EPI>), dim3((unsigned)tiles),
-                       dim3(64 * WMW * WNW), 0, s, a);
-    return check_launch("gemm_bf16_dma");
+    if constexpr (EPI == EPI_SWIGLU && (BN / WNW / 2) % 16 != 0) {
+        // a wave's columns must split into whole 16-wide gate and up fragments
+        return launch_dma<256, 256, 2, 4, 64, 2, 2, 1, EPI>(a, s);
+    } else {
+        const int out_cols = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
+        const long long tiles = (long long)((a.M + BM - 1) / BM) * ((a.N + out_cols - 1) / out_cols);
+        hipLaunchKernelGGL((gemm_bf16_dma_kernel<BM, BN, WMW, WNW, BK, STAGES, MINW, FEED, EPI>), dim3((unsigned)tiles),
+                           dim3(64 * WMW * WNW), 0, s, a);
+        return check_launch("gemm_bf16_dma");
+    }
 }
 
-// Pick the tile: DMA-fed 256 x 256 x 64 tiles once there are enough of them to
-// fill most CUs (copies spread over the MFMAs when there is more than one row of
-// tiles; a single row of tiles measured faster with them in one burst); small
-// GEMMs keep 128 x 128.  Every configuration sums each output's K in the same
-// order with the same MFMA, so the choice never changes a result bit.
+int num_cus() {
+    static int n = 0;
+    if (n == 0) {
+        int dev = 0, v = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+            n = v;
+        else
+            n = 256;
+    }
+    return n;
+}
+
+// Pick the tile.  Small GEMMs keep 128 x 128 register-staged tiles.  Otherwise
+// DMA-fed tiles of 64-deep K: among 256x256, 256x192 and 192x256 the one with
+// the least estimated time, rounds x tile work x feed factor, where rounds =
+// ceil(tiles / CUs) (one such workgroup per CU) and the feed factor charges half
+// of the extra bytes per flop of the smaller tiles (1.083 for 192-wide ones):
+// e.g. 3741 x 6144 takes 256x192 (480 tiles, 2 rounds) over 256x256 (360 tiles,
+// 2 rounds).  Copies are spread over the MFMAs unless there is only one row of
+// tiles (measured faster in one burst).  Every configuration sums each output's
+// K in the same order with the same MFMA, so the choice never changes a result bit.
 int pick_cfg(const GemmArgs& a, int epi) {
     const char* e = getenv("SB_GEMM_CFG");             // tuning / test override: a CFG_* index
     if (e && *e) {
@@ -512,8 +539,25 @@ int pick_cfg(const GemmArgs& a, int epi) {
     }
     const int ncols = (epi == EPI_SWIGLU) ? 2 * a.N : a.N;
     const long long big = (long long)((a.M + 255) / 256) * ((ncols + 255) / 256);
-    if (big >= 128) return a.M > 256 ? CFG_DMA_256x256_8W_K64_S2_SPREAD : CFG_DMA_256x256_8W_K64_S2;
-    return CFG_128x128_4W;
+    if (big < 128) return CFG_128x128_4W;
+    if (a.M <= 256) return CFG_DMA_256x256_8W_K64_S2;
+    struct Cand { int cfg, bm, bn; };
+    const Cand cands[3] = {{CFG_DMA_256x256_8W_K64_S2_SPREAD, 256, 256},
+                           {CFG_DMA_256x192_8W_K64_S2_SPREAD, 256, 192},
+                           {CFG_DMA_192x256_8W_K64_S2_SPREAD, 192, 256}};
+    const int cus = num_cus();
+    int best = cands[0].cfg;
+    double best_cost = 0.0;
+    for (int c = 0; c < 3; ++c) {
+        const Cand& k = cands[c];
+        if (epi == EPI_SWIGLU && k.bn == 192) continue;           // gate/up need 16-wide halves per wave
+        const long long tiles = (long long)((a.M + k.bm - 1) / k.bm) * ((ncols + k.bn - 1) / k.bn);
+        const long long rounds = (tiles + cus - 1) / cus;
+        const double feed = 1.0 + 0.5 * ((double)(k.bm + k.bn) / ((double)k.bm * k.bn) * 128.0 - 1.0);
+        const double cost = (double)rounds * k.bm * k.bn * feed;
+        if (c == 0 || cost < best_cost) { best = k.cfg; best_cost = cost; }
+    }
+    return best;
 }
 
 template <int EPI>
@@ -523,14 +567,16 @@ int launch_bf16(const GemmArgs& a, hipStream_t s) {
         case CFG_256x256_8W: return launch_bf16_cfg<256, 256, 2, 4, EPI>(a, s);
         case CFG_256x128_4W: return launch_bf16_cfg<256, 128, 2, 2, EPI>(a, s);
         case CFG_128x256_4W: return launch_bf16_cfg<128, 256, 2, 2, EPI>(a, s);
-        case CFG_DMA_256x256_8W_S4: return launch_dma<256, 256, 2, 4, 32, 4, 2, false, EPI>(a, s);
-        case CFG_DMA_256x128_4W_S3: return launch_dma<256, 128, 2, 2, 32, 3, 2, false, EPI>(a, s);
-        case CFG_DMA_128x256_4W_S3: return launch_dma<128, 256, 2, 2, 32, 3, 2, false, EPI>(a, s);
-        case CFG_DMA_256x256_8W_S5: return launch_dma<256, 256, 2, 4, 32, 5, 2, false, EPI>(a, s);
-        case CFG_DMA_256x256_8W_K64_S2: return launch_dma<256, 256, 2, 4, 64, 2, 2, false, EPI>(a, s);
-        case CFG_DMA_256x256_4W_K64_S2: return launch_dma<256, 256, 2, 2, 64, 2, 1, false, EPI>(a, s);
-        case CFG_DMA_256x256_8W_K64_S2_SPREAD: return launch_dma<256, 256, 2, 4, 64, 2, 2, true, EPI>(a, s);
-        case CFG_DMA_256x256_8W_S4_SPREAD: return launch_dma<256, 256, 2, 4, 32, 4, 2, true, EPI>(a, s);
+        case CFG_DMA_256x256_8W_S4: return launch_dma<256, 256, 2, 4, 32, 4, 2, 0, EPI>(a, s);
+        case CFG_DMA_256x128_4W_S3: return launch_dma<256, 128, 2, 2, 32, 3, 2, 0, EPI>(a, s);
+        case CFG_DMA_128x256_4W_S3: return launch_dma<128, 256, 2, 2, 32, 3, 2, 0, EPI>(a, s);
+        case CFG_DMA_256x256_8W_S5: return launch_dma<256, 256, 2, 4, 32, 5, 2, 0, EPI>(a, s);
+        case CFG_DMA_256x256_8W_K64_S2: return launch_dma<256, 256, 2, 4, 64, 2, 2, 0, EPI>(a, s);
+        case CFG_DMA_256x256_4W_K64_S2: return launch_dma<256, 256, 2, 2, 64, 2, 1, 0, EPI>(a, s);
+        case CFG_DMA_256x256_8W_K64_S2_SPREAD: return launch_dma<256, 256, 2, 4, 64, 2, 2, 1, EPI>(a, s);
+        case CFG_DMA_256x256_8W_S4_SPREAD: return launch_dma<256, 256, 2, 4, 32, 4, 2, 1, EPI>(a, s);
+        case CFG_DMA_256x192_8W_K64_S2_SPREAD: return launch_dma<256, 192, 2, 4, 64, 2, 2, 1, EPI>(a, s);
+        case CFG_DMA_192x256_8W_K64_S2_SPREAD: return launch_dma<192, 256, 2, 4, 64, 2, 2, 1, EPI>(a, s);
         default: return launch_bf16_cfg<128, 128, 2, 2, EPI>(a, s);
     }
 }
