@@ -13,13 +13,18 @@ request pool (host), the ragged metadata and attention work list (host) and
 its copy to the GPU, embedding, 32 selective-batched layers, final norm + LM
 head + greedy argmax, the copy of the 256 new token ids back, and Complete
 (host).  The scheduler state is rebuilt inside the step so that every step
-re-runs the same iteration (same batch, same slots).  ``value`` is processed
-tokens per second (sum of n_new over the batch / step time).
+re-runs the same iteration (same batch, same slots).  Steps are pipelined the
+way a serving loop runs them: the host side of step k (new pool, Select,
+metadata into the second staging buffer, launches) runs while the GPU still
+works on step k-1, which is then waited for and completed.  ``value`` is
+processed tokens per second (sum of n_new over the batch / step time).
 
-Also reported: per-kernel-class GPU time from HIP events recorded around
-every launch on the launch stream during the timed steps; the roofline of the
-dominant kernel (the FFN1 SwiGLU GEMM, MFMA-bound); decode-attention HBM
-bandwidth; and the CPU oracle timed on a bounded sample of the same workload.
+Also reported: HIP-event timing, on the launch stream during the timed steps,
+of the FFN1 GEMM and attention launches (only those two classes are timed
+there: every recorded event pair costs time); the roofline of the dominant
+kernel (the FFN1 SwiGLU GEMM, MFMA-bound); decode-attention HBM bandwidth; a
+per-class breakdown from three extra steps with every class timed; and the
+CPU oracle timed on a bounded sample of the same workload.
 """
 import argparse
 import json
@@ -136,29 +141,45 @@ def main():
                for i, (n, c) in enumerate(batch) if n > 1}
     last_tok = uniform_int(args.seed, "bench.last", 0, m.V - 1, B).tolist()
 
-    def load_pool():
-        """The pool of this iteration: decodes first (they arrived first), then the new prompts."""
+    def new_pool():
+        """A fresh K/V manager + scheduler over the shared arenas, holding the pool of this
+        iteration: decodes first (they arrived first), then the new prompts."""
+        kv = A.sb_kv_create(n_slots, eng.arena_slots, m.n_layers, m.nkv, m.d, sb.SB_BF16,
+                            eng.k_arena.data_ptr(), eng.v_arena.data_ptr())
+        A.sb_kv_set_stream(kv, stream_handle())
+        sched = A.sb_sched_create(B, kv)
         for i, (n, c) in enumerate(batch):
             if n == 1:
                 # mid-generation: prompt of c tokens, 1 generated token not fed yet -> ctx = c;
                 # max_tokens = ctx + n_new (the reservation this iteration needs)
-                eng.add_running(i, float(i), c, 2, c + 1, 1, last_tok[i])
+                A.sb_sched_add_running(sched, i, float(i), c, 2, c + 1, 1, last_tok[i])
             else:
-                eng.add(i, float(i), prompts[i], 2, n + 1)
+                A.sb_sched_add(sched, i, float(i), prompts[i], 2, n + 1)
+        return kv, sched
 
-    def reset():
-        eng.close()
-        eng.kv = A.sb_kv_create(n_slots, eng.arena_slots, m.n_layers, m.nkv, m.d, sb.SB_BF16,
-                                eng.k_arena.data_ptr(), eng.v_arena.data_ptr())
-        A.sb_kv_set_stream(eng.kv, stream_handle())
-        eng.sched = A.sb_sched_create(B, eng.kv)
-        load_pool()
+    pools = [None, None]
 
-    def step():
-        reset()
-        res = eng.step()
-        assert res is not None and len(res["ids"]) == B and int(res["n_new"].sum()) == T
-        return res
+    def launch(k):
+        """Host side of step k (fresh pool, Select, metadata) and enqueue of its GPU work."""
+        b = k % 2
+        if pools[b] is not None:                 # step k-2 used this pool and has finished
+            A.sb_sched_destroy(pools[b][1])
+            A.sb_kv_destroy(pools[b][0])
+        pools[b] = new_pool()
+        p = eng.launch(sched=pools[b][1], buf=b)
+        assert p is not None and len(p["ids"]) == B and int(p["n_new"].sum()) == T
+        return p
+
+    def run(n):
+        """n steps, pipelined: the host side of step k runs while the GPU works on step k-1;
+        step k-1 is then waited for and completed."""
+        prev = None
+        for k in range(n):
+            p = launch(k)
+            if prev is not None:
+                eng.finish(prev)
+            prev = p
+        eng.finish(prev)
 
     if args.calib_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
@@ -166,26 +187,37 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    for _ in range(args.warmup):
-        step()
+    run(args.warmup)
     torch.cuda.synchronize()
+    # timed steps: events only around the two kernels the roofline and bandwidth figures need
     A.sb_timing_reset()
-    A.sb_timing_enable(True)
+    A.sb_timing_enable(True, classes=[sb.KERNEL_CLASSES.index("gemm_ffn1"), sb.KERNEL_CLASSES.index("attention")])
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        res = step()
+    run(args.steps)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     A.sb_timing_enable(False)
-    kern = {}
-    for k, name in enumerate(sb.KERNEL_CLASSES):
-        ms, n = A.sb_timing_read(k)
-        if n:
-            kern[name] = {"ms_per_step": ms / args.steps, "launches_per_step": n / args.steps, "avg_ms": ms / n}
-    A.sb_timing_reset()
+
+    def read_classes(steps):
+        kern = {}
+        for k, name in enumerate(sb.KERNEL_CLASSES):
+            ms, n = A.sb_timing_read(k)
+            if n:
+                kern[name] = {"ms_per_step": ms / steps, "launches_per_step": n / steps, "avg_ms": ms / n}
+        A.sb_timing_reset()
+        return kern
+
+    kern = read_classes(args.steps)
+    # per-class breakdown: a few more steps with every class timed (not part of the timed region)
+    n_brk = 3
+    A.sb_timing_enable(True)
+    run(n_brk)
+    torch.cuda.synchronize()
+    A.sb_timing_enable(False)
+    brk = read_classes(n_brk)
     ms_step = 1000.0 * wall / args.steps
-    gpu_ms = sum(v["ms_per_step"] for v in kern.values())
+    gpu_ms = sum(v["ms_per_step"] for v in brk.values())
 
     # roofline of the dominant kernel: the FFN1 (SwiGLU) GEMM, one launch per layer
     f1 = kern["gemm_ffn1"]
@@ -200,7 +232,7 @@ def main():
     at = kern["attention"]
     attn_gbs = work["attn_bytes_per_layer"] / (at["avg_ms"] * 1e-3) / 1e9
     gemm_flops = sum(work["gemm_per_layer"].values()) * m.n_layers + work["lm_flops"]
-    gemm_ms = sum(kern[k]["ms_per_step"] for k in ("gemm_qkv", "gemm_o", "gemm_ffn1", "gemm_ffn2", "gemm_lm"))
+    gemm_ms = sum(brk[k]["ms_per_step"] for k in ("gemm_qkv", "gemm_o", "gemm_ffn1", "gemm_ffn2", "gemm_lm"))
     out = {
         "metric": "tokens/s per selective-batched iteration; MFMA % + attention HBM GB/s",
         "value": round(T / (ms_step * 1e-3), 1),
@@ -228,11 +260,15 @@ def main():
                       "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "avg_launch_ms": round(at["avg_ms"], 4),
                       "bytes_per_launch": work["attn_bytes_per_layer"],
                       "decode_kv_bytes_per_launch": work["attn_decode_bytes_per_layer"]},
-        "kernels_ms_per_step": {k: round(v["ms_per_step"], 3) for k, v in kern.items()},
+        "kernels_ms_per_step": {k: round(v["ms_per_step"], 3) for k, v in brk.items()},
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample ...", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(m.with_layers(args.layers), batch, args.seed)
+    for pool in pools:
+        if pool is not None:
+            A.sb_sched_destroy(pool[1])
+            A.sb_kv_destroy(pool[0])
     eng.close()
     print(json.dumps(out), flush=True)
 

@@ -228,10 +228,14 @@ int sb_lm_argmax(const sb_model_dims* dims, const sb_model_weights* w, const sb_
 
 /* ------------------------------------------------------------------ timing
  * Per-kernel-class HIP event timing of launches made by the library (for
- * benchmarks).  Enabling adds an event pair around every launch.            */
+ * benchmarks): an event pair is recorded on the launch stream around every
+ * launch of an enabled class, which itself costs time, so enable only the
+ * classes to be measured.                                                    */
 enum { SB_K_GEMM_QKV = 0, SB_K_GEMM_O, SB_K_GEMM_FFN1, SB_K_GEMM_FFN2, SB_K_GEMM_LM, SB_K_ATTN,
        SB_K_ATTN_COMBINE, SB_K_NORM, SB_K_ROPE_APPEND, SB_K_EMBED, SB_K_ARGMAX, SB_K_COUNT };
-int sb_timing_enable(int32_t on);
+#define SB_TIMING_ALL (-1)
+/* mask: bit k enables class k (SB_TIMING_ALL: every class, 0: off). */
+int sb_timing_enable(int32_t mask);
 /* Sum of elapsed ms and number of launches of class k since the last reset;
  * synchronizes on the recorded events. */
 int sb_timing_read(int32_t k, double* total_ms, int64_t* count);

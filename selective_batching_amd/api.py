@@ -179,8 +179,12 @@ def sb_lm_argmax(dims, mw, rg, x, logits, out_ids, ws, ws_bytes, stream=None):
     call("sb_lm_argmax", C.byref(dims), C.byref(mw), C.byref(rg), x, logits, out_ids, ws, ws_bytes, stream)
 
 
-def sb_timing_enable(on):
-    call("sb_timing_enable", 1 if on else 0)
+def sb_timing_enable(on, classes=None):
+    """on=False: off; on=True: every class, or only the kernel-class indices in ``classes``."""
+    mask = 0
+    if on:
+        mask = -1 if classes is None else sum(1 << k for k in classes)
+    call("sb_timing_enable", mask)
 
 
 def sb_timing_read(k):

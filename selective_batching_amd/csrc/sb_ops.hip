@@ -25,7 +25,7 @@ int check_launch(const char* what) {
 namespace {
 struct TimingState {
     std::mutex mu;
-    bool on = false;
+    uint32_t mask = 0;                     // bit k: time launches of class k
     std::vector<std::pair<hipEvent_t, hipEvent_t>> ev[SB_K_COUNT];
     std::vector<hipEvent_t> open[SB_K_COUNT];
 };
@@ -37,7 +37,7 @@ TimingState& timing() {
 
 void timing_begin(int kind, hipStream_t s) {
     auto& T = timing();
-    if (!T.on) return;
+    if (!(T.mask >> kind & 1u)) return;
     std::lock_guard<std::mutex> g(T.mu);
     hipEvent_t e;
     if (hipEventCreate(&e) != hipSuccess) return;
@@ -47,7 +47,7 @@ void timing_begin(int kind, hipStream_t s) {
 
 void timing_end(int kind, hipStream_t s) {
     auto& T = timing();
-    if (!T.on) return;
+    if (!(T.mask >> kind & 1u)) return;
     std::lock_guard<std::mutex> g(T.mu);
     if (T.open[kind].empty()) return;
     hipEvent_t b = T.open[kind].back();
@@ -471,8 +471,8 @@ extern "C" int sb_kv_read(const sb_kv* kv, int32_t layer, int32_t n, const int32
 }
 
 // ------------------------------------------------------------------ timing ABI
-extern "C" int sb_timing_enable(int32_t on) {
-    timing().on = on != 0;
+extern "C" int sb_timing_enable(int32_t mask) {
+    timing().mask = (uint32_t)mask;
     return SB_OK;
 }
 

@@ -119,14 +119,18 @@ class Engine:
         self.sched = A.sb_sched_create(max_bs, self.kv)
         self.max_keys_total = max_keys_total if max_keys_total is not None else max_bs * (n_slots + 1)
         self.meta_bytes = A.sb_ragged_bytes(self.dims, max_bs, max_tokens, self.max_keys_total)
-        self.staging = torch.empty(self.meta_bytes, dtype=torch.uint8, pin_memory=True)
+        # two host staging buffers (and two host id buffers): the host can build iteration k+1's
+        # metadata while iteration k's copy from the other buffer is still queued on the stream
+        self.staging_bufs = [torch.empty(self.meta_bytes, dtype=torch.uint8, pin_memory=True) for _ in range(2)]
+        self.staging = self.staging_bufs[0]
         self.meta = torch.empty(self.meta_bytes, dtype=torch.uint8, device=device)
         self.max_partials = m.nkv * (self.max_keys_total // 512 + 2 * max_bs)
         self.ws_bytes = A.sb_layer_workspace_bytes(self.dims, max_tokens, max_bs, self.max_partials)
         self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
         self.x = torch.empty(max_tokens * m.H, dtype=torch.float32, device=device)
         self.ids_dev = torch.empty(max_bs, dtype=torch.int32, device=device)
-        self.ids_host = torch.empty(max_bs, dtype=torch.int32, pin_memory=True)
+        self.ids_host_bufs = [torch.empty(max_bs, dtype=torch.int32, pin_memory=True) for _ in range(2)]
+        self.ids_host = self.ids_host_bufs[0]
         self.logits = torch.empty(max_bs * max(m.V, 1), dtype=torch.float32, device=device) if m.V > 0 else None
 
     def close(self):
@@ -151,8 +155,8 @@ class Engine:
         A.sb_sched_add_running(self.sched, rid, arrival, prompt_len, out_len, max_tokens, generated, last_token)
 
     # ------------------------------------------------------------ device passes
-    def build(self, n_new, ctx, slot_base, tokens):
-        return A.sb_ragged_build(self.dims, n_new, ctx, slot_base, tokens, self.staging.data_ptr(),
+    def build(self, n_new, ctx, slot_base, tokens, buf=0):
+        return A.sb_ragged_build(self.dims, n_new, ctx, slot_base, tokens, self.staging_bufs[buf].data_ptr(),
                                  self.meta.data_ptr(), self.meta_bytes, stream_handle())
 
     def forward(self, rg, layer_outputs=None, x_in=None, head=True):
@@ -175,25 +179,43 @@ class Engine:
                        self.ids_dev.data_ptr(), self.ws.data_ptr(), self.ws_bytes, s)
         return self.ids_dev[:rg.n_req]
 
-    def step(self, keep=False):
-        """One scheduler iteration; returns None for an empty pool, else a dict of the batch and its results."""
-        ids, n_new, ctx, base = A.sb_select_batch(self.sched, self.max_bs)
+    def launch(self, sched=None, buf=0, keep=False):
+        """Select the next iteration from ``sched`` (default: this engine's scheduler), build its
+        metadata in staging buffer ``buf`` and enqueue all of its GPU work, without waiting.  Returns
+        None for an empty pool, else the pending iteration for ``finish``.  Two iterations may be in
+        flight when they use different ``buf``; their GPU work runs in stream order."""
+        sched = self.sched if sched is None else sched
+        ids, n_new, ctx, base = A.sb_select_batch(sched, self.max_bs)
         if len(ids) == 0:
             return None
-        toks = A.sb_batch_tokens(self.sched, ids, self.max_tokens)
-        rg = self.build(n_new, ctx, base, toks)
+        toks = A.sb_batch_tokens(sched, ids, self.max_tokens)
+        rg = self.build(n_new, ctx, base, toks, buf)
         outs = [] if keep else None
         self.forward(rg, layer_outputs=outs)
         B = len(ids)
-        self.ids_host[:B].copy_(self.ids_dev[:B], non_blocking=True)
-        torch.cuda.current_stream().synchronize()
-        new = self.ids_host[:B].numpy().copy()
-        finished = A.sb_sched_complete(self.sched, ids, new)
-        res = {"ids": ids, "n_new": n_new, "ctx": ctx, "slot_base": base, "tokens": new, "finished": finished}
-        if keep:
-            res["layer_outputs"] = [o.cpu() for o in outs]
+        self.ids_host_bufs[buf][:B].copy_(self.ids_dev[:B], non_blocking=True)
+        done = torch.cuda.Event()
+        done.record()
+        return {"sched": sched, "buf": buf, "ids": ids, "n_new": n_new, "ctx": ctx, "slot_base": base,
+                "event": done, "outs": outs}
+
+    def finish(self, p):
+        """Wait for a launched iteration, hand its new tokens to its scheduler (Complete)."""
+        p["event"].synchronize()
+        B = len(p["ids"])
+        new = self.ids_host_bufs[p["buf"]][:B].numpy().copy()
+        finished = A.sb_sched_complete(p["sched"], p["ids"], new)
+        res = {"ids": p["ids"], "n_new": p["n_new"], "ctx": p["ctx"], "slot_base": p["slot_base"], "tokens": new,
+               "finished": finished}
+        if p["outs"] is not None:
+            res["layer_outputs"] = [o.cpu() for o in p["outs"]]
             res["logits"] = self.logits[:B * self.m.V].view(B, self.m.V).cpu()
         return res
+
+    def step(self, keep=False):
+        """One scheduler iteration; returns None for an empty pool, else a dict of the batch and its results."""
+        p = self.launch(keep=keep)
+        return None if p is None else self.finish(p)
 
     def output(self, rid):
         return A.sb_sched_output(self.sched, rid)

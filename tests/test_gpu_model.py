@@ -385,3 +385,47 @@ def test_gpt175b_shape_layer_sampled():
     batch = gpt175b_mixed_batch(seed=0)
     pre = sorted(range(96, 128), key=lambda i: batch[i][0])[:1]
     _sampled_layer_parity(GPT175B_LAYER, "bf16", batch, [0, 50, 95] + pre, 0, kv_std(GPT175B_LAYER))
+
+
+def test_pipelined_launches_match_sequential_steps():
+    """Two iterations in flight (launch A, launch B, then finish A, finish B) give the same tokens as
+    running them one after the other.  The GPU is kept busy first so that both launches are queued
+    before A's metadata copy runs: each launch must keep its own staging and id buffers."""
+    m = MINI
+    W = DeviceWeights(m, "bf16", host=make_weights(m, 3, "bf16"))
+    prompts = {"A": {r: uniform_int(11, f"pipe.A{r}", 0, m.V - 1, 5 + 7 * r).tolist() for r in range(6)},
+               "B": {r: uniform_int(12, f"pipe.B{r}", 0, m.V - 1, 40 - 5 * r).tolist() for r in range(6)}}
+    n_tok = max(sum(len(p) for p in ps.values()) for ps in prompts.values())
+    eng = Engine(m, "bf16", W, n_slots=512, max_bs=8, max_tokens=n_tok, max_keys_total=512)
+
+    def pool(name):
+        kv = sb.sb_kv_create(512, eng.arena_slots, m.n_layers, m.nkv, m.d, sb.SB_BF16,
+                             eng.k_arena.data_ptr(), eng.v_arena.data_ptr())
+        sb.sb_kv_set_stream(kv, stream_handle())
+        s = sb.sb_sched_create(8, kv)
+        for r, p in prompts[name].items():
+            sb.sb_sched_add(s, r, float(r), p, 4, len(p) + 4)
+        return kv, s
+
+    def drop(kv, s):
+        sb.sb_sched_destroy(s)
+        sb.sb_kv_destroy(kv)
+
+    try:
+        seq = {}
+        for name in ("A", "B"):
+            kv, s = pool(name)
+            seq[name] = eng.finish(eng.launch(sched=s))["tokens"]
+            drop(kv, s)
+        (kva, sa), (kvb, sbb) = pool("A"), pool("B")
+        x = torch.randn(4096, 4096, device="cuda")
+        for _ in range(20):
+            x = torch.tanh(x @ x)
+        pa = eng.launch(sched=sa, buf=0)
+        pb = eng.launch(sched=sbb, buf=1)
+        ra, rb = eng.finish(pa), eng.finish(pb)
+        drop(kva, sa)
+        drop(kvb, sbb)
+        assert np.array_equal(ra["tokens"], seq["A"]) and np.array_equal(rb["tokens"], seq["B"])
+    finally:
+        eng.close()
