@@ -106,6 +106,21 @@ def cpu_baseline(m, batch, seed):
                        f"({t_lm:.2f} s); fp64 numpy, BLAS threads = {cores}")}
 
 
+def ffn1_traffic():
+    """HBM bytes per FFN1 GEMM launch (FETCH_SIZE + WRITE_SIZE counter runs, scaled by a 1 GiB copy) as
+    recorded in profiles/ffn1_gemm_traffic.json, or None when the GEMM sources changed since."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "ffn1_gemm_traffic.json")
+    try:
+        rec = json.load(open(path))
+        for src, digest in rec["sources_sha256"].items():
+            if hashlib.sha256(open(os.path.join(ROOT, src), "rb").read()).hexdigest() != digest:
+                return None
+        return rec["read_bytes_per_launch"] + rec["write_bytes_per_launch"]
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -179,7 +194,8 @@ def main():
             if prev is not None:
                 eng.finish(prev)
             prev = p
-        eng.finish(prev)
+        if prev is not None:
+            eng.finish(prev)
 
     if args.calib_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
@@ -227,7 +243,7 @@ def main():
                  "256x256x64 tiles, copies spread over the MFMAs)")
     roofline = {"kernel": kern_name, "bound": "mfma",
                 "achieved": round(f1_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(f1_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "frac": round(f1_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": ffn1_traffic(),
                 "flops_per_launch": f1_flops, "avg_launch_ms": round(f1["avg_ms"], 4)}
     at = kern["attention"]
     attn_gbs = work["attn_bytes_per_layer"] / (at["avg_ms"] * 1e-3) / 1e9
