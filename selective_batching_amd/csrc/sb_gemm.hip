@@ -52,6 +52,90 @@ __device__ __forceinline__ void swiglu_store(const GemmArgs& a, int m, int f, fl
         Store<DT>::st((typename Store<DT>::T*)a.C + (long long)m * a.ldc + f, v);
 }
 
+// Four consecutive outputs of one row as one 16-byte (fp32) or 8-byte (bf16) access.
+__device__ __forceinline__ void store4(const GemmArgs& a, long long off, const f32x4& v) {
+    if (a.out_f32) {
+        *(f32x4*)((float*)a.C + off) = v;
+    } else {
+        const uint32_t lo = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+        const uint32_t hi = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+        *(u32x2*)((uint16_t*)a.C + off) = u32x2{lo, hi};
+    }
+}
+
+// Whether outputs n..n+3 of a row may be written as one vector access: ldc and the
+// base pointer aligned for it (checked once per launch, wave-uniform).
+__device__ __forceinline__ bool vec4_ok(const GemmArgs& a, int epi) {
+    const int align = (epi == EPI_RESID || a.out_f32) ? 16 : 8;
+    return (a.ldc & 3) == 0 && ((uintptr_t)a.C & (uintptr_t)(align - 1)) == 0;
+}
+
+// Epilogue of outputs (m, n..n+3): v[r] is the accumulator of column n + r.
+template <int EPI>
+__device__ __forceinline__ void epi_store4(const GemmArgs& a, bool vec, int m, int n, f32x4 v) {
+    if (m >= a.M) return;
+    if (vec && n + 3 < a.N) {
+        if (a.bias) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v[r] += bias_at<SB_BF16>(a.bias, n + r);
+        }
+        if (EPI == EPI_GELU) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v[r] = gelu_exact(v[r]);
+        }
+        const long long off = (long long)m * a.ldc + n;
+        if (EPI == EPI_RESID) {
+            f32x4* x = (f32x4*)((float*)a.C + off);
+            *x = *x + v;
+        } else {
+            store4(a, off, v);
+        }
+    } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            if (n + r < a.N) epi_store<SB_BF16, EPI>(a, m, n + r, v[r]);
+    }
+}
+
+// SwiGLU outputs (m, f..f+3) from gate accumulators g and up accumulators u.
+__device__ __forceinline__ void swiglu_store4(const GemmArgs& a, bool vec, int m, int f, const f32x4& g,
+                                              const f32x4& u) {
+    if (m >= a.M) return;
+    if (vec && f + 3 < a.N) {
+        f32x4 v;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = silu(g[r]) * u[r];
+        store4(a, (long long)m * a.ldc + f, v);
+    } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            if (f + r < a.N) swiglu_store<SB_BF16>(a, m, f + r, g[r], u[r]);
+    }
+}
+
+// Epilogue of one wave's MI x NI blocks of C^T = W A^T.  The MFMAs take the
+// W fragment as their first operand, so lane (lr = lane % 16, lc = lane / 16)
+// of block (i, j) holds row m_lane + 16 i and the four consecutive columns
+// n_lane + 16 j + {0..3}: rows are written as 16- or 8-byte pieces.  For
+// SwiGLU the wave's blocks j < NI/2 are gate columns and j + NI/2 the matching
+// up columns; n_lane then indexes the output (F) columns.
+template <int MI, int NI, int EPI>
+__device__ __forceinline__ void tile_epilogue(const GemmArgs& a, const f32x4 (&acc)[MI][NI], int m_lane, int n_lane) {
+    const bool vec = vec4_ok(a, EPI);
+    if constexpr (EPI == EPI_SWIGLU) {
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int j = 0; j < NI / 2; ++j)
+                swiglu_store4(a, vec, m_lane + 16 * i, n_lane + 16 * j, acc[i][j], acc[i][j + NI / 2]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int j = 0; j < NI; ++j) epi_store4<EPI>(a, vec, m_lane + 16 * i, n_lane + 16 * j, acc[i][j]);
+    }
+}
+
 // ================================================================== bf16 MFMA
 // Workgroup tile BM x BN (BN counts W rows; for SwiGLU each wave's WN rows
 // are WN/2 gate rows then the matching WN/2 up rows), WAVES_M x WAVES_N waves,
@@ -158,38 +242,15 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_bf16_kernel(GemmA
                 const bf16x8 af = __builtin_bit_cast(bf16x8, *(const u32x4*)&As[buf][(wm * WM + i * 16 + lrow) * LDSK + ks * 32 + lk]);
 #pragma unroll
                 for (int j = 0; j < NI; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfr[j], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[j], af, acc[i][j], 0, 0, 0);
             }
         }
         if (kt + 1 < nk) stash(buf ^ 1);
         __syncthreads();
     }
 
-    // 16x16 MFMA result: lane holds rows 4*(lane/16) + r, column lane % 16
-    const int rbase = m0 + wm * WM + (lane >> 4) * 4;
-    if (EPI == EPI_SWIGLU) {
-        const int fbase = tn * (BN / 2) + wn * (WN / 2) + lrow;
-#pragma unroll
-        for (int i = 0; i < MI; ++i)
-#pragma unroll
-            for (int j = 0; j < NI / 2; ++j)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int m = rbase + i * 16 + r, f = fbase + j * 16;
-                    if (m < a.M && f < a.N) swiglu_store<SB_BF16>(a, m, f, acc[i][j][r], acc[i][j + NI / 2][r]);
-                }
-    } else {
-        const int nbase = tn * BN + wn * WN + lrow;
-#pragma unroll
-        for (int i = 0; i < MI; ++i)
-#pragma unroll
-            for (int j = 0; j < NI; ++j)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int m = rbase + i * 16 + r, n = nbase + j * 16;
-                    if (m < a.M && n < a.N) epi_store<SB_BF16, EPI>(a, m, n, acc[i][j][r]);
-                }
-    }
+    const int n_lane = (EPI == EPI_SWIGLU ? tn * (BN / 2) + wn * (WN / 2) : tn * BN + wn * WN) + (lane >> 4) * 4;
+    tile_epilogue<MI, NI, EPI>(a, acc, m0 + wm * WM + lrow, n_lane);
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -355,7 +416,7 @@ __global__ __launch_bounds__(64 * WAVES_M_ * WAVES_N_, MINW) void gemm_bf16_dma_
                     const bf16x8 af = ldA(h, i);
 #pragma unroll
                     for (int j = 0; j < NI; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfr[j], acc[i][j], 0, 0, 0);
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[j], af, acc[i][j], 0, 0, 0);
                     if constexpr (FEED == 1) spread_copies(h * MI + i, nstage, nk0, more);
                 }
             }
@@ -384,30 +445,8 @@ __global__ __launch_bounds__(64 * WAVES_M_ * WAVES_N_, MINW) void gemm_bf16_dma_
         stage = (stage + 1 == STAGES) ? 0 : stage + 1;
     }
 
-    const int rbase = m0 + wm * WM + (lane >> 4) * 4;
-    if (EPI == EPI_SWIGLU) {
-        const int fbase = tn * (BN / 2) + wn * (WN / 2) + lr;
-#pragma unroll
-        for (int i = 0; i < MI; ++i)
-#pragma unroll
-            for (int j = 0; j < NI / 2; ++j)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int m = rbase + i * 16 + r, f = fbase + j * 16;
-                    if (m < a.M && f < a.N) swiglu_store<SB_BF16>(a, m, f, acc[i][j][r], acc[i][j + NI / 2][r]);
-                }
-    } else {
-        const int nbase = tn * BN + wn * WN + lr;
-#pragma unroll
-        for (int i = 0; i < MI; ++i)
-#pragma unroll
-            for (int j = 0; j < NI; ++j)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int m = rbase + i * 16 + r, n = nbase + j * 16;
-                    if (m < a.M && n < a.N) epi_store<SB_BF16, EPI>(a, m, n, acc[i][j][r]);
-                }
-    }
+    const int n_lane = (EPI == EPI_SWIGLU ? tn * (BN / 2) + wn * (WN / 2) : tn * BN + wn * WN) + (lane >> 4) * 4;
+    tile_epilogue<MI, NI, EPI>(a, acc, m0 + wm * WM + lr, n_lane);
 }
 
 // ================================================================== fp32 FMA
