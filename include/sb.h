@@ -180,8 +180,8 @@ void sb_sched_destroy(sb_sched* s);
  * until the copy is done (pinned memory recommended).                        */
 typedef struct {
     int32_t n_req, n_tokens;       /* B and T = sum of n_new                         */
-    int32_t n_items, n_partials;   /* attention work items; split partial tiles      */
-    int32_t n_groups, max_new;     /* split-combine groups; max n_new in the batch   */
+    int32_t n_items, n_partials;   /* attention work items; unit partial tiles       */
+    int32_t n_groups, max_new;     /* unit-combine groups; max n_new in the batch    */
     const int32_t* cu_seqlens;     /* device [B+1]                                   */
     const int32_t* ctx_lens;       /* device [B]                                     */
     const int32_t* last_row;       /* device [B]  cu_seqlens[i+1]-1                  */
@@ -189,10 +189,14 @@ typedef struct {
     const int32_t* tok_slot;       /* device [T]  K/V slot of each row               */
     const int32_t* tok_ids;        /* device [T]  token id of each row (or NULL)     */
     const int32_t* items;          /* device [n_items][8] attention work list        */
-    const int32_t* groups;         /* device [n_groups][8] split-combine list        */
+    const int32_t* groups;         /* device [n_groups][8] unit-combine list         */
 } sb_ragged;
 
 size_t sb_ragged_bytes(const sb_model_dims* dims, int32_t max_req, int32_t max_tokens, int64_t max_keys_total);
+/* Upper bound of sb_ragged.n_partials over batches of at most max_req requests
+ * holding at most max_keys_total keys (cached + new) in total: sizes the
+ * attention part of the workspace (sb_layer_workspace_bytes' max_partials). */
+int64_t sb_attn_max_partials(const sb_model_dims* dims, int32_t max_req, int64_t max_keys_total);
 /* n_new, ctx: host [n_req]; slot_base: host [n_req]; token_ids: host [sum n_new] or NULL. */
 int sb_ragged_build(const sb_model_dims* dims, int32_t n_req, const int32_t* n_new, const int32_t* ctx,
                     const int64_t* slot_base, const int32_t* token_ids, void* host_staging,

@@ -86,6 +86,7 @@ _PROTOS = {
     "sb_sched_stats": (C.c_int, [vp, P(i32), P(i64), P(i64)]),
     "sb_sched_destroy": (None, [vp]),
     "sb_ragged_bytes": (sz, [P(sb_model_dims), i32, i32, i64]),
+    "sb_attn_max_partials": (i64, [P(sb_model_dims), i32, i64]),
     "sb_ragged_build": (C.c_int, [P(sb_model_dims), i32, vp, vp, vp, vp, vp, vp, sz, vp, P(sb_ragged)]),
     "sb_layer_workspace_bytes": (sz, [P(sb_model_dims), i32, i32, i32]),
     "sb_embed": (C.c_int, [P(sb_model_dims), P(sb_model_weights), P(sb_ragged), vp, vp]),

@@ -153,6 +153,10 @@ def sb_ragged_bytes(dims, max_req, max_tokens, max_keys_total):
     return int(lib.sb_ragged_bytes(C.byref(dims), max_req, max_tokens, max_keys_total))
 
 
+def sb_attn_max_partials(dims, max_req, max_keys_total):
+    return int(lib.sb_attn_max_partials(C.byref(dims), max_req, max_keys_total))
+
+
 def sb_ragged_build(dims, n_new, ctx, slot_base, token_ids, host_staging, dev_meta, nbytes, stream=None):
     n_new, ctx, base = _i32(n_new), _i32(ctx), _i64(slot_base)
     toks = None if token_ids is None else _i32(token_ids)

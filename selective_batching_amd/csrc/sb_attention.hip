@@ -20,16 +20,17 @@
 // ordered so the S^T accumulators are directly the bf16 P^T operand; P is
 // fed as a hi + lo pair of bf16 values (two MFMAs), which keeps P.V at about
 // fp32 accuracy -- decode is HBM-bound, so the extra MFMA is free there.
-//   MODE_KEYS (<= 16 rows: decode, small chunks): the 4 waves take interleaved
-//     32-key chunks; K/V go straight from HBM into MFMA operand registers
-//     (16-byte loads, the next chunk's loads in flight while the current one
-//     computes); the 4 partial softmax states merge through LDS.
+//   MODE_RUNS (<= 16 rows per request and K/V head: decodes, small chunks):
+//     the 4 waves take interleaved 32-key chunks of a run of 512-key units;
+//     K/V go straight from HBM into MFMA operand registers (16-byte loads,
+//     the next chunk's loads in flight while the current one computes, also
+//     across unit boundaries).  At the end of each unit the 4 wave states
+//     merge through LDS; a request with more than one unit leaves one partial
+//     state per unit, merged by attn_combine in unit order, so the result
+//     does not depend on the rest of the batch.
 //   MODE_ROWS (prefill tiles of 64 rows): each wave owns 16 rows; the
 //     workgroup stages 32-key K/V tiles through LDS (double-buffered) so the
 //     4 waves share every K/V byte.
-// Long single-tile items are split into fixed 512-key ranges; their partial
-// states are merged by attn_combine in a fixed order (deterministic and
-// independent of the rest of the batch).
 #include <cfloat>
 
 #include "sb_device.h"
@@ -50,7 +51,7 @@ struct AttnArgs {
     const int* cu;
     const int* ctx;
     const int* tok_slot;
-    const int* items;
+    const int* items;         // work items, one per workgroup
     float* part_o;            // [n_part][16][d]
     float* part_ml;           // [n_part][16][2]
     int nq, nkv, G;
@@ -106,27 +107,19 @@ __device__ __forceinline__ void softmax_chunk(float (&sc)[8], float& m, float& l
 // Keys of a 32-key chunk starting at key cb: S^T block b covers local keys
 // 8*(m/4) + 4*b + (m%4) for MFMA row m, so that lane (g = lane/16) ends up
 // with keys 8g..8g+7 -- exactly the P^T operand layout of the 16x16x32 MFMA.
-template <int D, bool FROM_LDS>
-__device__ __forceinline__ void chunk_bf16(const AttnArgs& a, WaveState<D>& st, const bf16x8 (&qf)[D / 32],
-                                           const uint16_t* Kp, const uint16_t* Vp, long long kslot0,
-                                           int cb, int key_end, int row_limit, int lane,
-                                           const uint16_t* ldsK, const uint16_t* ldsV, int lds_key0) {
+template <int D>
+__device__ __forceinline__ void chunk_bf16(const AttnArgs& a, WaveState<D>& st, const bf16x8 (&qf)[D / 32], int cb,
+                                           int key_end, int row_limit, int lane, const uint16_t* ldsK,
+                                           const uint16_t* ldsV) {
     const int lr = lane & 15, g = lane >> 4;
     float sc[8];
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
         const int kl = 8 * (lr >> 2) + 4 * b + (lr & 3);          // local key of MFMA row lr
-        const int key = cb + kl;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < D / 32; ++s) {
-            u32x4 kraw;
-            if (FROM_LDS) {
-                kraw = *(const u32x4*)(ldsK + (lds_key0 + kl) * (D + 8) + s * 32 + g * 8);
-            } else {
-                const int kk = min(key, key_end - 1);              // clamp: masked below
-                kraw = *(const u32x4*)(Kp + (kslot0 + kk) * D + s * 32 + g * 8);
-            }
+            const u32x4 kraw = *(const u32x4*)(ldsK + kl * (D + 8) + s * 32 + g * 8);
             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kraw), qf[s], acc, 0, 0, 0);
         }
         // acc[r]: key cb + 8g + 4b + r, row lr
@@ -153,13 +146,7 @@ __device__ __forceinline__ void chunk_bf16(const AttnArgs& a, WaveState<D>& st, 
     const bool any = k8 < key_end;
 #pragma unroll
     for (int db = 0; db < D / 16; ++db) {
-        u32x4 vraw;
-        if (FROM_LDS) {
-            vraw = *(const u32x4*)(ldsV + ((lds_key0 + 8 * g) / 8) * (D * 8 + 16) + (db * 16 + lr) * 8);
-        } else {
-            const long long blk = (kslot0 + min(k8, key_end - 1)) >> 3;
-            vraw = *(const u32x4*)(Vp + (blk * D + db * 16 + lr) * 8);
-        }
+        u32x4 vraw = *(const u32x4*)(ldsV + g * (D * 8 + 16) + (db * 16 + lr) * 8);
         if (k8 + 8 > key_end) {
             // zero the keys past the range (their memory may hold anything)
             union { u32x4 v; uint16_t h[8]; } vv;
@@ -175,7 +162,7 @@ __device__ __forceinline__ void chunk_bf16(const AttnArgs& a, WaveState<D>& st, 
     }
 }
 
-// K/V registers of one 32-key chunk for the direct-from-HBM path (MODE_KEYS):
+// K/V registers of one 32-key chunk for the direct-from-HBM path (MODE_RUNS):
 // K operands of the two S^T blocks and V^T operands of every 16-dim block.
 template <int D>
 struct ChunkRegs {
@@ -288,11 +275,76 @@ __device__ __forceinline__ void chunk_f32(const AttnArgs& a, WaveState<D>& st, c
         }
 }
 
+// Softmax state of one row over some keys: running max m (log2 units), sum l
+// and unnormalised output o over N dims.  merge2 folds state b into state a;
+// requests whose keys span several units merge their units' states with it in
+// unit order, inside the workgroup or in attn_combine -- the same operations
+// either way, so the result never depends on where the merge ran.
+__device__ __forceinline__ void merge_weights(float ma, float mb, float& M, float& wa, float& wb) {
+    M = fmaxf(ma, mb);
+    wa = (ma == kNegInf) ? 0.f : exp2f(ma - M);
+    wb = (mb == kNegInf) ? 0.f : exp2f(mb - M);
+}
+__device__ __forceinline__ float merge_val(float a, float wa, float b, float wb) { return fmaf(a, wa, b * wb); }
+
+// Per thread of a MODE_RUNS workgroup: row r = tid / 16, dims d0 .. d0 + DPT of that row.
+template <int D>
+struct RowState {
+    static constexpr int DPT = D * 16 / 256;
+    float m, l, o[DPT];
+};
+
+// Merge the four waves' states of one unit through LDS (fixed wave order) into
+// this thread's (row, dims) share u.  Called by all 256 threads; leaves every
+// wave's state reset for the next unit.
+template <int D>
+__device__ __forceinline__ void merge_unit(WaveState<D>& st, char* smem, RowState<D>& u) {
+    constexpr int DPT = RowState<D>::DPT;
+    float (*red_o)[16][D + 1] = (float (*)[16][D + 1])smem;
+    float (*red_m)[16] = (float (*)[16])(smem + kWaves * 16 * (D + 1) * 4);
+    float (*red_l)[16] = (float (*)[16])(smem + (kWaves * 16 * (D + 1) + kWaves * 16) * 4);
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, g = lane >> 4;
+    float l = st.l;                                  // this wave's row sum over the 4 lanes of the row
+    l += shfl_xor(l, 16);
+    l += shfl_xor(l, 32);
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) red_o[wave][lr][db * 16 + 4 * g + r] = st.o[db][r];
+    if (g == 0) {
+        red_m[wave][lr] = st.m;
+        red_l[wave][lr] = l;
+    }
+    state_init(st);
+    __syncthreads();
+    const int r = tid / (256 / 16);
+    const int d0 = (tid % (256 / 16)) * DPT;
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, red_m[w][r]);
+    float wts[kWaves], L = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        wts[w] = (red_m[w][r] == kNegInf) ? 0.f : exp2f(red_m[w][r] - M);
+        L = fmaf(red_l[w][r], wts[w], L);
+    }
+    u.m = M;
+    u.l = L;
+#pragma unroll
+    for (int e = 0; e < DPT; ++e) {
+        float o = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) o = fmaf(red_o[w][r][d0 + e], wts[w], o);
+        u.o[e] = o;
+    }
+    __syncthreads();                                 // LDS free for the next unit
+}
+
 template <int DT, int D>
 __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     using T = typename Store<DT>::T;
     constexpr int KT = 32;                                   // keys per LDS stage (MODE_ROWS)
-    // MODE_ROWS stages K/V tiles; MODE_KEYS merges wave states: one workgroup
+    // MODE_ROWS stages K/V tiles; MODE_RUNS merges wave states: one workgroup
     // uses only one of the two, so they share the LDS allocation.
     constexpr int LDS_K = (DT == SB_BF16) ? 2 * KT * (D + 8) : 0;
     constexpr int LDS_V = (DT == SB_BF16) ? 2 * (KT / 8) * (D * 8 + 16) : 0;
@@ -301,16 +353,13 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     __shared__ __attribute__((aligned(16))) char smem[BYTES_ROWS > BYTES_RED ? BYTES_ROWS : BYTES_RED];
     uint16_t* ldsK = (uint16_t*)smem;
     uint16_t* ldsV = ldsK + LDS_K;
-    float (*red_o)[16][D + 1] = (float (*)[16][D + 1])smem;
-    float (*red_m)[16] = (float (*)[16])(smem + kWaves * 16 * (D + 1) * 4);
-    float (*red_l)[16] = (float (*)[16])(smem + (kWaves * 16 * (D + 1) + kWaves * 16) * 4);
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int lr = lane & 15, g = lane >> 4;
     const int* it = a.items + (long long)blockIdx.x * kItemInts;
     const int req = it[ITEM_REQ], kvh = it[ITEM_KVH], mode = it[ITEM_MODE];
     const int row0 = it[ITEM_ROW0], nrows = it[ITEM_NROWS];
-    const int kb = it[ITEM_KB], ke = it[ITEM_KE], part = it[ITEM_PART];
+    const int kb = it[ITEM_KB], ke = it[ITEM_KE], part0 = it[ITEM_PART];
     const int tok0 = a.cu[req], ctx = a.ctx[req];
     const long long kslot0 = (long long)a.tok_slot[tok0] - ctx;   // slot of key 0 of this request
     const T* Kp = (const T*)a.K + (long long)kvh * a.arena * D;
@@ -328,6 +377,92 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     WaveState<D> st;
     state_init(st);
 
+    if (mode == MODE_RUNS) {
+        // Wave w takes chunks w, w + 4, ... of every unit; the chunk after a wave's last one in a unit
+        // is its first one in the next unit, so the loads run ahead across unit boundaries.
+        // End of each unit: merge the waves' states; then either store the unit's partial state
+        // (the request's units are spread over several runs: part0 >= 0) or fold it into this
+        // thread's running state of the request (the run covers all of the request's units).
+        constexpr int DPT = RowState<D>::DPT;
+        const int rr = tid / (256 / 16), d0 = (tid % (256 / 16)) * DPT;
+        RowState<D> acc;
+        auto end_unit = [&](int u0) {
+            RowState<D> u;
+            merge_unit<D>(st, smem, u);
+            if (part0 >= 0) {
+                if (rr < nrows) {
+                    const long long p = part0 + (u0 - kb) / kUnitKeys;
+                    float* po = a.part_o + (p * 16 + rr) * D + d0;
+#pragma unroll
+                    for (int e = 0; e < DPT; ++e) po[e] = u.o[e];
+                    if (d0 == 0) {
+                        a.part_ml[(p * 16 + rr) * 2 + 0] = u.m;
+                        a.part_ml[(p * 16 + rr) * 2 + 1] = u.l;
+                    }
+                }
+            } else if (u0 == kb) {
+                acc = u;
+            } else {
+                float M, wa, wb;
+                merge_weights(acc.m, u.m, M, wa, wb);
+                acc.l = merge_val(acc.l, wa, u.l, wb);
+#pragma unroll
+                for (int e = 0; e < DPT; ++e) acc.o[e] = merge_val(acc.o[e], wa, u.o[e], wb);
+                acc.m = M;
+            }
+        };
+        auto next_chunk = [&](int cb) {
+            const int u0 = cb - (cb - kb) % kUnitKeys;
+            const int n = cb + 32 * kWaves;
+            return n < min(u0 + kUnitKeys, ke) ? n : u0 + kUnitKeys + 32 * wave;
+        };
+        if constexpr (DT == SB_BF16) {
+            bf16x8 qf[D / 32];
+#pragma unroll
+            for (int s = 0; s < D / 32; ++s) {
+                u32x4 v = row_ok ? *(const u32x4*)(qrow + s * 32 + g * 8) : u32x4{0u, 0u, 0u, 0u};
+                qf[s] = __builtin_bit_cast(bf16x8, v);
+            }
+            const uint16_t* Kb = (const uint16_t*)Kp;
+            const uint16_t* Vb = (const uint16_t*)Vp;
+            ChunkRegs<D> cur, nxt;
+            int cb = kb + 32 * wave;                       // this wave's current chunk (>= ke: none left)
+            load_chunk_bf16<D>(cur, Kb, Vb, kslot0, min(cb, ke - 1), ke, lane);
+            for (int u0 = kb; u0 < ke; u0 += kUnitKeys) {
+                const int ue = min(u0 + kUnitKeys, ke);
+                while (cb < ue) {
+                    const int nb = next_chunk(cb);
+                    // issued whether or not a next chunk exists (then it re-reads this one): an
+                    // unconditional load lets the compiler keep it in flight during the compute
+                    load_chunk_bf16<D>(nxt, Kb, Vb, kslot0, nb < ke ? nb : cb, ke, lane);
+                    compute_chunk_bf16<D>(a, st, qf, cur, cb, ke, row_limit, lane);
+                    cur = nxt;
+                    cb = nb;
+                }
+                end_unit(u0);
+            }
+        } else {
+            float qf[D / 4];
+#pragma unroll
+            for (int s = 0; s < D / 4; ++s) qf[s] = row_ok ? ((const float*)qrow)[4 * s + g] : 0.f;
+            for (int u0 = kb; u0 < ke; u0 += kUnitKeys) {
+                const int ue = min(u0 + kUnitKeys, ke);
+                for (int cb = u0 + 32 * wave; cb < ue; cb += 32 * kWaves)
+                    chunk_f32<D>(a, st, qf, (const float*)Kp, (const float*)Vp, kslot0, cb, ke, row_limit, lane);
+                end_unit(u0);
+            }
+        }
+        // a run that covers all of its request's units: normalise the merged state
+        if (part0 < 0 && rr < nrows) {
+            const int tk = rr / a.G, hd = kvh * a.G + rr % a.G;
+            T* orow = (T*)a.out + (long long)(tok0 + tk) * a.out_stride + (long long)hd * D + d0;
+#pragma unroll
+            for (int e = 0; e < DPT; ++e) Store<DT>::st(orow + e, acc.o[e] / acc.l);
+        }
+        return;
+    }
+
+    // MODE_ROWS: stage 32-key tiles of K (row-major, padded rows) and V (8-key blocks, padded) in LDS
     if constexpr (DT == SB_BF16) {
         bf16x8 qf[D / 32];
 #pragma unroll
@@ -335,82 +470,57 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
             u32x4 v = row_ok ? *(const u32x4*)(qrow + s * 32 + g * 8) : u32x4{0u, 0u, 0u, 0u};
             qf[s] = __builtin_bit_cast(bf16x8, v);
         }
-        if (mode == MODE_KEYS) {
-            // software pipeline: the next chunk's K/V loads are in flight while this chunk computes
-            const uint16_t* Kb = (const uint16_t*)Kp;
-            const uint16_t* Vb = (const uint16_t*)Vp;
-            int cb = kb + 32 * wave;
-            if (cb < ke) {
-                ChunkRegs<D> cur, nxt;
-                load_chunk_bf16<D>(cur, Kb, Vb, kslot0, cb, ke, lane);
-                for (; cb < ke; cb += 32 * kWaves) {
-                    const bool more = cb + 32 * kWaves < ke;
-                    if (more) load_chunk_bf16<D>(nxt, Kb, Vb, kslot0, cb + 32 * kWaves, ke, lane);
-                    compute_chunk_bf16<D>(a, st, qf, cur, cb, ke, row_limit, lane);
-                    if (more) cur = nxt;
+        const int wave_max_limit = min(ke, ctx + min(wrow0 + 15, row0 + nrows - 1) / a.G + 1);
+        const int ntiles = (ke - kb + KT - 1) / KT;
+        constexpr int KCH = KT * D / 8;                    // 16-byte chunks per K tile
+        constexpr int PER = (KCH + 255) / 256;
+        u32x4 rk[PER], rv[PER];
+        auto gload = [&](int t) {
+            const int k0 = kb + t * KT;
+#pragma unroll
+            for (int q = 0; q < PER; ++q) {
+                const int c = tid + 256 * q;
+                if (c < KCH) {
+                    const int kk = c / (D / 8), dc = (c % (D / 8)) * 8;
+                    const long long slot = kslot0 + min(k0 + kk, ke - 1);
+                    rk[q] = *(const u32x4*)((const uint16_t*)Kp + slot * D + dc);
+                    // V: chunk c covers blocks (c / D) of 8 keys, dim c % D
+                    const int vb = c / D, vd = c % D;
+                    const long long vslot = kslot0 + min(k0 + vb * 8, ((ke - 1) & ~7));
+                    rv[q] = *(const u32x4*)((const uint16_t*)Vp + ((vslot >> 3) * D + vd) * 8);
                 }
             }
-        } else {
-            // stage 64-key tiles of K (row-major, padded rows) and V (8-key blocks, padded) in LDS
-            const int wave_max_limit = min(ke, ctx + min(wrow0 + 15, row0 + nrows - 1) / a.G + 1);
-            const int ntiles = (ke - kb + KT - 1) / KT;
-            constexpr int KCH = KT * D / 8;                    // 16-byte chunks per K tile
-            constexpr int PER = (KCH + 255) / 256;
-            u32x4 rk[PER], rv[PER];
-            auto gload = [&](int t) {
-                const int k0 = kb + t * KT;
+        };
+        auto lstore = [&](int buf) {
 #pragma unroll
-                for (int q = 0; q < PER; ++q) {
-                    const int c = tid + 256 * q;
-                    if (c < KCH) {
-                        const int kk = c / (D / 8), dc = (c % (D / 8)) * 8;
-                        const long long slot = kslot0 + min(k0 + kk, ke - 1);
-                        rk[q] = *(const u32x4*)((const uint16_t*)Kp + slot * D + dc);
-                        // V: chunk c covers blocks (c / D) of 8 keys, dim c % D
-                        const int vb = c / D, vd = c % D;
-                        const long long vslot = kslot0 + min(k0 + vb * 8, ((ke - 1) & ~7));
-                        rv[q] = *(const u32x4*)((const uint16_t*)Vp + ((vslot >> 3) * D + vd) * 8);
-                    }
+            for (int q = 0; q < PER; ++q) {
+                const int c = tid + 256 * q;
+                if (c < KCH) {
+                    const int kk = c / (D / 8), dc = (c % (D / 8)) * 8;
+                    *(u32x4*)(ldsK + buf * KT * (D + 8) + kk * (D + 8) + dc) = rk[q];
+                    const int vb = c / D, vd = c % D;
+                    *(u32x4*)(ldsV + buf * (KT / 8) * (D * 8 + 16) + vb * (D * 8 + 16) + vd * 8) = rv[q];
                 }
-            };
-            auto lstore = [&](int buf) {
-#pragma unroll
-                for (int q = 0; q < PER; ++q) {
-                    const int c = tid + 256 * q;
-                    if (c < KCH) {
-                        const int kk = c / (D / 8), dc = (c % (D / 8)) * 8;
-                        *(u32x4*)(ldsK + buf * KT * (D + 8) + kk * (D + 8) + dc) = rk[q];
-                        const int vb = c / D, vd = c % D;
-                        *(u32x4*)(ldsV + buf * (KT / 8) * (D * 8 + 16) + vb * (D * 8 + 16) + vd * 8) = rv[q];
-                    }
-                }
-            };
-            gload(0);
-            lstore(0);
+            }
+        };
+        gload(0);
+        lstore(0);
+        __syncthreads();
+        for (int t = 0; t < ntiles; ++t) {
+            const int buf = t & 1;
+            if (t + 1 < ntiles) gload(t + 1);
+            const int k0 = kb + t * KT;
+            if (k0 < wave_max_limit)
+                chunk_bf16<D>(a, st, qf, k0, ke, row_limit, lane, ldsK + buf * KT * (D + 8),
+                              ldsV + buf * (KT / 8) * (D * 8 + 16));
+            if (t + 1 < ntiles) lstore(buf ^ 1);
             __syncthreads();
-            for (int t = 0; t < ntiles; ++t) {
-                const int buf = t & 1;
-                if (t + 1 < ntiles) gload(t + 1);
-                const int k0 = kb + t * KT;
-                if (k0 < wave_max_limit) {
-                    for (int c2 = 0; c2 < KT / 32; ++c2) {
-                        const int cb = k0 + 32 * c2;
-                        if (cb < wave_max_limit)
-                            chunk_bf16<D, true>(a, st, qf, Kp, Vp, kslot0, cb, ke, row_limit, lane,
-                                                ldsK + buf * KT * (D + 8), ldsV + buf * (KT / 8) * (D * 8 + 16), 32 * c2);
-                    }
-                }
-                if (t + 1 < ntiles) lstore(buf ^ 1);
-                __syncthreads();
-            }
         }
     } else {
         float qf[D / 4];
 #pragma unroll
         for (int s = 0; s < D / 4; ++s) qf[s] = row_ok ? ((const float*)qrow)[4 * s + g] : 0.f;
-        const int step = (mode == MODE_KEYS) ? 32 * kWaves : 32;
-        const int first = (mode == MODE_KEYS) ? kb + 32 * wave : kb;
-        for (int cb = first; cb < ke; cb += step)
+        for (int cb = kb; cb < ke; cb += 32)
             chunk_f32<D>(a, st, qf, (const float*)Kp, (const float*)Vp, kslot0, cb, ke, row_limit, lane);
     }
 
@@ -418,71 +528,17 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     float l = st.l;
     l += shfl_xor(l, 16);
     l += shfl_xor(l, 32);
-
-    if (mode == MODE_ROWS) {
-        if (!row_ok) return;
-        const float inv = 1.f / l;
-        T* orow = (T*)a.out + (long long)(tok0 + tok) * a.out_stride + (long long)head * D;
-#pragma unroll
-        for (int db = 0; db < D / 16; ++db)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) Store<DT>::st(orow + db * 16 + 4 * g + r, st.o[db][r] * inv);
-        return;
-    }
-
-    // MODE_KEYS: merge the 4 waves' states (fixed order) through LDS
+    if (!row_ok) return;
+    const float inv = 1.f / l;
+    T* orow = (T*)a.out + (long long)(tok0 + tok) * a.out_stride + (long long)head * D;
 #pragma unroll
     for (int db = 0; db < D / 16; ++db)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) red_o[wave][lr][db * 16 + 4 * g + r] = st.o[db][r];
-    if (g == 0) {
-        red_m[wave][lr] = st.m;
-        red_l[wave][lr] = l;
-    }
-    __syncthreads();
-    // thread -> (row, dim range): 16 rows x D dims over 256 threads
-    constexpr int DPT = D * 16 / 256;                          // dims per thread
-    const int r = tid / (256 / 16);
-    const int d0 = (tid % (256 / 16)) * DPT;
-    float M = kNegInf;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, red_m[w][r]);
-    float wts[kWaves], L = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-        wts[w] = (red_m[w][r] == kNegInf) ? 0.f : exp2f(red_m[w][r] - M);
-        L += red_l[w][r] * wts[w];
-    }
-    const int rr = row0 + r;
-    if (rr >= row0 + nrows) return;
-    if (part < 0) {
-        const int tk = rr / a.G, hd = kvh * a.G + rr % a.G;
-        T* orow = (T*)a.out + (long long)(tok0 + tk) * a.out_stride + (long long)hd * D;
-        const float inv = 1.f / L;
-#pragma unroll
-        for (int e = 0; e < DPT; ++e) {
-            float o = 0.f;
-#pragma unroll
-            for (int w = 0; w < kWaves; ++w) o += red_o[w][r][d0 + e] * wts[w];
-            Store<DT>::st(orow + d0 + e, o * inv);
-        }
-    } else {
-        float* po = a.part_o + ((long long)part * 16 + r) * D;
-#pragma unroll
-        for (int e = 0; e < DPT; ++e) {
-            float o = 0.f;
-#pragma unroll
-            for (int w = 0; w < kWaves; ++w) o += red_o[w][r][d0 + e] * wts[w];
-            po[d0 + e] = o;
-        }
-        if (d0 == 0) {
-            a.part_ml[((long long)part * 16 + r) * 2 + 0] = M;
-            a.part_ml[((long long)part * 16 + r) * 2 + 1] = L;
-        }
-    }
+        for (int r = 0; r < 4; ++r) Store<DT>::st(orow + db * 16 + 4 * g + r, st.o[db][r] * inv);
 }
 
-// Merge the fixed-length key splits of one (request, K/V head) tile, in split order.
+// Merge the unit partials of one (request, K/V head) tile, in unit order, with
+// the same two-state merge the attention workgroups use for whole requests.
 template <int DT, int D>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, const int* groups) {
     using T = typename Store<DT>::T;
@@ -493,18 +549,18 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, const int
     for (int idx = threadIdx.x; idx < 16 * D; idx += 256) {
         const int r = idx / D, e = idx % D;
         if (r >= nrows) break;
-        float M = kNegInf;
-        for (int p = 0; p < np; ++p) M = fmaxf(M, a.part_ml[((long long)(p0 + p) * 16 + r) * 2]);
-        float L = 0.f, o = 0.f;
-        for (int p = 0; p < np; ++p) {
-            const float mp = a.part_ml[((long long)(p0 + p) * 16 + r) * 2];
-            if (mp == kNegInf) continue;
-            const float w = exp2f(mp - M);
-            L += a.part_ml[((long long)(p0 + p) * 16 + r) * 2 + 1] * w;
-            o += a.part_o[((long long)(p0 + p) * 16 + r) * D + e] * w;
+        const long long q0 = (long long)p0 * 16 + r;
+        float m = a.part_ml[q0 * 2], l = a.part_ml[q0 * 2 + 1], o = a.part_o[q0 * D + e];
+        for (int p = 1; p < np; ++p) {
+            const long long q = (long long)(p0 + p) * 16 + r;
+            float M, wa, wb;
+            merge_weights(m, a.part_ml[q * 2], M, wa, wb);
+            l = merge_val(l, wa, a.part_ml[q * 2 + 1], wb);
+            o = merge_val(o, wa, a.part_o[q * D + e], wb);
+            m = M;
         }
         const int rr = row0 + r, tk = rr / a.G, hd = kvh * a.G + rr % a.G;
-        Store<DT>::st((T*)a.out + (long long)(tok0 + tk) * a.out_stride + (long long)hd * D + e, o / L);
+        Store<DT>::st((T*)a.out + (long long)(tok0 + tk) * a.out_stride + (long long)hd * D + e, o / l);
     }
 }
 

@@ -465,17 +465,23 @@ Layout layout_for(int64_t B, int64_t T, int64_t n_items, int64_t n_groups) {
     return L;
 }
 
+// Row tiles: per (request, K/V head) ceil(rows / 64) <= rows / 64 + 1; runs: at most one per unit.
 int64_t max_items_bound(const sb_model_dims* d, int64_t B, int64_t T, int64_t keys) {
-    int64_t g = d->n_heads / d->n_kv_heads;
-    return (int64_t)d->n_kv_heads * ((T * g) / sb::kRowsPerTile + 2 * B + keys / sb::kSplitKeys + 1);
+    const int64_t g = d->n_heads / d->n_kv_heads, nkv = d->n_kv_heads;
+    return nkv * ((T * g) / sb::kRowsPerTile + B) + sb::max_units_bound(nkv, B, keys);
 }
 }  // namespace
 
 extern "C" size_t sb_ragged_bytes(const sb_model_dims* dims, int32_t max_req, int32_t max_tokens, int64_t max_keys_total) {
     if (sb::validate_dims(dims) || max_req < 0 || max_tokens < 0 || max_keys_total < 0) return 0;
-    int64_t items = max_items_bound(dims, max_req, max_tokens, max_keys_total);
-    int64_t groups = (int64_t)dims->n_kv_heads * max_req;
+    const int64_t items = max_items_bound(dims, max_req, max_tokens, max_keys_total);
+    const int64_t groups = (int64_t)dims->n_kv_heads * max_req;
     return layout_for(max_req, max_tokens, items, groups).total * sizeof(int32_t);
+}
+
+extern "C" int64_t sb_attn_max_partials(const sb_model_dims* dims, int32_t max_req, int64_t max_keys_total) {
+    if (sb::validate_dims(dims) || max_req < 0 || max_keys_total < 0) return 0;
+    return sb::max_units_bound(dims->n_kv_heads, max_req, max_keys_total);
 }
 
 extern "C" int sb_ragged_build(const sb_model_dims* dims, int32_t n_req, const int32_t* n_new, const int32_t* ctx,
@@ -502,33 +508,44 @@ extern "C" int sb_ragged_build(const sb_model_dims* dims, int32_t n_req, const i
     if (T >= (int64_t(1) << 31)) return fail(SB_ERR_INVALID, "too many tokens");
 
     // ---- attention work list (Split as offsets: each item names its request's rows and key range)
-    struct Item { int32_t v[sb::kItemInts]; int64_t cost; int64_t seq; };
+    struct Item { int32_t v[sb::kItemInts]; int64_t cost; };
     std::vector<Item> items;
     std::vector<std::array<int32_t, sb::kGroupInts>> groups;
+    // units of the single-tile (request, K/V head) pairs, to size the runs
+    int64_t n_units = 0;
+    for (int32_t i = 0; i < n_req; ++i)
+        if (n_new[i] * G <= sb::kRowsPerWave)
+            n_units += (int64_t)nkv * ((ctx[i] + n_new[i] + sb::kUnitKeys - 1) / sb::kUnitKeys);
+    // units per run: about kTargetRuns runs per launch -- long runs keep a workgroup streaming one
+    // request's keys, enough runs keep every CU busy.  Only the grouping depends on the batch.
+    const int32_t upr = (int32_t)std::max<int64_t>(1, (n_units + sb::kTargetRuns - 1) / sb::kTargetRuns);
     int32_t n_part = 0;
     for (int32_t i = 0; i < n_req; ++i) {
         const int32_t rows = n_new[i] * G;          // (token, query head of the group) rows
         const int32_t nk = ctx[i] + n_new[i];       // keys visible to the last row
         for (int32_t g = 0; g < nkv; ++g) {
             if (rows <= sb::kRowsPerWave) {
-                // one 16-row tile; the four waves split its keys; long histories split across workgroups
-                const int32_t ns = (nk + sb::kSplitKeys - 1) / sb::kSplitKeys;
-                const int32_t p0 = ns > 1 ? n_part : -1;
-                for (int32_t s = 0; s < ns; ++s) {
+                // one 16-row tile over units of kUnitKeys keys, grouped into runs of upr units; a
+                // request that fits one run merges its units itself, else each unit leaves a partial
+                const int32_t nu = (nk + sb::kUnitKeys - 1) / sb::kUnitKeys;
+                const int32_t p0 = nu > upr ? n_part : -1;
+                if (p0 >= 0) {
+                    groups.push_back({i, g, 0, rows, p0, nu, 0, 0});
+                    n_part += nu;
+                }
+                for (int32_t u = 0; u < nu; u += upr) {
                     Item it{};
                     it.v[sb::ITEM_REQ] = i;
                     it.v[sb::ITEM_KVH] = g;
-                    it.v[sb::ITEM_MODE] = sb::MODE_KEYS;
+                    it.v[sb::ITEM_MODE] = sb::MODE_RUNS;
                     it.v[sb::ITEM_ROW0] = 0;
                     it.v[sb::ITEM_NROWS] = rows;
-                    it.v[sb::ITEM_KB] = s * sb::kSplitKeys;
-                    it.v[sb::ITEM_KE] = std::min(nk, (s + 1) * sb::kSplitKeys);
-                    it.v[sb::ITEM_PART] = ns > 1 ? n_part++ : -1;
+                    it.v[sb::ITEM_KB] = u * sb::kUnitKeys;
+                    it.v[sb::ITEM_KE] = std::min(nk, (u + upr) * sb::kUnitKeys);
+                    it.v[sb::ITEM_PART] = p0 >= 0 ? p0 + u : -1;
                     it.cost = it.v[sb::ITEM_KE] - it.v[sb::ITEM_KB];
-                    it.seq = (int64_t)items.size();
                     items.push_back(it);
                 }
-                if (ns > 1) groups.push_back({i, g, 0, rows, p0, ns, 0, 0});
             } else {
                 // 64-row tiles; the four waves take 16 rows each and share K/V tiles through LDS
                 for (int32_t r0 = 0; r0 < rows; r0 += sb::kRowsPerTile) {
@@ -544,7 +561,6 @@ extern "C" int sb_ragged_build(const sb_model_dims* dims, int32_t n_req, const i
                     it.v[sb::ITEM_KE] = ctx[i] + last_tok + 1;
                     it.v[sb::ITEM_PART] = -1;
                     it.cost = 4 * (int64_t)it.v[sb::ITEM_KE];
-                    it.seq = (int64_t)items.size();
                     items.push_back(it);
                 }
             }

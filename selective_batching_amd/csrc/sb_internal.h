@@ -20,15 +20,31 @@ inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 inline size_t dtype_size(int dt) { return dt == SB_BF16 ? 2 : 4; }
 
 // Attention work decomposition (shared by the work-list builder and the kernel).
+// Every work item is one workgroup of kWaves waves:
+//  * MODE_ROWS: a tile of up to 64 (token, head) rows of one request and K/V
+//    head against keys [0, ke); each wave owns 16 rows.
+//  * MODE_RUNS: the <= 16 rows of one request and K/V head against a run of
+//    keys [kb, ke): a whole number of kUnitKeys-key units (the request's last
+//    unit may be short).  The waves take interleaved 32-key chunks of each
+//    unit and merge their states at its end, so each unit is reduced the same
+//    way wherever it falls.  A request with more than one unit leaves one
+//    partial state per unit (index ITEM_PART + unit - kb / kUnitKeys), merged
+//    by the combine step in unit order: results depend only on the request,
+//    never on how the builder grouped units into runs.
 constexpr int kRowsPerWave = 16;          // one 16x16 MFMA tile of (token, head) rows
 constexpr int kWaves = 4;                 // waves per attention workgroup
 constexpr int kRowsPerTile = kRowsPerWave * kWaves;
-constexpr int kSplitKeys = 512;           // fixed key-split length of single-tile items
+constexpr int kUnitKeys = 512;            // keys per independently reduced unit
+constexpr int kTargetRuns = 1024;         // runs per launch the builder aims at (balance vs. run length)
 constexpr int kItemInts = 8;
 constexpr int kGroupInts = 8;
 enum { ITEM_REQ = 0, ITEM_KVH, ITEM_MODE, ITEM_ROW0, ITEM_NROWS, ITEM_KB, ITEM_KE, ITEM_PART };
-enum { MODE_ROWS = 0, MODE_KEYS = 1 };
+enum { MODE_ROWS = 0, MODE_RUNS = 1 };
 enum { GRP_REQ = 0, GRP_KVH, GRP_ROW0, GRP_NROWS, GRP_PART0, GRP_NPARTS };
+
+// Upper bound of the units (and so of the partials and runs) of a batch of at most B requests holding
+// `keys` keys in all, per K/V head: every request adds at most one short unit.
+inline int64_t max_units_bound(int64_t nkv, int64_t B, int64_t keys) { return nkv * (keys / kUnitKeys + B); }
 
 int validate_dims(const sb_model_dims* d);
 

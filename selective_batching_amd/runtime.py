@@ -124,7 +124,7 @@ class Engine:
         self.staging_bufs = [torch.empty(self.meta_bytes, dtype=torch.uint8, pin_memory=True) for _ in range(2)]
         self.staging = self.staging_bufs[0]
         self.meta = torch.empty(self.meta_bytes, dtype=torch.uint8, device=device)
-        self.max_partials = m.nkv * (self.max_keys_total // 512 + 2 * max_bs)
+        self.max_partials = A.sb_attn_max_partials(self.dims, max_bs, self.max_keys_total)
         self.ws_bytes = A.sb_layer_workspace_bytes(self.dims, max_tokens, max_bs, self.max_partials)
         self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
         self.x = torch.empty(max_tokens * m.H, dtype=torch.float32, device=device)

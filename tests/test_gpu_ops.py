@@ -275,3 +275,60 @@ def test_gemm_configs_bitwise_identical(epi, monkeypatch):
         outs.append(out.view(torch.int16).cpu())
     for cfg in range(1, N_GEMM_CFGS):
         assert torch.equal(outs[cfg], outs[0]), f"cfg {cfg} differs from cfg 0"
+
+
+def test_attention_unit_merge_is_batch_invariant():
+    """A request's attention output does not depend on the batch around it.  Alone, its 512-key units are
+    spread over several workgroups and merged by the combine step; among 400 long requests one workgroup
+    runs all of its units and merges them itself.  Both must give the same bits (and match the oracle)."""
+    m = GQA_BF16
+    dims = make_dims(m, "bf16")
+    G = m.nq // m.nkv
+    batch = [(1, 1500 + (i % 7) * 37) for i in range(400)]
+    print_case("attention batch invariance", m.name, len(batch))
+    n_slots = sum(n + c for n, c in batch) + 8 * len(batch)
+    arena = sb.sb_kv_arena_slots(n_slots, len(batch))
+    nbytes = sb.sb_kv_arena_bytes(arena, 1, m.nkv, m.d, sb.SB_BF16)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(11)
+    ka = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda").normal_(generator=gen)
+    va = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda").normal_(generator=gen)
+    kv = sb.sb_kv_create(n_slots, arena, 1, m.nkv, m.d, sb.SB_BF16, ka.data_ptr(), va.data_ptr())
+    try:
+        bases = [sb.sb_kv_reserve(kv, i, n + c) for i, (n, c) in enumerate(batch)]
+        qkv_all = dev(normal(12, "qkv", (len(batch), m.qkv_out), dtype="bf16"), "bf16")
+
+        def run(idx):
+            sub = [batch[i] for i in idx]
+            T = len(idx)
+            nb = sb.sb_ragged_bytes(dims, T, T, n_slots)
+            staging = torch.empty(nb, dtype=torch.uint8, pin_memory=True)
+            meta = torch.empty(nb, dtype=torch.uint8, device="cuda")
+            rg = sb.sb_ragged_build(dims, [n for n, _ in sub], [c for _, c in sub], [bases[i] for i in idx], None,
+                                    staging.data_ptr(), meta.data_ptr(), nb, stream_handle())
+            qkv = qkv_all[list(idx)].contiguous()
+            o = torch.zeros((T, m.nq * m.d), dtype=torch.bfloat16, device="cuda")
+            ws = torch.empty(max(rg.n_partials, 1) * 16 * (m.d + 2) * 4, dtype=torch.uint8, device="cuda")
+            sb.sb_op_attention(dims, rg, kv, 0, qkv.data_ptr(), o.data_ptr(), ws.data_ptr(), ws.numel(),
+                               stream_handle())
+            _sync()
+            return o, rg.n_groups
+
+        o_big, groups_big = run(range(len(batch)))
+        for r in (0, 3, 6):
+            o_one, groups_one = run([r])
+            assert groups_one == m.nkv                 # alone: split over workgroups, combined
+            assert torch.equal(o_one[0].view(torch.int16), o_big[r].view(torch.int16)), f"request {r}"
+        assert groups_big < m.nkv * len(batch)          # in the big batch most requests merge in one workgroup
+        # and the result is the attention of the stored q, K, V
+        n, c = batch[0]
+        slots = torch.arange(bases[0], bases[0] + c + n, dtype=torch.int32, device="cuda")
+        kk = torch.zeros((c + n, m.nkv, m.d), dtype=torch.bfloat16, device="cuda")
+        vv = torch.zeros_like(kk)
+        sb.sb_kv_read(kv, 0, c + n, slots.data_ptr(), kk.data_ptr(), vv.data_ptr(), stream_handle())
+        _sync()
+        q = host(qkv_all[0:1, :m.nq * m.d]).reshape(1, m.nq, m.d)
+        want = OM.attention(q, host(kk), host(vv), c, G).reshape(1, -1)
+        assert_close_elem(host(o_big[0:1]), want, "bf16", "attention of a merged request")
+    finally:
+        sb.sb_kv_destroy(kv)

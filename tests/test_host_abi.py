@@ -225,49 +225,82 @@ def test_ragged_metadata_pinned_batches(name):
     assert list(_arr(rg.tok_slot, T)) == want_slots
 
 
+UNIT = 512   # keys per independently reduced unit (the library's kUnitKeys)
+
+
 def _coverage(m, batch, rg):
-    """Every (request, kv head, row) must see every visible key exactly once across the work items."""
+    """Every (request, kv head, row) must see every visible key exactly once across the work items: row tiles
+    (mode 0) and runs of whole key units (mode 1); a request split over several runs leaves one partial per
+    unit, named in order by one combine group."""
     G = m.nq // m.nkv
     items = _arr(rg.items, rg.n_items * 8).reshape(-1, 8)
-    seen = {}
+    spans = {}          # (request, kv head, row) -> key intervals seen by that row
     for req, kvh, mode, row0, nrows, kb, ke, part in items:
-        assert 0 <= kb < ke
-        assert nrows <= (64 if mode == 0 else 16)
         n_new, ctx = batch[req]
+        assert 0 <= kb < ke <= n_new + ctx
+        if mode == 0:
+            assert nrows <= 64 and kb == 0 and part == -1
+        else:
+            assert mode == 1 and row0 == 0 and nrows == n_new * G <= 16
+            assert kb % UNIT == 0 and ((ke - kb) % UNIT == 0 or ke == n_new + ctx)
         for r in range(row0, row0 + nrows):
             tok = r // G
             assert tok < n_new
-            lim = min(ke, ctx + tok + 1)
-            for k in range(kb, lim):
-                key = (req, kvh, r, k)
-                assert key not in seen
-                seen[key] = 1
-    want = sum(m.nkv * sum(c + j + 1 for j in range(n) for _ in range(G)) for n, c in batch)
-    assert len(seen) == want
-    # split items come with a combine group naming exactly their partial tiles
+            hi = min(ke, ctx + tok + 1)
+            if hi > kb:
+                spans.setdefault((req, kvh, r), []).append((kb, hi))
+    # each row's intervals tile [0, ctx + tok + 1) exactly: no key missed, none seen twice
+    for req, (n_new, ctx) in enumerate(batch):
+        for kvh in range(m.nkv):
+            for r in range(n_new * G):
+                iv = sorted(spans.pop((req, kvh, r)))
+                assert iv[0][0] == 0 and iv[-1][1] == ctx + r // G + 1
+                assert all(a[1] == b[0] for a, b in zip(iv, iv[1:]))
+    assert not spans
     groups = _arr(rg.groups, rg.n_groups * 8).reshape(-1, 8)
-    parts = sorted(int(p) for p in items[:, 7] if p >= 0)
-    assert parts == list(range(rg.n_partials))
-    assert sum(int(gp[5]) for gp in groups) == rg.n_partials
+    p0 = {}
+    for req, kvh, row0, nrows, gp0, np_, _, _ in groups:
+        n_new, ctx = batch[req]
+        assert np_ == -(-(n_new + ctx) // UNIT) > 1 and row0 == 0 and nrows == n_new * G
+        p0[(req, kvh)] = gp0
+    assert sorted(int(g[4]) + u for g in groups for u in range(g[5])) == list(range(rg.n_partials))
+    runs = items[items[:, 2] == 1]
+    for req, kvh, _, _, _, kb, ke, part in runs:
+        if part >= 0:       # one of several runs of the request: partials of its units, in unit order
+            assert part == p0[(req, kvh)] + kb // UNIT
+        else:               # the run covers all of the request's units
+            assert (req, kvh) not in p0 and kb == 0 and ke == sum(batch[req])
 
 
 @pytest.mark.parametrize("m,dtype", [(TOY, "fp32"), (MINI, "bf16"), (LLAMA8B, "bf16")])
 @pytest.mark.parametrize("seed", range(4))
 def test_attention_work_list_covers_each_pair_once(m, dtype, seed):
     batch = random_ragged_batch(seed, 6, 1100, 40)
-    rg, _, _ = host_ragged(m, dtype, batch)
+    rg, buf, _ = host_ragged(m, dtype, batch)
     _coverage(m, batch, rg)
 
 
 def test_attention_work_list_llama_mixed_batch_counts():
     batch = llama_mixed_batch(seed=0)
-    rg, _, _ = host_ragged(LLAMA8B, "bf16", batch)
+    rg, buf, _ = host_ragged(LLAMA8B, "bf16", batch)
     assert rg.n_req == 256 and rg.n_tokens == sum(n for n, _ in batch)
+    _coverage(LLAMA8B, batch, rg)
     items = _arr(rg.items, rg.n_items * 8).reshape(-1, 8)
     cost = np.where(items[:, 2] == 0, 4 * items[:, 6], items[:, 6] - items[:, 5])
     assert np.all(np.diff(cost) <= 0)                       # heaviest first
-    # pair count of the whole batch (Σ over requests of Σ_j (ctx + j + 1), per query head)
+    # at this size every decode's units fit one run: no partials, no combine
+    assert rg.n_partials == 0 and rg.n_groups == 0
     assert FL.useful_pairs(batch) > 0
+
+
+def test_attention_work_list_small_batch_one_unit_per_run():
+    """Few keys in all: one unit per run, so even a single long request spreads over many workgroups, and
+    the partials stay within the bound the workspace is sized by."""
+    batch = [(1, 2047)]
+    rg, buf, _ = host_ragged(LLAMA8B, "bf16", batch)
+    _coverage(LLAMA8B, batch, rg)
+    assert rg.n_items == 8 * 4 and rg.n_partials == 8 * 4 and rg.n_groups == 8
+    assert rg.n_partials <= sb.sb_attn_max_partials(make_dims(LLAMA8B, "bf16"), 1, 2048)
 
 
 def test_ragged_rejects_bad_input():
