@@ -89,68 +89,119 @@ __global__ __launch_bounds__(256) void embed_kernel(const int* ids, const int* p
     }
 }
 
+// Four / eight consecutive elements of a dtype row as one 8- or 16-byte access (bf16) or
+// one / two 16-byte accesses (fp32); the pointer is aligned to the access.
+template <int DT>
+__device__ __forceinline__ void load4(const typename Store<DT>::T* p, float (&v)[4]) {
+    if constexpr (DT == SB_BF16) {
+        const u32x2 w = *(const u32x2*)p;
+        v[0] = __uint_as_float(w.x << 16); v[1] = __uint_as_float(w.x & 0xffff0000u);
+        v[2] = __uint_as_float(w.y << 16); v[3] = __uint_as_float(w.y & 0xffff0000u);
+    } else {
+        const float4 w = *(const float4*)p;
+        v[0] = w.x; v[1] = w.y; v[2] = w.z; v[3] = w.w;
+    }
+}
+template <int DT>
+__device__ __forceinline__ void store4(typename Store<DT>::T* p, const float (&v)[4]) {
+    if constexpr (DT == SB_BF16) {
+        *(u32x2*)p = u32x2{(uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16),
+                           (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16)};
+    } else {
+        *(float4*)p = make_float4(v[0], v[1], v[2], v[3]);
+    }
+}
+template <int DT>
+__device__ __forceinline__ void load8(const typename Store<DT>::T* p, float (&v)[8]) {
+    float a[4], b[4];
+    load4<DT>(p, a);
+    load4<DT>(p + 4, b);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) { v[c] = a[c]; v[4 + c] = b[c]; }
+}
+template <int DT>
+__device__ __forceinline__ void store8(typename Store<DT>::T* p, const float (&v)[8]) {
+    const float a[4] = {v[0], v[1], v[2], v[3]}, b[4] = {v[4], v[5], v[6], v[7]};
+    store4<DT>(p, a);
+    store4<DT>(p + 4, b);
+}
+
 // LayerNorm (kind 0) or RMSNorm (kind 1) of fp32 rows into dtype rows; fp32
 // statistics, two passes over registers (mean, then centred second moment).
-constexpr int kNormMaxPerThread = 12;   // float4 chunks per thread: hidden <= 12288
-template <int DT>
+// WPR = 1: one wave per row (four rows per workgroup), sums by lane shuffles
+// only; WPR = 4: one row per workgroup (wide rows), sums through LDS.  16-byte
+// loads along the row; PER float4 chunks per lane: hidden <= 256 PER / WPR.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+template <int DT, int PER, int WPR>
 __global__ __launch_bounds__(256) void norm_kernel(const float* x, const int* row_map, const void* gam, const void* bet,
-                                                   void* out, int H, int kind, float eps) {
+                                                   void* out, int rows, int H, int kind, float eps) {
     using T = typename Store<DT>::T;
     __shared__ float red[4];
-    const int r = blockIdx.x;
+    constexpr int LANES = 64 * WPR;                        // threads per row
+    const int lane = threadIdx.x % LANES;
+    const int r = blockIdx.x * (4 / WPR) + threadIdx.x / LANES;
+    if (r >= rows) return;                                 // whole rows only: block-uniform when WPR = 4
+    auto row_sum = [&](float v) { return WPR == 1 ? wave_sum(v) : block_sum(v, red); };
     const long long src = row_map ? row_map[r] : r;
     const float4* xr = (const float4*)(x + src * H);
     const int n4 = H / 4;
-    float4 v[kNormMaxPerThread];
+    float4 v[PER];
     float s = 0.f;
 #pragma unroll
-    for (int q = 0; q < kNormMaxPerThread; ++q) {
-        const int i = threadIdx.x + 256 * q;
+    for (int q = 0; q < PER; ++q) {
+        const int i = lane + LANES * q;
         if (i < n4) {
             v[q] = xr[i];
             s += (v[q].x + v[q].y) + (v[q].z + v[q].w);
         }
     }
-    float mean = 0.f;
-    if (kind == 0) mean = block_sum(s, red) / H;
+    const float mean = kind == 0 ? row_sum(s) / H : 0.f;
     float s2 = 0.f;
 #pragma unroll
-    for (int q = 0; q < kNormMaxPerThread; ++q) {
-        const int i = threadIdx.x + 256 * q;
+    for (int q = 0; q < PER; ++q) {
+        const int i = lane + LANES * q;
         if (i < n4) {
             const float a = v[q].x - mean, b = v[q].y - mean, c = v[q].z - mean, d = v[q].w - mean;
             s2 += (a * a + b * b) + (c * c + d * d);
         }
     }
-    const float rstd = 1.0f / sqrtf(block_sum(s2, red) / H + eps);
+    const float rstd = 1.0f / sqrtf(row_sum(s2) / H + eps);
     const T* g = (const T*)gam;
     const T* b = (const T*)bet;
     T* o = (T*)out + (long long)r * H;
 #pragma unroll
-    for (int q = 0; q < kNormMaxPerThread; ++q) {
-        const int i = threadIdx.x + 256 * q;
+    for (int q = 0; q < PER; ++q) {
+        const int i = lane + LANES * q;
         if (i < n4) {
             const float xs[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
+            float gv[4], bv[4] = {0.f, 0.f, 0.f, 0.f}, y[4];
+            load4<DT>(g + 4 * i, gv);
+            if (b) load4<DT>(b + 4 * i, bv);
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const int e = 4 * i + c;
-                float y = (xs[c] - mean) * rstd * Store<DT>::ld(g + e);
-                if (b) y += Store<DT>::ld(b + e);
-                Store<DT>::st(o + e, y);
-            }
+            for (int c = 0; c < 4; ++c) y[c] = (xs[c] - mean) * rstd * gv[c] + bv[c];
+            store4<DT>(o + 4 * i, y);
         }
     }
 }
 
 // Per token: rotate q (in place in qkv) and k by the token's position
 // (Llama-style, rotate-half pairs (i, i + d/2), angle pos * theta^(-2i/d),
-// evaluated in double precision), then append k and v to the K/V manager's
-// arenas at the token's slot.
+// evaluated in double precision once per token), then append k and v to the
+// K/V manager's arenas at the token's slot.  Each thread takes 8 consecutive
+// dims of one half-head and the matching 8 of the other half (16-byte
+// accesses); rotated k is also written back to qkv.
+constexpr int kRopeMaxHalf = 64;        // head_dim <= 128
 template <int DT>
-__global__ __launch_bounds__(128) void rope_append_kernel(void* qkv, long long stride, const int* pos, const int* slot,
+__global__ __launch_bounds__(256) void rope_append_kernel(void* qkv, long long stride, const int* pos, const int* slot,
                                                           void* kplane, void* vplane, long long arena, int nq, int nkv,
                                                           int D, int rope, double log_theta) {
     using T = typename Store<DT>::T;
+    __shared__ float cs[kRopeMaxHalf], sn[kRopeMaxHalf];
     const int t = blockIdx.x;
     T* row = (T*)qkv + (long long)t * stride;
     const long long s = slot[t];
@@ -158,26 +209,50 @@ __global__ __launch_bounds__(128) void rope_append_kernel(void* qkv, long long s
     if (rope) {
         for (int i = threadIdx.x; i < half; i += blockDim.x) {
             const double inv = exp(-(2.0 * i / D) * log_theta);
-            double sn, cs;
-            sincos((double)pos[t] * inv, &sn, &cs);
-            const float c = (float)cs, sv = (float)sn;
-            for (int h = 0; h < nq + nkv; ++h) {
-                T* p = row + (long long)h * D;
-                const float x1 = Store<DT>::ld(p + i), x2 = Store<DT>::ld(p + i + half);
-                Store<DT>::st(p + i, x1 * c - x2 * sv);
-                Store<DT>::st(p + i + half, x2 * c + x1 * sv);
-            }
+            double sv, cv;
+            sincos((double)pos[t] * inv, &sv, &cv);
+            cs[i] = (float)cv;
+            sn[i] = (float)sv;
         }
         __syncthreads();
     }
-    const T* krow = row + (long long)nq * D;
-    const T* vrow = krow + (long long)nkv * D;
     T* K = (T*)kplane;
     T* V = (T*)vplane;
-    for (int idx = threadIdx.x; idx < nkv * D; idx += blockDim.x) {
-        const int g = idx / D, e = idx % D;
-        K[((long long)g * arena + s) * D + e] = krow[idx];
-        V[(long long)g * arena * D + (((s >> 3) * D + e) << 3) + (s & 7)] = vrow[idx];
+    const int cph = half / 8;                              // 8-dim chunks per half-head
+    for (int w = threadIdx.x; w < (nq + nkv) * cph; w += blockDim.x) {
+        const int h = w / cph, i0 = (w % cph) * 8;
+        if (!rope && h < nq) continue;                     // q untouched without rotation
+        T* p = row + (long long)h * D;
+        float x1[8], x2[8];
+        load8<DT>(p + i0, x1);
+        load8<DT>(p + i0 + half, x2);
+        if (rope) {
+            float y1[8], y2[8];
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                y1[c] = x1[c] * cs[i0 + c] - x2[c] * sn[i0 + c];
+                y2[c] = x2[c] * cs[i0 + c] + x1[c] * sn[i0 + c];
+            }
+#pragma unroll
+            for (int c = 0; c < 8; ++c) { x1[c] = y1[c]; x2[c] = y2[c]; }
+            store8<DT>(p + i0, x1);
+            store8<DT>(p + i0 + half, x2);
+        }
+        if (h >= nq) {
+            T* kp = K + ((long long)(h - nq) * arena + s) * D;
+            store8<DT>(kp + i0, x1);
+            store8<DT>(kp + i0 + half, x2);
+        }
+    }
+    // v: 8 consecutive dims per thread into the blocked layout [slot / 8][dim][slot % 8]
+    const T* vrow = row + (long long)(nq + nkv) * D;
+    for (int w = threadIdx.x; w < nkv * D / 8; w += blockDim.x) {
+        const int g = w / (D / 8), e0 = (w % (D / 8)) * 8;
+        float x[8];
+        load8<DT>(vrow + (long long)g * D + e0, x);
+        T* vp = V + (long long)g * arena * D + (((s >> 3) * D + e0) << 3) + (s & 7);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) Store<DT>::st(vp + 8 * c, x[c]);
     }
 }
 
@@ -207,17 +282,32 @@ __global__ __launch_bounds__(256) void kv_copy_kernel(const int* slots, void* kp
 }
 
 // Greedy token: index of the largest logit, lowest index among equal maxima.
-__global__ __launch_bounds__(256) void argmax_kernel(const float* logits, int V, int* out) {
+// One 1024-thread workgroup per row, 16-byte loads (the row is long: 128256
+// logits of the 8B-shaped vocabulary), each thread scanning ascending indices.
+constexpr int kArgmaxThreads = 1024;
+__device__ __forceinline__ void argmax_take(float v, int i, float& bv, int& bi, int sentinel) {
+    if (v > bv || (bi == sentinel && v == bv)) {   // ascending scan: keep the first maximum
+        bv = v;
+        bi = i;
+    }
+}
+__global__ __launch_bounds__(kArgmaxThreads) void argmax_kernel(const float* logits, int V, int* out) {
     const int r = blockIdx.x;
     const float* x = logits + (long long)r * V;
     float bv = -INFINITY;
     int bi = V;
-    for (int i = threadIdx.x; i < V; i += 256) {
-        const float v = x[i];
-        if (v > bv || (bi == V && v == bv)) {   // ascending scan: keep the first maximum
-            bv = v;
-            bi = i;
+    if ((V & 3) == 0) {
+        const float4* x4 = (const float4*)x;
+#pragma unroll 4
+        for (int k = threadIdx.x; k < V / 4; k += kArgmaxThreads) {
+            const float4 v = x4[k];
+            argmax_take(v.x, 4 * k, bv, bi, V);
+            argmax_take(v.y, 4 * k + 1, bv, bi, V);
+            argmax_take(v.z, 4 * k + 2, bv, bi, V);
+            argmax_take(v.w, 4 * k + 3, bv, bi, V);
         }
+    } else {
+        for (int i = threadIdx.x; i < V; i += kArgmaxThreads) argmax_take(x[i], i, bv, bi, V);
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
@@ -228,15 +318,16 @@ __global__ __launch_bounds__(256) void argmax_kernel(const float* logits, int V,
             bi = oi;
         }
     }
-    __shared__ float sv[4];
-    __shared__ int si[4];
+    constexpr int NW = kArgmaxThreads / 64;
+    __shared__ float sv[NW];
+    __shared__ int si[NW];
     if ((threadIdx.x & 63) == 0) {
         sv[threadIdx.x >> 6] = bv;
         si[threadIdx.x >> 6] = bi;
     }
     __syncthreads();
     if (threadIdx.x == 0) {
-        for (int w = 1; w < 4; ++w)
+        for (int w = 1; w < NW; ++w)
             if (sv[w] > bv || (sv[w] == bv && si[w] < bi)) {
                 bv = sv[w];
                 bi = si[w];
@@ -250,27 +341,39 @@ __global__ __launch_bounds__(256) void argmax_kernel(const float* logits, int V,
 int launch_norm(int dtype, int kind, int rows, int H, const float* x, const int* row_map, const void* g,
                 const void* b, float eps, void* out, hipStream_t s) {
     if (rows <= 0) return SB_OK;
-    if (H % 4 || H > 4 * 256 * kNormMaxPerThread) return fail(SB_ERR_INVALID, "norm: hidden must be a multiple of 4 and <= 12288");
+    if (H % 4 || H > 12288) return fail(SB_ERR_INVALID, "norm: hidden must be a multiple of 4 and <= 12288");
     TimedScope ts(SB_K_NORM, s);
-    if (dtype == SB_BF16)
-        hipLaunchKernelGGL(norm_kernel<SB_BF16>, dim3(rows), dim3(256), 0, s, x, row_map, g, b, out, H, kind, eps);
-    else
-        hipLaunchKernelGGL(norm_kernel<SB_F32>, dim3(rows), dim3(256), 0, s, x, row_map, g, b, out, H, kind, eps);
+    const dim3 block(256);
+    auto go = [&](auto kern, int rows_per_block) {
+        hipLaunchKernelGGL(kern, dim3((rows + rows_per_block - 1) / rows_per_block), block, 0, s, x, row_map, g, b,
+                           out, rows, H, kind, eps);
+    };
+    if (dtype == SB_BF16) {
+        if (H <= 1024) go(norm_kernel<SB_BF16, 4, 1>, 4);
+        else if (H <= 4096) go(norm_kernel<SB_BF16, 16, 1>, 4);
+        else go(norm_kernel<SB_BF16, 12, 4>, 1);
+    } else {
+        if (H <= 1024) go(norm_kernel<SB_F32, 4, 1>, 4);
+        else if (H <= 4096) go(norm_kernel<SB_F32, 16, 1>, 4);
+        else go(norm_kernel<SB_F32, 12, 4>, 1);
+    }
     return check_launch("norm");
 }
 
 int launch_rope_append(const sb_model_dims* d, const sb_ragged* rg, void* qkv, void* kp, void* vp, long long arena,
                        hipStream_t s) {
     if (rg->n_tokens <= 0) return SB_OK;
+    if (d->head_dim % 16 || d->head_dim / 2 > kRopeMaxHalf)
+        return fail(SB_ERR_INVALID, "rope/append: head_dim must be a multiple of 16 and <= %d", 2 * kRopeMaxHalf);
     TimedScope ts(SB_K_ROPE_APPEND, s);
     const long long stride = (long long)(d->n_heads + 2 * d->n_kv_heads) * d->head_dim;
     const int rope = d->arch == SB_ARCH_LLAMA;
     const double lt = log((double)d->rope_theta);
     if (d->dtype == SB_BF16)
-        hipLaunchKernelGGL(rope_append_kernel<SB_BF16>, dim3(rg->n_tokens), dim3(128), 0, s, qkv, stride, rg->tok_pos,
+        hipLaunchKernelGGL(rope_append_kernel<SB_BF16>, dim3(rg->n_tokens), dim3(256), 0, s, qkv, stride, rg->tok_pos,
                            rg->tok_slot, kp, vp, arena, d->n_heads, d->n_kv_heads, d->head_dim, rope, lt);
     else
-        hipLaunchKernelGGL(rope_append_kernel<SB_F32>, dim3(rg->n_tokens), dim3(128), 0, s, qkv, stride, rg->tok_pos,
+        hipLaunchKernelGGL(rope_append_kernel<SB_F32>, dim3(rg->n_tokens), dim3(256), 0, s, qkv, stride, rg->tok_pos,
                            rg->tok_slot, kp, vp, arena, d->n_heads, d->n_kv_heads, d->head_dim, rope, lt);
     return check_launch("rope_append");
 }
@@ -278,7 +381,7 @@ int launch_rope_append(const sb_model_dims* d, const sb_ragged* rg, void* qkv, v
 int launch_argmax(int rows, int V, const float* logits, int* out, hipStream_t s) {
     if (rows <= 0) return SB_OK;
     TimedScope ts(SB_K_ARGMAX, s);
-    hipLaunchKernelGGL(argmax_kernel, dim3(rows), dim3(256), 0, s, logits, V, out);
+    hipLaunchKernelGGL(argmax_kernel, dim3(rows), dim3(kArgmaxThreads), 0, s, logits, V, out);
     return check_launch("argmax");
 }
 
