@@ -46,6 +46,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode-loop", action="store_true", help="skip the mini-model generation loop")
     ap.add_argument("--layers", type=int, default=32, help="decoder layers (the workload has 32)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one 1 GiB device-to-device copy before the steps (calibrates HBM counters)")
@@ -104,6 +105,61 @@ def cpu_baseline(m, batch, seed):
             "sample": (f"{len(dec_idx)} decodes + {len(pre_idx)} prefill of the same batch ({tokens} tokens), "
                        f"one decoder layer timed ({t_layer:.2f} s) x {m.n_layers} layers + LM head "
                        f"({t_lm:.2f} s); fp64 numpy, BLAS threads = {cores}")}
+
+
+def decode_loop(seed, steps=64, reps=3):
+    """Generation loop on the mini model (4 layers, hidden 256, 8 heads, FFN 1024, vocab 4096, bf16):
+    64 requests in decode with cached context U[16, 256] (random K/V history), each generating ``steps``
+    more tokens.  Timed twice: the synchronous loop (each iteration waits for its ids before the next
+    Select) and the chained one (iteration t+1 selected and launched before t's ids reach the host).
+    Best of ``reps`` runs of each."""
+    import torch
+    from selective_batching_amd.runtime import DeviceWeights, Engine
+    from synth import MINI, mini_decode_batch, uniform_int
+    m = MINI
+    batch = mini_decode_batch(seed=seed)
+    B = len(batch)
+    W = DeviceWeights(m, "bf16", host=None, seed=seed)
+    n_slots = sum(c + steps + 1 for _, c in batch) + 8 * B
+    eng = Engine(m, "bf16", W, n_slots=n_slots, max_bs=B, max_tokens=B, max_keys_total=n_slots, zero_arena=False)
+    for a in (eng.k_arena, eng.v_arena):
+        a.view(torch.bfloat16).normal_(0.0, 1.0)
+    last = uniform_int(seed, "decode.last", 0, m.V - 1, B).tolist()
+    rid = [0]
+
+    def fill(n_steps):
+        for i, (_, c) in enumerate(batch):
+            eng.add_running(rid[0], float(i), c, n_steps + 1, c + n_steps + 1, 1, last[i])
+            rid[0] += 1
+
+    def sync(n_steps):
+        fill(n_steps)
+        k = 0
+        while eng.step() is not None:
+            k += 1
+        return k
+
+    def chained(n_steps):
+        fill(n_steps)
+        return eng.run_chained()
+
+    out = {}
+    for name, fn in (("synchronous", sync), ("chained", chained)):
+        fn(4)                                         # warm-up
+        best = None
+        for _ in range(reps):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            n = fn(steps)
+            torch.cuda.synchronize()
+            dt = time.perf_counter() - t0
+            assert n == steps
+            best = dt if best is None else min(best, dt)
+        out[name] = {"ms_per_step": round(1e3 * best / steps, 4), "tokens_per_s": round(B * steps / best, 1)}
+    eng.close()
+    return {"workload": (f"mini GPT (4 layers, hidden 256, 8 heads, FFN 1024, vocab 4096) bf16, random init; {B} "
+                         f"requests in decode, cached context U[16,256], {steps} generated tokens each"),
+            **out, "chained_speedup": round(out["synchronous"]["ms_per_step"] / out["chained"]["ms_per_step"], 3)}
 
 
 def ffn1_traffic():
@@ -278,6 +334,9 @@ def main():
                       "decode_kv_bytes_per_launch": work["attn_decode_bytes_per_layer"]},
         "kernels_ms_per_step": {k: round(v["ms_per_step"], 3) for k, v in brk.items()},
     }
+    if not args.no_decode_loop:
+        print("[bench] mini-model decode loop ...", file=sys.stderr, flush=True)
+        out["decode_loop"] = decode_loop(args.seed)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample ...", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(m.with_layers(args.layers), batch, args.seed)

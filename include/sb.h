@@ -165,6 +165,30 @@ int sb_batch_tokens(const sb_sched* s, int32_t n, const int64_t* ids, int32_t ca
  * requests are freed and their ids written to finished_ids (capacity n). */
 int sb_sched_complete(sb_sched* s, int32_t n, const int64_t* ids, const int32_t* new_tokens,
                       int32_t* n_finished, int64_t* finished_ids);
+
+/* Deferred completion, so the next iteration can be selected and launched
+ * while this one still runs on the GPU.  Completion depends only on counts
+ * (a request finishes when it has generated out_len tokens, [W] Algorithm 1
+ * lines on Complete), never on token values: this call does everything
+ * sb_sched_complete does -- advances every member, finishes and frees the
+ * ones that are done -- but leaves each member's new token value pending
+ * under *ticket.  Until sb_sched_set_tokens(ticket) supplies the values,
+ * sb_batch_tokens refuses (SB_ERR_STATE) a batch that needs one of them and
+ * sb_batch_token_refs refers to them instead. */
+int sb_sched_complete_deferred(sb_sched* s, int32_t n, const int64_t* ids, int32_t* n_finished,
+                               int64_t* finished_ids, int64_t* ticket);
+/* Values of a deferred completion's tokens (host [n], batch order of that
+ * iteration, n = its batch size).  SB_ERR_NOT_FOUND for an unknown or already
+ * settled ticket, SB_ERR_INVALID if n differs. */
+int sb_sched_set_tokens(sb_sched* s, int64_t ticket, int32_t n, const int32_t* tokens);
+/* As sb_batch_tokens, but a member whose last token is still pending gets the
+ * reference -(1 + j) instead of a token id, j being its row in the batch of the
+ * iteration that generated it (its row of that iteration's device id buffer,
+ * resolved by sb_embed_chained).  *ref_ticket receives that iteration's
+ * ticket, or -1 if no reference was needed; SB_ERR_STATE if the pending
+ * tokens come from more than one iteration. */
+int sb_batch_token_refs(const sb_sched* s, int32_t n, const int64_t* ids, int32_t cap, int32_t* tokens,
+                        int32_t* n_tokens, int64_t* ref_ticket);
 /* Generated tokens of a live or finished request (host, capacity cap). */
 int sb_sched_output(const sb_sched* s, int64_t req_id, int32_t cap, int32_t* tokens, int32_t* n);
 int sb_sched_stats(const sb_sched* s, int32_t* pool_size, int64_t* n_rsrv, int64_t* n_finished);
@@ -197,7 +221,9 @@ size_t sb_ragged_bytes(const sb_model_dims* dims, int32_t max_req, int32_t max_t
  * holding at most max_keys_total keys (cached + new) in total: sizes the
  * attention part of the workspace (sb_layer_workspace_bytes' max_partials). */
 int64_t sb_attn_max_partials(const sb_model_dims* dims, int32_t max_req, int64_t max_keys_total);
-/* n_new, ctx: host [n_req]; slot_base: host [n_req]; token_ids: host [sum n_new] or NULL. */
+/* n_new, ctx: host [n_req]; slot_base: host [n_req]; token_ids: host [sum n_new] or NULL.
+ * A token id is in [0, vocab) or a reference -(1 + j), j < 2^20, to row j of the
+ * previous iteration's device ids (sb_batch_token_refs); SB_ERR_INVALID otherwise. */
 int sb_ragged_build(const sb_model_dims* dims, int32_t n_req, const int32_t* n_new, const int32_t* ctx,
                     const int64_t* slot_base, const int32_t* token_ids, void* host_staging,
                     void* dev_meta, size_t bytes, void* stream, sb_ragged* out);
@@ -214,6 +240,13 @@ size_t sb_layer_workspace_bytes(const sb_model_dims* dims, int32_t max_tokens, i
 /* Token embedding (+ learned position for GPT) of every row: x[t] = E[id_t] (+ P[pos_t]). */
 int sb_embed(const sb_model_dims* dims, const sb_model_weights* w, const sb_ragged* rg, float* x,
              void* stream);
+/* The same, resolving token references -(1 + j) to prev_ids[j] (device int32
+ * [prev_n]: the previous iteration's sb_lm_argmax output, read in stream order,
+ * so it is never copied through the host).  A reference with j >= prev_n, or
+ * any id outside [0, vocab), embeds a clamped id: it cannot read outside the
+ * tables; the host-side checks of sb_ragged_build keep literal ids in range. */
+int sb_embed_chained(const sb_model_dims* dims, const sb_model_weights* w, const sb_ragged* rg,
+                     const int32_t* prev_ids, int32_t prev_n, float* x, void* stream);
 
 /* One decoder layer over the ragged batch ([W] Figure 5 data flow), in place on x:
  *   h = norm1(x); qkv = h W_qkv^T (+b); [RoPE q,k]; append k,v to the K/V

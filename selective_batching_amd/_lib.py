@@ -82,6 +82,9 @@ _PROTOS = {
     "sb_select_batch": (C.c_int, [vp, i32, vp, vp, vp, vp, P(i32)]),
     "sb_batch_tokens": (C.c_int, [vp, i32, vp, i32, vp, P(i32)]),
     "sb_sched_complete": (C.c_int, [vp, i32, vp, vp, P(i32), vp]),
+    "sb_sched_complete_deferred": (C.c_int, [vp, i32, vp, P(i32), vp, P(i64)]),
+    "sb_sched_set_tokens": (C.c_int, [vp, i64, i32, vp]),
+    "sb_batch_token_refs": (C.c_int, [vp, i32, vp, i32, vp, P(i32), P(i64)]),
     "sb_sched_output": (C.c_int, [vp, i64, i32, vp, P(i32)]),
     "sb_sched_stats": (C.c_int, [vp, P(i32), P(i64), P(i64)]),
     "sb_sched_destroy": (None, [vp]),
@@ -90,6 +93,7 @@ _PROTOS = {
     "sb_ragged_build": (C.c_int, [P(sb_model_dims), i32, vp, vp, vp, vp, vp, vp, sz, vp, P(sb_ragged)]),
     "sb_layer_workspace_bytes": (sz, [P(sb_model_dims), i32, i32, i32]),
     "sb_embed": (C.c_int, [P(sb_model_dims), P(sb_model_weights), P(sb_ragged), vp, vp]),
+    "sb_embed_chained": (C.c_int, [P(sb_model_dims), P(sb_model_weights), P(sb_ragged), vp, i32, vp, vp]),
     "sb_layer_step": (C.c_int, [P(sb_model_dims), P(sb_layer_weights), P(sb_ragged), vp, i32, vp, vp, sz, vp]),
     "sb_lm_argmax": (C.c_int, [P(sb_model_dims), P(sb_model_weights), P(sb_ragged), vp, vp, vp, vp, sz, vp]),
     "sb_timing_enable": (C.c_int, [i32]),

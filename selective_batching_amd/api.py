@@ -131,6 +131,31 @@ def sb_sched_complete(s, ids, new_tokens):
     return fin[:nf.value].copy()
 
 
+def sb_sched_complete_deferred(s, ids):
+    """Count-based Complete with the token values left pending; returns (finished ids, ticket)."""
+    ids = _i64(ids)
+    fin = np.zeros(max(len(ids), 1), np.int64)
+    nf = C.c_int32()
+    ticket = C.c_int64()
+    call("sb_sched_complete_deferred", s, len(ids), _ptr(ids), C.byref(nf), _ptr(fin), C.byref(ticket))
+    return fin[:nf.value].copy(), ticket.value
+
+
+def sb_sched_set_tokens(s, ticket, tokens):
+    toks = _i32(tokens)
+    call("sb_sched_set_tokens", s, ticket, len(toks), _ptr(toks))
+
+
+def sb_batch_token_refs(s, ids, cap):
+    """Token ids of the batch, pending ones as references -(1 + row); returns (tokens, ticket or -1)."""
+    ids = _i64(ids)
+    out = np.zeros(max(cap, 1), np.int32)
+    n = C.c_int32()
+    ticket = C.c_int64()
+    call("sb_batch_token_refs", s, len(ids), _ptr(ids), cap, _ptr(out), C.byref(n), C.byref(ticket))
+    return out[:n.value].copy(), ticket.value
+
+
 def sb_sched_output(s, req_id, cap=1 << 16):
     out = np.zeros(cap, np.int32)
     n = C.c_int32()
@@ -173,6 +198,10 @@ def sb_layer_workspace_bytes(dims, max_tokens, max_req, max_partials):
 
 def sb_embed(dims, mw, rg, x, stream=None):
     call("sb_embed", C.byref(dims), C.byref(mw), C.byref(rg), x, stream)
+
+
+def sb_embed_chained(dims, mw, rg, prev_ids, prev_n, x, stream=None):
+    call("sb_embed_chained", C.byref(dims), C.byref(mw), C.byref(rg), prev_ids, prev_n, x, stream)
 
 
 def sb_layer_step(dims, lw, rg, kv, layer, x, ws, ws_bytes, stream=None):

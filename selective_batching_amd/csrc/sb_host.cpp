@@ -234,6 +234,8 @@ struct Req {
     int64_t slot_base;
     std::vector<int32_t> prompt;
     std::vector<int32_t> out;
+    int64_t pending_ticket = -1;                    // deferred completion whose token value is not known yet
+    int32_t pending_row = -1;                       // this request's row in that iteration's batch
 };
 }  // namespace
 
@@ -245,6 +247,9 @@ struct sb_sched {
     std::unordered_map<int64_t, std::vector<int32_t>> done;
     int64_t next_order = 0;
     int64_t n_finished = 0;
+    // deferred completions: ticket -> (request id, position of the pending token in its output), batch order
+    std::map<int64_t, std::vector<std::pair<int64_t, int32_t>>> tickets;
+    int64_t next_ticket = 0;
 };
 
 extern "C" int sb_sched_create(int32_t max_bs, sb_kv* kv, sb_sched** out) {
@@ -378,6 +383,9 @@ extern "C" int sb_batch_tokens(const sb_sched* s, int32_t n, const int64_t* ids,
             t += r->prompt_len;
         } else {
             if (t + 1 > cap) return fail(SB_ERR_CAPACITY, "token capacity %d exceeded", cap);
+            if (r->pending_ticket >= 0)
+                return fail(SB_ERR_STATE, "request %lld: its last token is still pending (use sb_batch_token_refs)",
+                            (long long)ids[i]);
             if (tokens) tokens[t] = r->out.back();
             t += 1;
         }
@@ -386,8 +394,43 @@ extern "C" int sb_batch_tokens(const sb_sched* s, int32_t n, const int64_t* ids,
     return SB_OK;
 }
 
-extern "C" int sb_sched_complete(sb_sched* s, int32_t n, const int64_t* ids, const int32_t* new_tokens,
-                                 int32_t* n_finished, int64_t* finished_ids) {
+extern "C" int sb_batch_token_refs(const sb_sched* s, int32_t n, const int64_t* ids, int32_t cap, int32_t* tokens,
+                                   int32_t* n_tokens, int64_t* ref_ticket) {
+    if (!s || (n > 0 && !ids) || !n_tokens || !ref_ticket) return fail(SB_ERR_INVALID, "NULL argument");
+    int32_t t = 0;
+    int64_t ticket = -1;
+    for (int32_t i = 0; i < n; ++i) {
+        auto it = s->by_id.find(ids[i]);
+        if (it == s->by_id.end()) return fail(SB_ERR_NOT_FOUND, "request %lld not in the pool", (long long)ids[i]);
+        const Req* r = it->second.get();
+        if (r->state != ST_RUNNING) return fail(SB_ERR_STATE, "request %lld is not in the running batch", (long long)ids[i]);
+        if (r->generated == 0) {
+            if (t + r->prompt_len > cap) return fail(SB_ERR_CAPACITY, "token capacity %d exceeded", cap);
+            if (tokens) std::memcpy(tokens + t, r->prompt.data(), sizeof(int32_t) * r->prompt_len);
+            t += r->prompt_len;
+        } else {
+            if (t + 1 > cap) return fail(SB_ERR_CAPACITY, "token capacity %d exceeded", cap);
+            int32_t v = r->out.back();
+            if (r->pending_ticket >= 0) {
+                if (ticket >= 0 && ticket != r->pending_ticket)
+                    return fail(SB_ERR_STATE, "pending tokens of the batch come from more than one iteration");
+                ticket = r->pending_ticket;
+                v = -1 - r->pending_row;
+            }
+            if (tokens) tokens[t] = v;
+            t += 1;
+        }
+    }
+    *n_tokens = t;
+    *ref_ticket = ticket;
+    return SB_OK;
+}
+
+namespace {
+// Complete of Algorithm 1: every member generated one token (value new_tokens[i], or pending under
+// `ticket` when new_tokens is NULL and ticket >= 0); members that reached out_len finish and free slots.
+int complete_batch(sb_sched* s, int32_t n, const int64_t* ids, const int32_t* new_tokens, int64_t ticket,
+                   int32_t* n_finished, int64_t* finished_ids) {
     if (!s || (n > 0 && !ids)) return fail(SB_ERR_INVALID, "NULL argument");
     for (int32_t i = 0; i < n; ++i) {
         auto it = s->by_id.find(ids[i]);
@@ -395,9 +438,15 @@ extern "C" int sb_sched_complete(sb_sched* s, int32_t n, const int64_t* ids, con
         if (it->second->state != ST_RUNNING) return fail(SB_ERR_STATE, "request %lld did not run", (long long)ids[i]);
     }
     int32_t nf = 0;
+    std::vector<std::pair<int64_t, int32_t>> slots_of_ticket;
     for (int32_t i = 0; i < n; ++i) {
         Req* r = s->by_id.at(ids[i]).get();
         r->state = ST_INCREMENT;
+        if (ticket >= 0) {
+            slots_of_ticket.push_back({r->id, (int32_t)r->out.size()});
+            r->pending_ticket = ticket;
+            r->pending_row = i;
+        }
         r->out.push_back(new_tokens ? new_tokens[i] : 0);
         r->generated += 1;
         if (r->generated == r->out_len) {
@@ -411,7 +460,51 @@ extern "C" int sb_sched_complete(sb_sched* s, int32_t n, const int64_t* ids, con
             s->by_id.erase(r->id);
         }
     }
+    if (ticket >= 0) s->tickets[ticket] = std::move(slots_of_ticket);
     if (n_finished) *n_finished = nf;
+    return SB_OK;
+}
+}  // namespace
+
+extern "C" int sb_sched_complete(sb_sched* s, int32_t n, const int64_t* ids, const int32_t* new_tokens,
+                                 int32_t* n_finished, int64_t* finished_ids) {
+    return complete_batch(s, n, ids, new_tokens, -1, n_finished, finished_ids);
+}
+
+extern "C" int sb_sched_complete_deferred(sb_sched* s, int32_t n, const int64_t* ids, int32_t* n_finished,
+                                          int64_t* finished_ids, int64_t* ticket) {
+    if (!s || !ticket) return fail(SB_ERR_INVALID, "NULL argument");
+    const int64_t tk = s->next_ticket;
+    int st = complete_batch(s, n, ids, nullptr, tk, n_finished, finished_ids);
+    if (st) return st;
+    s->next_ticket++;
+    *ticket = tk;
+    return SB_OK;
+}
+
+extern "C" int sb_sched_set_tokens(sb_sched* s, int64_t ticket, int32_t n, const int32_t* tokens) {
+    if (!s || (n > 0 && !tokens)) return fail(SB_ERR_INVALID, "NULL argument");
+    auto t = s->tickets.find(ticket);
+    if (t == s->tickets.end()) return fail(SB_ERR_NOT_FOUND, "unknown or already settled ticket %lld", (long long)ticket);
+    if ((int32_t)t->second.size() != n)
+        return fail(SB_ERR_INVALID, "ticket %lld covers %zu requests, %d tokens given", (long long)ticket,
+                    t->second.size(), n);
+    for (int32_t i = 0; i < n; ++i) {
+        const int64_t id = t->second[i].first;
+        const int32_t pos = t->second[i].second;
+        auto live = s->by_id.find(id);
+        if (live != s->by_id.end()) {
+            Req* r = live->second.get();
+            r->out[pos] = tokens[i];
+            if (r->pending_ticket == ticket) {
+                r->pending_ticket = -1;
+                r->pending_row = -1;
+            }
+        } else {
+            s->done.at(id)[pos] = tokens[i];
+        }
+    }
+    s->tickets.erase(t);
     return SB_OK;
 }
 
@@ -445,6 +538,7 @@ extern "C" void sb_sched_destroy(sb_sched* s) { delete s; }
 // ============================================================== ragged metadata
 
 namespace {
+constexpr int32_t kMaxTokenRef = 1 << 20;            // token references -(1 + j), j < 2^20
 struct Layout {
     size_t cu, ctx, last, pos, slot, ids, items, groups, total;  // int32 offsets
 };
@@ -495,6 +589,14 @@ extern "C" int sb_ragged_build(const sb_model_dims* dims, int32_t n_req, const i
     const int32_t nkv = dims->n_kv_heads;
     int64_t T = 0, keys = 0;
     int32_t max_new = 0;
+    if (token_ids) {
+        int64_t nt = 0;
+        for (int32_t i = 0; i < n_req; ++i) nt += n_new[i] > 0 ? n_new[i] : 0;
+        for (int64_t t = 0; t < nt; ++t)
+            if (token_ids[t] < -kMaxTokenRef || (dims->vocab > 0 && token_ids[t] >= dims->vocab))
+                return fail(SB_ERR_INVALID, "token %lld: id %d outside [-%d, vocab)", (long long)t, token_ids[t],
+                            kMaxTokenRef);
+    }
     for (int32_t i = 0; i < n_req; ++i) {
         if (n_new[i] < 1 || ctx[i] < 0) return fail(SB_ERR_INVALID, "request %d: n_new must be >= 1 and ctx >= 0", i);
         if (slot_base[i] < 0 || slot_base[i] % 8) return fail(SB_ERR_INVALID, "request %d: slot_base must be a non-negative multiple of 8", i);

@@ -73,13 +73,21 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
     return t;
 }
 
-// x[t] = E[id_t] (+ P[pos_t]) in fp32
+// x[t] = E[id_t] (+ P[pos_t]) in fp32.  A negative id -(1 + j) refers to the
+// token the previous iteration generated in its batch row j (prev[j], still on
+// the device); ids are clamped into the tables so no value can read outside them.
 template <int DT>
 __global__ __launch_bounds__(256) void embed_kernel(const int* ids, const int* pos, const void* tok, const void* pe,
-                                                    float* x, int H) {
+                                                    const int* prev, int prev_n, int vocab, float* x, int H) {
     using T = typename Store<DT>::T;
     const int t = blockIdx.x;
-    const T* e = (const T*)tok + (long long)ids[t] * H;
+    int id = ids[t];
+    if (id < 0) {
+        const int j = -1 - id;
+        id = (prev && j < prev_n) ? prev[j] : 0;
+    }
+    id = min(max(id, 0), vocab - 1);
+    const T* e = (const T*)tok + (long long)id * H;
     const T* p = pe ? (const T*)pe + (long long)pos[t] * H : nullptr;
     float* xo = x + (long long)t * H;
     for (int i = threadIdx.x; i < H; i += blockDim.x) {
@@ -433,11 +441,13 @@ static int check_ws(const sb_model_dims* d, const sb_ragged* rg, size_t ws_bytes
     return SB_OK;
 }
 
-extern "C" int sb_embed(const sb_model_dims* dims, const sb_model_weights* w, const sb_ragged* rg, float* x,
-                        void* stream) {
+extern "C" int sb_embed_chained(const sb_model_dims* dims, const sb_model_weights* w, const sb_ragged* rg,
+                                const int32_t* prev_ids, int32_t prev_n, float* x, void* stream) {
     int st = validate_dims(dims);
     if (st) return st;
     if (!w || !rg || !x || !w->tok_emb || !rg->tok_ids) return fail(SB_ERR_INVALID, "sb_embed: NULL argument (token ids required)");
+    if (dims->vocab <= 0) return fail(SB_ERR_INVALID, "sb_embed: vocab must be positive");
+    if (prev_n < 0 || (prev_n > 0 && !prev_ids)) return fail(SB_ERR_INVALID, "sb_embed: bad previous ids");
     if (rg->n_tokens <= 0) return SB_OK;
     const void* pe = dims->arch == SB_ARCH_GPT ? w->pos_emb : nullptr;
     if (dims->arch == SB_ARCH_GPT && !pe) return fail(SB_ERR_INVALID, "sb_embed: GPT needs pos_emb");
@@ -445,11 +455,16 @@ extern "C" int sb_embed(const sb_model_dims* dims, const sb_model_weights* w, co
     TimedScope ts(SB_K_EMBED, s);
     if (dims->dtype == SB_BF16)
         hipLaunchKernelGGL(embed_kernel<SB_BF16>, dim3(rg->n_tokens), dim3(256), 0, s, rg->tok_ids, rg->tok_pos,
-                           w->tok_emb, pe, x, dims->hidden);
+                           w->tok_emb, pe, prev_ids, prev_n, dims->vocab, x, dims->hidden);
     else
         hipLaunchKernelGGL(embed_kernel<SB_F32>, dim3(rg->n_tokens), dim3(256), 0, s, rg->tok_ids, rg->tok_pos,
-                           w->tok_emb, pe, x, dims->hidden);
+                           w->tok_emb, pe, prev_ids, prev_n, dims->vocab, x, dims->hidden);
     return check_launch("embed");
+}
+
+extern "C" int sb_embed(const sb_model_dims* dims, const sb_model_weights* w, const sb_ragged* rg, float* x,
+                        void* stream) {
+    return sb_embed_chained(dims, w, rg, nullptr, 0, x, stream);
 }
 
 static int layer_gemm(const sb_model_dims* d, int epi, int kind, int M, int N, int K, const void* A, const void* W,

@@ -128,7 +128,10 @@ class Engine:
         self.ws_bytes = A.sb_layer_workspace_bytes(self.dims, max_tokens, max_bs, self.max_partials)
         self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
         self.x = torch.empty(max_tokens * m.H, dtype=torch.float32, device=device)
-        self.ids_dev = torch.empty(max_bs, dtype=torch.int32, device=device)
+        # one device id buffer per staging buffer: a chained launch reads the previous iteration's ids
+        # from the other buffer while writing its own
+        self.ids_dev_bufs = [torch.empty(max_bs, dtype=torch.int32, device=device) for _ in range(2)]
+        self.ids_dev = self.ids_dev_bufs[0]
         self.ids_host_bufs = [torch.empty(max_bs, dtype=torch.int32, pin_memory=True) for _ in range(2)]
         self.ids_host = self.ids_host_bufs[0]
         self.logits = torch.empty(max_bs * max(m.V, 1), dtype=torch.float32, device=device) if m.V > 0 else None
@@ -159,13 +162,17 @@ class Engine:
         return A.sb_ragged_build(self.dims, n_new, ctx, slot_base, tokens, self.staging_bufs[buf].data_ptr(),
                                  self.meta.data_ptr(), self.meta_bytes, stream_handle())
 
-    def forward(self, rg, layer_outputs=None, x_in=None, head=True):
-        """embed (or x_in) -> every layer -> final norm / LM head / argmax on the ragged batch ``rg``."""
+    def forward(self, rg, layer_outputs=None, x_in=None, head=True, buf=0, prev=None):
+        """embed (or x_in) -> every layer -> final norm / LM head / argmax on the ragged batch ``rg``.
+        ``prev``: (device ids tensor, count) of the previous iteration, for token references; the new
+        ids go to id buffer ``buf``."""
         s = stream_handle()
         T, H = rg.n_tokens, self.m.H
         xv = self.x[:T * H]
         if x_in is not None:
             xv.copy_(x_in.reshape(-1))
+        elif prev is not None:
+            A.sb_embed_chained(self.dims, self.w.model_struct, rg, prev[0].data_ptr(), prev[1], xv.data_ptr(), s)
         else:
             A.sb_embed(self.dims, self.w.model_struct, rg, xv.data_ptr(), s)
         for l in range(self.n_layers):
@@ -175,47 +182,107 @@ class Engine:
                 layer_outputs.append(xv.view(T, H).clone())
         if not head:
             return None
+        ids_dev = self.ids_dev_bufs[buf]
         A.sb_lm_argmax(self.dims, self.w.model_struct, rg, xv.data_ptr(), self.logits.data_ptr(),
-                       self.ids_dev.data_ptr(), self.ws.data_ptr(), self.ws_bytes, s)
-        return self.ids_dev[:rg.n_req]
+                       ids_dev.data_ptr(), self.ws.data_ptr(), self.ws_bytes, s)
+        return ids_dev[:rg.n_req]
 
-    def launch(self, sched=None, buf=0, keep=False):
+    def launch(self, sched=None, buf=0, keep=False, chain=None):
         """Select the next iteration from ``sched`` (default: this engine's scheduler), build its
         metadata in staging buffer ``buf`` and enqueue all of its GPU work, without waiting.  Returns
         None for an empty pool, else the pending iteration for ``finish``.  Two iterations may be in
-        flight when they use different ``buf``; their GPU work runs in stream order."""
+        flight when they use different ``buf``; their GPU work runs in stream order.
+
+        ``chain``: the previous iteration, already completed with ``complete_counts`` but whose token
+        values may still be on the device: members that continue from it embed its ids straight from
+        its device buffer (the other ``buf``), so this launch never waits for them."""
         sched = self.sched if sched is None else sched
         ids, n_new, ctx, base = A.sb_select_batch(sched, self.max_bs)
         if len(ids) == 0:
             return None
-        toks = A.sb_batch_tokens(sched, ids, self.max_tokens)
+        prev = None
+        if chain is not None:
+            toks, ticket = A.sb_batch_token_refs(sched, ids, self.max_tokens)
+            if ticket >= 0:
+                assert ticket == chain["ticket"] and chain["buf"] != buf
+                prev = (self.ids_dev_bufs[chain["buf"]], len(chain["ids"]))
+        else:
+            toks = A.sb_batch_tokens(sched, ids, self.max_tokens)
         rg = self.build(n_new, ctx, base, toks, buf)
         outs = [] if keep else None
-        self.forward(rg, layer_outputs=outs)
+        ids_dev = self.forward(rg, layer_outputs=outs, buf=buf, prev=prev)
         B = len(ids)
-        self.ids_host_bufs[buf][:B].copy_(self.ids_dev[:B], non_blocking=True)
+        self.ids_host_bufs[buf][:B].copy_(ids_dev[:B], non_blocking=True)
         done = torch.cuda.Event()
         done.record()
         return {"sched": sched, "buf": buf, "ids": ids, "n_new": n_new, "ctx": ctx, "slot_base": base,
-                "event": done, "outs": outs}
+                "event": done, "outs": outs, "ticket": None}
+
+    def _result(self, p, new):
+        res = {"ids": p["ids"], "n_new": p["n_new"], "ctx": p["ctx"], "slot_base": p["slot_base"], "tokens": new,
+               "finished": p.get("finished")}
+        if p["outs"] is not None:
+            B = len(p["ids"])
+            res["layer_outputs"] = [o.cpu() for o in p["outs"]]
+            res["logits"] = self.logits[:B * self.m.V].view(B, self.m.V).cpu()
+        return res
 
     def finish(self, p):
         """Wait for a launched iteration, hand its new tokens to its scheduler (Complete)."""
         p["event"].synchronize()
         B = len(p["ids"])
         new = self.ids_host_bufs[p["buf"]][:B].numpy().copy()
-        finished = A.sb_sched_complete(p["sched"], p["ids"], new)
-        res = {"ids": p["ids"], "n_new": p["n_new"], "ctx": p["ctx"], "slot_base": p["slot_base"], "tokens": new,
-               "finished": finished}
-        if p["outs"] is not None:
-            res["layer_outputs"] = [o.cpu() for o in p["outs"]]
-            res["logits"] = self.logits[:B * self.m.V].view(B, self.m.V).cpu()
-        return res
+        p["finished"] = A.sb_sched_complete(p["sched"], p["ids"], new)
+        return self._result(p, new)
+
+    def complete_counts(self, p):
+        """Complete a launched iteration without waiting for it: every member advances one token,
+        finished ones free their slots (counts only); the values follow in ``settle``."""
+        p["finished"], p["ticket"] = A.sb_sched_complete_deferred(p["sched"], p["ids"])
+
+    def settle(self, p):
+        """Wait for an iteration completed by ``complete_counts`` and record its token values."""
+        p["event"].synchronize()
+        B = len(p["ids"])
+        new = self.ids_host_bufs[p["buf"]][:B].numpy().copy()
+        A.sb_sched_set_tokens(p["sched"], p["ticket"], new)
+        return self._result(p, new)
 
     def step(self, keep=False):
         """One scheduler iteration; returns None for an empty pool, else a dict of the batch and its results."""
         p = self.launch(keep=keep)
         return None if p is None else self.finish(p)
+
+    def run_chained(self, reqs=(), on_iteration=None):
+        """Serve ``reqs`` (objects with rid, arrival, prompt, out_len, max_tokens) and whatever is already
+        in the pool until all are done, one iteration ahead of the host: iteration t+1 is selected and
+        launched -- its decodes embedding iteration t's ids on the device -- before the host waits for
+        iteration t's ids.  Arrivals follow the iteration clock: a request joins the pool at the first
+        iteration t >= its arrival; an idle clock jumps to the next arrival.  ``on_iteration(result)``
+        receives each settled iteration (with its clock in result["t"]).  Returns the iteration count."""
+        import math
+        pending = sorted(reqs, key=lambda r: (r.arrival, r.rid))
+        i, clock, n_iter, prev = 0, 0, 0, None
+        while True:
+            if prev is not None:
+                self.complete_counts(prev)
+            while i < len(pending) and pending[i].arrival <= clock:
+                r = pending[i]
+                self.add(r.rid, r.arrival, r.prompt, r.out_len, r.max_tokens)
+                i += 1
+            p = self.launch(buf=n_iter % 2, chain=prev)
+            if prev is not None:
+                res = self.settle(prev)
+                res["t"] = prev["t"]
+                if on_iteration is not None:
+                    on_iteration(res)
+            if p is None:
+                if i >= len(pending):
+                    return n_iter
+                clock, prev = int(math.ceil(pending[i].arrival)), None
+                continue
+            p["t"] = clock
+            prev, n_iter, clock = p, n_iter + 1, clock + 1
 
     def output(self, rid):
         return A.sb_sched_output(self.sched, rid)

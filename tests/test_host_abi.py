@@ -189,6 +189,125 @@ def test_native_scheduler_errors():
     assert list(fin) == [1] and sb.sb_kv_stats(kv)["n_rsrv"] == 0
 
 
+def _fake_token(rid, k, V=1000):
+    """Stand-in for the model: the k-th generated token of request rid."""
+    return (rid * 7919 + k * 104729 + 13) % V
+
+
+def _deferred_vs_sync(reqs, max_bs, n_slots):
+    """Drive two schedulers with the same arrivals: one completes with the token values, the other one
+    iteration ahead (deferred completion; the decodes' tokens resolved from the previous iteration's
+    'device' ids through their references).  Batches, fed tokens and outputs must agree."""
+    kvs = [sb.sb_kv_create(n_slots, sb.sb_kv_arena_slots(n_slots, max_bs), 1, 1, 8, sb.SB_F32) for _ in range(2)]
+    sy, de = sb.sb_sched_create(max_bs, kvs[0]), sb.sb_sched_create(max_bs, kvs[1])
+    pending = sorted(reqs, key=lambda r: (r.arrival, r.rid))
+    made = {r.rid: 0 for r in reqs}            # tokens generated so far (the fake model's clock per request)
+    i, t, n_iter, prev = 0, 0, 0, None          # prev: (ids, device ids, ticket) of the deferred side
+    while True:
+        if prev is not None:
+            _, ticket = sb.sb_sched_complete_deferred(de, prev[0])
+            prev = (prev[0], prev[1], ticket)
+        while i < len(pending) and pending[i].arrival <= t:
+            r = pending[i]
+            for s_ in (sy, de):
+                sb.sb_sched_add(s_, r.rid, r.arrival, r.prompt, r.out_len, r.max_tokens)
+            i += 1
+        ids, n_new, ctx, _ = sb.sb_select_batch(sy, max_bs)
+        ids_d, n_new_d, ctx_d, _ = sb.sb_select_batch(de, max_bs)
+        assert list(ids) == list(ids_d) and list(n_new) == list(n_new_d) and list(ctx) == list(ctx_d)
+        if len(ids):
+            want = sb.sb_batch_tokens(sy, ids, 4096)
+            refs, ticket = sb.sb_batch_token_refs(de, ids, 4096)
+            if prev is None:
+                assert ticket == -1
+            if ticket >= 0:
+                assert ticket == prev[2]
+                if (refs < 0).any():
+                    with pytest.raises(sb.SBError) as e:            # values unknown: plain tokens refuse
+                        sb.sb_batch_tokens(de, ids, 4096)
+                    assert e.value.status == sb.SB_ERR_STATE
+            got = np.array([prev[1][-1 - v] if v < 0 else v for v in refs], np.int32)
+            assert list(got) == list(want)
+            out = np.array([_fake_token(int(r), made[int(r)]) for r in ids], np.int32)
+            for r in ids:
+                made[int(r)] += 1
+            sb.sb_sched_complete(sy, ids, out)
+        if prev is not None:
+            sb.sb_sched_set_tokens(de, prev[2], prev[1])
+            with pytest.raises(sb.SBError) as e:
+                sb.sb_sched_set_tokens(de, prev[2], prev[1])       # settled once only
+            assert e.value.status == sb.SB_ERR_NOT_FOUND
+        if not len(ids):
+            prev = None
+            if i >= len(pending):
+                break
+            t = int(math.ceil(pending[i].arrival))
+            continue
+        prev, n_iter, t = (ids, out, None), n_iter + 1, t + 1
+    for r in reqs:
+        assert list(sb.sb_sched_output(de, r.rid)) == list(sb.sb_sched_output(sy, r.rid)) == \
+            [_fake_token(r.rid, k) for k in range(r.out_len)]
+    for s_ in (sy, de):
+        sb.sb_sched_destroy(s_)
+    for kv in kvs:
+        assert sb.sb_kv_stats(kv)["n_rsrv"] == 0
+        sb.sb_kv_destroy(kv)
+    return n_iter
+
+
+def test_deferred_completion_p4_timeline_and_figure5():
+    """Completion one iteration behind (NEXT-1 of the plan: select and launch t+1 before t's ids reach
+    the host) schedules exactly as the synchronous loop: the lecture's 10-iteration grid, Figure 5 with
+    the reservation binding (x4 blocked at 30 slots)."""
+    assert _deferred_vs_sync(p4_grid_requests(seed=0), 3, 10**9) == 10
+    for n_slots in (64, 30):
+        _deferred_vs_sync(figure5_requests(seed=0, vocab=1000, out_len=8), 4, n_slots)
+
+
+@pytest.mark.parametrize("case", range(3))
+def test_deferred_completion_random_traces(case):
+    reqs = poisson_trace(seed=10 + case, n=120, rate=[0.5, 2.0, 0.2][case], plo=1, phi=30, olo=1, ohi=20,
+                         reserve_out=20, vocab=1000, with_prompts=True)
+    _deferred_vs_sync(reqs, [4, 16, 2][case], [150, 400, 60][case])
+
+
+def test_deferred_completion_errors():
+    kv = sb.sb_kv_create(64, sb.sb_kv_arena_slots(64, 4), 1, 1, 8, sb.SB_F32)
+    s = sb.sb_sched_create(4, kv)
+    sb.sb_sched_add(s, 0, 0.0, [5, 6], 3, 8)
+    ids, *_ = sb.sb_select_batch(s, 4)
+    _, t0 = sb.sb_sched_complete_deferred(s, ids)
+    with pytest.raises(sb.SBError) as e:
+        sb.sb_sched_set_tokens(s, t0, [1, 2])                      # one request in that batch
+    assert e.value.status == sb.SB_ERR_INVALID
+    with pytest.raises(sb.SBError) as e:
+        sb.sb_sched_set_tokens(s, t0 + 5, [1])
+    assert e.value.status == sb.SB_ERR_NOT_FOUND
+    ids, *_ = sb.sb_select_batch(s, 4)
+    refs, tk = sb.sb_batch_token_refs(s, ids, 16)
+    assert list(refs) == [-1] and tk == t0
+    _, t1 = sb.sb_sched_complete_deferred(s, ids)                   # second pending token, newer ticket
+    ids, *_ = sb.sb_select_batch(s, 4)
+    refs, tk = sb.sb_batch_token_refs(s, ids, 16)
+    assert list(refs) == [-1] and tk == t1
+    sb.sb_sched_set_tokens(s, t1, [42])
+    sb.sb_sched_set_tokens(s, t0, [41])
+    assert list(sb.sb_sched_output(s, 0)) == [41, 42]
+    assert list(sb.sb_batch_tokens(s, ids, 16)) == [42]
+    sb.sb_sched_destroy(s)
+    sb.sb_kv_destroy(kv)
+
+
+def test_ragged_rejects_token_ids_out_of_range():
+    dims = make_dims(TOY, "fp32")
+    buf = np.zeros(1 << 16, np.int32)
+    sb.sb_ragged_build(dims, [2], [0], [0], [-1, TOY.V - 1], buf.ctypes.data, None, buf.nbytes)   # ref + literal
+    for bad in ([TOY.V, 0], [0, -(1 << 20) - 1]):
+        with pytest.raises(sb.SBError) as e:
+            sb.sb_ragged_build(dims, [2], [0], [0], bad, buf.ctypes.data, None, buf.nbytes)
+        assert e.value.status == sb.SB_ERR_INVALID
+
+
 # ---------------------------------------------------------------- ragged metadata
 def host_ragged(m, dtype, batch, slot_base=None, tokens=None):
     dims = make_dims(m, dtype)
