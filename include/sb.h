@@ -263,6 +263,15 @@ int sb_lm_argmax(const sb_model_dims* dims, const sb_model_weights* w, const sb_
                  const float* x, float* logits, int32_t* out_ids, void* workspace, size_t ws_bytes,
                  void* stream);
 
+/* One iteration's whole device side in one call (one host call instead of
+ * 2 + n_layers): sb_embed_chained (prev_ids may be NULL), sb_layer_step for
+ * layers 0 .. n_layers-1 with layers[l] (host array of n_layers structs),
+ * then sb_lm_argmax.  Arguments, ownership and errors as for those calls; the
+ * first failing step's status is returned and nothing after it is enqueued. */
+int sb_forward(const sb_model_dims* dims, const sb_model_weights* w, const sb_layer_weights* layers, int32_t n_layers,
+               const sb_ragged* rg, const sb_kv* kv, const int32_t* prev_ids, int32_t prev_n, float* x,
+               float* logits, int32_t* out_ids, void* workspace, size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------------------------ timing
  * Per-kernel-class HIP event timing of launches made by the library (for
  * benchmarks): an event pair is recorded on the launch stream around every

@@ -94,6 +94,8 @@ _PROTOS = {
     "sb_layer_workspace_bytes": (sz, [P(sb_model_dims), i32, i32, i32]),
     "sb_embed": (C.c_int, [P(sb_model_dims), P(sb_model_weights), P(sb_ragged), vp, vp]),
     "sb_embed_chained": (C.c_int, [P(sb_model_dims), P(sb_model_weights), P(sb_ragged), vp, i32, vp, vp]),
+    "sb_forward": (C.c_int, [P(sb_model_dims), P(sb_model_weights), vp, i32, P(sb_ragged), vp, vp, i32, vp, vp, vp,
+                             vp, sz, vp]),
     "sb_layer_step": (C.c_int, [P(sb_model_dims), P(sb_layer_weights), P(sb_ragged), vp, i32, vp, vp, sz, vp]),
     "sb_lm_argmax": (C.c_int, [P(sb_model_dims), P(sb_model_weights), P(sb_ragged), vp, vp, vp, vp, sz, vp]),
     "sb_timing_enable": (C.c_int, [i32]),

@@ -204,6 +204,13 @@ def sb_embed_chained(dims, mw, rg, prev_ids, prev_n, x, stream=None):
     call("sb_embed_chained", C.byref(dims), C.byref(mw), C.byref(rg), prev_ids, prev_n, x, stream)
 
 
+def sb_forward(dims, mw, layer_array, n_layers, rg, kv, prev_ids, prev_n, x, logits, out_ids, ws, ws_bytes,
+               stream=None):
+    """layer_array: a ctypes array of sb_layer_weights (kept by the caller)."""
+    call("sb_forward", C.byref(dims), C.byref(mw), C.cast(layer_array, C.c_void_p) if layer_array is not None else None,
+         n_layers, C.byref(rg), kv, prev_ids, prev_n, x, logits, out_ids, ws, ws_bytes, stream)
+
+
 def sb_layer_step(dims, lw, rg, kv, layer, x, ws, ws_bytes, stream=None):
     call("sb_layer_step", C.byref(dims), C.byref(lw), C.byref(rg), kv, layer, x, ws, ws_bytes, stream)
 

@@ -557,6 +557,17 @@ extern "C" int sb_lm_argmax(const sb_model_dims* d, const sb_model_weights* w, c
     return launch_argmax(rg->n_req, d->vocab, lg, out_ids, s);
 }
 
+extern "C" int sb_forward(const sb_model_dims* d, const sb_model_weights* mw, const sb_layer_weights* layers,
+                          int32_t n_layers, const sb_ragged* rg, const sb_kv* kv, const int32_t* prev_ids,
+                          int32_t prev_n, float* x, float* logits, int32_t* out_ids, void* workspace,
+                          size_t ws_bytes, void* stream) {
+    if (n_layers < 0 || (n_layers > 0 && !layers)) return fail(SB_ERR_INVALID, "sb_forward: bad layer array");
+    int st = sb_embed_chained(d, mw, rg, prev_ids, prev_n, x, stream);
+    for (int32_t l = 0; !st && l < n_layers; ++l) st = sb_layer_step(d, &layers[l], rg, kv, l, x, workspace, ws_bytes, stream);
+    if (!st) st = sb_lm_argmax(d, mw, rg, x, logits, out_ids, workspace, ws_bytes, stream);
+    return st;
+}
+
 extern "C" int sb_kv_write(const sb_kv* kv, int32_t layer, int32_t n, const int32_t* slots, const void* k, const void* v,
                            void* stream) {
     if (!kv || (n > 0 && (!slots || !k || !v))) return fail(SB_ERR_INVALID, "sb_kv_write: NULL argument");

@@ -93,6 +93,7 @@ class DeviceWeights:
                               "lnf_g": rnd((m.H,), 0.1, 1.0), "lnf_b": rnd((m.H,), 0.02) if gpt else None,
                               "pos_emb": rnd((m.max_pos, m.H), 0.02) if gpt else None}
         self.layer_structs = [sb_layer_weights(**{k: _addr(t[k]) for k in LAYER_KEYS}) for t in self.layers]
+        self.layer_array = (sb_layer_weights * max(len(self.layer_structs), 1))(*self.layer_structs)
         self.model_struct = sb_model_weights(**{k: _addr(self.model[k]) for k in MODEL_KEYS})
 
 
@@ -169,6 +170,14 @@ class Engine:
         s = stream_handle()
         T, H = rg.n_tokens, self.m.H
         xv = self.x[:T * H]
+        ids_dev = self.ids_dev_bufs[buf]
+        if x_in is None and layer_outputs is None and head:
+            # the common case: the whole device side of the iteration in one library call
+            A.sb_forward(self.dims, self.w.model_struct, self.w.layer_array, self.n_layers, rg, self.kv,
+                         prev[0].data_ptr() if prev is not None else None, prev[1] if prev is not None else 0,
+                         xv.data_ptr(), self.logits.data_ptr(), ids_dev.data_ptr(), self.ws.data_ptr(),
+                         self.ws_bytes, s)
+            return ids_dev[:rg.n_req]
         if x_in is not None:
             xv.copy_(x_in.reshape(-1))
         elif prev is not None:
@@ -182,7 +191,6 @@ class Engine:
                 layer_outputs.append(xv.view(T, H).clone())
         if not head:
             return None
-        ids_dev = self.ids_dev_bufs[buf]
         A.sb_lm_argmax(self.dims, self.w.model_struct, rg, xv.data_ptr(), self.logits.data_ptr(),
                        ids_dev.data_ptr(), self.ws.data_ptr(), self.ws_bytes, s)
         return ids_dev[:rg.n_req]
