@@ -151,14 +151,25 @@ int sb_sched_add(sb_sched* s, int64_t req_id, double arrival, int32_t prompt_len
 int sb_sched_add_running(sb_sched* s, int64_t req_id, double arrival, int32_t prompt_len,
                          const int32_t* prompt_tokens, int32_t out_len, int32_t max_tokens,
                          int32_t generated, int32_t last_token);
+/* Chunked prefill ("从静态批处理到连续批处理", section Chunked Prefill; "CS349D
+ * Lecture 2", exercise 9): from the next Select on, an iteration feeds at most
+ * token_budget tokens.  Decoding requests go first (one token each, arrival
+ * order); then requests still in their prompt, in arrival order, each feed
+ * min(chunk, prompt tokens left, budget left) prompt tokens -- the first time
+ * a request is scheduled it reserves max_tokens as in Algorithm 1 and a
+ * failed reservation stops the scan.  Only the chunk that ends a prompt yields
+ * a token: sb_sched_complete ignores the other members' new_tokens entries.
+ * Both 0 (the default) turns it off: whole prompts, Algorithm 1 exactly.
+ * SB_ERR_INVALID unless both are positive or both 0. */
+int sb_sched_set_chunking(sb_sched* s, int32_t token_budget, int32_t chunk);
 /* Select the next batch (host arrays of capacity cap).  For member i:
- * n_new[i] = tokens fed this iteration (prompt_len, or 1), ctx[i] = tokens
- * already cached, slot_base[i] = first slot of its reservation.
+ * n_new[i] = tokens fed this iteration (the prompt or a chunk of it, or 1),
+ * ctx[i] = tokens already cached, slot_base[i] = first slot of its reservation.
  * *n_out == 0 is legal (empty pool). */
 int sb_select_batch(sb_sched* s, int32_t cap, int64_t* ids, int32_t* n_new, int32_t* ctx,
                     int64_t* slot_base, int32_t* n_out);
 /* Token ids fed this iteration by the n selected requests, flattened in batch
- * order: the prompt of a first iteration, else the last generated token. */
+ * order: the prompt (or this iteration's chunk of it), else the last generated token. */
 int sb_batch_tokens(const sb_sched* s, int32_t n, const int64_t* ids, int32_t cap, int32_t* tokens,
                     int32_t* n_tokens);
 /* The iteration returned one token per member (new_tokens, host).  Finished

@@ -30,7 +30,7 @@ def generate_one_at_a_time(m, W, prompt, out_len, store=None):
     return toks, margins
 
 
-def generate_continuous(m, W, reqs, max_bs, n_slots, record=None, store=None):
+def generate_continuous(m, W, reqs, max_bs, n_slots, record=None, store=None, budget=None, chunk=None):
     """Greedy generation of ``reqs`` under the iteration-level scheduler.
 
     Each iteration runs the flattened selective-batched forward over the
@@ -46,12 +46,15 @@ def generate_continuous(m, W, reqs, max_bs, n_slots, record=None, store=None):
         batch = [(n_new, ctx) for _, n_new, ctx in work]
         ids = []
         for rid, n_new, ctx in work:
-            ids.append(list(by_id[rid].prompt) if ctx == 0 and not toks[rid] else [toks[rid][-1]])
+            prompt = list(by_id[rid].prompt)
+            # a prompt (or a chunk of it) with the tokens before it cached, else the last generated token
+            ids.append(prompt[ctx:ctx + n_new] if ctx < len(prompt) else [toks[rid][-1]])
         outs, logits = FL.forward_flat(m, W, ids, batch, [caches[rid] for rid, _, _ in work], store)
-        for i, (rid, _, _) in enumerate(work):
-            toks[rid].append(M.greedy(logits[i]))
+        for i, (rid, n_new, ctx) in enumerate(work):
+            if ctx + n_new >= len(by_id[rid].prompt):      # a chunk that ends short of the prompt yields nothing
+                toks[rid].append(M.greedy(logits[i]))
         if record is not None:
             record.append({"t": t, "work": work, "ids": ids, "outs": outs, "logits": logits})
 
-    log = replay(reqs, max_bs, n_slots, engine)
+    log = replay(reqs, max_bs, n_slots, engine, budget, chunk)
     return toks, log

@@ -16,6 +16,20 @@ Readings taken where the pages are garbled or silent:
   * a request whose ``max_tokens`` exceeds ``n_slots`` can never be admitted
     and is rejected when it is submitted;
   * one worker (one batch in flight), so no request is RUNNING when Select runs.
+
+Chunked prefill ("从静态批处理到连续批处理", section Chunked Prefill; "CS349D
+Lecture 2", exercise 9): with a per-iteration token budget, long prompts are fed
+in chunks, SeqWork(n_new = chunk, n_past = prompt tokens already processed).
+The pages fix the idea but not every rule; the reading taken here:
+  * decodes first: every request past its prompt takes one token, in arrival
+    order, while the budget and max_bs allow;
+  * then requests still in their prompt, in arrival order, each take
+    min(chunk, prompt tokens left, budget left) tokens; the first scheduling
+    reserves max_tokens as in Algorithm 1 and a failed reservation stops the
+    scan; an exhausted budget or max_bs stops it too;
+  * only the chunk that completes a prompt yields a token (the first one).
+With an unlimited budget and chunk this is Algorithm 1 itself (with one worker
+every decoding request arrived before every waiting one).
 """
 import math
 
@@ -31,7 +45,8 @@ class TooLarge(ValueError):
 class SReq:
     """Scheduler view of a request."""
 
-    __slots__ = ("rid", "arrival", "order", "prompt_len", "out_len", "max_tokens", "state", "generated")
+    __slots__ = ("rid", "arrival", "order", "prompt_len", "out_len", "max_tokens", "state", "generated", "prefilled",
+                 "cur_new")
 
     def __init__(self, rid, arrival, order, prompt_len, out_len, max_tokens):
         self.rid = rid
@@ -42,6 +57,8 @@ class SReq:
         self.max_tokens = max_tokens
         self.state = INITIATION
         self.generated = 0
+        self.prefilled = 0      # prompt tokens already processed (their K/V cached)
+        self.cur_new = 0        # tokens fed in the current iteration
 
 
 def select(pool, n_rsrv, max_bs, n_slots):
@@ -65,6 +82,32 @@ def select(pool, n_rsrv, max_bs, n_slots):
     return batch, n_rsrv
 
 
+def select_chunked(pool, n_rsrv, max_bs, n_slots, budget, chunk):
+    """``Select`` with a token budget and prompts fed in chunks: returns (batch of (request, n_new), n_rsrv)."""
+    cand = sorted((r for r in pool if r.state != RUNNING), key=lambda r: (r.arrival, r.order))
+    batch, left = [], budget
+    for r in cand:                                   # decodes first, one token each
+        if r.prefilled < r.prompt_len:
+            continue
+        if len(batch) == max_bs or left == 0:
+            break
+        batch.append((r, 1))
+        left -= 1
+    for r in cand:                                   # then prompt chunks, arrival order
+        if r.prefilled == r.prompt_len:
+            continue
+        if len(batch) == max_bs or left == 0:
+            break
+        if r.state == INITIATION:
+            if n_rsrv + r.max_tokens > n_slots:
+                break
+            n_rsrv += r.max_tokens
+        n = min(chunk, r.prompt_len - r.prefilled, left)
+        batch.append((r, n))
+        left -= n
+    return batch, n_rsrv
+
+
 def work_of(r):
     """(n_new, ctx) a batch member processes this iteration.
 
@@ -80,11 +123,14 @@ def work_of(r):
 class Scheduler:
     """Pool, counters and the per-iteration state transitions (one worker)."""
 
-    def __init__(self, max_bs, n_slots):
+    def __init__(self, max_bs, n_slots, budget=None, chunk=None):
         if max_bs <= 0:
             raise ValueError("max_bs must be positive")
+        if (budget is None) != (chunk is None) or (budget is not None and (budget < 1 or chunk < 1)):
+            raise ValueError("budget and chunk: both positive, or both None")
         self.max_bs = max_bs
         self.n_slots = n_slots
+        self.budget, self.chunk = budget, chunk
         self.n_rsrv = 0
         self.pool = []
         self._order = 0
@@ -100,16 +146,39 @@ class Scheduler:
         return r
 
     def select(self):
-        batch, self.n_rsrv = select(self.pool, self.n_rsrv, self.max_bs, self.n_slots)
+        if self.budget is None:
+            batch, self.n_rsrv = select(self.pool, self.n_rsrv, self.max_bs, self.n_slots)
+            for r in batch:
+                r.cur_new = work_of(r)[0]
+        else:
+            chosen, self.n_rsrv = select_chunked(self.pool, self.n_rsrv, self.max_bs, self.n_slots, self.budget,
+                                                 self.chunk)
+            batch = []
+            for r, n in chosen:
+                r.cur_new = n
+                batch.append(r)
         for r in batch:
             r.state = RUNNING
         return batch
 
+    def work(self, r):
+        """(n_new, ctx) of a member this iteration."""
+        if self.budget is None:
+            return work_of(r)
+        if r.prefilled < r.prompt_len:
+            return r.cur_new, r.prefilled
+        return 1, r.prompt_len + r.generated - 1
+
     def complete(self, batch):
-        """The iteration returned one token per member: move to INCREMENT, retire finished ones."""
+        """Every member that finished its prompt or decoded yields one token: move to INCREMENT, retire
+        finished ones."""
         finished = []
         for r in batch:
             r.state = INCREMENT
+            if r.prefilled < r.prompt_len:
+                r.prefilled = r.prompt_len if self.budget is None else r.prefilled + r.cur_new
+                if r.prefilled < r.prompt_len:
+                    continue                       # a prompt chunk that does not end the prompt: no token
             r.generated += 1
             if r.generated == r.out_len:
                 self.n_rsrv -= r.max_tokens
@@ -120,7 +189,7 @@ class Scheduler:
         return finished
 
 
-def replay(reqs, max_bs, n_slots, engine=None):
+def replay(reqs, max_bs, n_slots, engine=None, budget=None, chunk=None):
     """Run the iteration loop on a logical clock t = 0, 1, 2, ...
 
     ``reqs``: objects with ``rid, arrival, prompt (or prompt_len), out_len,
@@ -129,9 +198,12 @@ def replay(reqs, max_bs, n_slots, engine=None):
     ``engine(t, batch_work)`` -- if given -- is called with the list of
     ``(rid, n_new, ctx)`` of the iteration, in batch order.
 
+    ``budget``/``chunk``: chunked prefill (module docstring); a member yields a token iff
+    ``ctx + n_new >= prompt length``.
+
     Returns the per-iteration log ``[(t, [(rid, n_new, ctx), ...], n_rsrv_after_select)]``.
     """
-    s = Scheduler(max_bs, n_slots)
+    s = Scheduler(max_bs, n_slots, budget, chunk)
     pending = sorted(reqs, key=lambda r: (r.arrival, r.rid))
     i = 0
     t = 0
@@ -148,7 +220,7 @@ def replay(reqs, max_bs, n_slots, engine=None):
         batch = s.select()
         if not batch:
             raise RuntimeError("non-empty pool produced an empty batch")
-        work = [(r.rid, *work_of(r)) for r in batch]
+        work = [(r.rid, *s.work(r)) for r in batch]
         log.append((t, work, s.n_rsrv))
         if engine is not None:
             engine(t, work)

@@ -82,6 +82,7 @@ _PROTOS = {
     "sb_select_batch": (C.c_int, [vp, i32, vp, vp, vp, vp, P(i32)]),
     "sb_batch_tokens": (C.c_int, [vp, i32, vp, i32, vp, P(i32)]),
     "sb_sched_complete": (C.c_int, [vp, i32, vp, vp, P(i32), vp]),
+    "sb_sched_set_chunking": (C.c_int, [vp, i32, i32]),
     "sb_sched_complete_deferred": (C.c_int, [vp, i32, vp, P(i32), vp, P(i64)]),
     "sb_sched_set_tokens": (C.c_int, [vp, i64, i32, vp]),
     "sb_batch_token_refs": (C.c_int, [vp, i32, vp, i32, vp, P(i32), P(i64)]),

@@ -103,6 +103,10 @@ def sb_sched_add_running(s, req_id, arrival, prompt_len, out_len, max_tokens, ge
          last_token)
 
 
+def sb_sched_set_chunking(s, token_budget, chunk):
+    call("sb_sched_set_chunking", s, token_budget, chunk)
+
+
 def sb_select_batch(s, cap):
     ids = np.zeros(cap, np.int64)
     n_new = np.zeros(cap, np.int32)

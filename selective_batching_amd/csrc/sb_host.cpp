@@ -234,6 +234,8 @@ struct Req {
     int64_t slot_base;
     std::vector<int32_t> prompt;
     std::vector<int32_t> out;
+    int32_t prefilled = 0;                          // prompt tokens already processed (K/V cached)
+    int32_t cur_new = 0;                            // tokens fed in the current iteration
     int64_t pending_ticket = -1;                    // deferred completion whose token value is not known yet
     int32_t pending_row = -1;                       // this request's row in that iteration's batch
 };
@@ -247,6 +249,7 @@ struct sb_sched {
     std::unordered_map<int64_t, std::vector<int32_t>> done;
     int64_t next_order = 0;
     int64_t n_finished = 0;
+    int32_t budget = 0, chunk = 0;                  // chunked prefill (0: whole prompts, Algorithm 1)
     // deferred completions: ticket -> (request id, position of the pending token in its output), batch order
     std::map<int64_t, std::vector<std::pair<int64_t, int32_t>>> tickets;
     int64_t next_ticket = 0;
@@ -328,6 +331,7 @@ extern "C" int sb_sched_add_running(sb_sched* s, int64_t req_id, double arrival,
     r->max_tokens = max_tokens;
     r->state = ST_INCREMENT;
     r->generated = generated;
+    r->prefilled = prompt_len;
     r->slot_base = base;
     r->prompt.assign(prompt_len, 0);
     if (prompt_tokens) std::memcpy(r->prompt.data(), prompt_tokens, sizeof(int32_t) * prompt_len);
@@ -336,32 +340,69 @@ extern "C" int sb_sched_add_running(sb_sched* s, int64_t req_id, double arrival,
     return insert_req(s, std::move(r));
 }
 
+extern "C" int sb_sched_set_chunking(sb_sched* s, int32_t token_budget, int32_t chunk) {
+    if (!s) return fail(SB_ERR_INVALID, "sched is NULL");
+    if (token_budget < 0 || chunk < 0 || (token_budget == 0) != (chunk == 0))
+        return fail(SB_ERR_INVALID, "token_budget and chunk: both positive, or both 0 (off)");
+    s->budget = token_budget;
+    s->chunk = chunk;
+    return SB_OK;
+}
+
 extern "C" int sb_select_batch(sb_sched* s, int32_t cap, int64_t* ids, int32_t* n_new, int32_t* ctx,
                                int64_t* slot_base, int32_t* n_out) {
     if (!s || !n_out) return fail(SB_ERR_INVALID, "NULL argument");
     *n_out = 0;
     if (cap < std::min<int64_t>(s->max_bs, (int64_t)s->pool.size()))
         return fail(SB_ERR_CAPACITY, "cap %d < min(max_bs, pool size)", cap);
-    std::vector<Req*> batch;
-    for (Req* r : s->pool) {                              // arrival order
-        if (r->state == ST_RUNNING) continue;
-        if ((int32_t)batch.size() == s->max_bs) break;
-        if (r->state == ST_INITIATION) {
-            int64_t base = -1;
-            int st = sb_kv_reserve(s->kv, r->id, r->max_tokens, &base);
-            if (st == SB_ERR_NO_SLOTS) break;             // stop, never skip: FCFS
-            if (st) return st;
-            r->slot_base = base;
+    std::vector<std::pair<Req*, int32_t>> batch;    // member, tokens it feeds this iteration
+    auto admit = [&](Req* r, int* st) {             // first scheduling: reserve max_tokens (stop on failure)
+        *st = SB_OK;
+        if (r->state != ST_INITIATION) return true;
+        int64_t base = -1;
+        *st = sb_kv_reserve(s->kv, r->id, r->max_tokens, &base);
+        if (*st == SB_ERR_NO_SLOTS) {
+            *st = SB_OK;
+            return false;
         }
-        batch.push_back(r);
+        if (*st) return false;
+        r->slot_base = base;
+        return true;
+    };
+    int st = SB_OK;
+    if (s->budget == 0) {
+        for (Req* r : s->pool) {                          // arrival order
+            if (r->state == ST_RUNNING) continue;
+            if ((int32_t)batch.size() == s->max_bs) break;
+            if (!admit(r, &st)) break;                    // stop, never skip: FCFS
+            batch.push_back({r, r->prefilled < r->prompt_len ? r->prompt_len - r->prefilled : 1});
+        }
+    } else {
+        int64_t left = s->budget;
+        for (Req* r : s->pool) {                          // decodes first, one token each
+            if (r->state == ST_RUNNING || r->prefilled < r->prompt_len) continue;
+            if ((int32_t)batch.size() == s->max_bs || left == 0) break;
+            batch.push_back({r, 1});
+            left -= 1;
+        }
+        for (Req* r : s->pool) {                          // then prompt chunks, arrival order
+            if (r->state == ST_RUNNING || r->prefilled == r->prompt_len) continue;
+            if ((int32_t)batch.size() == s->max_bs || left == 0) break;
+            if (!admit(r, &st)) break;
+            const int32_t n = (int32_t)std::min<int64_t>({(int64_t)s->chunk, (int64_t)(r->prompt_len - r->prefilled), left});
+            batch.push_back({r, n});
+            left -= n;
+        }
     }
+    if (st) return st;
     for (size_t i = 0; i < batch.size(); ++i) {
-        Req* r = batch[i];
+        Req* r = batch[i].first;
         r->state = ST_RUNNING;
+        r->cur_new = batch[i].second;
         if (ids) ids[i] = r->id;
-        const bool first = r->generated == 0;
-        if (n_new) n_new[i] = first ? r->prompt_len : 1;
-        if (ctx) ctx[i] = first ? 0 : r->prompt_len + r->generated - 1;
+        const bool prompt = r->prefilled < r->prompt_len;
+        if (n_new) n_new[i] = r->cur_new;
+        if (ctx) ctx[i] = prompt ? r->prefilled : r->prompt_len + r->generated - 1;
         if (slot_base) slot_base[i] = r->slot_base;
     }
     *n_out = (int32_t)batch.size();
@@ -377,10 +418,10 @@ extern "C" int sb_batch_tokens(const sb_sched* s, int32_t n, const int64_t* ids,
         if (it == s->by_id.end()) return fail(SB_ERR_NOT_FOUND, "request %lld not in the pool", (long long)ids[i]);
         const Req* r = it->second.get();
         if (r->state != ST_RUNNING) return fail(SB_ERR_STATE, "request %lld is not in the running batch", (long long)ids[i]);
-        if (r->generated == 0) {
-            if (t + r->prompt_len > cap) return fail(SB_ERR_CAPACITY, "token capacity %d exceeded", cap);
-            if (tokens) std::memcpy(tokens + t, r->prompt.data(), sizeof(int32_t) * r->prompt_len);
-            t += r->prompt_len;
+        if (r->prefilled < r->prompt_len) {                 // (a chunk of) the prompt
+            if (t + r->cur_new > cap) return fail(SB_ERR_CAPACITY, "token capacity %d exceeded", cap);
+            if (tokens) std::memcpy(tokens + t, r->prompt.data() + r->prefilled, sizeof(int32_t) * r->cur_new);
+            t += r->cur_new;
         } else {
             if (t + 1 > cap) return fail(SB_ERR_CAPACITY, "token capacity %d exceeded", cap);
             if (r->pending_ticket >= 0)
@@ -404,10 +445,10 @@ extern "C" int sb_batch_token_refs(const sb_sched* s, int32_t n, const int64_t* 
         if (it == s->by_id.end()) return fail(SB_ERR_NOT_FOUND, "request %lld not in the pool", (long long)ids[i]);
         const Req* r = it->second.get();
         if (r->state != ST_RUNNING) return fail(SB_ERR_STATE, "request %lld is not in the running batch", (long long)ids[i]);
-        if (r->generated == 0) {
-            if (t + r->prompt_len > cap) return fail(SB_ERR_CAPACITY, "token capacity %d exceeded", cap);
-            if (tokens) std::memcpy(tokens + t, r->prompt.data(), sizeof(int32_t) * r->prompt_len);
-            t += r->prompt_len;
+        if (r->prefilled < r->prompt_len) {                 // (a chunk of) the prompt
+            if (t + r->cur_new > cap) return fail(SB_ERR_CAPACITY, "token capacity %d exceeded", cap);
+            if (tokens) std::memcpy(tokens + t, r->prompt.data() + r->prefilled, sizeof(int32_t) * r->cur_new);
+            t += r->cur_new;
         } else {
             if (t + 1 > cap) return fail(SB_ERR_CAPACITY, "token capacity %d exceeded", cap);
             int32_t v = r->out.back();
@@ -442,6 +483,13 @@ int complete_batch(sb_sched* s, int32_t n, const int64_t* ids, const int32_t* ne
     for (int32_t i = 0; i < n; ++i) {
         Req* r = s->by_id.at(ids[i]).get();
         r->state = ST_INCREMENT;
+        if (r->prefilled < r->prompt_len) {
+            r->prefilled += r->cur_new;
+            if (r->prefilled < r->prompt_len) {              // a chunk short of the prompt's end: no token
+                if (ticket >= 0) slots_of_ticket.push_back({r->id, -1});
+                continue;
+            }
+        }
         if (ticket >= 0) {
             slots_of_ticket.push_back({r->id, (int32_t)r->out.size()});
             r->pending_ticket = ticket;
@@ -492,6 +540,7 @@ extern "C" int sb_sched_set_tokens(sb_sched* s, int64_t ticket, int32_t n, const
     for (int32_t i = 0; i < n; ++i) {
         const int64_t id = t->second[i].first;
         const int32_t pos = t->second[i].second;
+        if (pos < 0) continue;                               // that member yielded no token
         auto live = s->by_id.find(id);
         if (live != s->by_id.end()) {
             Req* r = live->second.get();

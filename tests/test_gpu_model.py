@@ -241,9 +241,9 @@ def test_llama8b_shape_layer_stepwise():
         sb.sb_kv_destroy(kv)
 
 
-def _gpu_generate(m, dtype, W, reqs, max_bs, n_slots):
+def _gpu_generate(m, dtype, W, reqs, max_bs, n_slots, chunking=None):
     eng = Engine(m, dtype, W, n_slots=n_slots, max_bs=max_bs, max_tokens=sum(len(r.prompt) for r in reqs) + max_bs,
-                 max_keys_total=sum(r.max_tokens for r in reqs))
+                 max_keys_total=sum(r.max_tokens for r in reqs), chunking=chunking)
     try:
         import math
         pending = sorted(reqs, key=lambda r: (r.arrival, r.rid))
@@ -431,11 +431,11 @@ def test_pipelined_launches_match_sequential_steps():
         eng.close()
 
 
-def _gpu_generate_chained(m, dtype, W, reqs, max_bs, n_slots):
+def _gpu_generate_chained(m, dtype, W, reqs, max_bs, n_slots, chunking=None):
     """As _gpu_generate, but one iteration ahead of the host (Engine.run_chained): decodes embed the
     previous iteration's ids straight from its device buffer."""
     eng = Engine(m, dtype, W, n_slots=n_slots, max_bs=max_bs, max_tokens=sum(len(r.prompt) for r in reqs) + max_bs,
-                 max_keys_total=sum(r.max_tokens for r in reqs))
+                 max_keys_total=sum(r.max_tokens for r in reqs), chunking=chunking)
     try:
         log = []
         eng.run_chained(reqs, on_iteration=lambda res: log.append(
@@ -475,3 +475,38 @@ def test_generation_chained_bf16_trace_matches_synchronous():
     sync, slog = _gpu_generate(m, "bf16", W, reqs, 6, n_slots)
     assert log == slog
     assert got == sync
+
+
+@pytest.mark.parametrize("chunking", [(4, 2), (6, 3)])
+def test_chunked_prefill_generation_matches_oracle(chunking):
+    """Toy fp32 model, Figure-5 requests with prompts fed in chunks under a token budget: the GPU's
+    schedule and ids equal the oracle's chunked continuous batching (ids bit-exact), equal one-at-a-time
+    generation, and the chained loop gives the same."""
+    m = TOY
+    Wh = make_weights(m, 0, "fp32")
+    W = DeviceWeights(m, "fp32", host=Wh)
+    reqs = figure5_requests(seed=0, vocab=m.V, out_len=8)
+    gpu, log = _gpu_generate(m, "fp32", W, reqs, 4, 64, chunking)
+    want, olog = OG.generate_continuous(m, Wh, reqs, max_bs=4, n_slots=64, budget=chunking[0], chunk=chunking[1])
+    assert log == [(t, w) for t, w, _ in olog]
+    plen = {r.rid: len(r.prompt) for r in reqs}
+    assert any(0 < c < plen[rid] for _, w in log for rid, n, c in w)   # a prompt chunk on top of cached tokens
+    chained, clog = _gpu_generate_chained(m, "fp32", W, reqs, 4, 64, chunking)
+    assert clog == log
+    for r in reqs:
+        solo, margins = OG.generate_one_at_a_time(m, Wh, r.prompt, r.out_len)
+        assert gpu[r.rid] == want[r.rid] == chained[r.rid] == solo
+        assert min(margins) > 1e-4
+
+
+def test_chunked_prefill_bf16_trace_chained_matches_synchronous():
+    """GQA + RoPE bf16, a trace with long prompts split over several iterations: chained == synchronous."""
+    from synth import poisson_trace
+    m = TINY_LLAMA
+    W = DeviceWeights(m, "bf16", host=make_weights(m, 5, "bf16"))
+    reqs = poisson_trace(seed=8, n=30, rate=0.5, vocab=m.V, plo=20, phi=120, olo=1, ohi=16, reserve_out=16,
+                         with_prompts=True)
+    got, log = _gpu_generate_chained(m, "bf16", W, reqs, 6, 2000, (48, 32))
+    sync, slog = _gpu_generate(m, "bf16", W, reqs, 6, 2000, (48, 32))
+    assert log == slog and got == sync
+    assert max(sum(n for _, n, _ in w) for _, w in log) <= 48

@@ -95,10 +95,12 @@ def test_kv_placement_disjoint_aligned_and_compacts(seed):
 
 
 # ---------------------------------------------------------------- scheduler vs oracle
-def native_replay(reqs, max_bs, n_slots):
+def native_replay(reqs, max_bs, n_slots, budget=None, chunk=None):
     """The oracle's logical-clock loop, with the scheduling decisions made by libsb."""
     kv = sb.sb_kv_create(n_slots, sb.sb_kv_arena_slots(n_slots, max_bs), 1, 1, 8, sb.SB_F32)
     s = sb.sb_sched_create(max_bs, kv)
+    if budget is not None:
+        sb.sb_sched_set_chunking(s, budget, chunk)
     pending = sorted(reqs, key=lambda r: (r.arrival, r.rid))
     i, t, log = 0, 0, []
     while i < len(pending) or sb.sb_sched_stats(s)["pool"]:
@@ -144,6 +146,40 @@ def test_native_scheduler_matches_oracle_trace_2000():
     reqs = poisson_trace(seed=0, n=2000, rate=0.5)
     for n_slots in (20000, 65536):
         assert native_replay(reqs, 64, n_slots) == OS.replay(reqs, 64, n_slots)
+
+
+@pytest.mark.parametrize("case", range(5))
+def test_native_chunked_scheduler_matches_oracle(case):
+    """Chunked prefill under a token budget: libsb's decisions equal the oracle's, iteration by iteration
+    (the hand-worked example, then random traces with binding reservations and budgets)."""
+    if case == 0:
+        from golden import load as gload
+        g = gload("chunked_prefill.txt")
+
+        class R:
+            def __init__(self, rid, a, p, o):
+                self.rid, self.arrival, self.prompt, self.out_len, self.max_tokens = rid, a, [0] * p, o, p + o
+        reqs = [R(i, a, p, o) for i, (a, p, o) in enumerate(zip(g["arrivals"], g["prompt"], g["out_len"]))]
+        assert native_replay(reqs, 4, 10**9, 6, 4) == OS.replay(reqs, 4, 10**9, budget=6, chunk=4)
+        return
+    budget, chunk, max_bs, n_slots = [None, (16, 8, 4, 300), (64, 16, 8, 700), (7, 3, 3, 150), (512, 128, 16, 3000)][case]
+    reqs = poisson_trace(seed=200 + case, n=150, rate=[0, 0.5, 1.0, 0.3, 2.0][case], plo=1, phi=80, olo=1, ohi=25,
+                         reserve_out=25)
+    assert native_replay(reqs, max_bs, n_slots, budget, chunk) == \
+        OS.replay(reqs, max_bs, n_slots, budget=budget, chunk=chunk)
+
+
+def test_chunking_argument_errors():
+    kv = sb.sb_kv_create(10, sb.sb_kv_arena_slots(10, 2), 1, 1, 8, sb.SB_F32)
+    s = sb.sb_sched_create(2, kv)
+    for bad in ((0, 4), (8, 0), (-1, -1)):
+        with pytest.raises(sb.SBError) as e:
+            sb.sb_sched_set_chunking(s, *bad)
+        assert e.value.status == sb.SB_ERR_INVALID
+    sb.sb_sched_set_chunking(s, 8, 4)
+    sb.sb_sched_set_chunking(s, 0, 0)
+    sb.sb_sched_destroy(s)
+    sb.sb_kv_destroy(kv)
 
 
 def test_native_scheduler_tokens_and_outputs():
@@ -194,12 +230,16 @@ def _fake_token(rid, k, V=1000):
     return (rid * 7919 + k * 104729 + 13) % V
 
 
-def _deferred_vs_sync(reqs, max_bs, n_slots):
+def _deferred_vs_sync(reqs, max_bs, n_slots, chunking=None):
     """Drive two schedulers with the same arrivals: one completes with the token values, the other one
     iteration ahead (deferred completion; the decodes' tokens resolved from the previous iteration's
     'device' ids through their references).  Batches, fed tokens and outputs must agree."""
     kvs = [sb.sb_kv_create(n_slots, sb.sb_kv_arena_slots(n_slots, max_bs), 1, 1, 8, sb.SB_F32) for _ in range(2)]
     sy, de = sb.sb_sched_create(max_bs, kvs[0]), sb.sb_sched_create(max_bs, kvs[1])
+    if chunking is not None:
+        for s_ in (sy, de):
+            sb.sb_sched_set_chunking(s_, *chunking)
+    plen = {r.rid: len(r.prompt) for r in reqs}
     pending = sorted(reqs, key=lambda r: (r.arrival, r.rid))
     made = {r.rid: 0 for r in reqs}            # tokens generated so far (the fake model's clock per request)
     i, t, n_iter, prev = 0, 0, 0, None          # prev: (ids, device ids, ticket) of the deferred side
@@ -228,9 +268,11 @@ def _deferred_vs_sync(reqs, max_bs, n_slots):
                     assert e.value.status == sb.SB_ERR_STATE
             got = np.array([prev[1][-1 - v] if v < 0 else v for v in refs], np.int32)
             assert list(got) == list(want)
-            out = np.array([_fake_token(int(r), made[int(r)]) for r in ids], np.int32)
-            for r in ids:
-                made[int(r)] += 1
+            # members that yield a token: decodes and the chunk that ends a prompt (others: ignored value)
+            emits = [int(c) + int(n) >= plen[int(r)] for r, n, c in zip(ids, n_new, ctx)]
+            out = np.array([_fake_token(int(r), made[int(r)]) if e else -7 for r, e in zip(ids, emits)], np.int32)
+            for r, e in zip(ids, emits):
+                made[int(r)] += e
             sb.sb_sched_complete(sy, ids, out)
         if prev is not None:
             sb.sb_sched_set_tokens(de, prev[2], prev[1])
@@ -262,6 +304,15 @@ def test_deferred_completion_p4_timeline_and_figure5():
     assert _deferred_vs_sync(p4_grid_requests(seed=0), 3, 10**9) == 10
     for n_slots in (64, 30):
         _deferred_vs_sync(figure5_requests(seed=0, vocab=1000, out_len=8), 4, n_slots)
+
+
+@pytest.mark.parametrize("chunking", [(16, 8), (5, 2)])
+def test_deferred_completion_with_chunked_prefill(chunking):
+    """Deferred completion with prompt chunks that yield no token: references still point at the rows
+    that did yield one."""
+    reqs = poisson_trace(seed=21, n=60, rate=0.7, plo=1, phi=40, olo=1, ohi=15, reserve_out=15, vocab=1000,
+                         with_prompts=True)
+    _deferred_vs_sync(reqs, 6, 400, chunking)
 
 
 @pytest.mark.parametrize("case", range(3))

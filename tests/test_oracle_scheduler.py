@@ -162,3 +162,75 @@ def test_empty_pool_clock_jumps():
     log = S.replay(reqs, max_bs=4, n_slots=100)
     starts = [t for t, _, _ in log]
     assert starts[0] == int(np.ceil(reqs[0].arrival))
+
+
+# ---------------------------------------------------------------- chunked prefill
+class _CReq:
+    def __init__(self, rid, arrival, prompt_len, out_len, max_tokens):
+        self.rid, self.arrival, self.prompt_len, self.out_len, self.max_tokens = rid, arrival, prompt_len, out_len, \
+            max_tokens
+
+
+def test_chunked_prefill_hand_worked_example():
+    g = load("chunked_prefill.txt")
+    names = "ABC"
+    reqs = [_CReq(i, a, p, o, p + o) for i, (a, p, o) in enumerate(zip(g["arrivals"], g["prompt"], g["out_len"]))]
+    log = S.replay(reqs, g["max_bs"][0], 10**9, budget=g["budget"][0], chunk=g["chunk"][0])
+    got = {f"t{t}": [f"{names[rid]}:{n}:{c}" for rid, n, c in work] for t, work, _ in log}
+    want = {k: v for k, v in g.items() if k.startswith("t") and k[1:].isdigit()}
+    assert got == want
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_chunked_prefill_unbounded_is_algorithm1(seed):
+    """An unlimited budget and chunk reduce the chunked Select to Algorithm 1 exactly (the p4 grid, and
+    random traces with reservations that bind)."""
+    reqs = p4_grid_requests(seed=0)
+    assert S.replay(reqs, 3, 10**9, budget=10**9, chunk=10**9) == S.replay(reqs, 3, 10**9)
+    reqs = poisson_trace(seed=seed, n=200, rate=[0.5, 2.0, 1.0, 0.3][seed], plo=1, phi=40, olo=1, ohi=30,
+                         reserve_out=30)
+    for max_bs, n_slots in ((4, 200), (16, 500), (2, 10**6)):
+        assert S.replay(reqs, max_bs, n_slots, budget=10**9, chunk=10**9) == S.replay(reqs, max_bs, n_slots)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_chunked_prefill_invariants(seed):
+    """Budget respected, each prompt fed once in order in chunks <= chunk, decodes before prompt chunks
+    (and every decoding request served while budget and max_bs allow), out_len tokens per request,
+    reservations within the slots, FCFS admission."""
+    budget, chunk, max_bs, n_slots = [(16, 8, 4, 300), (64, 16, 8, 800), (7, 3, 3, 120), (128, 128, 16, 2000),
+                                      (5, 5, 2, 100), (33, 10, 6, 400)][seed]
+    reqs = poisson_trace(seed=100 + seed, n=150, rate=[0.5, 1.0, 0.3, 2.0, 0.2, 0.8][seed], plo=1, phi=60, olo=1,
+                         ohi=25, reserve_out=25)
+    log = S.replay(reqs, max_bs, n_slots, budget=budget, chunk=chunk)
+    by = {r.rid: r for r in reqs}
+    fed = {r.rid: 0 for r in reqs}            # prompt tokens fed so far
+    made = {r.rid: 0 for r in reqs}           # tokens yielded
+    admitted = []
+    live = set()
+    for t, work, n_rsrv in log:
+        assert sum(n for _, n, _ in work) <= budget and len(work) <= max_bs and n_rsrv <= n_slots
+        seen_prefill = False
+        for rid, n, c in work:
+            plen = len(by[rid].prompt)
+            if c < plen:                                          # a prompt chunk
+                seen_prefill = True
+                assert c == fed[rid] and 1 <= n <= chunk and c + n <= plen
+                if c == 0:
+                    admitted.append(rid)
+                fed[rid] += n
+                if fed[rid] == plen:
+                    made[rid] += 1
+            else:                                                 # a decode
+                assert not seen_prefill and n == 1 and fed[rid] == plen
+                assert c == plen + made[rid] - 1
+                made[rid] += 1
+            live.add(rid)
+        decoding = {rid for rid in live if fed[rid] == len(by[rid].prompt) and made[rid] < by[rid].out_len}
+        in_batch = {rid for rid, _, _ in work}
+        if seen_prefill:                      # prompt chunks only after every eligible decode
+            assert (decoding - in_batch) == set() or len(work) == max_bs
+        live = {rid for rid in live if made[rid] < by[rid].out_len}
+    assert all(made[r.rid] == r.out_len and fed[r.rid] == len(r.prompt) for r in reqs)
+    order = sorted(reqs, key=lambda r: (r.arrival, r.rid))
+    assert admitted == [r.rid for r in order]
