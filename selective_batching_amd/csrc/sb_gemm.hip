@@ -13,6 +13,7 @@
 // fp32: a plain LDS-tiled FMA kernel with a fixed, sequential K order.
 // Epilogues fuse bias, exact GeLU, SwiGLU (SiLU(gate) * up) or the residual
 // add into the fp32 stream x.
+#include <algorithm>
 #include <cstdlib>
 
 #include "sb_device.h"
@@ -523,6 +524,7 @@ enum {
     CFG_DMA_256x256_8W_K64_S2, CFG_DMA_256x256_4W_K64_S2,                                     // DMA-fed, BK 64
     CFG_DMA_256x256_8W_K64_S2_SPREAD, CFG_DMA_256x256_8W_S4_SPREAD,                           // copies spread over MFMAs
     CFG_DMA_256x192_8W_K64_S2_SPREAD, CFG_DMA_192x256_8W_K64_S2_SPREAD,                       // fewer-tile shapes
+    CFG_DMA_64x32_4W_K64_S8, CFG_DMA_64x16_2W_K64_S6, CFG_DMA_64x64_4W_K64_S6,                // skinny: deep K pipelines
     CFG_COUNT
 };
 
@@ -561,7 +563,39 @@ int num_cus() {
     return n;
 }
 
-// Pick the tile.  Small GEMMs keep 128 x 128 register-staged tiles.  Otherwise
+// GEMMs too small for a full round of big tiles (decode-heavy iterations: M of a few
+// hundred rows) are latency-bound: each workgroup walks K serially (one MFMA chain per
+// output, so K is never split) and takes about c microseconds per 64-deep K step
+// whatever its tile.  Estimated time = max(rounds of tiles x K steps x c, weight bytes
+// at 5 TB/s), with c and the resident workgroups per CU measured on MI355X for each
+// candidate: 128 x 128 register-staged (0.77 us, 2 per CU), 64 x 32 with 8 DMA stages
+// (0.30 us, 1 per CU; not for SwiGLU, whose 16-wide halves need 32 columns per wave)
+// and 64 x 64 with 6 stages (0.36 us, 1 per CU).  E.g. the 8B-shaped FFN2 (N 4096,
+// K 14336) at M 64 takes 64 x 32: 128 tiles, one round, 224 steps: ~67 us instead
+// of 172 us with 128 x 128 tiles.
+int pick_small(const GemmArgs& a, int epi) {
+    struct Cand { int cfg, bm, bn, per_cu; double us_per_step; };
+    const Cand cands[3] = {{CFG_128x128_4W, 128, 128, 2, 0.77},
+                           {CFG_DMA_64x32_4W_K64_S8, 64, 32, 1, 0.30},
+                           {CFG_DMA_64x64_4W_K64_S6, 64, 64, 1, 0.36}};
+    const int cus = num_cus();
+    const double steps = (double)a.K / 64.0;
+    const double wbytes = (double)(epi == EPI_SWIGLU ? 2 * a.N : a.N) * a.K * 2.0;
+    int best = CFG_128x128_4W;
+    double best_t = 0.0;
+    for (int c = 0; c < 3; ++c) {
+        const Cand& k = cands[c];
+        if (epi == EPI_SWIGLU && k.bn == 32) continue;
+        const int out_cols = (epi == EPI_SWIGLU) ? k.bn / 2 : k.bn;
+        const long long tiles = (long long)((a.M + k.bm - 1) / k.bm) * ((a.N + out_cols - 1) / out_cols);
+        const long long rounds = (tiles + (long long)cus * k.per_cu - 1) / ((long long)cus * k.per_cu);
+        const double t = std::max((double)rounds * steps * k.us_per_step, wbytes / 5e6);
+        if (c == 0 || t < best_t) { best = k.cfg; best_t = t; }
+    }
+    return best;
+}
+
+// Pick the tile.  Small GEMMs: pick_small.  Otherwise
 // DMA-fed tiles of 64-deep K: among 256x256, 256x192 and 192x256 the one with
 // the least estimated time, rounds x tile work x feed factor, where rounds =
 // ceil(tiles / CUs) (one such workgroup per CU) and the feed factor charges half
@@ -578,7 +612,7 @@ int pick_cfg(const GemmArgs& a, int epi) {
     }
     const int ncols = (epi == EPI_SWIGLU) ? 2 * a.N : a.N;
     const long long big = (long long)((a.M + 255) / 256) * ((ncols + 255) / 256);
-    if (big < 128) return CFG_128x128_4W;
+    if (big < 128) return pick_small(a, epi);
     if (a.M <= 256) return CFG_DMA_256x256_8W_K64_S2;
     struct Cand { int cfg, bm, bn; };
     const Cand cands[3] = {{CFG_DMA_256x256_8W_K64_S2_SPREAD, 256, 256},
@@ -616,6 +650,9 @@ int launch_bf16(const GemmArgs& a, hipStream_t s) {
         case CFG_DMA_256x256_8W_S4_SPREAD: return launch_dma<256, 256, 2, 4, 32, 4, 2, 1, EPI>(a, s);
         case CFG_DMA_256x192_8W_K64_S2_SPREAD: return launch_dma<256, 192, 2, 4, 64, 2, 2, 1, EPI>(a, s);
         case CFG_DMA_192x256_8W_K64_S2_SPREAD: return launch_dma<192, 256, 2, 4, 64, 2, 2, 1, EPI>(a, s);
+        case CFG_DMA_64x32_4W_K64_S8: return launch_dma<64, 32, 2, 2, 64, 8, 2, 0, EPI>(a, s);
+        case CFG_DMA_64x16_2W_K64_S6: return launch_dma<64, 16, 2, 1, 64, 6, 2, 0, EPI>(a, s);
+        case CFG_DMA_64x64_4W_K64_S6: return launch_dma<64, 64, 2, 2, 64, 6, 2, 0, EPI>(a, s);
         default: return launch_bf16_cfg<128, 128, 2, 2, EPI>(a, s);
     }
 }
