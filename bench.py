@@ -47,6 +47,7 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode-loop", action="store_true", help="skip the mini-model generation loop")
+    ap.add_argument("--no-trace", action="store_true", help="skip the serving-trace window and the policy replay")
     ap.add_argument("--layers", type=int, default=32, help="decoder layers (the workload has 32)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one 1 GiB device-to-device copy before the steps (calibrates HBM counters)")
@@ -160,6 +161,88 @@ def decode_loop(seed, steps=64, reps=3):
     return {"workload": (f"mini GPT (4 layers, hidden 256, 8 heads, FFN 1024, vocab 4096) bf16, random init; {B} "
                          f"requests in decode, cached context U[16,256], {steps} generated tokens each"),
             **out, "chained_speedup": round(out["synchronous"]["ms_per_step"] / out["chained"]["ms_per_step"], 3)}
+
+
+def reservation_policies(seed, n_slots=20000):
+    """The 8B-shaped serving trace (2000 Poisson arrivals at 0.5 per iteration, prompt U[32,512], output
+    U[1,512], max_bs 64) replayed through libsb's scheduler under the three reservation policies with the
+    K/V pool binding at ``n_slots``: iterations to drain the trace, mean batch, generated tokens per
+    iteration and the time-weighted fractions of slots reserved vs holding K/V.  Host work only."""
+    import math
+    import numpy as np
+    from selective_batching_amd import api as A
+    import selective_batching_amd as sb
+    from synth import poisson_trace
+    reqs = poisson_trace(seed=seed, n=2000, rate=0.5)
+    out = {"workload": f"2000-request Poisson trace (rate 0.5/iteration, prompt U[32,512], output U[1,512]), "
+                       f"max_bs 64, {n_slots} K/V slots (binding)"}
+    for name, code in (("max", sb.SB_RESERVE_MAX), ("pow2", sb.SB_RESERVE_POW2), ("oracle", sb.SB_RESERVE_ORACLE)):
+        kv = A.sb_kv_create(n_slots, A.sb_kv_arena_slots(n_slots, 64), 1, 1, 8, sb.SB_BF16)
+        s = A.sb_sched_create(64, kv)
+        pending = sorted(reqs, key=lambda r: (r.arrival, r.rid))
+        i = t = iters = members = gen = 0
+        res_sum = st_sum = 0
+        while i < len(pending) or A.sb_sched_stats(s)["pool"]:
+            while i < len(pending) and pending[i].arrival <= t:
+                r = pending[i]
+                A.sb_sched_add(s, r.rid, r.arrival, r.prompt, r.out_len,
+                               A.sb_reservation_tokens(code, len(r.prompt), r.out_len, 512))
+                i += 1
+            if not A.sb_sched_stats(s)["pool"]:
+                t = int(math.ceil(pending[i].arrival))
+                continue
+            ids, n_new, ctx, _ = A.sb_select_batch(s, 64)
+            rv, sv = A.sb_kv_usage(s)
+            res_sum += rv
+            st_sum += sv
+            iters += 1
+            members += len(ids)
+            gen += len(ids)
+            A.sb_sched_complete(s, ids, np.zeros(len(ids), np.int32))
+            t += 1
+        A.sb_sched_destroy(s)
+        A.sb_kv_destroy(kv)
+        out[name] = {"iterations": iters, "mean_batch": round(members / iters, 2),
+                     "generated_per_iteration": round(gen / iters, 2),
+                     "reserved_frac": round(res_sum / iters / n_slots, 4), "stored_frac": round(st_sum / iters / n_slots, 4)}
+    return out
+
+
+def trace_run(W, m, seed, iters=600, steady_from=200):
+    """The first ``iters`` iterations of the 8B-shaped serving trace on the GPU (Poisson arrivals at 0.5 per
+    iteration, prompt U[32,512], output U[1,512], max_tokens = prompt + 512, max_bs 64, K/V pool not
+    binding), run chained (iteration t+1 launched before t's ids reach the host).  Reports processed
+    (prompt + decode) and generated tokens per second over the window and over its steady part (from
+    iteration ``steady_from``, once the batch is full)."""
+    import torch
+    from selective_batching_amd.runtime import Engine
+    from synth import poisson_trace
+    reqs = poisson_trace(seed=seed, n=2000, rate=0.5, vocab=m.V, with_prompts=True)
+    n_slots = 64 * 1024 + 64 * 8
+    eng = Engine(m, "bf16", W, n_slots=n_slots, max_bs=64, max_tokens=64 * 512, max_keys_total=n_slots,
+                 zero_arena=False)
+    marks = []
+
+    def on_it(res):
+        torch.cuda.synchronize()            # (already settled: its ids are on the host)
+        marks.append((time.perf_counter(), int(res["n_new"].sum()), len(res["ids"])))
+
+    t0 = time.perf_counter()
+    n = eng.run_chained(reqs, on_iteration=on_it, max_iters=iters)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    eng.close()
+    proc = sum(p for _, p, _ in marks)
+    gen = sum(g for _, _, g in marks)
+    st = marks[steady_from:]
+    dt = st[-1][0] - marks[steady_from - 1][0]
+    return {"workload": ("8B-shaped decoder on the 2000-request Poisson trace (rate 0.5/iteration, prompt U[32,512], "
+                         f"output U[1,512], max_tokens = prompt + 512, max_bs 64): first {n} iterations, chained"),
+            "iterations": n, "processed_tokens_per_s": round(proc / wall, 1), "generated_tokens_per_s": round(gen / wall, 1),
+            "steady": {"from_iteration": steady_from, "processed_tokens_per_s": round(sum(p for _, p, _ in st) / dt, 1),
+                       "generated_tokens_per_s": round(sum(g for _, _, g in st) / dt, 1),
+                       "mean_batch": round(sum(g for _, _, g in st) / len(st), 2),
+                       "ms_per_iteration": round(1e3 * dt / len(st), 3)}}
 
 
 def ffn1_traffic():
@@ -334,6 +417,10 @@ def main():
                       "decode_kv_bytes_per_launch": work["attn_decode_bytes_per_layer"]},
         "kernels_ms_per_step": {k: round(v["ms_per_step"], 3) for k, v in brk.items()},
     }
+    if not args.no_trace:
+        print("[bench] serving trace (chained) ...", file=sys.stderr, flush=True)
+        out["trace"] = trace_run(W, m, args.seed)
+        out["reservation_policies"] = reservation_policies(args.seed)
     if not args.no_decode_loop:
         print("[bench] mini-model decode loop ...", file=sys.stderr, flush=True)
         out["decode_loop"] = decode_loop(args.seed)

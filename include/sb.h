@@ -203,6 +203,21 @@ int sb_batch_token_refs(const sb_sched* s, int32_t n, const int64_t* ids, int32_
 /* Generated tokens of a live or finished request (host, capacity cap). */
 int sb_sched_output(const sb_sched* s, int64_t req_id, int32_t cap, int32_t* tokens, int32_t* n);
 int sb_sched_stats(const sb_sched* s, int32_t* pool_size, int64_t* n_rsrv, int64_t* n_finished);
+
+/* Reservation policies ("CS349D Lecture 2", section 6.1, KV 预留): how many
+ * slots (max_tokens) a request reserves when first scheduled.  MAX: prompt +
+ * the longest output allowed (max_out), all a real system can know; POW2: the
+ * prompt + the output length rounded up to a power of two (a length
+ * prediction over-reserving at most 2x); ORACLE: prompt + out_len - 1, exactly
+ * the tokens that ever get K/V.  SB_ERR_INVALID unless
+ * 1 <= out_len <= max_out <= 2^30 and prompt_len >= 1. */
+enum { SB_RESERVE_MAX = 0, SB_RESERVE_POW2 = 1, SB_RESERVE_ORACLE = 2 };
+int sb_reservation_tokens(int32_t policy, int32_t prompt_len, int32_t out_len, int32_t max_out, int32_t* max_tokens);
+/* K/V slots reserved (n_rsrv) and slots holding K/V (section 6.1's 'reserved'
+ * vs 'actually stored'): every token written so far by a pool request, the
+ * current iteration's tokens included for the members of a selected batch
+ * (call it between sb_select_batch and the Complete). */
+int sb_kv_usage(const sb_sched* s, int64_t* reserved, int64_t* stored);
 void sb_sched_destroy(sb_sched* s);
 
 /* ------------------------------------------------------------------ ragged batch

@@ -229,6 +229,55 @@ def replay(reqs, max_bs, n_slots, engine=None, budget=None, chunk=None):
     return log
 
 
+# ---------------------------------------------------------------- reservation policies
+# "CS349D Lecture 2", section 6.1 (KV 预留：被占着 ≠ 被用着): Orca reserves a request's K/V slots when it is
+# first scheduled; how many is a policy.  Readings: Max = the prompt plus the longest output allowed;
+# Pow2 = the prompt plus the output length rounded up to a power of two (a length prediction that
+# over-reserves by at most 2x); Oracle = exactly the tokens that ever get K/V: prompt + out_len - 1
+# (the last generated token is never fed back).
+POLICIES = ("max", "pow2", "oracle")
+
+
+def reservation(policy, prompt_len, out_len, max_out):
+    """max_tokens a request reserves under ``policy``."""
+    if policy == "max":
+        return prompt_len + max_out
+    if policy == "pow2":
+        p = 1
+        while p < out_len:
+            p *= 2
+        return prompt_len + p
+    if policy == "oracle":
+        return prompt_len + out_len - 1
+    raise ValueError(policy)
+
+
+def kv_usage(log, reqs, n_slots):
+    """Time-weighted K/V occupancy of a replay on the iteration clock (lecture section 6.1's two columns):
+    'reserved' = slots reserved while the iteration runs (n_rsrv after Select), 'stored' = slots holding
+    K/V at the end of the iteration (every token fed so far by a request that holds its reservation during
+    that iteration).  Each iteration weighs one time unit.  Returns (reserved, stored) as fractions of
+    ``n_slots`` and the per-iteration stored counts."""
+    plen = {r.rid: (len(r.prompt) if hasattr(r, "prompt") else r.prompt_len) for r in reqs}
+    out_len = {r.rid: r.out_len for r in reqs}
+    fed, made, stored_t = {}, {}, []
+    res_sum = st_sum = 0
+    for t, work, n_rsrv in log:
+        for rid, n_new, ctx in work:
+            fed[rid] = ctx + n_new                      # K/V of every token fed so far
+        stored = sum(fed.values())
+        stored_t.append(stored)
+        res_sum += n_rsrv
+        st_sum += stored
+        for rid, n_new, ctx in work:                    # a member yields a token iff its work passes its prompt
+            if ctx + n_new >= plen[rid]:
+                made[rid] = made.get(rid, 0) + 1
+                if made[rid] == out_len[rid]:
+                    del fed[rid]                        # finished: its slots are freed after this iteration
+    n = max(len(log), 1)
+    return res_sum / n / n_slots, st_sum / n / n_slots, stored_t
+
+
 def timeline(log, reqs):
     """Render a replay log as one row of P/D/wait marks per request (lecture section 4.1 style).
 

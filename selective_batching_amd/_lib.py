@@ -15,6 +15,7 @@ SB_ERR_DEVICE, SB_ERR_WORKSPACE, SB_ERR_STATE, SB_ERR_CAPACITY = -5, -6, -7, -8
 SB_F32, SB_BF16 = 0, 1
 SB_ARCH_GPT, SB_ARCH_LLAMA = 0, 1
 SB_EPI_STORE, SB_EPI_GELU, SB_EPI_RESID, SB_EPI_SWIGLU = 0, 1, 2, 3
+SB_RESERVE_MAX, SB_RESERVE_POW2, SB_RESERVE_ORACLE = 0, 1, 2
 (SB_K_GEMM_QKV, SB_K_GEMM_O, SB_K_GEMM_FFN1, SB_K_GEMM_FFN2, SB_K_GEMM_LM, SB_K_ATTN, SB_K_ATTN_COMBINE,
  SB_K_NORM, SB_K_ROPE_APPEND, SB_K_EMBED, SB_K_ARGMAX, SB_K_COUNT) = range(12)
 KERNEL_CLASSES = ["gemm_qkv", "gemm_o", "gemm_ffn1", "gemm_ffn2", "gemm_lm", "attention", "attention_combine",
@@ -83,6 +84,8 @@ _PROTOS = {
     "sb_batch_tokens": (C.c_int, [vp, i32, vp, i32, vp, P(i32)]),
     "sb_sched_complete": (C.c_int, [vp, i32, vp, vp, P(i32), vp]),
     "sb_sched_set_chunking": (C.c_int, [vp, i32, i32]),
+    "sb_reservation_tokens": (C.c_int, [i32, i32, i32, i32, P(i32)]),
+    "sb_kv_usage": (C.c_int, [vp, P(i64), P(i64)]),
     "sb_sched_complete_deferred": (C.c_int, [vp, i32, vp, P(i32), vp, P(i64)]),
     "sb_sched_set_tokens": (C.c_int, [vp, i64, i32, vp]),
     "sb_batch_token_refs": (C.c_int, [vp, i32, vp, i32, vp, P(i32), P(i64)]),

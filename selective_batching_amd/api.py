@@ -103,6 +103,18 @@ def sb_sched_add_running(s, req_id, arrival, prompt_len, out_len, max_tokens, ge
          last_token)
 
 
+def sb_reservation_tokens(policy, prompt_len, out_len, max_out):
+    v = C.c_int32()
+    call("sb_reservation_tokens", policy, prompt_len, out_len, max_out, C.byref(v))
+    return v.value
+
+
+def sb_kv_usage(s):
+    r, st = C.c_int64(), C.c_int64()
+    call("sb_kv_usage", s, C.byref(r), C.byref(st))
+    return r.value, st.value
+
+
 def sb_sched_set_chunking(s, token_budget, chunk):
     call("sb_sched_set_chunking", s, token_budget, chunk)
 

@@ -6,6 +6,7 @@
 // 5.1 of "CS349D Lecture 2 · 批处理与调度"; select_batch in "Orca: The
 // beginning of Morden LLM serving" (Scheduling Algorithm).
 #include <algorithm>
+#include <climits>
 #include <array>
 #include <cstdio>
 #include <cstring>
@@ -571,6 +572,42 @@ extern "C" int sb_sched_output(const sb_sched* s, int64_t req_id, int32_t cap, i
     *n = (int32_t)v->size();
     if ((int32_t)v->size() > cap) return fail(SB_ERR_CAPACITY, "capacity %d < %zu tokens", cap, v->size());
     if (tokens && !v->empty()) std::memcpy(tokens, v->data(), sizeof(int32_t) * v->size());
+    return SB_OK;
+}
+
+extern "C" int sb_reservation_tokens(int32_t policy, int32_t prompt_len, int32_t out_len, int32_t max_out,
+                                     int32_t* max_tokens) {
+    if (!max_tokens) return fail(SB_ERR_INVALID, "NULL argument");
+    if (prompt_len < 1 || out_len < 1 || out_len > max_out || max_out > (1 << 30))
+        return fail(SB_ERR_INVALID, "need 1 <= out_len <= max_out <= 2^30 and prompt_len >= 1");
+    int64_t v;
+    switch (policy) {
+        case SB_RESERVE_MAX: v = (int64_t)prompt_len + max_out; break;
+        case SB_RESERVE_POW2: {
+            int64_t p = 1;
+            while (p < out_len) p *= 2;
+            v = (int64_t)prompt_len + p;
+            break;
+        }
+        case SB_RESERVE_ORACLE: v = (int64_t)prompt_len + out_len - 1; break;
+        default: return fail(SB_ERR_INVALID, "unknown reservation policy %d", policy);
+    }
+    if (v > INT32_MAX) return fail(SB_ERR_INVALID, "reservation overflows int32");
+    *max_tokens = (int32_t)v;
+    return SB_OK;
+}
+
+extern "C" int sb_kv_usage(const sb_sched* s, int64_t* reserved, int64_t* stored) {
+    if (!s || !reserved || !stored) return fail(SB_ERR_INVALID, "NULL argument");
+    int64_t st = 0;
+    for (const Req* r : s->pool) {
+        if (r->state == ST_RUNNING)                  // this iteration's tokens counted as written
+            st += (r->prefilled < r->prompt_len ? r->prefilled : (int64_t)r->prompt_len + r->generated - 1) + r->cur_new;
+        else
+            st += r->prefilled + std::max(r->generated - 1, 0);
+    }
+    *reserved = s->kv->n_rsrv;
+    *stored = st;
     return SB_OK;
 }
 

@@ -265,13 +265,14 @@ class Engine:
         p = self.launch(keep=keep)
         return None if p is None else self.finish(p)
 
-    def run_chained(self, reqs=(), on_iteration=None):
+    def run_chained(self, reqs=(), on_iteration=None, max_iters=None):
         """Serve ``reqs`` (objects with rid, arrival, prompt, out_len, max_tokens) and whatever is already
         in the pool until all are done, one iteration ahead of the host: iteration t+1 is selected and
         launched -- its decodes embedding iteration t's ids on the device -- before the host waits for
         iteration t's ids.  Arrivals follow the iteration clock: a request joins the pool at the first
         iteration t >= its arrival; an idle clock jumps to the next arrival.  ``on_iteration(result)``
-        receives each settled iteration (with its clock in result["t"]).  Returns the iteration count."""
+        receives each settled iteration (with its clock in result["t"]).  ``max_iters``: stop launching
+        after that many iterations (the requests still in the pool stay there).  Returns the iteration count."""
         import math
         pending = sorted(reqs, key=lambda r: (r.arrival, r.rid))
         i, clock, n_iter, prev = 0, 0, 0, None
@@ -282,14 +283,14 @@ class Engine:
                 r = pending[i]
                 self.add(r.rid, r.arrival, r.prompt, r.out_len, r.max_tokens)
                 i += 1
-            p = self.launch(buf=n_iter % 2, chain=prev)
+            p = self.launch(buf=n_iter % 2, chain=prev) if max_iters is None or n_iter < max_iters else None
             if prev is not None:
                 res = self.settle(prev)
                 res["t"] = prev["t"]
                 if on_iteration is not None:
                     on_iteration(res)
             if p is None:
-                if i >= len(pending):
+                if i >= len(pending) or (max_iters is not None and n_iter >= max_iters):
                     return n_iter
                 clock, prev = int(math.ceil(pending[i].arrival)), None
                 continue

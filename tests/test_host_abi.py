@@ -95,7 +95,7 @@ def test_kv_placement_disjoint_aligned_and_compacts(seed):
 
 
 # ---------------------------------------------------------------- scheduler vs oracle
-def native_replay(reqs, max_bs, n_slots, budget=None, chunk=None):
+def native_replay(reqs, max_bs, n_slots, budget=None, chunk=None, usage=None):
     """The oracle's logical-clock loop, with the scheduling decisions made by libsb."""
     kv = sb.sb_kv_create(n_slots, sb.sb_kv_arena_slots(n_slots, max_bs), 1, 1, 8, sb.SB_F32)
     s = sb.sb_sched_create(max_bs, kv)
@@ -113,6 +113,8 @@ def native_replay(reqs, max_bs, n_slots, budget=None, chunk=None):
             continue
         ids, n_new, ctx, _ = sb.sb_select_batch(s, max_bs)
         log.append((t, [(int(a), int(b), int(c)) for a, b, c in zip(ids, n_new, ctx)], sb.sb_sched_stats(s)["n_rsrv"]))
+        if usage is not None:
+            usage.append(sb.sb_kv_usage(s))
         sb.sb_sched_complete(s, ids, np.zeros(len(ids), np.int32))
         t += 1
     sb.sb_sched_destroy(s)
@@ -167,6 +169,32 @@ def test_native_chunked_scheduler_matches_oracle(case):
                          reserve_out=25)
     assert native_replay(reqs, max_bs, n_slots, budget, chunk) == \
         OS.replay(reqs, max_bs, n_slots, budget=budget, chunk=chunk)
+
+
+@pytest.mark.parametrize("policy", ["max", "pow2", "oracle"])
+def test_native_reservation_policies_and_kv_usage_match_oracle(policy):
+    """sb_reservation_tokens == the oracle's policy; sb_kv_usage == the oracle's reserved / stored slots on
+    every iteration of a trace (with and without chunked prefill)."""
+    code = {"max": sb.SB_RESERVE_MAX, "pow2": sb.SB_RESERVE_POW2, "oracle": sb.SB_RESERVE_ORACLE}[policy]
+    for p, n in ((1, 1), (5, 2), (10, 25), (300, 511), (40, 512)):
+        assert sb.sb_reservation_tokens(code, p, n, 512) == OS.reservation(policy, p, n, 512)
+    reqs = poisson_trace(seed=31, n=200, rate=0.8, plo=1, phi=80, olo=1, ohi=40, reserve_out=40)
+    for r in reqs:
+        r.max_tokens = sb.sb_reservation_tokens(code, len(r.prompt), r.out_len, 40)
+    for budget, chunk in ((None, None), (24, 8)):
+        usage = []
+        log = native_replay(reqs, 12, 900, budget, chunk, usage)
+        olog = OS.replay(reqs, 12, 900, budget=budget, chunk=chunk)
+        assert log == olog
+        _, _, stored = OS.kv_usage(olog, reqs, 900)
+        assert [u[0] for u in usage] == [n for _, _, n in olog] and [u[1] for u in usage] == stored
+
+
+def test_reservation_policy_errors():
+    for args in ((3, 1, 2, 4), (0, 1, 0, 4), (0, 0, 2, 4), (0, 1, 5, 4)):
+        with pytest.raises(sb.SBError) as e:
+            sb.sb_reservation_tokens(*args)
+        assert e.value.status == sb.SB_ERR_INVALID
 
 
 def test_chunking_argument_errors():

@@ -234,3 +234,44 @@ def test_chunked_prefill_invariants(seed):
     assert all(made[r.rid] == r.out_len and fed[r.rid] == len(r.prompt) for r in reqs)
     order = sorted(reqs, key=lambda r: (r.arrival, r.rid))
     assert admitted == [r.rid for r in order]
+
+
+# ---------------------------------------------------------------- reservation policies / K/V usage
+def test_reservation_policy_closed_forms():
+    """Lecture section 6.1: Max reserves the longest output, Pow2 rounds the output up to a power of two
+    (an output of 25 reserves 32 positions), Oracle exactly the tokens that get K/V."""
+    assert S.reservation("max", 10, 25, 512) == 10 + 512
+    assert S.reservation("pow2", 10, 25, 512) == 10 + 32
+    assert [S.reservation("pow2", 0, n, 512) for n in (1, 2, 3, 32, 33, 512)] == [1, 2, 4, 32, 64, 512]
+    assert S.reservation("oracle", 10, 25, 512) == 10 + 25 - 1
+    for p, n in ((1, 1), (7, 300), (512, 512)):
+        assert S.reservation("oracle", p, n, 512) <= S.reservation("pow2", p, n, 512) <= S.reservation("max", p, n, 512)
+        assert S.reservation("pow2", p, n, 512) - p < 2 * n
+
+
+def test_kv_usage_hand_worked():
+    """One request, prompt 3, out 2, Oracle reservation 4 of 10 slots: iteration 0 prefills (3 tokens
+    stored), iteration 1 decodes (4 stored) and finishes: reserved 0.4, stored (3 + 4) / 2 / 10 = 0.35."""
+    class R:
+        rid, arrival, prompt, out_len, max_tokens = 0, 0.0, [1, 2, 3], 2, 4
+    log = S.replay([R()], 1, 10)
+    res, st, per = S.kv_usage(log, [R()], 10)
+    assert per == [3, 4] and res == pytest.approx(0.4) and st == pytest.approx(0.35)
+
+
+@pytest.mark.parametrize("policy", S.POLICIES)
+def test_kv_usage_invariants(policy):
+    """Stored never exceeds reserved; under Oracle a request's stored K/V reaches its reservation exactly
+    on its last iteration; tighter policies finish the same work in no more iterations here."""
+    reqs = poisson_trace(seed=5, n=300, rate=1.0, plo=1, phi=60, olo=1, ohi=60, reserve_out=60)
+    for r in reqs:
+        r.max_tokens = S.reservation(policy, len(r.prompt), r.out_len, 60)
+    log = S.replay(reqs, 16, 800)
+    res, st, per = S.kv_usage(log, reqs, 800)
+    assert all(s_ <= n_rsrv for s_, (_, _, n_rsrv) in zip(per, log)) and st <= res <= 1.0
+    if policy == "oracle":
+        last = {}
+        for t, work, _ in log:
+            for rid, n, c in work:
+                last[rid] = c + n
+        assert all(last[r.rid] == r.max_tokens for r in reqs)
