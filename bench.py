@@ -245,6 +245,45 @@ def trace_run(W, m, seed, iters=600, steady_from=200):
                        "ms_per_iteration": round(1e3 * dt / len(st), 3)}}
 
 
+def scheduling_compare(W, m, seed, n=96):
+    """The first ``n`` requests of the 8B-shaped serving trace (Poisson arrivals at 0.5 per iteration,
+    prompt U[32,512], output U[1,512], max_bs 64) run to completion on the same kernels under
+    iteration-level scheduling (Algorithm 1) and under request-level (static) batching, both chained.
+    Reports iterations, wall time, generated tokens per second and the mean time to first token and to
+    completion on the iteration clock."""
+    import torch
+    from selective_batching_amd.runtime import Engine
+    from synth import poisson_trace
+    reqs = poisson_trace(seed=seed, n=n, rate=0.5, vocab=m.V, with_prompts=True)
+    arrive = {r.rid: r.arrival for r in reqs}
+    out = {"workload": (f"first {n} requests of the 8B-shaped serving trace (Poisson 0.5/iteration, prompt "
+                        "U[32,512], output U[1,512]), max_bs 64, run to completion on the same kernels")}
+    for name, static in (("iteration_level", False), ("request_level", True)):
+        n_slots = 64 * 1024 + 64 * 8
+        eng = Engine(m, "bf16", W, n_slots=n_slots, max_bs=64, max_tokens=64 * 512, max_keys_total=n_slots,
+                     zero_arena=False, request_level=static)
+        first, last = {}, {}
+
+        def on_it(res):
+            for rid in res["ids"]:
+                first.setdefault(int(rid), res["t"])
+                last[int(rid)] = res["t"]
+
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        iters = eng.run_chained(reqs, on_iteration=on_it)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        eng.close()
+        gen = sum(r.out_len for r in reqs)
+        out[name] = {"iterations": iters, "wall_s": round(wall, 3), "generated_tokens_per_s": round(gen / wall, 1),
+                     "mean_ttft_iterations": round(sum(first[k] - arrive[k] + 1 for k in first) / n, 2),
+                     "mean_latency_iterations": round(sum(last[k] - arrive[k] + 1 for k in last) / n, 2)}
+    out["throughput_ratio"] = round(out["iteration_level"]["generated_tokens_per_s"] /
+                                    out["request_level"]["generated_tokens_per_s"], 3)
+    return out
+
+
 def ffn1_traffic():
     """HBM bytes per FFN1 GEMM launch (FETCH_SIZE + WRITE_SIZE counter runs, scaled by a 1 GiB copy) as
     recorded in profiles/ffn1_gemm_traffic.json, or None when the GEMM sources changed since."""
@@ -421,6 +460,8 @@ def main():
         print("[bench] serving trace (chained) ...", file=sys.stderr, flush=True)
         out["trace"] = trace_run(W, m, args.seed)
         out["reservation_policies"] = reservation_policies(args.seed)
+        print("[bench] iteration-level vs request-level scheduling ...", file=sys.stderr, flush=True)
+        out["scheduling"] = scheduling_compare(W, m, args.seed)
     if not args.no_decode_loop:
         print("[bench] mini-model decode loop ...", file=sys.stderr, flush=True)
         out["decode_loop"] = decode_loop(args.seed)

@@ -162,6 +162,14 @@ int sb_sched_add_running(sb_sched* s, int64_t req_id, double arrival, int32_t pr
  * Both 0 (the default) turns it off: whole prompts, Algorithm 1 exactly.
  * SB_ERR_INVALID unless both are positive or both 0. */
 int sb_sched_set_chunking(sb_sched* s, int32_t token_budget, int32_t chunk);
+/* Request-level (static) batching, the baseline iteration-level scheduling is
+ * compared against ("CS349D Lecture 2", section 4.1, static grid): with on != 0,
+ * Select forms a new batch (as Algorithm 1: arrival order, max_bs, reservation)
+ * only once the previous batch has entirely finished, and until then returns
+ * that batch's unfinished members; nobody joins mid-batch.  Finished members
+ * leave the computed batch (no padding work on ragged kernels) but their seats
+ * are not refilled.  SB_ERR_INVALID while chunking is on. */
+int sb_sched_set_request_level(sb_sched* s, int32_t on);
 /* Select the next batch (host arrays of capacity cap).  For member i:
  * n_new[i] = tokens fed this iteration (the prompt or a chunk of it, or 1),
  * ctx[i] = tokens already cached, slot_base[i] = first slot of its reservation.

@@ -30,6 +30,14 @@ The pages fix the idea but not every rule; the reading taken here:
   * only the chunk that completes a prompt yields a token (the first one).
 With an unlimited budget and chunk this is Algorithm 1 itself (with one worker
 every decoding request arrived before every waiting one).
+
+Request-level (static) batching, the baseline the pages compare against ("CS349D
+Lecture 2", section 4.1, the static grid; "从静态批处理到连续批处理", 静态批处理的
+困境): a batch starts only when the previous one has entirely finished, takes up
+to max_bs waiting requests in arrival order (reserving as above), and runs until
+its longest member is done; nobody joins mid-batch.  On ragged kernels a finished
+member needs no padding work: it leaves the computed batch but its seat stays
+empty until the batch ends (reading taken here: its compute is not charged).
 """
 import math
 
@@ -123,7 +131,7 @@ def work_of(r):
 class Scheduler:
     """Pool, counters and the per-iteration state transitions (one worker)."""
 
-    def __init__(self, max_bs, n_slots, budget=None, chunk=None):
+    def __init__(self, max_bs, n_slots, budget=None, chunk=None, static=False):
         if max_bs <= 0:
             raise ValueError("max_bs must be positive")
         if (budget is None) != (chunk is None) or (budget is not None and (budget < 1 or chunk < 1)):
@@ -131,6 +139,10 @@ class Scheduler:
         self.max_bs = max_bs
         self.n_slots = n_slots
         self.budget, self.chunk = budget, chunk
+        if static and budget is not None:
+            raise ValueError("request-level batching feeds whole prompts")
+        self.static = static
+        self.seated = []                 # request-level batching: the running batch's unfinished members
         self.n_rsrv = 0
         self.pool = []
         self._order = 0
@@ -146,7 +158,13 @@ class Scheduler:
         return r
 
     def select(self):
-        if self.budget is None:
+        if self.static:
+            if not self.seated:          # the previous batch has entirely finished: form a new one
+                self.seated, self.n_rsrv = select(self.pool, self.n_rsrv, self.max_bs, self.n_slots)
+            batch = list(self.seated)
+            for r in batch:
+                r.cur_new = work_of(r)[0]
+        elif self.budget is None:
             batch, self.n_rsrv = select(self.pool, self.n_rsrv, self.max_bs, self.n_slots)
             for r in batch:
                 r.cur_new = work_of(r)[0]
@@ -186,10 +204,11 @@ class Scheduler:
         if finished:
             gone = {id(r) for r in finished}
             self.pool = [r for r in self.pool if id(r) not in gone]
+            self.seated = [r for r in self.seated if id(r) not in gone]
         return finished
 
 
-def replay(reqs, max_bs, n_slots, engine=None, budget=None, chunk=None):
+def replay(reqs, max_bs, n_slots, engine=None, budget=None, chunk=None, static=False):
     """Run the iteration loop on a logical clock t = 0, 1, 2, ...
 
     ``reqs``: objects with ``rid, arrival, prompt (or prompt_len), out_len,
@@ -203,7 +222,7 @@ def replay(reqs, max_bs, n_slots, engine=None, budget=None, chunk=None):
 
     Returns the per-iteration log ``[(t, [(rid, n_new, ctx), ...], n_rsrv_after_select)]``.
     """
-    s = Scheduler(max_bs, n_slots, budget, chunk)
+    s = Scheduler(max_bs, n_slots, budget, chunk, static)
     pending = sorted(reqs, key=lambda r: (r.arrival, r.rid))
     i = 0
     t = 0
@@ -276,6 +295,24 @@ def kv_usage(log, reqs, n_slots):
                     del fed[rid]                        # finished: its slots are freed after this iteration
     n = max(len(log), 1)
     return res_sum / n / n_slots, st_sum / n / n_slots, stored_t
+
+
+def timeline_static(log, reqs):
+    """As ``timeline`` for a request-level replay, with '-' for a seat its finished request still holds
+    until the rest of its batch is done."""
+    rows = timeline(log, reqs)
+    n_it = log[-1][0] + 1 if log else 0
+    grid = {rid: list(row.ljust(n_it)) for rid, row in rows.items()}
+    # batches: maximal runs of iterations whose members are a subset of the first iteration's (all prefill)
+    starts = [i for i, (_, work, _) in enumerate(log) if all(ctx == 0 for _, _, ctx in work)]
+    for b, i0 in enumerate(starts):
+        i1 = starts[b + 1] if b + 1 < len(starts) else len(log)
+        t_end = log[i1 - 1][0]
+        for rid, _, _ in log[i0][1]:
+            last = max(t for t, work, _ in log[i0:i1] if any(w[0] == rid for w in work))
+            for t in range(last + 1, t_end + 1):
+                grid[rid][t] = "-"
+    return {rid: "".join(v).rstrip() for rid, v in grid.items()}
 
 
 def timeline(log, reqs):

@@ -84,6 +84,7 @@ _PROTOS = {
     "sb_batch_tokens": (C.c_int, [vp, i32, vp, i32, vp, P(i32)]),
     "sb_sched_complete": (C.c_int, [vp, i32, vp, vp, P(i32), vp]),
     "sb_sched_set_chunking": (C.c_int, [vp, i32, i32]),
+    "sb_sched_set_request_level": (C.c_int, [vp, i32]),
     "sb_reservation_tokens": (C.c_int, [i32, i32, i32, i32, P(i32)]),
     "sb_kv_usage": (C.c_int, [vp, P(i64), P(i64)]),
     "sb_sched_complete_deferred": (C.c_int, [vp, i32, vp, P(i32), vp, P(i64)]),

@@ -115,6 +115,10 @@ def sb_kv_usage(s):
     return r.value, st.value
 
 
+def sb_sched_set_request_level(s, on):
+    call("sb_sched_set_request_level", s, 1 if on else 0)
+
+
 def sb_sched_set_chunking(s, token_budget, chunk):
     call("sb_sched_set_chunking", s, token_budget, chunk)
 

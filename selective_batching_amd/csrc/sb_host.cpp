@@ -251,6 +251,8 @@ struct sb_sched {
     int64_t next_order = 0;
     int64_t n_finished = 0;
     int32_t budget = 0, chunk = 0;                  // chunked prefill (0: whole prompts, Algorithm 1)
+    bool request_level = false;                     // static batching: whole batches start and end together
+    std::vector<Req*> seated;                       // its running batch's unfinished members (batch order)
     // deferred completions: ticket -> (request id, position of the pending token in its output), batch order
     std::map<int64_t, std::vector<std::pair<int64_t, int32_t>>> tickets;
     int64_t next_ticket = 0;
@@ -341,8 +343,17 @@ extern "C" int sb_sched_add_running(sb_sched* s, int64_t req_id, double arrival,
     return insert_req(s, std::move(r));
 }
 
+extern "C" int sb_sched_set_request_level(sb_sched* s, int32_t on) {
+    if (!s) return fail(SB_ERR_INVALID, "sched is NULL");
+    if (on && s->budget) return fail(SB_ERR_INVALID, "request-level batching feeds whole prompts (chunking is on)");
+    if (!on) s->seated.clear();
+    s->request_level = on != 0;
+    return SB_OK;
+}
+
 extern "C" int sb_sched_set_chunking(sb_sched* s, int32_t token_budget, int32_t chunk) {
     if (!s) return fail(SB_ERR_INVALID, "sched is NULL");
+    if (token_budget && s->request_level) return fail(SB_ERR_INVALID, "chunking needs iteration-level scheduling");
     if (token_budget < 0 || chunk < 0 || (token_budget == 0) != (chunk == 0))
         return fail(SB_ERR_INVALID, "token_budget and chunk: both positive, or both 0 (off)");
     s->budget = token_budget;
@@ -371,7 +382,9 @@ extern "C" int sb_select_batch(sb_sched* s, int32_t cap, int64_t* ids, int32_t* 
         return true;
     };
     int st = SB_OK;
-    if (s->budget == 0) {
+    if (s->request_level && !s->seated.empty()) {
+        for (Req* r : s->seated) batch.push_back({r, 1}); // the running batch continues, nobody joins
+    } else if (s->budget == 0) {
         for (Req* r : s->pool) {                          // arrival order
             if (r->state == ST_RUNNING) continue;
             if ((int32_t)batch.size() == s->max_bs) break;
@@ -396,6 +409,8 @@ extern "C" int sb_select_batch(sb_sched* s, int32_t cap, int64_t* ids, int32_t* 
         }
     }
     if (st) return st;
+    if (s->request_level && s->seated.empty())
+        for (auto& b : batch) s->seated.push_back(b.first);
     for (size_t i = 0; i < batch.size(); ++i) {
         Req* r = batch[i].first;
         r->state = ST_RUNNING;
@@ -505,6 +520,8 @@ int complete_batch(sb_sched* s, int32_t n, const int64_t* ids, const int32_t* ne
             nf++;
             s->n_finished++;
             s->pool.erase(std::find(s->pool.begin(), s->pool.end(), r));
+            auto seat = std::find(s->seated.begin(), s->seated.end(), r);
+            if (seat != s->seated.end()) s->seated.erase(seat);
             s->done[r->id] = std::move(r->out);
             s->by_id.erase(r->id);
         }

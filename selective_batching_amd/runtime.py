@@ -101,9 +101,9 @@ class Engine:
     """K/V manager + scheduler + device buffers for one model on one GPU."""
 
     def __init__(self, m, dtype: str, weights: DeviceWeights, n_slots: int, max_bs: int, max_tokens: int,
-                 max_keys_total: int = None, device="cuda", zero_arena=True, chunking=None):
+                 max_keys_total: int = None, device="cuda", zero_arena=True, chunking=None, request_level=False):
         """``max_tokens``: most tokens one iteration feeds (with ``chunking`` = (token budget, chunk) the
-        budget bounds it)."""
+        budget bounds it).  ``request_level``: static batching (the baseline) instead of Algorithm 1."""
         self.m, self.dtype, self.w = m, dtype, weights
         self.dims = make_dims(m, dtype)
         self.max_bs, self.max_tokens = max_bs, max_tokens
@@ -122,6 +122,8 @@ class Engine:
         self.sched = A.sb_sched_create(max_bs, self.kv)
         if chunking is not None:
             A.sb_sched_set_chunking(self.sched, *chunking)
+        if request_level:
+            A.sb_sched_set_request_level(self.sched, True)
         self.max_keys_total = max_keys_total if max_keys_total is not None else max_bs * (n_slots + 1)
         self.meta_bytes = A.sb_ragged_bytes(self.dims, max_bs, max_tokens, self.max_keys_total)
         # two host staging buffers (and two host id buffers): the host can build iteration k+1's

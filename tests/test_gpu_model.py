@@ -241,9 +241,9 @@ def test_llama8b_shape_layer_stepwise():
         sb.sb_kv_destroy(kv)
 
 
-def _gpu_generate(m, dtype, W, reqs, max_bs, n_slots, chunking=None):
+def _gpu_generate(m, dtype, W, reqs, max_bs, n_slots, chunking=None, request_level=False):
     eng = Engine(m, dtype, W, n_slots=n_slots, max_bs=max_bs, max_tokens=sum(len(r.prompt) for r in reqs) + max_bs,
-                 max_keys_total=sum(r.max_tokens for r in reqs), chunking=chunking)
+                 max_keys_total=sum(r.max_tokens for r in reqs), chunking=chunking, request_level=request_level)
     try:
         import math
         pending = sorted(reqs, key=lambda r: (r.arrival, r.rid))
@@ -431,11 +431,11 @@ def test_pipelined_launches_match_sequential_steps():
         eng.close()
 
 
-def _gpu_generate_chained(m, dtype, W, reqs, max_bs, n_slots, chunking=None):
+def _gpu_generate_chained(m, dtype, W, reqs, max_bs, n_slots, chunking=None, request_level=False):
     """As _gpu_generate, but one iteration ahead of the host (Engine.run_chained): decodes embed the
     previous iteration's ids straight from its device buffer."""
     eng = Engine(m, dtype, W, n_slots=n_slots, max_bs=max_bs, max_tokens=sum(len(r.prompt) for r in reqs) + max_bs,
-                 max_keys_total=sum(r.max_tokens for r in reqs), chunking=chunking)
+                 max_keys_total=sum(r.max_tokens for r in reqs), chunking=chunking, request_level=request_level)
     try:
         log = []
         eng.run_chained(reqs, on_iteration=lambda res: log.append(
@@ -510,3 +510,28 @@ def test_chunked_prefill_bf16_trace_chained_matches_synchronous():
     sync, slog = _gpu_generate(m, "bf16", W, reqs, 6, 2000, (48, 32))
     assert log == slog and got == sync
     assert max(sum(n for _, n, _ in w) for _, w in log) <= 48
+
+
+def test_static_batching_generation_same_tokens():
+    """Request-level (static) batching on the same kernels: the lecture's six-request grid (18 iterations)
+    and a Poisson trace; the schedule equals the oracle's static replay and the ids equal those of
+    iteration-level scheduling (toy fp32: and the oracle's; bf16: bitwise), chained or not."""
+    from synth import p4_grid_requests, poisson_trace
+    from oracle import scheduler as OS
+    m = TOY
+    Wh = make_weights(m, 0, "fp32")
+    W = DeviceWeights(m, "fp32", host=Wh)
+    reqs = p4_grid_requests(seed=0, vocab=m.V)
+    got, log = _gpu_generate(m, "fp32", W, reqs, 3, 10**4, request_level=True)
+    assert len(log) == 18 and [w for _, w in log] == [w for _, w, _ in OS.replay(reqs, 3, 10**4, static=True)]
+    cont, _ = _gpu_generate(m, "fp32", W, reqs, 3, 10**4)
+    want, _ = OG.generate_continuous(m, Wh, reqs, max_bs=3, n_slots=10**4)
+    assert got == cont == want
+    mb = TINY_LLAMA
+    Wb = DeviceWeights(mb, "bf16", host=make_weights(mb, 6, "bf16"))
+    reqs = poisson_trace(seed=9, n=30, rate=0.6, vocab=mb.V, plo=1, phi=40, olo=1, ohi=20, reserve_out=20,
+                         with_prompts=True)
+    st, slog = _gpu_generate_chained(mb, "bf16", Wb, reqs, 6, 2000, request_level=True)
+    co, _ = _gpu_generate(mb, "bf16", Wb, reqs, 6, 2000)
+    assert st == co
+    assert [w for _, w in slog] == [w for _, w, _ in OS.replay(reqs, 6, 2000, static=True)]

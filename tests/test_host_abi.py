@@ -95,10 +95,12 @@ def test_kv_placement_disjoint_aligned_and_compacts(seed):
 
 
 # ---------------------------------------------------------------- scheduler vs oracle
-def native_replay(reqs, max_bs, n_slots, budget=None, chunk=None, usage=None):
+def native_replay(reqs, max_bs, n_slots, budget=None, chunk=None, usage=None, static=False):
     """The oracle's logical-clock loop, with the scheduling decisions made by libsb."""
     kv = sb.sb_kv_create(n_slots, sb.sb_kv_arena_slots(n_slots, max_bs), 1, 1, 8, sb.SB_F32)
     s = sb.sb_sched_create(max_bs, kv)
+    if static:
+        sb.sb_sched_set_request_level(s, True)
     if budget is not None:
         sb.sb_sched_set_chunking(s, budget, chunk)
     pending = sorted(reqs, key=lambda r: (r.arrival, r.rid))
@@ -195,6 +197,25 @@ def test_reservation_policy_errors():
         with pytest.raises(sb.SBError) as e:
             sb.sb_reservation_tokens(*args)
         assert e.value.status == sb.SB_ERR_INVALID
+
+
+def test_native_request_level_matches_oracle():
+    """Static batching in libsb: the lecture's static grid (18 iterations) and random traces with
+    reservations that bind, decision for decision against the oracle."""
+    reqs = p4_grid_requests(seed=0)
+    log = native_replay(reqs, 3, 10**9, static=True)
+    assert log == OS.replay(reqs, 3, 10**9, static=True) and len(log) == 18
+    for seed, (max_bs, n_slots) in enumerate(((4, 200), (8, 300), (16, 10**6))):
+        reqs = poisson_trace(seed=60 + seed, n=120, rate=1.0, plo=1, phi=40, olo=1, ohi=30, reserve_out=30)
+        assert native_replay(reqs, max_bs, n_slots, static=True) == OS.replay(reqs, max_bs, n_slots, static=True)
+    kv = sb.sb_kv_create(10, sb.sb_kv_arena_slots(10, 2), 1, 1, 8, sb.SB_F32)
+    s = sb.sb_sched_create(2, kv)
+    sb.sb_sched_set_chunking(s, 8, 4)
+    with pytest.raises(sb.SBError) as e:
+        sb.sb_sched_set_request_level(s, True)              # chunks and whole-batch scheduling exclude
+    assert e.value.status == sb.SB_ERR_INVALID
+    sb.sb_sched_destroy(s)
+    sb.sb_kv_destroy(kv)
 
 
 def test_chunking_argument_errors():

@@ -275,3 +275,41 @@ def test_kv_usage_invariants(policy):
             for rid, n, c in work:
                 last[rid] = c + n
         assert all(last[r.rid] == r.max_tokens for r in reqs)
+
+
+# ---------------------------------------------------------------- request-level (static) batching
+def test_static_batching_timeline_exact():
+    """The lecture's static grid: same six requests, max_bs 3, whole batches: 18 iterations, every row."""
+    g = load("p4_static_timeline.txt")
+    reqs = p4_grid_requests(seed=0)
+    log = S.replay(reqs, max_bs=3, n_slots=10**9, static=True)
+    assert len(log) == g["iterations"][0] == load("p4_timeline.txt")["static_iterations"][0]
+    rows = S.timeline_static(log, reqs)
+    for r in reqs:
+        assert rows[r.rid] == g[f"r{r.rid}"], (r.rid, rows[r.rid])
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_static_batching_invariants(seed):
+    """Batches are disjoint, start only when the previous one is done, take waiting requests in arrival
+    order, never admit a request mid-batch; every request still gets out_len tokens; max_bs = 1 is the
+    same as iteration-level scheduling."""
+    reqs = poisson_trace(seed=40 + seed, n=120, rate=[0.3, 1.0, 3.0, 0.5][seed], plo=1, phi=30, olo=1, ohi=20,
+                         reserve_out=20)
+    log = S.replay(reqs, 8, 400, static=True)
+    seen = set()
+    current = set()
+    for t, work, _ in log:
+        ids = {rid for rid, _, _ in work}
+        if all(c == 0 for _, _, c in work):            # a new batch: the previous one has finished
+            assert not (ids & seen)
+            current = set(ids)
+            seen |= ids
+        else:
+            assert ids <= current and all(c > 0 for _, _, c in work)
+    n_tok = {}
+    for _, work, _ in log:
+        for rid, _, _ in work:
+            n_tok[rid] = n_tok.get(rid, 0) + 1
+    assert all(n_tok[r.rid] == r.out_len for r in reqs)
+    assert S.replay(reqs, 1, 400, static=True) == S.replay(reqs, 1, 400)
