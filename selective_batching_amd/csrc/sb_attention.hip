@@ -25,12 +25,14 @@
 //     K/V go straight from HBM into MFMA operand registers (16-byte loads,
 //     the next chunk's loads in flight while the current one computes, also
 //     across unit boundaries).  At the end of each unit the 4 wave states
-//     merge through LDS; a request with more than one unit leaves one partial
-//     state per unit, merged by attn_combine in unit order, so the result
-//     does not depend on the rest of the batch.
+//     merge through LDS.  A run that covers all of its request's units folds
+//     the unit states in unit order itself; otherwise each unit leaves a
+//     partial state, merged by attn_combine in unit order with the same
+//     two-state merge, so the result does not depend on the rest of the batch.
 //   MODE_ROWS (prefill tiles of 64 rows): each wave owns 16 rows; the
-//     workgroup stages 32-key K/V tiles through LDS (double-buffered) so the
-//     4 waves share every K/V byte.
+//     workgroup stages 64-key K/V tiles through LDS (two buffers) so the 4
+//     waves share every K/V byte, with the global loads of the next two tiles
+//     in flight in registers while a tile computes.
 #include <cfloat>
 
 #include "sb_device.h"
@@ -59,6 +61,36 @@ struct AttnArgs {
 };
 
 __device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Probabilities of one chunk (8 per lane, finite, in [0, 1]) as the P^T operand of
+// two MFMAs: hi = bf16(p) and lo = bf16(p - hi) (p - hi is exact in fp32), so P.V
+// keeps about 16 significant bits of p.  Conversions round to nearest even
+// (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    const f32x2 v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+__device__ __forceinline__ void split_p(const float (&p)[8], bf16x8& hi, bf16x8& lo) {
+    u32x4 h, l;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        h[i] = pack_bf16x2(p[2 * i], p[2 * i + 1]);
+        l[i] = pack_bf16x2(p[2 * i] - __uint_as_float(h[i] << 16), p[2 * i + 1] - __uint_as_float(h[i] & 0xffff0000u));
+    }
+    hi = __builtin_bit_cast(bf16x8, h);
+    lo = __builtin_bit_cast(bf16x8, l);
+}
+
+// o *= alpha, skipped when no row of the wave changed its max (alpha == 1 exactly)
+template <int N>
+__device__ __forceinline__ void rescale(f32x4 (&o)[N], float alpha) {
+    if (__ballot(alpha != 1.f) == 0) return;
+#pragma unroll
+    for (int i = 0; i < N; ++i) o[i] *= alpha;
+}
 
 // One wave's online-softmax state for its 16 rows (row = lane % 16).
 template <int D>
@@ -129,36 +161,21 @@ __device__ __forceinline__ void chunk_bf16(const AttnArgs& a, WaveState<D>& st, 
             sc[4 * b + r] = (k < key_end && k < row_limit) ? acc[r] * a.scale_log2 : kNegInf;
         }
     }
+    // V^T operand: V[keys cb+8g .. +8][dim 16db + lr] = 16 contiguous bytes of the staged tile
+    // (keys at or past key_end were zeroed when the tile was staged)
+    u32x4 vr[D / 16];
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) vr[db] = *(const u32x4*)(ldsV + g * (D * 8 + 16) + (db * 16 + lr) * 8);
     float alpha;
     softmax_chunk(sc, st.m, st.l, alpha);
-#pragma unroll
-    for (int i = 0; i < D / 16; ++i) st.o[i] *= alpha;
-    // P^T operand: keys 8g..8g+7 of the chunk for row lr, as hi + lo bf16 parts
-    // (p - bf16(p) is exact in fp32), so P.V keeps ~16 significant bits of p
-    union { bf16x8 v; uint16_t h[8]; } pp, pl;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        pp.h[i] = f2bf(sc[i]);
-        pl.h[i] = f2bf(sc[i] - bf2f(pp.h[i]));
-    }
-    // V^T operand: V[keys cb+8g .. +8][dim 16db + lr] = 16 contiguous bytes of the blocked layout
-    const int k8 = cb + 8 * g;
-    const bool any = k8 < key_end;
+    rescale(st.o, alpha);
+    bf16x8 ph, pl;
+    split_p(sc, ph, pl);
 #pragma unroll
     for (int db = 0; db < D / 16; ++db) {
-        u32x4 vraw = *(const u32x4*)(ldsV + g * (D * 8 + 16) + (db * 16 + lr) * 8);
-        if (k8 + 8 > key_end) {
-            // zero the keys past the range (their memory may hold anything)
-            union { u32x4 v; uint16_t h[8]; } vv;
-            vv.v = vraw;
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                if (!any || k8 + i >= key_end) vv.h[i] = 0;
-            vraw = vv.v;
-        }
-        const bf16x8 vv8 = __builtin_bit_cast(bf16x8, vraw);
-        st.o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv8, pp.v, st.o[db], 0, 0, 0);
-        st.o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv8, pl.v, st.o[db], 0, 0, 0);
+        const bf16x8 vv8 = __builtin_bit_cast(bf16x8, vr[db]);
+        st.o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv8, ph, st.o[db], 0, 0, 0);
+        st.o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv8, pl, st.o[db], 0, 0, 0);
     }
 }
 
@@ -205,14 +222,9 @@ __device__ __forceinline__ void compute_chunk_bf16(const AttnArgs& a, WaveState<
     }
     float alpha;
     softmax_chunk(sc, st.m, st.l, alpha);
-#pragma unroll
-    for (int i = 0; i < D / 16; ++i) st.o[i] *= alpha;
-    union { bf16x8 v; uint16_t h[8]; } pp, pl;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        pp.h[i] = f2bf(sc[i]);
-        pl.h[i] = f2bf(sc[i] - bf2f(pp.h[i]));
-    }
+    rescale(st.o, alpha);
+    bf16x8 ph, pl;
+    split_p(sc, ph, pl);
     const int k8 = cb + 8 * g;
     const bool tail = k8 + 8 > key_end, any = k8 < key_end;
 #pragma unroll
@@ -227,8 +239,8 @@ __device__ __forceinline__ void compute_chunk_bf16(const AttnArgs& a, WaveState<
             vraw = vv.v;
         }
         const bf16x8 vv8 = __builtin_bit_cast(bf16x8, vraw);
-        st.o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv8, pp.v, st.o[db], 0, 0, 0);
-        st.o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv8, pl.v, st.o[db], 0, 0, 0);
+        st.o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv8, ph, st.o[db], 0, 0, 0);
+        st.o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv8, pl, st.o[db], 0, 0, 0);
     }
 }
 
@@ -343,7 +355,7 @@ __device__ __forceinline__ void merge_unit(WaveState<D>& st, char* smem, RowStat
 template <int DT, int D>
 __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     using T = typename Store<DT>::T;
-    constexpr int KT = 32;                                   // keys per LDS stage (MODE_ROWS)
+    constexpr int KT = 64;                                   // keys per LDS stage (MODE_ROWS)
     // MODE_ROWS stages K/V tiles; MODE_RUNS merges wave states: one workgroup
     // uses only one of the two, so they share the LDS allocation.
     constexpr int LDS_K = (DT == SB_BF16) ? 2 * KT * (D + 8) : 0;
@@ -472,49 +484,77 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
         }
         const int wave_max_limit = min(ke, ctx + min(wrow0 + 15, row0 + nrows - 1) / a.G + 1);
         const int ntiles = (ke - kb + KT - 1) / KT;
-        constexpr int KCH = KT * D / 8;                    // 16-byte chunks per K tile
+        constexpr int KCH = KT * D / 8;                    // 16-byte chunks per K tile (and per V tile)
         constexpr int PER = (KCH + 255) / 256;
-        u32x4 rk[PER], rv[PER];
-        auto gload = [&](int t) {
-            const int k0 = kb + t * KT;
+        constexpr int KSTR = KT * (D + 8), VSTR = (KT / 8) * (D * 8 + 16);   // one LDS buffer
+        struct Stage { u32x4 k[PER], v[PER]; };
+        // global loads of tile t (clamped to the last tile: the loads are issued unconditionally
+        // so the compiler keeps them in flight across the compute of the tiles before)
+        auto gload = [&](Stage& r, int t) {
+            const int k0 = kb + min(t, ntiles - 1) * KT;
 #pragma unroll
             for (int q = 0; q < PER; ++q) {
                 const int c = tid + 256 * q;
                 if (c < KCH) {
                     const int kk = c / (D / 8), dc = (c % (D / 8)) * 8;
                     const long long slot = kslot0 + min(k0 + kk, ke - 1);
-                    rk[q] = *(const u32x4*)((const uint16_t*)Kp + slot * D + dc);
-                    // V: chunk c covers blocks (c / D) of 8 keys, dim c % D
+                    r.k[q] = *(const u32x4*)((const uint16_t*)Kp + slot * D + dc);
+                    // V: chunk c covers block c / D of 8 keys, dim c % D
                     const int vb = c / D, vd = c % D;
                     const long long vslot = kslot0 + min(k0 + vb * 8, ((ke - 1) & ~7));
-                    rv[q] = *(const u32x4*)((const uint16_t*)Vp + ((vslot >> 3) * D + vd) * 8);
+                    r.v[q] = *(const u32x4*)((const uint16_t*)Vp + ((vslot >> 3) * D + vd) * 8);
                 }
             }
         };
-        auto lstore = [&](int buf) {
+        // stage tile t; V of keys at or past ke is zeroed (a P of 0 times stale memory could be NaN)
+        auto lstore = [&](const Stage& r, int buf, int t) {
+            const int k0 = kb + t * KT;
 #pragma unroll
             for (int q = 0; q < PER; ++q) {
                 const int c = tid + 256 * q;
                 if (c < KCH) {
                     const int kk = c / (D / 8), dc = (c % (D / 8)) * 8;
-                    *(u32x4*)(ldsK + buf * KT * (D + 8) + kk * (D + 8) + dc) = rk[q];
+                    *(u32x4*)(ldsK + buf * KSTR + kk * (D + 8) + dc) = r.k[q];
                     const int vb = c / D, vd = c % D;
-                    *(u32x4*)(ldsV + buf * (KT / 8) * (D * 8 + 16) + vb * (D * 8 + 16) + vd * 8) = rv[q];
+                    u32x4 vv = r.v[q];
+                    const int kv0 = k0 + vb * 8;
+                    if (kv0 + 8 > ke) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const uint32_t keep = (kv0 + 2 * e < ke ? 0xffffu : 0u) | (kv0 + 2 * e + 1 < ke ? 0xffff0000u : 0u);
+                            vv[e] &= keep;
+                        }
+                    }
+                    *(u32x4*)(ldsV + buf * VSTR + vb * (D * 8 + 16) + vd * 8) = vv;
                 }
             }
         };
-        gload(0);
-        lstore(0);
+        auto compute = [&](int t, int buf) {
+#pragma unroll
+            for (int h = 0; h < KT / 32; ++h) {
+                const int k0 = kb + t * KT + 32 * h;
+                if (k0 < wave_max_limit)
+                    chunk_bf16<D>(a, st, qf, k0, ke, row_limit, lane, ldsK + buf * KSTR + 32 * h * (D + 8),
+                                  ldsV + buf * VSTR + 4 * h * (D * 8 + 16));
+            }
+        };
+        // registers r0 / r1 hold the even / odd tiles in flight; LDS buffer t & 1 holds tile t
+        Stage r0, r1;
+        gload(r0, 0);
+        gload(r1, 1);
+        lstore(r0, 0, 0);
         __syncthreads();
-        for (int t = 0; t < ntiles; ++t) {
-            const int buf = t & 1;
-            if (t + 1 < ntiles) gload(t + 1);
-            const int k0 = kb + t * KT;
-            if (k0 < wave_max_limit)
-                chunk_bf16<D>(a, st, qf, k0, ke, row_limit, lane, ldsK + buf * KT * (D + 8),
-                              ldsV + buf * (KT / 8) * (D * 8 + 16));
-            if (t + 1 < ntiles) lstore(buf ^ 1);
+        gload(r0, 2);
+        for (int t = 0; t < ntiles; t += 2) {
+            compute(t, 0);
+            if (t + 1 < ntiles) lstore(r1, 1, t + 1);      // buffer 1 was last read before the previous barrier
             __syncthreads();
+            if (t + 1 >= ntiles) break;
+            gload(r1, t + 3);
+            compute(t + 1, 1);
+            if (t + 2 < ntiles) lstore(r0, 0, t + 2);
+            __syncthreads();
+            gload(r0, t + 4);
         }
     } else {
         float qf[D / 4];

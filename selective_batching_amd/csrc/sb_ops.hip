@@ -138,17 +138,35 @@ __device__ __forceinline__ void store8(typename Store<DT>::T* p, const float (&v
 // statistics, two passes over registers (mean, then centred second moment).
 // WPR = 1: one wave per row (four rows per workgroup), sums by lane shuffles
 // only; WPR = 4: one row per workgroup (wide rows), sums through LDS.  16-byte
-// loads along the row; PER float4 chunks per lane: hidden <= 256 PER / WPR.
+// loads along the row; PER float4 chunks per lane: hidden <= 256 PER WPR.
+// Fewer rows than about four per CU take a workgroup per row (more CUs
+// streaming, a quarter of the dependent loads per lane).
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
     return v;
 }
 
+// Raw 4-element piece of a dtype row (8 bytes of bf16 or 16 of fp32), widened later.
+template <int DT>
+struct Raw4 { using T = u32x2; };
+template <>
+struct Raw4<SB_F32> { using T = float4; };
+template <int DT>
+__device__ __forceinline__ void widen4(const typename Raw4<DT>::T& w, float (&v)[4]) {
+    if constexpr (DT == SB_BF16) {
+        v[0] = __uint_as_float(w.x << 16); v[1] = __uint_as_float(w.x & 0xffff0000u);
+        v[2] = __uint_as_float(w.y << 16); v[3] = __uint_as_float(w.y & 0xffff0000u);
+    } else {
+        v[0] = w.x; v[1] = w.y; v[2] = w.z; v[3] = w.w;
+    }
+}
+
 template <int DT, int PER, int WPR>
 __global__ __launch_bounds__(256) void norm_kernel(const float* x, const int* row_map, const void* gam, const void* bet,
                                                    void* out, int rows, int H, int kind, float eps) {
     using T = typename Store<DT>::T;
+    using R = typename Raw4<DT>::T;
     __shared__ float red[4];
     constexpr int LANES = 64 * WPR;                        // threads per row
     const int lane = threadIdx.x % LANES;
@@ -157,30 +175,36 @@ __global__ __launch_bounds__(256) void norm_kernel(const float* x, const int* ro
     auto row_sum = [&](float v) { return WPR == 1 ? wave_sum(v) : block_sum(v, red); };
     const long long src = row_map ? row_map[r] : r;
     const float4* xr = (const float4*)(x + src * H);
+    const T* g = (const T*)gam;
+    const T* b = (const T*)bet;
     const int n4 = H / 4;
+    // the row, the gain and the shift are all requested before the first reduction
     float4 v[PER];
-    float s = 0.f;
+    R gr[PER], br[PER];
 #pragma unroll
     for (int q = 0; q < PER; ++q) {
         const int i = lane + LANES * q;
         if (i < n4) {
             v[q] = xr[i];
-            s += (v[q].x + v[q].y) + (v[q].z + v[q].w);
+            gr[q] = *(const R*)(g + 4 * i);
+            if (b) br[q] = *(const R*)(b + 4 * i);
         }
     }
+    float s = 0.f;
+#pragma unroll
+    for (int q = 0; q < PER; ++q)
+        if (lane + LANES * q < n4) s += (v[q].x + v[q].y) + (v[q].z + v[q].w);
     const float mean = kind == 0 ? row_sum(s) / H : 0.f;
     float s2 = 0.f;
 #pragma unroll
     for (int q = 0; q < PER; ++q) {
         const int i = lane + LANES * q;
         if (i < n4) {
-            const float a = v[q].x - mean, b = v[q].y - mean, c = v[q].z - mean, d = v[q].w - mean;
-            s2 += (a * a + b * b) + (c * c + d * d);
+            const float a = v[q].x - mean, bb = v[q].y - mean, c = v[q].z - mean, d = v[q].w - mean;
+            s2 += (a * a + bb * bb) + (c * c + d * d);
         }
     }
     const float rstd = 1.0f / sqrtf(row_sum(s2) / H + eps);
-    const T* g = (const T*)gam;
-    const T* b = (const T*)bet;
     T* o = (T*)out + (long long)r * H;
 #pragma unroll
     for (int q = 0; q < PER; ++q) {
@@ -188,8 +212,8 @@ __global__ __launch_bounds__(256) void norm_kernel(const float* x, const int* ro
         if (i < n4) {
             const float xs[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
             float gv[4], bv[4] = {0.f, 0.f, 0.f, 0.f}, y[4];
-            load4<DT>(g + 4 * i, gv);
-            if (b) load4<DT>(b + 4 * i, bv);
+            widen4<DT>(gr[q], gv);
+            if (b) widen4<DT>(br[q], bv);
 #pragma unroll
             for (int c = 0; c < 4; ++c) y[c] = (xs[c] - mean) * rstd * gv[c] + bv[c];
             store4<DT>(o + 4 * i, y);
@@ -346,6 +370,9 @@ __global__ __launch_bounds__(kArgmaxThreads) void argmax_kernel(const float* log
 
 }  // namespace
 
+// below this many rows a workgroup takes one row (see norm_kernel)
+constexpr int kNormRowsPerBlockMin = 1024;
+
 int launch_norm(int dtype, int kind, int rows, int H, const float* x, const int* row_map, const void* g,
                 const void* b, float eps, void* out, hipStream_t s) {
     if (rows <= 0) return SB_OK;
@@ -358,10 +385,12 @@ int launch_norm(int dtype, int kind, int rows, int H, const float* x, const int*
     };
     if (dtype == SB_BF16) {
         if (H <= 1024) go(norm_kernel<SB_BF16, 4, 1>, 4);
+        else if (H <= 4096 && rows < kNormRowsPerBlockMin) go(norm_kernel<SB_BF16, 4, 4>, 1);
         else if (H <= 4096) go(norm_kernel<SB_BF16, 16, 1>, 4);
         else go(norm_kernel<SB_BF16, 12, 4>, 1);
     } else {
         if (H <= 1024) go(norm_kernel<SB_F32, 4, 1>, 4);
+        else if (H <= 4096 && rows < kNormRowsPerBlockMin) go(norm_kernel<SB_F32, 4, 4>, 1);
         else if (H <= 4096) go(norm_kernel<SB_F32, 16, 1>, 4);
         else go(norm_kernel<SB_F32, 12, 4>, 1);
     }

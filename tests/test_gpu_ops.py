@@ -73,14 +73,15 @@ def test_gemm_fp32_logits_out_and_ragged_rows():
 # ---------------------------------------------------------------- norms
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 @pytest.mark.parametrize("kind", [0, 1])
-@pytest.mark.parametrize("H", [64, 256, 4096, 12288])
-def test_norm_matches_oracle(dtype, kind, H):
-    print_case("norm", dtype, kind, H)
-    rows = 5
+@pytest.mark.parametrize("H,rows", [(64, 5), (256, 5), (2048, 5), (4096, 5), (12288, 5), (2048, 1031), (4096, 1031)])
+def test_norm_matches_oracle(dtype, kind, H, rows):
+    """Both launch shapes: a workgroup per row (few rows, wide rows) and a wave per row."""
+    print_case("norm", dtype, kind, H, rows)
     x = normal(H, "x", (rows + 2, H), std=2.0, mean=0.3)
     g = normal(H, "g", (H,), std=0.1, mean=1.0, dtype=dtype)
     b = normal(H, "b", (H,), std=0.1, dtype=dtype) if kind == 0 else None
-    row_map = np.array([6, 0, 3, 3, 1], np.int32)
+    row_map = np.array([6, 0, 3, 3, 1], np.int32) if rows == 5 else \
+        np.random.default_rng(H).integers(0, rows + 2, rows).astype(np.int32)
     out = torch.zeros((rows, H), dtype={"fp32": torch.float32, "bf16": torch.bfloat16}[dtype], device="cuda")
     dx = torch.from_numpy(x).cuda()
     dmap = torch.from_numpy(row_map).cuda()
