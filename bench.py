@@ -111,9 +111,10 @@ def cpu_baseline(m, batch, seed):
 def decode_loop(seed, steps=64, reps=3):
     """Generation loop on the mini model (4 layers, hidden 256, 8 heads, FFN 1024, vocab 4096, bf16):
     64 requests in decode with cached context U[16, 256] (random K/V history), each generating ``steps``
-    more tokens.  Timed twice: the synchronous loop (each iteration waits for its ids before the next
-    Select) and the chained one (iteration t+1 selected and launched before t's ids reach the host).
-    Best of ``reps`` runs of each."""
+    more tokens.  Timed three ways: the synchronous loop (each iteration waits for its ids before the
+    next Select), the chained one (iteration t+1 selected and launched before t's ids reach the host),
+    and the chained one with each iteration's device side replayed from a HIP graph (one launch per
+    iteration instead of one per kernel).  Best of ``reps`` runs of each."""
     import torch
     from selective_batching_amd.runtime import DeviceWeights, Engine
     from synth import MINI, mini_decode_batch, uniform_int
@@ -145,8 +146,10 @@ def decode_loop(seed, steps=64, reps=3):
         return eng.run_chained()
 
     out = {}
-    for name, fn in (("synchronous", sync), ("chained", chained)):
-        fn(4)                                         # warm-up
+    for name, fn, graphs in (("synchronous", sync, False), ("chained", chained, False),
+                             ("chained_graphs", chained, True)):
+        eng.graphs = graphs
+        fn(4)                                         # warm-up (with graphs: captures the steady shape)
         best = None
         for _ in range(reps):
             torch.cuda.synchronize()
@@ -160,7 +163,8 @@ def decode_loop(seed, steps=64, reps=3):
     eng.close()
     return {"workload": (f"mini GPT (4 layers, hidden 256, 8 heads, FFN 1024, vocab 4096) bf16, random init; {B} "
                          f"requests in decode, cached context U[16,256], {steps} generated tokens each"),
-            **out, "chained_speedup": round(out["synchronous"]["ms_per_step"] / out["chained"]["ms_per_step"], 3)}
+            **out, "chained_speedup": round(out["synchronous"]["ms_per_step"] / out["chained"]["ms_per_step"], 3),
+            "chained_graphs_speedup": round(out["synchronous"]["ms_per_step"] / out["chained_graphs"]["ms_per_step"], 3)}
 
 
 def reservation_policies(seed, n_slots=20000):

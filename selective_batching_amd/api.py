@@ -241,10 +241,15 @@ def sb_lm_argmax(dims, mw, rg, x, logits, out_ids, ws, ws_bytes, stream=None):
 
 def sb_timing_enable(on, classes=None):
     """on=False: off; on=True: every class, or only the kernel-class indices in ``classes``."""
+    global timing_mask
     mask = 0
     if on:
         mask = -1 if classes is None else sum(1 << k for k in classes)
     call("sb_timing_enable", mask)
+    timing_mask = mask
+
+
+timing_mask = 0     # the class mask last set through sb_timing_enable
 
 
 def sb_timing_read(k):

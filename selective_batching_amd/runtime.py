@@ -101,10 +101,16 @@ class Engine:
     """K/V manager + scheduler + device buffers for one model on one GPU."""
 
     def __init__(self, m, dtype: str, weights: DeviceWeights, n_slots: int, max_bs: int, max_tokens: int,
-                 max_keys_total: int = None, device="cuda", zero_arena=True, chunking=None, request_level=False):
+                 max_keys_total: int = None, device="cuda", zero_arena=True, chunking=None, request_level=False,
+                 graphs=False):
         """``max_tokens``: most tokens one iteration feeds (with ``chunking`` = (token budget, chunk) the
-        budget bounds it).  ``request_level``: static batching (the baseline) instead of Algorithm 1."""
+        budget bounds it).  ``request_level``: static batching (the baseline) instead of Algorithm 1.
+        ``graphs``: replay the device side of an iteration from a HIP graph when an iteration of the same
+        shape has run before (see ``forward``)."""
         self.m, self.dtype, self.w = m, dtype, weights
+        self.graphs = graphs
+        self._graph_seen = {}          # iteration shape -> times seen (captured on the second)
+        self._graph_cache = {}         # iteration shape -> captured torch.cuda.CUDAGraph
         self.dims = make_dims(m, dtype)
         self.max_bs, self.max_tokens = max_bs, max_tokens
         self.device = device
@@ -179,10 +185,12 @@ class Engine:
         ids_dev = self.ids_dev_bufs[buf]
         if x_in is None and layer_outputs is None and head:
             # the common case: the whole device side of the iteration in one library call
-            A.sb_forward(self.dims, self.w.model_struct, self.w.layer_array, self.n_layers, rg, self.kv,
-                         prev[0].data_ptr() if prev is not None else None, prev[1] if prev is not None else 0,
-                         xv.data_ptr(), self.logits.data_ptr(), ids_dev.data_ptr(), self.ws.data_ptr(),
-                         self.ws_bytes, s)
+            ptrs = (prev[0].data_ptr() if prev is not None else None, prev[1] if prev is not None else 0,
+                    xv.data_ptr(), self.logits.data_ptr(), ids_dev.data_ptr())
+            if self.graphs and A.timing_mask == 0:
+                self._forward_graph(rg, ptrs)
+            else:
+                self._sb_forward(rg, ptrs, s)
             return ids_dev[:rg.n_req]
         if x_in is not None:
             xv.copy_(x_in.reshape(-1))
@@ -200,6 +208,39 @@ class Engine:
         A.sb_lm_argmax(self.dims, self.w.model_struct, rg, xv.data_ptr(), self.logits.data_ptr(),
                        ids_dev.data_ptr(), self.ws.data_ptr(), self.ws_bytes, s)
         return ids_dev[:rg.n_req]
+
+    def _sb_forward(self, rg, ptrs, stream):
+        prev_ids, prev_n, x, logits, ids = ptrs
+        A.sb_forward(self.dims, self.w.model_struct, self.w.layer_array, self.n_layers, rg, self.kv, prev_ids, prev_n,
+                     x, logits, ids, self.ws.data_ptr(), self.ws_bytes, stream)
+
+    # graphs kept per engine; beyond this many shapes the cache starts over
+    MAX_GRAPHS = 16
+
+    def _forward_graph(self, rg, ptrs):
+        """The launches of sb_forward depend only on the host fields of ``rg`` (counts and the device
+        addresses of its arrays) and on the buffers in ``ptrs``; what the kernels read from those
+        buffers (metadata, ids, K/V) may change freely.  So an iteration whose shape key matches a
+        captured one replays that graph: one launch instead of one per kernel (a decode loop at a
+        steady batch is launch-bound).  A shape is captured the second time it is seen, so a stream
+        of ever-new shapes (arrivals) runs eagerly and pays no capture.  sb_forward issues kernel
+        launches only (no memsets, copies or host waits), which is what makes it capturable."""
+        key = (tuple(getattr(rg, f) for f, _ in rg._fields_), ptrs)
+        g = self._graph_cache.get(key)
+        if g is None:
+            seen = self._graph_seen.get(key, 0) + 1
+            self._graph_seen[key] = seen
+            if seen < 2:
+                self._sb_forward(rg, ptrs, stream_handle())
+                return
+            if len(self._graph_cache) >= self.MAX_GRAPHS:
+                self._graph_cache.clear()
+                self._graph_seen = {key: seen}
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                self._sb_forward(rg, ptrs, stream_handle())
+            self._graph_cache[key] = g
+        g.replay()
 
     def launch(self, sched=None, buf=0, keep=False, chain=None):
         """Select the next iteration from ``sched`` (default: this engine's scheduler), build its

@@ -241,9 +241,10 @@ def test_llama8b_shape_layer_stepwise():
         sb.sb_kv_destroy(kv)
 
 
-def _gpu_generate(m, dtype, W, reqs, max_bs, n_slots, chunking=None, request_level=False):
+def _gpu_generate(m, dtype, W, reqs, max_bs, n_slots, chunking=None, request_level=False, graphs=False):
     eng = Engine(m, dtype, W, n_slots=n_slots, max_bs=max_bs, max_tokens=sum(len(r.prompt) for r in reqs) + max_bs,
-                 max_keys_total=sum(r.max_tokens for r in reqs), chunking=chunking, request_level=request_level)
+                 max_keys_total=sum(r.max_tokens for r in reqs), chunking=chunking, request_level=request_level,
+                 graphs=graphs)
     try:
         import math
         pending = sorted(reqs, key=lambda r: (r.arrival, r.rid))
@@ -431,11 +432,12 @@ def test_pipelined_launches_match_sequential_steps():
         eng.close()
 
 
-def _gpu_generate_chained(m, dtype, W, reqs, max_bs, n_slots, chunking=None, request_level=False):
+def _gpu_generate_chained(m, dtype, W, reqs, max_bs, n_slots, chunking=None, request_level=False, graphs=False):
     """As _gpu_generate, but one iteration ahead of the host (Engine.run_chained): decodes embed the
     previous iteration's ids straight from its device buffer."""
     eng = Engine(m, dtype, W, n_slots=n_slots, max_bs=max_bs, max_tokens=sum(len(r.prompt) for r in reqs) + max_bs,
-                 max_keys_total=sum(r.max_tokens for r in reqs), chunking=chunking, request_level=request_level)
+                 max_keys_total=sum(r.max_tokens for r in reqs), chunking=chunking, request_level=request_level,
+                 graphs=graphs)
     try:
         log = []
         eng.run_chained(reqs, on_iteration=lambda res: log.append(
@@ -535,3 +537,60 @@ def test_static_batching_generation_same_tokens():
     co, _ = _gpu_generate(mb, "bf16", Wb, reqs, 6, 2000)
     assert st == co
     assert [w for _, w in slog] == [w for _, w, _ in OS.replay(reqs, 6, 2000, static=True)]
+
+
+@pytest.mark.parametrize("chained", [False, True])
+def test_figure5_generation_graph_replay_equals_oracle(chained):
+    """Toy fp32 model, Figure-5 requests, iterations replayed from HIP graphs once their shape repeats
+    (every decode-only iteration after the first): ids bit-exact against the oracle, schedule identical."""
+    m = TOY
+    Wh = make_weights(m, 0, "fp32")
+    W = DeviceWeights(m, "fp32", host=Wh)
+    reqs = figure5_requests(seed=0, vocab=m.V, out_len=8)
+    gen = _gpu_generate_chained if chained else _gpu_generate
+    got, log = gen(m, "fp32", W, reqs, 4, 64, graphs=True)
+    want, olog = OG.generate_continuous(m, Wh, reqs, max_bs=4, n_slots=64)
+    assert [w for _, w in log] == [w for _, w, _ in olog]
+    for r in reqs:
+        assert got[r.rid] == want[r.rid]
+
+
+@pytest.mark.parametrize("chained", [False, True])
+def test_decode_loop_graph_replay_matches_eager(chained):
+    """bf16 decode loop at a steady batch (16 requests with random K/V history, 12 steps): with graph
+    replay every iteration after the second runs from a captured graph, with the host's Select /
+    metadata copies / Complete (and, synchronous, a wait) between replays.  Every request's ids must
+    equal the eager loop's, bitwise, and the replays must actually have happened."""
+    m = MINI.with_layers(2)
+    W = DeviceWeights(m, "bf16", host=make_weights(m, 5, "bf16"))
+    ctxs = uniform_int(5, "graph.ctx", 16, 200, 16).tolist()
+    last = uniform_int(5, "graph.last", 0, m.V - 1, 16).tolist()
+    steps = 12
+    print_case("graph replay decode loop", chained)
+
+    def run(graphs):
+        n_slots = sum(c + steps + 1 for c in ctxs) + 8 * 16
+        eng = Engine(m, "bf16", W, n_slots=n_slots, max_bs=16, max_tokens=16, max_keys_total=n_slots,
+                     zero_arena=False, graphs=graphs)
+        try:
+            gen = torch.Generator(device="cuda")
+            gen.manual_seed(9)
+            for a in (eng.k_arena, eng.v_arena):
+                a.view(torch.bfloat16).normal_(0.0, 1.0, generator=gen)
+            for i, c in enumerate(ctxs):
+                eng.add_running(i, float(i), c, steps + 1, c + steps + 1, 1, last[i])
+            if chained:
+                n = eng.run_chained()
+            else:
+                n = 0
+                while eng.step() is not None:
+                    n += 1
+            assert n == steps
+            return [list(eng.output(i)) for i in range(16)], len(eng._graph_cache)
+        finally:
+            eng.close()
+
+    eager, n0 = run(False)
+    replayed, n1 = run(True)
+    assert n0 == 0 and n1 >= 1
+    assert replayed == eager
