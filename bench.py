@@ -51,7 +51,45 @@ def parse():
     ap.add_argument("--layers", type=int, default=32, help="decoder layers (the workload has 32)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one 1 GiB device-to-device copy before the steps (calibrates HBM counters)")
+    ap.add_argument("--op-gemm", default=None, metavar="M,N,K,EPI",
+                    help="instead of the iteration: time one bf16 GEMM of this shape (EPI: store, gelu, resid or "
+                         "swiglu; N counts output columns) over --steps launches, for kernel-level profiling")
     return ap.parse_args()
+
+
+def op_gemm(spec, steps, warmup, seed):
+    """One token-wise GEMM alone, launched ``steps`` times on synthetic bf16 operands (A ~ N(0, 0.25),
+    W ~ N(0, 0.02^2)); the launcher picks the tile as it does inside the iteration."""
+    import torch
+    from selective_batching_amd import api as A
+    from selective_batching_amd.runtime import stream_handle
+    import selective_batching_amd as sb
+    M, N, K, epi = spec.split(",")
+    M, N, K = int(M), int(N), int(K)
+    code = {"store": sb.SB_EPI_STORE, "gelu": sb.SB_EPI_GELU, "resid": sb.SB_EPI_RESID, "swiglu": sb.SB_EPI_SWIGLU}[epi]
+    rows = 2 * N if epi == "swiglu" else N
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    a = (torch.randn(M, K, device="cuda", generator=g) * 0.5).to(torch.bfloat16)
+    w = (torch.randn(rows, K, device="cuda", generator=g) * 0.02).to(torch.bfloat16)
+    c = torch.zeros(M, N, dtype=torch.float32 if epi == "resid" else torch.bfloat16, device="cuda")
+
+    def run():
+        A.sb_op_gemm(sb.SB_BF16, code, M, N, K, a.data_ptr(), K, w.data_ptr(), K, None, c.data_ptr(), N, 0,
+                     N if epi == "swiglu" else 0, stream_handle())
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / max(steps, 1)
+    print(json.dumps({"op": "gemm_bf16", "M": M, "N": N, "K": K, "epilogue": epi, "launches": steps,
+                      "avg_us": round(ms * 1e3, 2), "tflops": round(2.0 * M * rows * K / ms / 1e9, 1),
+                      "weight_gbs": round(rows * K * 2 / ms / 1e6, 1)}), flush=True)
 
 
 def algorithmic_work(m, batch, n_layers):
@@ -309,6 +347,10 @@ def main():
         print("bench.py runs on one GPU only: this build has no multi-GPU path (requests shard by data "
               "parallelism with no exchange; see the design notes).", file=sys.stderr)
         sys.exit(2)
+
+    if args.op_gemm:
+        op_gemm(args.op_gemm, args.steps, args.warmup, args.seed)
+        return
 
     import numpy as np
     import torch

@@ -5,11 +5,12 @@
 // ("连续批处理完全拆解", section 观察; "CS349D Lecture 2", section 4.2).  T is
 // arbitrary (ragged), so rows beyond T are masked; N and K come from the model.
 //
-// bf16: v_mfma_f32_16x16x32_bf16 tiles; 256 x 256 workgroup tiles of 8 waves
-// (wave tile 128 x 64, two waves per SIMD) for large GEMMs, 128 x 128 for
-// small ones; two LDS stages fed two K tiles ahead by 16-byte global loads,
-// padded LDS rows (no bank conflicts on the 16-byte operand reads), XCD-aware
-// grouped tile order.
+// bf16: v_mfma_f32_16x16x32_bf16 tiles.  Large GEMMs: 256 x 256 (or 256 x 192,
+// 192 x 256, 256 x 384) workgroup tiles of 8 waves, two waves per SIMD, two LDS
+// stages of 64-deep K filled straight from global memory (global_load_lds,
+// XOR-swizzled rows: no bank conflicts on the operand reads), XCD-aware grouped
+// tile order.  Small GEMMs (decode-heavy batches): 128 x 128 register-staged
+// tiles or 64-row tiles with deep K rings, by a cost model.
 // fp32: a plain LDS-tiled FMA kernel with a fixed, sequential K order.
 // Epilogues fuse bias, exact GeLU, SwiGLU (SiLU(gate) * up) or the residual
 // add into the fp32 stream x.
@@ -525,6 +526,7 @@ enum {
     CFG_DMA_256x256_8W_K64_S2_SPREAD, CFG_DMA_256x256_8W_S4_SPREAD,                           // copies spread over MFMAs
     CFG_DMA_256x192_8W_K64_S2_SPREAD, CFG_DMA_192x256_8W_K64_S2_SPREAD,                       // fewer-tile shapes
     CFG_DMA_64x32_4W_K64_S8, CFG_DMA_64x16_2W_K64_S6, CFG_DMA_64x64_4W_K64_S6,                // skinny: deep K pipelines
+    CFG_DMA_256x384_8W_K64_S2_SPREAD,                                                         // all of LDS
     CFG_COUNT
 };
 
@@ -595,15 +597,19 @@ int pick_small(const GemmArgs& a, int epi) {
     return best;
 }
 
-// Pick the tile.  Small GEMMs: pick_small.  Otherwise
-// DMA-fed tiles of 64-deep K: among 256x256, 256x192 and 192x256 the one with
-// the least estimated time, rounds x tile work x feed factor, where rounds =
-// ceil(tiles / CUs) (one such workgroup per CU) and the feed factor charges half
-// of the extra bytes per flop of the smaller tiles (1.083 for 192-wide ones):
-// e.g. 3741 x 6144 takes 256x192 (480 tiles, 2 rounds) over 256x256 (360 tiles,
-// 2 rounds).  Copies are spread over the MFMAs unless there is only one row of
-// tiles (measured faster in one burst).  Every configuration sums each output's
-// K in the same order with the same MFMA, so the choice never changes a result bit.
+// Pick the tile.  Small GEMMs: pick_small.  Otherwise DMA-fed tiles of 64-deep
+// K: among 256x256, 256x192, 192x256 and 256x384 the one with the least
+// estimated time, rounds x tile area x feed factor, where rounds = ceil(tiles /
+// CUs) (one such workgroup per CU: a partial last round costs a whole one) and
+// the feed factor is the measured time per unit of tile area relative to
+// 256x256 on MI355X (1.083 for the 192-wide tiles, which move more bytes per
+// flop; 0.956 for 256x384, which moves fewer).  E.g. 3741 x 6144 (QKV) takes
+// 256x384 (240 tiles, one round) over 256x192 (480 tiles, two rounds); the FFN1
+// gate/up GEMM (28672 W rows) stays on 256x256 (7 rounds of 1680 tiles against
+// 5 rounds of 1125 larger ones, the last 39% full).  Copies are spread over the
+// MFMAs unless there is only one row of tiles (measured faster in one burst).
+// Every configuration sums each output's K in the same order with the same
+// MFMA, so the choice never changes a result bit.
 int pick_cfg(const GemmArgs& a, int epi) {
     const char* e = getenv("SB_GEMM_CFG");             // tuning / test override: a CFG_* index
     if (e && *e) {
@@ -614,20 +620,21 @@ int pick_cfg(const GemmArgs& a, int epi) {
     const long long big = (long long)((a.M + 255) / 256) * ((ncols + 255) / 256);
     if (big < 128) return pick_small(a, epi);
     if (a.M <= 256) return CFG_DMA_256x256_8W_K64_S2;
-    struct Cand { int cfg, bm, bn; };
-    const Cand cands[3] = {{CFG_DMA_256x256_8W_K64_S2_SPREAD, 256, 256},
-                           {CFG_DMA_256x192_8W_K64_S2_SPREAD, 256, 192},
-                           {CFG_DMA_192x256_8W_K64_S2_SPREAD, 192, 256}};
+    struct Cand { int cfg, bm, bn; double feed; };
+    const Cand cands[4] = {{CFG_DMA_256x256_8W_K64_S2_SPREAD, 256, 256, 1.0},
+                           {CFG_DMA_256x192_8W_K64_S2_SPREAD, 256, 192, 1.083},
+                           {CFG_DMA_192x256_8W_K64_S2_SPREAD, 192, 256, 1.083},
+                           {CFG_DMA_256x384_8W_K64_S2_SPREAD, 256, 384, 0.956}};
     const int cus = num_cus();
     int best = cands[0].cfg;
     double best_cost = 0.0;
-    for (int c = 0; c < 3; ++c) {
+    for (int c = 0; c < 4; ++c) {
         const Cand& k = cands[c];
         if (epi == EPI_SWIGLU && k.bn == 192) continue;           // gate/up need 16-wide halves per wave
+        if (epi == EPI_GELU && k.bn == 384) continue;             // erf's registers do not fit beside 192 accumulators
         const long long tiles = (long long)((a.M + k.bm - 1) / k.bm) * ((ncols + k.bn - 1) / k.bn);
         const long long rounds = (tiles + cus - 1) / cus;
-        const double feed = 1.0 + 0.5 * ((double)(k.bm + k.bn) / ((double)k.bm * k.bn) * 128.0 - 1.0);
-        const double cost = (double)rounds * k.bm * k.bn * feed;
+        const double cost = (double)rounds * k.bm * k.bn * k.feed;
         if (c == 0 || cost < best_cost) { best = k.cfg; best_cost = cost; }
     }
     return best;
@@ -653,6 +660,7 @@ int launch_bf16(const GemmArgs& a, hipStream_t s) {
         case CFG_DMA_64x32_4W_K64_S8: return launch_dma<64, 32, 2, 2, 64, 8, 2, 0, EPI>(a, s);
         case CFG_DMA_64x16_2W_K64_S6: return launch_dma<64, 16, 2, 1, 64, 6, 2, 0, EPI>(a, s);
         case CFG_DMA_64x64_4W_K64_S6: return launch_dma<64, 64, 2, 2, 64, 6, 2, 0, EPI>(a, s);
+        case CFG_DMA_256x384_8W_K64_S2_SPREAD: return launch_dma<256, 384, 2, 4, 64, 2, 2, 1, EPI>(a, s);
         default: return launch_bf16_cfg<128, 128, 2, 2, EPI>(a, s);
     }
 }
