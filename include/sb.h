@@ -301,7 +301,12 @@ int sb_lm_argmax(const sb_model_dims* dims, const sb_model_weights* w, const sb_
  * 2 + n_layers): sb_embed_chained (prev_ids may be NULL), sb_layer_step for
  * layers 0 .. n_layers-1 with layers[l] (host array of n_layers structs),
  * then sb_lm_argmax.  Arguments, ownership and errors as for those calls; the
- * first failing step's status is returned and nothing after it is enqueued. */
+ * first failing step's status is returned and nothing after it is enqueued.
+ * It only enqueues kernels on `stream` (no allocation, copy, memset or host
+ * wait), and which kernels it launches depends only on the host fields of
+ * `rg`, on `n_layers` and on the pointers passed: a caller may capture it in a
+ * HIP graph and replay that graph for later iterations with the same fields
+ * and buffers, whatever the buffers then hold. */
 int sb_forward(const sb_model_dims* dims, const sb_model_weights* w, const sb_layer_weights* layers, int32_t n_layers,
                const sb_ragged* rg, const sb_kv* kv, const int32_t* prev_ids, int32_t prev_n, float* x,
                float* logits, int32_t* out_ids, void* workspace, size_t ws_bytes, void* stream);
