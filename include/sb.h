@@ -306,7 +306,8 @@ int sb_lm_argmax(const sb_model_dims* dims, const sb_model_weights* w, const sb_
  * wait), and which kernels it launches depends only on the host fields of
  * `rg`, on `n_layers` and on the pointers passed: a caller may capture it in a
  * HIP graph and replay that graph for later iterations with the same fields
- * and buffers, whatever the buffers then hold. */
+ * and buffers, whatever the buffers then hold.  Kernel timing (sb_timing_enable)
+ * records events around launches: keep it off while capturing. */
 int sb_forward(const sb_model_dims* dims, const sb_model_weights* w, const sb_layer_weights* layers, int32_t n_layers,
                const sb_ragged* rg, const sb_kv* kv, const int32_t* prev_ids, int32_t prev_n, float* x,
                float* logits, int32_t* out_ids, void* workspace, size_t ws_bytes, void* stream);
