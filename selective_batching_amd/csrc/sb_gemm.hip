@@ -255,6 +255,133 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_bf16_kernel(GemmA
     tile_epilogue<MI, NI, EPI>(a, acc, m0 + wm * WM + lrow, n_lane);
 }
 
+// ================================================================== bf16 MFMA, register ring
+// Small problems (decode-heavy batches): few workgroups, each walking all of K,
+// so what bounds them is the bytes one workgroup keeps in flight.  Loads go to
+// registers first -- a ring of PF 64-deep K tiles per thread, each load issued
+// PF steps before its tile is used -- and each tile is copied to LDS (two
+// buffers, padded rows) one step before its MFMAs.  Same operand layout, MFMA
+// and K order as gemm_bf16_kernel, so results are bitwise those of every other
+// configuration.
+template <int BM, int BN, int WAVES_M, int WAVES_N, int PF, int EPI>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_bf16_ring_kernel(GemmArgs a) {
+    static_assert(PF % 2 == 0, "ring slot parity selects the LDS buffer");
+    constexpr int THREADS = 64 * WAVES_M * WAVES_N;
+    constexpr int BK = 64, LDSK = BK + 8;            // 144-byte rows: conflict-free 16-byte reads
+    constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
+    constexpr int MI = WM / 16, NI = WN / 16;
+    constexpr int CH = BK / 8;                       // 16-byte chunks per row
+    constexpr int A_CH = BM * CH / THREADS, B_CH = BN * CH / THREADS;
+    static_assert(A_CH * THREADS == BM * CH && B_CH * THREADS == BN * CH, "tile / thread mismatch");
+    __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LDSK];
+    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * LDSK];
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+    const int tiles_m = (a.M + BM - 1) / BM;
+    const int out_cols = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
+    const int tiles_n = (a.N + out_cols - 1) / out_cols;
+    const int pid = xcd_remap(blockIdx.x, tiles_m * tiles_n);
+    const int tm = pid % tiles_m, tn = pid / tiles_m;     // row tiles of one column block: same XCD
+    const int m0 = tm * BM;
+
+    const uint16_t* A = (const uint16_t*)a.A;
+    const uint16_t* W = (const uint16_t*)a.W;
+    // global row of every chunk this thread moves (clamped: rows past the end are loaded but never stored);
+    // consecutive threads take consecutive 16-byte chunks, so one load instruction reads whole lines
+    const uint16_t* pa[A_CH];
+    const uint16_t* pb[B_CH];
+#pragma unroll
+    for (int q = 0; q < A_CH; ++q) {
+        const int c = tid + THREADS * q, row = c / CH, kc = (c % CH) * 8;
+        pa[q] = A + (long long)min(m0 + row, a.M - 1) * a.lda + kc;
+    }
+#pragma unroll
+    for (int q = 0; q < B_CH; ++q) {
+        const int c = tid + THREADS * q, row = c / CH, kc = (c % CH) * 8;
+        int gr;
+        if (EPI == EPI_SWIGLU) {
+            const int w = row / WN, cc = row % WN;
+            const int f = tn * (BN / 2) + w * (WN / 2) + (cc % (WN / 2));
+            gr = min(f, a.N - 1) + (cc >= WN / 2 ? a.F : 0);
+        } else {
+            gr = min(tn * BN + row, a.N - 1);
+        }
+        pb[q] = W + (long long)gr * a.ldw + kc;
+    }
+
+    const int nk = a.K / BK;
+    u32x4 ra[PF][A_CH], rb[PF][B_CH];
+    auto load = [&](int s, int kt) {                 // ring slot s <- K tile kt (clamped to the last)
+        const int k0 = min(kt, nk - 1) * BK;
+#pragma unroll
+        for (int q = 0; q < A_CH; ++q) ra[s][q] = *(const u32x4*)(pa[q] + k0);
+#pragma unroll
+        for (int q = 0; q < B_CH; ++q) rb[s][q] = *(const u32x4*)(pb[q] + k0);
+    };
+    auto stash = [&](int s, int buf) {
+#pragma unroll
+        for (int q = 0; q < A_CH; ++q) {
+            const int c = tid + THREADS * q;
+            *(u32x4*)&As[buf][(c / CH) * LDSK + (c % CH) * 8] = ra[s][q];
+        }
+#pragma unroll
+        for (int q = 0; q < B_CH; ++q) {
+            const int c = tid + THREADS * q;
+            *(u32x4*)&Bs[buf][(c / CH) * LDSK + (c % CH) * 8] = rb[s][q];
+        }
+    };
+
+    f32x4 acc[MI][NI];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NI; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int lrow = lane & 15, lk = (lane >> 4) * 8;
+    auto compute = [&](int buf) {
+#pragma unroll
+        for (int ks = 0; ks < BK / 32; ++ks) {
+            bf16x8 bfr[NI];
+#pragma unroll
+            for (int j = 0; j < NI; ++j)
+                bfr[j] = __builtin_bit_cast(bf16x8, *(const u32x4*)&Bs[buf][(wn * WN + j * 16 + lrow) * LDSK + ks * 32 + lk]);
+#pragma unroll
+            for (int i = 0; i < MI; ++i) {
+                const bf16x8 af = __builtin_bit_cast(bf16x8, *(const u32x4*)&As[buf][(wm * WM + i * 16 + lrow) * LDSK + ks * 32 + lk]);
+#pragma unroll
+                for (int j = 0; j < NI; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[j], af, acc[i][j], 0, 0, 0);
+            }
+        }
+    };
+
+    // loads go out in ring order, in the prologue and in the loop, so that before each step
+    // only that step's loads have to be waited for
+#pragma unroll
+    for (int s = 0; s < PF; ++s) {
+        load(s, s);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // step kt: copy ring slot kt % PF to LDS buffer kt & 1 (read last by step kt - 2, which every
+    // wave finished before the barrier of step kt - 1), barrier, refill the slot with tile
+    // kt + PF, MFMAs of buffer kt & 1.  Only the MFMAs depend on kt < nk: the copies and loads of
+    // the steps past the end (at most PF - 1, of the clamped last tile) keep one fixed load order
+    // on every path, which is what lets the waits stay PF - 1 steps deep across the loop.
+    for (int kt0 = 0; kt0 < nk; kt0 += PF) {
+#pragma unroll
+        for (int s = 0; s < PF; ++s) {
+            stash(s, s & 1);
+            __syncthreads();
+            load(s, kt0 + s + PF);
+            if (kt0 + s < nk) compute(s & 1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+
+    const int n_lane = (EPI == EPI_SWIGLU ? tn * (BN / 2) + wn * (WN / 2) : tn * BN + wn * WN) + (lane >> 4) * 4;
+    tile_epilogue<MI, NI, EPI>(a, acc, m0 + wm * WM + lrow, n_lane);
+}
+
 typedef __attribute__((address_space(3))) void lds_void;
 
 // vmcnt <= n (other counters untouched): gfx9 encoding, vmcnt in bits 3:0 and 15:14
@@ -527,6 +654,7 @@ enum {
     CFG_DMA_256x192_8W_K64_S2_SPREAD, CFG_DMA_192x256_8W_K64_S2_SPREAD,                       // fewer-tile shapes
     CFG_DMA_64x32_4W_K64_S8, CFG_DMA_64x16_2W_K64_S6, CFG_DMA_64x64_4W_K64_S6,                // skinny: deep K pipelines
     CFG_DMA_256x384_8W_K64_S2_SPREAD,                                                         // all of LDS
+    CFG_RING_64x32_PF8, CFG_RING_64x64_PF6, CFG_RING_32x32_PF8, CFG_RING_32x64_PF8,          // register rings
     CFG_COUNT
 };
 
@@ -552,6 +680,19 @@ int launch_dma(const GemmArgs& a, hipStream_t s) {
     }
 }
 
+template <int BM, int BN, int WMW, int WNW, int PF, int EPI>
+int launch_ring(const GemmArgs& a, hipStream_t s) {
+    if constexpr (EPI == EPI_SWIGLU && (BN / WNW / 2) % 16 != 0) {
+        return launch_ring<BM, 2 * BN, WMW, WNW, PF, EPI>(a, s);      // gate/up need 16-wide halves per wave
+    } else {
+        const int out_cols = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
+        const long long tiles = (long long)((a.M + BM - 1) / BM) * ((a.N + out_cols - 1) / out_cols);
+        hipLaunchKernelGGL((gemm_bf16_ring_kernel<BM, BN, WMW, WNW, PF, EPI>), dim3((unsigned)tiles),
+                           dim3(64 * WMW * WNW), 0, s, a);
+        return check_launch("gemm_bf16_ring");
+    }
+}
+
 int num_cus() {
     static int n = 0;
     if (n == 0) {
@@ -566,32 +707,41 @@ int num_cus() {
 }
 
 // GEMMs too small for a full round of big tiles (decode-heavy iterations: M of a few
-// hundred rows) are latency-bound: each workgroup walks K serially (one MFMA chain per
-// output, so K is never split) and takes about c microseconds per 64-deep K step
-// whatever its tile.  Estimated time = max(rounds of tiles x K steps x c, weight bytes
-// at 5 TB/s), with c and the resident workgroups per CU measured on MI355X for each
-// candidate: 128 x 128 register-staged (0.77 us, 2 per CU), 64 x 32 with 8 DMA stages
-// (0.30 us, 1 per CU; not for SwiGLU, whose 16-wide halves need 32 columns per wave)
-// and 64 x 64 with 6 stages (0.36 us, 1 per CU).  E.g. the 8B-shaped FFN2 (N 4096,
-// K 14336) at M 64 takes 64 x 32: 128 tiles, one round, 224 steps: ~67 us instead
-// of 172 us with 128 x 128 tiles.
+// hundred rows or less).  Each workgroup walks all of K (one MFMA chain per output,
+// K is never split), so the busiest CU's operand bytes over the rate one CU takes
+// them in bound the time: estimated t = max(weight bytes at 6 TB/s, busiest x K
+// tiles x tile bytes / min(cu_rate, wg_rate x busiest)), busiest = ceil(tiles /
+// CUs) workgroups on the fullest CU.  wg_rate (one workgroup alone on a CU) and
+// cu_rate (the CU's ceiling with several) are measured on MI355X, in GB/s: 128 x
+// 128 register-staged 42 / 55; 64 x 32 and 64 x 64 DMA-fed with 8 and 6 stages 40
+// and 44 (one per CU: their rings fill LDS); the register-ring tiles 45 / 60.  A
+// 64-deep K tile of a BM x BN workgroup is (BM + BN) x 128 bytes.  SwiGLU needs
+// 16-wide gate and up halves per wave, which the 32-column tiles do not have.
+// E.g. the 8B-shaped FFN2 (N 4096, K 14336) at M 64 takes the 32 x 32 ring: 256
+// tiles, one per CU, 1.84 MB each: ~44 us instead of 66 us with 64 x 32 tiles.
 int pick_small(const GemmArgs& a, int epi) {
-    struct Cand { int cfg, bm, bn, per_cu; double us_per_step; };
-    const Cand cands[3] = {{CFG_128x128_4W, 128, 128, 2, 0.77},
-                           {CFG_DMA_64x32_4W_K64_S8, 64, 32, 1, 0.30},
-                           {CFG_DMA_64x64_4W_K64_S6, 64, 64, 1, 0.36}};
+    struct Cand { int cfg, bm, bn; double wg_gbs, cu_gbs; };
+    const Cand cands[7] = {{CFG_128x128_4W, 128, 128, 42.0, 55.0},
+                           {CFG_DMA_64x32_4W_K64_S8, 64, 32, 40.0, 40.0},
+                           {CFG_DMA_64x64_4W_K64_S6, 64, 64, 44.0, 44.0},
+                           {CFG_RING_64x32_PF8, 64, 32, 45.0, 60.0},
+                           {CFG_RING_64x64_PF6, 64, 64, 45.0, 60.0},
+                           {CFG_RING_32x32_PF8, 32, 32, 45.0, 60.0},
+                           {CFG_RING_32x64_PF8, 32, 64, 45.0, 60.0}};
     const int cus = num_cus();
-    const double steps = (double)a.K / 64.0;
+    const double nk = (double)a.K / 64.0;
     const double wbytes = (double)(epi == EPI_SWIGLU ? 2 * a.N : a.N) * a.K * 2.0;
     int best = CFG_128x128_4W;
     double best_t = 0.0;
-    for (int c = 0; c < 3; ++c) {
+    for (int c = 0; c < 7; ++c) {
         const Cand& k = cands[c];
         if (epi == EPI_SWIGLU && k.bn == 32) continue;
         const int out_cols = (epi == EPI_SWIGLU) ? k.bn / 2 : k.bn;
         const long long tiles = (long long)((a.M + k.bm - 1) / k.bm) * ((a.N + out_cols - 1) / out_cols);
-        const long long rounds = (tiles + (long long)cus * k.per_cu - 1) / ((long long)cus * k.per_cu);
-        const double t = std::max((double)rounds * steps * k.us_per_step, wbytes / 5e6);
+        const double busiest = (double)((tiles + cus - 1) / cus);
+        const double bytes = busiest * nk * (k.bm + k.bn) * 128.0;
+        const double rate = std::min(k.cu_gbs, k.wg_gbs * busiest) * 1e3;        // bytes per us
+        const double t = std::max(bytes / rate, wbytes / 6e6);
         if (c == 0 || t < best_t) { best = k.cfg; best_t = t; }
     }
     return best;
@@ -661,6 +811,10 @@ int launch_bf16(const GemmArgs& a, hipStream_t s) {
         case CFG_DMA_64x16_2W_K64_S6: return launch_dma<64, 16, 2, 1, 64, 6, 2, 0, EPI>(a, s);
         case CFG_DMA_64x64_4W_K64_S6: return launch_dma<64, 64, 2, 2, 64, 6, 2, 0, EPI>(a, s);
         case CFG_DMA_256x384_8W_K64_S2_SPREAD: return launch_dma<256, 384, 2, 4, 64, 2, 2, 1, EPI>(a, s);
+        case CFG_RING_64x32_PF8: return launch_ring<64, 32, 2, 2, 8, EPI>(a, s);
+        case CFG_RING_64x64_PF6: return launch_ring<64, 64, 2, 2, 6, EPI>(a, s);
+        case CFG_RING_32x32_PF8: return launch_ring<32, 32, 2, 2, 8, EPI>(a, s);
+        case CFG_RING_32x64_PF8: return launch_ring<32, 64, 2, 2, 8, EPI>(a, s);
         default: return launch_bf16_cfg<128, 128, 2, 2, EPI>(a, s);
     }
 }
