@@ -714,14 +714,17 @@ int num_cus() {
 // CUs) workgroups on the fullest CU.  wg_rate (one workgroup alone on a CU) and
 // cu_rate (the CU's ceiling with several) are measured on MI355X, in GB/s: 128 x
 // 128 register-staged 42 / 55; 64 x 32 and 64 x 64 DMA-fed with 8 and 6 stages 40
-// and 44 (one per CU: their rings fill LDS); the register-ring tiles 45 / 60.  A
+// and 44, 256 x 256 DMA-fed 40 (one per CU: their rings fill LDS); the
+// register-ring tiles 45 / 60.  Up to 256 rows the big tile competes here too (an
+// LM head over 64 rows streams its 1 GB of weights faster from 64 x 64 rings).  A
 // 64-deep K tile of a BM x BN workgroup is (BM + BN) x 128 bytes.  SwiGLU needs
 // 16-wide gate and up halves per wave, which the 32-column tiles do not have.
 // E.g. the 8B-shaped FFN2 (N 4096, K 14336) at M 64 takes the 32 x 32 ring: 256
 // tiles, one per CU, 1.84 MB each: ~44 us instead of 66 us with 64 x 32 tiles.
 int pick_small(const GemmArgs& a, int epi) {
     struct Cand { int cfg, bm, bn; double wg_gbs, cu_gbs; };
-    const Cand cands[7] = {{CFG_128x128_4W, 128, 128, 42.0, 55.0},
+    const Cand cands[8] = {{CFG_128x128_4W, 128, 128, 42.0, 55.0},
+                           {CFG_DMA_256x256_8W_K64_S2, 256, 256, 40.0, 40.0},
                            {CFG_DMA_64x32_4W_K64_S8, 64, 32, 40.0, 40.0},
                            {CFG_DMA_64x64_4W_K64_S6, 64, 64, 44.0, 44.0},
                            {CFG_RING_64x32_PF8, 64, 32, 45.0, 60.0},
@@ -733,7 +736,7 @@ int pick_small(const GemmArgs& a, int epi) {
     const double wbytes = (double)(epi == EPI_SWIGLU ? 2 * a.N : a.N) * a.K * 2.0;
     int best = CFG_128x128_4W;
     double best_t = 0.0;
-    for (int c = 0; c < 7; ++c) {
+    for (int c = 0; c < 8; ++c) {
         const Cand& k = cands[c];
         if (epi == EPI_SWIGLU && k.bn == 32) continue;
         const int out_cols = (epi == EPI_SWIGLU) ? k.bn / 2 : k.bn;
@@ -768,8 +771,7 @@ int pick_cfg(const GemmArgs& a, int epi) {
     }
     const int ncols = (epi == EPI_SWIGLU) ? 2 * a.N : a.N;
     const long long big = (long long)((a.M + 255) / 256) * ((ncols + 255) / 256);
-    if (big < 128) return pick_small(a, epi);
-    if (a.M <= 256) return CFG_DMA_256x256_8W_K64_S2;
+    if (big < 128 || a.M <= 256) return pick_small(a, epi);
     struct Cand { int cfg, bm, bn; double feed; };
     const Cand cands[4] = {{CFG_DMA_256x256_8W_K64_S2_SPREAD, 256, 256, 1.0},
                            {CFG_DMA_256x192_8W_K64_S2_SPREAD, 256, 192, 1.083},
