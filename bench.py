@@ -111,6 +111,48 @@ def algorithmic_work(m, batch, n_layers):
             "weight_bytes": (qkv + o + f1 + f2) * 2 * n_layers + m.V * m.H * 2}
 
 
+def kernel_roofline(m, work, brk):
+    """Each kernel class of the iteration against its roofline: achieved rate from the per-class event
+    timing, its fraction of the peak that bounds it, and of min(peak, arithmetic intensity x HBM
+    bandwidth).  Algorithmic work only (each operand moved once, no padding)."""
+    T, B, L, H = work["T"], work["B"], m.n_layers, m.H
+    tf = MFMA_BF16_PEAK_TFLOPS * 1e12
+    bw = HBM_PEAK_GBS * 1e9
+    w_rows = {"gemm_qkv": (m.qkv_out, H), "gemm_o": (H, m.nq * m.d), "gemm_ffn1": (2 * m.F, H),
+              "gemm_ffn2": (H, m.F)}
+    out = {}
+    for name, (n, k) in w_rows.items():
+        if name not in brk:
+            continue
+        out_cols = n // 2 if name == "gemm_ffn1" else n
+        c_bytes = T * out_cols * (4 * 2 if name in ("gemm_o", "gemm_ffn2") else 2)   # residual: fp32 read + write
+        flops = 2.0 * T * n * k * L
+        byts = (T * k * 2 + n * k * 2 + c_bytes) * L
+        sec = brk[name]["ms_per_step"] * 1e-3
+        out[name] = {"bound": "mfma", "tflops": round(flops / sec / 1e12, 1), "frac_of_peak": round(flops / sec / tf, 4),
+                     "frac_of_attainable": round(flops / sec / min(tf, flops / byts * bw), 4)}
+    if "gemm_lm" in brk:
+        flops = float(work["lm_flops"])
+        byts = m.V * H * 2 + B * H * 2 + B * m.V * 4
+        sec = brk["gemm_lm"]["ms_per_step"] * 1e-3
+        att = min(tf, flops / byts * bw)
+        out["gemm_lm"] = {"bound": "mfma" if att >= tf else "hbm", "tflops": round(flops / sec / 1e12, 1),
+                          "frac_of_peak": round(flops / sec / tf, 4), "frac_of_attainable": round(flops / sec / att, 4)}
+    hbm_bytes = {
+        "attention": work["attn_bytes_per_layer"] * L,
+        "norm": (2 * L * T + B) * H * (4 + 2),                               # fp32 row in, bf16 row out
+        "rope_append": L * T * ((m.nq + 2 * m.nkv) * m.d * 2 + (m.nq + m.nkv) * m.d * 2 + 2 * m.nkv * m.d * 2),
+        "embed": T * H * (2 + 4),
+        "argmax": B * m.V * 4,
+    }
+    for name, byts in hbm_bytes.items():
+        if name not in brk:
+            continue
+        gbs = byts / (brk[name]["ms_per_step"] * 1e-3) / 1e9
+        out[name] = {"bound": "hbm", "gbs": round(gbs, 1), "frac_of_peak": round(gbs * 1e9 / bw, 4)}
+    return out
+
+
 def cpu_baseline(m, batch, seed):
     """The oracle (fp64 numpy, per-request plain definition) on a bounded sample of the workload."""
     import numpy as np
@@ -144,6 +186,55 @@ def cpu_baseline(m, batch, seed):
             "sample": (f"{len(dec_idx)} decodes + {len(pre_idx)} prefill of the same batch ({tokens} tokens), "
                        f"one decoder layer timed ({t_layer:.2f} s) x {m.n_layers} layers + LM head "
                        f"({t_lm:.2f} s); fp64 numpy, BLAS threads = {cores}")}
+
+
+def cpu_mini(seed):
+    """The oracle on one decode iteration of the mini model (the pages' own CPU measurement: 64 decode
+    requests on a small GPT, one at a time vs batched): every request through the plain per-request
+    definition, then the same iteration through the flattened [T, H] self-check.  fp64 numpy, with
+    all host threads and on one thread; best of three each."""
+    import copy
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    from oracle import flat as FL
+    from oracle import model as OM
+    from synth import MINI, kv_std, make_weights, mini_decode_batch, synthetic_kv, uniform_int
+    m = MINI
+    W = make_weights(m, seed, "bf16")
+    batch = mini_decode_batch(seed=seed)
+    ids = uniform_int(seed, "cpu_mini.ids", 0, m.V - 1, len(batch)).tolist()
+    caches = []
+    for i, (_, c) in enumerate(batch):
+        per_layer = []
+        for l in range(m.n_layers):
+            k, v = synthetic_kv(seed, f"cpu_mini.{i}.{l}", c, m.nkv, m.d, kv_std(m), "bf16")
+            per_layer.append({"k": k.astype(np.float64), "v": v.astype(np.float64)})
+        caches.append(per_layer)
+
+    def per_request():
+        cs = copy.deepcopy(caches)
+        return [OM.forward_request(m, W, [ids[i]], c, cs[i])[1] for i, (_, c) in enumerate(batch)]
+
+    def flattened():
+        cs = copy.deepcopy(caches)
+        return FL.forward_flat(m, W, [[t] for t in ids], batch, cs)[1]
+
+    def best(fn):
+        ts = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            fn()
+            ts.append(time.perf_counter() - t0)
+        return round(1e3 * min(ts), 2)
+    cores = len(os.sched_getaffinity(0))
+    out = {"workload": f"one decode iteration of the mini GPT (4 layers, hidden 256, vocab 4096), {len(batch)} "
+                       "requests with cached context U[16,256]; fp64 numpy oracle",
+           "cores": cores}
+    out["per_request_ms"], out["flattened_ms"] = best(per_request), best(flattened)
+    with threadpool_limits(1):
+        out["per_request_ms_1_core"], out["flattened_ms_1_core"] = best(per_request), best(flattened)
+    out["batched_speedup"] = round(out["per_request_ms"] / out["flattened_ms"], 2)
+    return out
 
 
 def decode_loop(seed, steps=64, reps=3):
@@ -501,6 +592,7 @@ def main():
                       "bytes_per_launch": work["attn_bytes_per_layer"],
                       "decode_kv_bytes_per_launch": work["attn_decode_bytes_per_layer"]},
         "kernels_ms_per_step": {k: round(v["ms_per_step"], 3) for k, v in brk.items()},
+        "kernel_roofline": kernel_roofline(m, work, brk),
     }
     if not args.no_trace:
         print("[bench] serving trace (chained) ...", file=sys.stderr, flush=True)
@@ -514,6 +606,7 @@ def main():
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample ...", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(m.with_layers(args.layers), batch, args.seed)
+        out["cpu_mini_iteration"] = cpu_mini(args.seed)
     for pool in pools:
         if pool is not None:
             A.sb_sched_destroy(pool[1])
