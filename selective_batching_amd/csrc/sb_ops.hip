@@ -276,15 +276,13 @@ __global__ __launch_bounds__(256) void rope_append_kernel(void* qkv, long long s
             store8<DT>(kp + i0 + half, x2);
         }
     }
-    // v: 8 consecutive dims per thread into the blocked layout [slot / 8][dim][slot % 8]
+    // v into the blocked layout [slot / 8][dim][slot % 8]: one element per lane, consecutive lanes
+    // on consecutive dims, so a wave's stores fall in 64 consecutive 16-byte rows (8 lines) rather
+    // than in 64 different lines
     const T* vrow = row + (long long)(nq + nkv) * D;
-    for (int w = threadIdx.x; w < nkv * D / 8; w += blockDim.x) {
-        const int g = w / (D / 8), e0 = (w % (D / 8)) * 8;
-        float x[8];
-        load8<DT>(vrow + (long long)g * D + e0, x);
-        T* vp = V + (long long)g * arena * D + (((s >> 3) * D + e0) << 3) + (s & 7);
-#pragma unroll
-        for (int c = 0; c < 8; ++c) Store<DT>::st(vp + 8 * c, x[c]);
+    for (int u = threadIdx.x; u < nkv * D; u += blockDim.x) {
+        const int g = u / D, e = u % D;
+        V[(long long)g * arena * D + (((s >> 3) * D + e) << 3) + (s & 7)] = vrow[(long long)g * D + e];
     }
 }
 
