@@ -254,12 +254,41 @@ def test_gemm_every_tile_config(cfg, epi, K, monkeypatch):
         assert_close_elem(host(out), OM.silu(OM.linear(A, W[:N])) * OM.linear(A, W[N:]), "bf16", f"cfg {cfg} swiglu")
 
 
+@pytest.mark.parametrize("cfg", range(N_GEMM_CFGS))
+@pytest.mark.parametrize("epi", ["resid", "swiglu"])
+@pytest.mark.parametrize("M", [1, 33])
+def test_gemm_every_tile_config_few_rows(cfg, epi, M, monkeypatch):
+    """Each configuration (forced) with fewer rows than its tile: one row, or a ragged 33 (row clamping,
+    masked stores); K = 192 (three 64-deep tiles, fewer than the deeper rings)."""
+    monkeypatch.setenv("SB_GEMM_CFG", str(cfg))
+    N, K = 96, 192
+    print_case("gemm cfg few rows", cfg, epi, M, N, K)
+    A = normal(cfg + 50, "A", (M, K), dtype="bf16")
+    W = normal(cfg + 50, "W", (2 * N if epi == "swiglu" else N, K), std=0.05, dtype="bf16")
+    x0 = normal(cfg + 50, "x0", (M, N)).astype(np.float64)
+    dA, dW = dev(A, "bf16"), dev(W, "bf16")
+    if epi == "resid":
+        out = torch.from_numpy(x0.astype(np.float32)).cuda()
+        sb.sb_op_gemm(sb.SB_BF16, sb.SB_EPI_RESID, M, N, K, dA.data_ptr(), K, dW.data_ptr(), K, None, out.data_ptr(),
+                      N, 0, 0, stream_handle())
+        _sync()
+        assert_close_rms(host(out), x0 + OM.linear(A, W), TOL["fp32"], f"cfg {cfg} resid M {M}")
+    else:
+        out = torch.zeros((M, N), dtype=torch.bfloat16, device="cuda")
+        sb.sb_op_gemm(sb.SB_BF16, sb.SB_EPI_SWIGLU, M, N, K, dA.data_ptr(), K, dW.data_ptr(), K, None, out.data_ptr(),
+                      N, 0, N, stream_handle())
+        _sync()
+        assert_close_elem(host(out), OM.silu(OM.linear(A, W[:N])) * OM.linear(A, W[N:]), "bf16",
+                          f"cfg {cfg} swiglu M {M}")
+
+
 @pytest.mark.parametrize("epi", ["bias", "swiglu"])
-def test_gemm_configs_bitwise_identical(epi, monkeypatch):
+@pytest.mark.parametrize("M", [300, 33])
+def test_gemm_configs_bitwise_identical(epi, M, monkeypatch):
     """Every tile configuration gives the same bits: each output sums K in 32-wide MFMA steps in
     ascending order whatever the tile, so the launcher's choice (which depends on M, i.e. on the
     batch) never changes a result."""
-    M, N, K = 300, 640, 512
+    N, K = 640, 512
     A = normal(7, "A", (M, K), dtype="bf16")
     W = normal(7, "W", (2 * N if epi == "swiglu" else N, K), std=0.05, dtype="bf16")
     b = normal(7, "b", (N,), std=0.5, dtype="bf16")
