@@ -35,6 +35,11 @@ class SBError(RuntimeError):
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run `python selective_batching_amd/build.py` "
                       "(or __graft_entry__.build()) first")
+# PyTorch carries its own HIP runtime.  Loaded first, it is the one libsb.so binds to (same soname),
+# so the library and the streams and memory it is handed share one runtime; loaded after libsb.so,
+# a second runtime would come up beside the system one the library had bound, and the library's
+# calls would not see the device.
+import torch  # noqa: F401,E402
 lib = C.CDLL(LIB_PATH)
 
 i32, i64, f32, f64, vp, sz = C.c_int32, C.c_int64, C.c_float, C.c_double, C.c_void_p, C.c_size_t
