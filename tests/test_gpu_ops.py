@@ -1,4 +1,6 @@
 """GPU parity of each step of the iteration (op-level C entry points) against the oracle."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -362,3 +364,21 @@ def test_attention_unit_merge_is_batch_invariant():
         assert_close_elem(host(o_big[0:1]), want, "bf16", "attention of a merged request")
     finally:
         sb.sb_kv_destroy(kv)
+
+
+def test_package_imported_before_torch():
+    """A fresh process that imports the package before torch still runs the library on the device
+    (the package loads torch's HIP runtime before libsb.so, so there is one runtime)."""
+    import subprocess
+    import sys
+    code = ("import selective_batching_amd as sb\n"
+            "import torch\n"
+            "x = torch.zeros(2, 300, device='cuda'); x[0, 7] = 1.0; x[1, 299] = 2.0\n"
+            "out = torch.full((2,), -1, dtype=torch.int32, device='cuda')\n"
+            "sb.sb_op_argmax(2, 300, x.data_ptr(), out.data_ptr(), torch.cuda.current_stream().cuda_stream)\n"
+            "torch.cuda.synchronize()\n"
+            "print(out.tolist())\n")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300,
+                       cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert r.stdout.strip().splitlines()[-1] == "[7, 299]"
