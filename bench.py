@@ -436,8 +436,8 @@ def ffn1_traffic():
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path (requests shard by data "
-              "parallelism with no exchange; see the design notes).", file=sys.stderr)
+        print("bench.py runs on one GPU only: the library has no multi-GPU path (requests would shard by data "
+              "parallelism with no exchange between GPUs).", file=sys.stderr)
         sys.exit(2)
 
     if args.op_gemm:
