@@ -35,8 +35,10 @@ int sb_op_gemm(int32_t dtype, int32_t epilogue, int32_t M, int32_t N, int32_t K,
 int sb_op_norm(int32_t dtype, int32_t kind, int32_t rows, int32_t hidden, const float* x, const int32_t* row_map,
                const void* g, const void* b, float eps, void* out, void* stream);
 
-/* RoPE of q and k inside qkv (Llama-style dims only) and append of k, v to
- * layer `layer` of the K/V manager at rg->tok_slot. */
+/* RoPE of q in place inside qkv (Llama-style dims only) and append of k
+ * (rotated likewise) and v to layer `layer` of the K/V manager at
+ * rg->tok_slot; qkv's k and v parts are left as they are.  qkv must be
+ * 16-byte aligned (SB_ERR_INVALID otherwise). */
 int sb_op_rope_append(const sb_model_dims* dims, const sb_ragged* rg, const sb_kv* kv, int32_t layer, void* qkv,
                       void* stream);
 

@@ -224,20 +224,128 @@ __global__ __launch_bounds__(256) void norm_kernel(const float* x, const int* ro
 // Per token: rotate q (in place in qkv) and k by the token's position
 // (Llama-style, rotate-half pairs (i, i + d/2), angle pos * theta^(-2i/d),
 // evaluated in double precision once per token), then append k and v to the
-// K/V manager's arenas at the token's slot.  Each thread takes 8 consecutive
-// dims of one half-head and the matching 8 of the other half (16-byte
-// accesses); rotated k is also written back to qkv.
+// K/V manager's arenas at the token's slot (k rotated there; qkv's k part is
+// left as it was).  A rotation item is 8 consecutive dims of one half-head with
+// the matching 8 of the other half (q heads with rotation, k heads always):
+// 16-byte accesses in bf16; v moves one element per lane.  Every thread issues
+// the loads of its first items before the token's cos/sin are evaluated, so the
+// double-precision evaluation overlaps the memory latency.
 constexpr int kRopeMaxHalf = 64;        // head_dim <= 128
+constexpr int kRopeItemsPerThread = 2;  // items a thread has in flight at once
+
+template <int DT>
+struct Piece8 {                          // 8 consecutive elements, raw
+    u32x4 r[DT == SB_BF16 ? 1 : 2];
+};
+template <int DT>
+__device__ __forceinline__ Piece8<DT> ld_piece(const typename Store<DT>::T* p) {
+    Piece8<DT> x;
+    x.r[0] = *(const u32x4*)p;
+    if constexpr (DT != SB_BF16) x.r[1] = *(const u32x4*)(p + 4);
+    return x;
+}
+template <int DT>
+__device__ __forceinline__ void st_piece(typename Store<DT>::T* p, const Piece8<DT>& x) {
+    *(u32x4*)p = x.r[0];
+    if constexpr (DT != SB_BF16) *(u32x4*)(p + 4) = x.r[1];
+}
+template <int DT>
+__device__ __forceinline__ void piece_to_f32(const Piece8<DT>& x, float (&v)[8]) {
+    if constexpr (DT == SB_BF16) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            v[2 * c] = __uint_as_float(x.r[0][c] << 16);
+            v[2 * c + 1] = __uint_as_float(x.r[0][c] & 0xffff0000u);
+        }
+    } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) { v[c] = __uint_as_float(x.r[0][c]); v[4 + c] = __uint_as_float(x.r[1][c]); }
+    }
+}
+template <int DT>
+__device__ __forceinline__ Piece8<DT> f32_to_piece(const float (&v)[8]) {
+    Piece8<DT> x;
+    if constexpr (DT == SB_BF16) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) x.r[0][c] = (uint32_t)f2bf(v[2 * c]) | ((uint32_t)f2bf(v[2 * c + 1]) << 16);
+    } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) { x.r[0][c] = __float_as_uint(v[c]); x.r[1][c] = __float_as_uint(v[4 + c]); }
+    }
+    return x;
+}
+
 template <int DT>
 __global__ __launch_bounds__(256) void rope_append_kernel(void* qkv, long long stride, const int* pos, const int* slot,
                                                           void* kplane, void* vplane, long long arena, int nq, int nkv,
                                                           int D, int rope, double log_theta) {
     using T = typename Store<DT>::T;
+    constexpr int IPT = kRopeItemsPerThread;
+    constexpr int VPT = 4;                                  // v elements a thread has in flight at once
     __shared__ float cs[kRopeMaxHalf], sn[kRopeMaxHalf];
     const int t = blockIdx.x;
     T* row = (T*)qkv + (long long)t * stride;
+    T* K = (T*)kplane;
+    T* V = (T*)vplane;
+    const int half = D / 2, cph = half / 8;                 // 8-dim pieces per half-head
+    const int h0 = rope ? 0 : nq;                           // first rotated head (q untouched without rotation)
+    const int n_rot = (nq + nkv - h0) * cph;                // rotation items
+    const int n_v = nkv * D;                                // v elements
     const long long s = slot[t];
-    const int half = D / 2;
+    const T* vrow = row + (long long)(nq + nkv) * D;
+    Piece8<DT> x1[IPT], x2[IPT];
+    T vv[VPT];
+    auto fetch = [&](int base, int vbase) {
+#pragma unroll
+        for (int j = 0; j < IPT; ++j) {
+            const int w = base + j * blockDim.x + threadIdx.x;
+            if (w < n_rot) {
+                const T* p = row + (long long)(h0 + w / cph) * D + (w % cph) * 8;
+                x1[j] = ld_piece<DT>(p);
+                x2[j] = ld_piece<DT>(p + half);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < VPT; ++j) {
+            const int u = vbase + j * blockDim.x + threadIdx.x;
+            if (u < n_v) vv[j] = vrow[u];
+        }
+    };
+    auto process = [&](int base, int vbase) {
+#pragma unroll
+        for (int j = 0; j < IPT; ++j) {
+            const int w = base + j * blockDim.x + threadIdx.x;
+            if (w >= n_rot) continue;
+            const int h = h0 + w / cph, i0 = (w % cph) * 8;
+            Piece8<DT> y1 = x1[j], y2 = x2[j];
+            if (rope) {
+                float a[8], b[8], c1[8], c2[8];
+                piece_to_f32<DT>(x1[j], a);
+                piece_to_f32<DT>(x2[j], b);
+#pragma unroll
+                for (int c = 0; c < 8; ++c) {
+                    c1[c] = a[c] * cs[i0 + c] - b[c] * sn[i0 + c];
+                    c2[c] = b[c] * cs[i0 + c] + a[c] * sn[i0 + c];
+                }
+                y1 = f32_to_piece<DT>(c1);
+                y2 = f32_to_piece<DT>(c2);
+            }
+            T* p = h < nq ? row + (long long)h * D + i0 : K + ((long long)(h - nq) * arena + s) * D + i0;
+            st_piece<DT>(p, y1);
+            st_piece<DT>(p + half, y2);
+        }
+        // v into the blocked layout [slot / 8][dim][slot % 8]: one element per lane, consecutive lanes
+        // on consecutive dims, so a wave's stores fall in 64 consecutive 16-byte rows (8 lines)
+#pragma unroll
+        for (int j = 0; j < VPT; ++j) {
+            const int u = vbase + j * blockDim.x + threadIdx.x;
+            if (u < n_v) {
+                const int g = u / D, e = u % D;
+                V[(long long)g * arena * D + (((s >> 3) * D + e) << 3) + (s & 7)] = vv[j];
+            }
+        }
+    };
+    fetch(0, 0);
     if (rope) {
         for (int i = threadIdx.x; i < half; i += blockDim.x) {
             const double inv = exp(-(2.0 * i / D) * log_theta);
@@ -248,41 +356,11 @@ __global__ __launch_bounds__(256) void rope_append_kernel(void* qkv, long long s
         }
         __syncthreads();
     }
-    T* K = (T*)kplane;
-    T* V = (T*)vplane;
-    const int cph = half / 8;                              // 8-dim chunks per half-head
-    for (int w = threadIdx.x; w < (nq + nkv) * cph; w += blockDim.x) {
-        const int h = w / cph, i0 = (w % cph) * 8;
-        if (!rope && h < nq) continue;                     // q untouched without rotation
-        T* p = row + (long long)h * D;
-        float x1[8], x2[8];
-        load8<DT>(p + i0, x1);
-        load8<DT>(p + i0 + half, x2);
-        if (rope) {
-            float y1[8], y2[8];
-#pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                y1[c] = x1[c] * cs[i0 + c] - x2[c] * sn[i0 + c];
-                y2[c] = x2[c] * cs[i0 + c] + x1[c] * sn[i0 + c];
-            }
-#pragma unroll
-            for (int c = 0; c < 8; ++c) { x1[c] = y1[c]; x2[c] = y2[c]; }
-            store8<DT>(p + i0, x1);
-            store8<DT>(p + i0 + half, x2);
-        }
-        if (h >= nq) {
-            T* kp = K + ((long long)(h - nq) * arena + s) * D;
-            store8<DT>(kp + i0, x1);
-            store8<DT>(kp + i0 + half, x2);
-        }
-    }
-    // v into the blocked layout [slot / 8][dim][slot % 8]: one element per lane, consecutive lanes
-    // on consecutive dims, so a wave's stores fall in 64 consecutive 16-byte rows (8 lines) rather
-    // than in 64 different lines
-    const T* vrow = row + (long long)(nq + nkv) * D;
-    for (int u = threadIdx.x; u < nkv * D; u += blockDim.x) {
-        const int g = u / D, e = u % D;
-        V[(long long)g * arena * D + (((s >> 3) * D + e) << 3) + (s & 7)] = vrow[(long long)g * D + e];
+    process(0, 0);
+    for (int base = IPT * blockDim.x, vbase = VPT * blockDim.x; base < n_rot || vbase < n_v;
+         base += IPT * blockDim.x, vbase += VPT * blockDim.x) {
+        fetch(base, vbase);
+        process(base, vbase);
     }
 }
 
@@ -400,6 +478,8 @@ int launch_rope_append(const sb_model_dims* d, const sb_ragged* rg, void* qkv, v
     if (rg->n_tokens <= 0) return SB_OK;
     if (d->head_dim % 16 || d->head_dim / 2 > kRopeMaxHalf)
         return fail(SB_ERR_INVALID, "rope/append: head_dim must be a multiple of 16 and <= %d", 2 * kRopeMaxHalf);
+    if (((uintptr_t)qkv | (uintptr_t)kp | (uintptr_t)vp) % 16)
+        return fail(SB_ERR_INVALID, "rope/append: qkv and the K/V planes must be 16-byte aligned");
     TimedScope ts(SB_K_ROPE_APPEND, s);
     const long long stride = (long long)(d->n_heads + 2 * d->n_kv_heads) * d->head_dim;
     const int rope = d->arch == SB_ARCH_LLAMA;

@@ -195,6 +195,13 @@ def test_llama8b_shape_layer_stepwise():
         sync(); qkv_pre = host(qkv)
         sb.sb_op_rope_append(dims, rg, kv, 0, qkv.data_ptr(), s)
         sync(); qkv_rot = host(qkv)
+        # the appended (rotated) k and the v of every new token, read back from the K/V manager
+        new_slots = torch.from_numpy(np.concatenate([np.arange(bases[i] + c, bases[i] + c + n)
+                                                     for i, (n, c) in enumerate(batch)]).astype(np.int32)).cuda()
+        k_new = torch.empty((T, m.nkv * m.d), dtype=torch.bfloat16, device="cuda")
+        v_new = torch.empty((T, m.nkv * m.d), dtype=torch.bfloat16, device="cuda")
+        sb.sb_kv_read(kv, 0, T, new_slots.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), s)
+        sync(); k_app, v_app = host(k_new), host(v_new)
         sb.sb_op_attention(dims, rg, kv, 0, qkv.data_ptr(), o.data_ptr(), pw.data_ptr(), pw.numel(), s)
         sync(); o1 = host(o)
         sb.sb_op_gemm(sb.SB_BF16, sb.SB_EPI_RESID, T, m.H, m.nq * m.d, o.data_ptr(), m.nq * m.d, dw["w_o"].data_ptr(),
@@ -223,9 +230,11 @@ def test_llama8b_shape_layer_stepwise():
             q = M.rope(qkv_pre[r, :nq_d].reshape(n, m.nq, m.d), pos, m.rope_theta)
             k = M.rope(qkv_pre[r, nq_d:nq_d + nkv_d].reshape(n, m.nkv, m.d), pos, m.rope_theta)
             assert_close_elem(qkv_rot[r, :nq_d], q.reshape(n, nq_d), dtype, f"req {i} rope q")
-            assert_close_elem(qkv_rot[r, nq_d:nq_d + nkv_d], k.reshape(n, nkv_d), dtype, f"req {i} rope k")
+            assert_close_elem(k_app[r], k.reshape(n, nkv_d), dtype, f"req {i} rope k (appended)")
+            assert np.array_equal(v_app[r], qkv_pre[r, nq_d + nkv_d:]), f"req {i} appended v"
+            assert np.array_equal(qkv_rot[r, nq_d:], qkv_pre[r, nq_d:]), f"req {i} qkv k/v parts left as they were"
             qg = qkv_rot[r, :nq_d].reshape(n, m.nq, m.d)
-            kg = qkv_rot[r, nq_d:nq_d + nkv_d].reshape(n, m.nkv, m.d)
+            kg = k_app[r].reshape(n, m.nkv, m.d)
             v = qkv_pre[r, nq_d + nkv_d:].reshape(n, m.nkv, m.d)
             K = np.concatenate([caches[i][0], kg]); V = np.concatenate([caches[i][1], v])
             att = M.attention(qg, K, V, c, m.group).reshape(n, nq_d)
