@@ -60,6 +60,8 @@ struct GemmArgs {
 };
 
 int launch_gemm(int dtype, int epi, const GemmArgs& a, hipStream_t s);
+// Compute units of the current device (256 on MI355X; 256 if the query fails).
+int num_cus();
 
 // ------------------------------------------------------------------ timing hooks
 void timing_begin(int kind, hipStream_t s);

@@ -693,19 +693,6 @@ int launch_ring(const GemmArgs& a, hipStream_t s) {
     }
 }
 
-int num_cus() {
-    static int n = 0;
-    if (n == 0) {
-        int dev = 0, v = 0;
-        if (hipGetDevice(&dev) == hipSuccess &&
-            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-            n = v;
-        else
-            n = 256;
-    }
-    return n;
-}
-
 // GEMMs too small for a full round of big tiles (decode-heavy iterations: M of a few
 // hundred rows or less).  Each workgroup walks all of K (one MFMA chain per output,
 // K is never split), so the busiest CU's operand bytes over the rate one CU takes
@@ -830,6 +817,19 @@ int launch_f32(const GemmArgs& a, hipStream_t s) {
 }
 
 }  // namespace
+
+int num_cus() {
+    static int n = 0;
+    if (n == 0) {
+        int dev = 0, v = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+            n = v;
+        else
+            n = 256;
+    }
+    return n;
+}
 
 int launch_gemm(int dtype, int epi, const GemmArgs& a, hipStream_t s) {
     if (a.M <= 0) return SB_OK;

@@ -136,11 +136,21 @@ __device__ __forceinline__ void store8(typename Store<DT>::T* p, const float (&v
 
 // LayerNorm (kind 0) or RMSNorm (kind 1) of fp32 rows into dtype rows; fp32
 // statistics, two passes over registers (mean, then centred second moment).
-// WPR = 1: one wave per row (four rows per workgroup), sums by lane shuffles
-// only; WPR = 4: one row per workgroup (wide rows), sums through LDS.  16-byte
-// loads along the row; PER float4 chunks per lane: hidden <= 256 PER WPR.
-// Fewer rows than about four per CU take a workgroup per row (more CUs
-// streaming, a quarter of the dependent loads per lane).
+// Every kernel below sums a row in one canonical order, so a row's result does
+// not depend on how many rows were normalised together (which kernel ran):
+// piece i of the row (elements 4i .. 4i+3) contributes (a + b) + (c + d) (its
+// square terms likewise); lane l of 64 adds the pieces l, l + 64, l + 128, ...
+// in ascending order; the 64 lane sums meet in an xor butterfly.
+//   norm_kernel<.., WPR = 1>: one wave per row (four rows per workgroup), the
+//     order above directly (hidden <= 256 PER).
+//   norm_kernel<.., WPR = 4>: one row per workgroup, for few rows (more CUs
+//     streaming, a quarter of the dependent loads per lane) or wide rows; the
+//     256 threads leave their piece sums in LDS and one wave adds them in the
+//     order above.
+//   norm_stream_kernel: many rows; each wave walks rows gw, gw + W, ... with
+//     the next row's loads in flight while it reduces and stores the current
+//     one, the gain and shift staged once per workgroup in LDS.
+// 16-byte loads along the row.
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
@@ -162,17 +172,36 @@ __device__ __forceinline__ void widen4(const typename Raw4<DT>::T& w, float (&v)
     }
 }
 
+// The per-piece terms and the output of one piece, shared by every norm kernel.
+__device__ __forceinline__ float piece_sum(const float4& v) { return (v.x + v.y) + (v.z + v.w); }
+__device__ __forceinline__ float piece_sq(const float4& v, float mean) {
+    const float a = v.x - mean, b = v.y - mean, c = v.z - mean, d = v.w - mean;
+    return (a * a + b * b) + (c * c + d * d);
+}
+template <int DT>
+__device__ __forceinline__ void norm_piece_out(typename Store<DT>::T* o, const float4& v, float mean, float rstd,
+                                               const typename Raw4<DT>::T& gr, const typename Raw4<DT>::T* br) {
+    const float xs[4] = {v.x, v.y, v.z, v.w};
+    float gv[4], bv[4] = {0.f, 0.f, 0.f, 0.f}, y[4];
+    widen4<DT>(gr, gv);
+    if (br) widen4<DT>(*br, bv);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) y[c] = (xs[c] - mean) * rstd * gv[c] + bv[c];
+    store4<DT>(o, y);
+}
+
+constexpr int kNormMaxPieces = 12288 / 4;
+
 template <int DT, int PER, int WPR>
 __global__ __launch_bounds__(256) void norm_kernel(const float* x, const int* row_map, const void* gam, const void* bet,
                                                    void* out, int rows, int H, int kind, float eps) {
     using T = typename Store<DT>::T;
     using R = typename Raw4<DT>::T;
-    __shared__ float red[4];
+    __shared__ float red[WPR == 1 ? 1 : kNormMaxPieces + 1];
     constexpr int LANES = 64 * WPR;                        // threads per row
     const int lane = threadIdx.x % LANES;
     const int r = blockIdx.x * (4 / WPR) + threadIdx.x / LANES;
     if (r >= rows) return;                                 // whole rows only: block-uniform when WPR = 4
-    auto row_sum = [&](float v) { return WPR == 1 ? wave_sum(v) : block_sum(v, red); };
     const long long src = row_map ? row_map[r] : r;
     const float4* xr = (const float4*)(x + src * H);
     const T* g = (const T*)gam;
@@ -190,34 +219,92 @@ __global__ __launch_bounds__(256) void norm_kernel(const float* x, const int* ro
             if (b) br[q] = *(const R*)(b + 4 * i);
         }
     }
-    float s = 0.f;
+    // the canonical row sum of term(q) over this thread's pieces
+    auto row_sum = [&](auto term) {
+        if constexpr (WPR == 1) {
+            float s = 0.f;
 #pragma unroll
-    for (int q = 0; q < PER; ++q)
-        if (lane + LANES * q < n4) s += (v[q].x + v[q].y) + (v[q].z + v[q].w);
-    const float mean = kind == 0 ? row_sum(s) / H : 0.f;
-    float s2 = 0.f;
+            for (int q = 0; q < PER; ++q)
+                if (lane + LANES * q < n4) s += term(q);
+            return wave_sum(s);
+        } else {
 #pragma unroll
-    for (int q = 0; q < PER; ++q) {
-        const int i = lane + LANES * q;
-        if (i < n4) {
-            const float a = v[q].x - mean, bb = v[q].y - mean, c = v[q].z - mean, d = v[q].w - mean;
-            s2 += (a * a + bb * bb) + (c * c + d * d);
+            for (int q = 0; q < PER; ++q)
+                if (lane + LANES * q < n4) red[lane + LANES * q] = term(q);
+            __syncthreads();
+            if (threadIdx.x < 64) {
+                float s = 0.f;
+                for (int i = threadIdx.x; i < n4; i += 64) s += red[i];
+                s = wave_sum(s);
+                if (threadIdx.x == 0) red[kNormMaxPieces] = s;
+            }
+            __syncthreads();
+            const float tot = red[kNormMaxPieces];
+            __syncthreads();                               // red is rewritten by the next sum
+            return tot;
         }
-    }
-    const float rstd = 1.0f / sqrtf(row_sum(s2) / H + eps);
+    };
+    const float mean = kind == 0 ? row_sum([&](int q) { return piece_sum(v[q]); }) / H : 0.f;
+    const float rstd = 1.0f / sqrtf(row_sum([&](int q) { return piece_sq(v[q], mean); }) / H + eps);
     T* o = (T*)out + (long long)r * H;
 #pragma unroll
     for (int q = 0; q < PER; ++q) {
         const int i = lane + LANES * q;
-        if (i < n4) {
-            const float xs[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
-            float gv[4], bv[4] = {0.f, 0.f, 0.f, 0.f}, y[4];
-            widen4<DT>(gr[q], gv);
-            if (b) widen4<DT>(br[q], bv);
+        if (i < n4) norm_piece_out<DT>(o + 4 * i, v[q], mean, rstd, gr[q], b ? &br[q] : nullptr);
+    }
+}
+
+template <int DT, int PER>
+__global__ __launch_bounds__(256) void norm_stream_kernel(const float* x, const int* row_map, const void* gam,
+                                                          const void* bet, void* out, int rows, int H, int kind,
+                                                          float eps) {
+    using T = typename Store<DT>::T;
+    using R = typename Raw4<DT>::T;
+    __shared__ R gs[64 * PER], bs[64 * PER];
+    const int lane = threadIdx.x & 63;
+    const int n4 = H / 4;
+    const T* g = (const T*)gam;
+    const T* b = (const T*)bet;
+    for (int i = threadIdx.x; i < n4; i += blockDim.x) {
+        gs[i] = *(const R*)(g + 4 * i);
+        if (b) bs[i] = *(const R*)(b + 4 * i);
+    }
+    __syncthreads();
+    const int W = gridDim.x * (blockDim.x >> 6);
+    int r = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    if (r >= rows) return;
+    // a row's pieces lane, lane + 64, ...; past the row's end the last piece again (never used), so
+    // every load is issued unconditionally and the next row's stay in flight during this row's work
+    auto load_row = [&](float4 (&v)[PER], int rr) {
+        const long long src = row_map ? row_map[rr] : rr;
+        const float4* xr = (const float4*)(x + src * H);
 #pragma unroll
-            for (int c = 0; c < 4; ++c) y[c] = (xs[c] - mean) * rstd * gv[c] + bv[c];
-            store4<DT>(o + 4 * i, y);
+        for (int q = 0; q < PER; ++q) v[q] = xr[min(lane + 64 * q, n4 - 1)];
+    };
+    float4 cur[PER], nxt[PER];
+    load_row(cur, r);
+    for (; r < rows; r += W) {
+        load_row(nxt, min(r + W, rows - 1));
+        float s = 0.f;
+        if (kind == 0) {
+#pragma unroll
+            for (int q = 0; q < PER; ++q)
+                if (lane + 64 * q < n4) s += piece_sum(cur[q]);
         }
+        const float mean = kind == 0 ? wave_sum(s) / H : 0.f;
+        float s2 = 0.f;
+#pragma unroll
+        for (int q = 0; q < PER; ++q)
+            if (lane + 64 * q < n4) s2 += piece_sq(cur[q], mean);
+        const float rstd = 1.0f / sqrtf(wave_sum(s2) / H + eps);
+        T* o = (T*)out + (long long)r * H;
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            const int i = lane + 64 * q;
+            if (i < n4) norm_piece_out<DT>(o + 4 * i, cur[q], mean, rstd, gs[i], b ? &bs[i] : nullptr);
+        }
+#pragma unroll
+        for (int q = 0; q < PER; ++q) cur[q] = nxt[q];
     }
 }
 
@@ -446,29 +533,32 @@ __global__ __launch_bounds__(kArgmaxThreads) void argmax_kernel(const float* log
 
 }  // namespace
 
-// below this many rows a workgroup takes one row (see norm_kernel)
+// below this many rows a workgroup takes one row (see norm_kernel); from it on, the streaming
+// kernel with kNormStreamBlocksPerCU workgroups of four waves per CU
 constexpr int kNormRowsPerBlockMin = 1024;
+constexpr int kNormStreamBlocksPerCU = 2;
 
 int launch_norm(int dtype, int kind, int rows, int H, const float* x, const int* row_map, const void* g,
                 const void* b, float eps, void* out, hipStream_t s) {
     if (rows <= 0) return SB_OK;
-    if (H % 4 || H > 12288) return fail(SB_ERR_INVALID, "norm: hidden must be a multiple of 4 and <= 12288");
+    if (H % 4 || H > 4 * kNormMaxPieces) return fail(SB_ERR_INVALID, "norm: hidden must be a multiple of 4 and <= 12288");
     TimedScope ts(SB_K_NORM, s);
     const dim3 block(256);
-    auto go = [&](auto kern, int rows_per_block) {
-        hipLaunchKernelGGL(kern, dim3((rows + rows_per_block - 1) / rows_per_block), block, 0, s, x, row_map, g, b,
-                           out, rows, H, kind, eps);
+    auto go = [&](auto kern, int blocks) {
+        hipLaunchKernelGGL(kern, dim3(blocks), block, 0, s, x, row_map, g, b, out, rows, H, kind, eps);
     };
+    const int per4 = (rows + 3) / 4;
+    const int stream_blocks = std::min(per4, kNormStreamBlocksPerCU * num_cus());
     if (dtype == SB_BF16) {
-        if (H <= 1024) go(norm_kernel<SB_BF16, 4, 1>, 4);
-        else if (H <= 4096 && rows < kNormRowsPerBlockMin) go(norm_kernel<SB_BF16, 4, 4>, 1);
-        else if (H <= 4096) go(norm_kernel<SB_BF16, 16, 1>, 4);
-        else go(norm_kernel<SB_BF16, 12, 4>, 1);
+        if (H <= 1024) go(norm_kernel<SB_BF16, 4, 1>, per4);
+        else if (H <= 4096 && rows < kNormRowsPerBlockMin) go(norm_kernel<SB_BF16, 4, 4>, rows);
+        else if (H <= 4096) go(norm_stream_kernel<SB_BF16, 16>, stream_blocks);
+        else go(norm_kernel<SB_BF16, 12, 4>, rows);
     } else {
-        if (H <= 1024) go(norm_kernel<SB_F32, 4, 1>, 4);
-        else if (H <= 4096 && rows < kNormRowsPerBlockMin) go(norm_kernel<SB_F32, 4, 4>, 1);
-        else if (H <= 4096) go(norm_kernel<SB_F32, 16, 1>, 4);
-        else go(norm_kernel<SB_F32, 12, 4>, 1);
+        if (H <= 1024) go(norm_kernel<SB_F32, 4, 1>, per4);
+        else if (H <= 4096 && rows < kNormRowsPerBlockMin) go(norm_kernel<SB_F32, 4, 4>, rows);
+        else if (H <= 4096) go(norm_stream_kernel<SB_F32, 16>, stream_blocks);
+        else go(norm_kernel<SB_F32, 12, 4>, rows);
     }
     return check_launch("norm");
 }

@@ -75,9 +75,11 @@ def test_gemm_fp32_logits_out_and_ragged_rows():
 # ---------------------------------------------------------------- norms
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 @pytest.mark.parametrize("kind", [0, 1])
-@pytest.mark.parametrize("H,rows", [(64, 5), (256, 5), (2048, 5), (4096, 5), (12288, 5), (2048, 1031), (4096, 1031)])
+@pytest.mark.parametrize("H,rows", [(64, 5), (256, 5), (2048, 5), (4096, 5), (12288, 5), (2048, 1031), (4096, 1031),
+                                    (1028, 1500), (4096, 3741)])
 def test_norm_matches_oracle(dtype, kind, H, rows):
-    """Both launch shapes: a workgroup per row (few rows, wide rows) and a wave per row."""
+    """Every launch shape: a workgroup per row (few rows, wide rows), a wave per row, and waves streaming
+    several rows each (1028: a partial last group of pieces per lane; 3741: the 8B-shaped batch)."""
     print_case("norm", dtype, kind, H, rows)
     x = normal(H, "x", (rows + 2, H), std=2.0, mean=0.3)
     g = normal(H, "g", (H,), std=0.1, mean=1.0, dtype=dtype)
@@ -94,6 +96,33 @@ def test_norm_matches_oracle(dtype, kind, H, rows):
     xs = x[row_map].astype(np.float64)
     want = OM.layer_norm(xs, g, b, 1e-5) if kind == 0 else OM.rms_norm(xs, g, 1e-5)
     assert_close_elem(host(out), want, dtype, f"norm {dtype} kind {kind} H {H}")
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("kind", [0, 1])
+@pytest.mark.parametrize("H", [1028, 2048, 4096])
+def test_norm_independent_of_row_count(dtype, kind, H):
+    """A row's normalised values do not depend on how many rows are normalised with it: 7 rows alone
+    (a workgroup per row) and the same rows among 1500 (waves streaming rows) give the same bits."""
+    print_case("norm row-count invariance", dtype, kind, H)
+    rows = 1500
+    x = normal(H + 1, "x", (rows, H), std=2.0, mean=0.3)
+    g = normal(H + 1, "g", (H,), std=0.1, mean=1.0, dtype=dtype)
+    b = normal(H + 1, "b", (H,), std=0.1, dtype=dtype) if kind == 0 else None
+    tdt = {"fp32": torch.float32, "bf16": torch.bfloat16}[dtype]
+    dx = torch.from_numpy(x).cuda()
+    dg, dbb = dev(g, dtype), (dev(b, dtype) if b is not None else None)
+    pick = np.array([1499, 0, 700, 3, 3, 1024, 58], np.int32)
+    outs = []
+    for n, row_map in ((rows, None), (len(pick), pick)):
+        out = torch.zeros((n, H), dtype=tdt, device="cuda")
+        dmap = torch.from_numpy(row_map).cuda() if row_map is not None else None
+        sb.sb_op_norm(DT[dtype], kind, n, H, dx.data_ptr(), dmap.data_ptr() if dmap is not None else None,
+                      dg.data_ptr(), dbb.data_ptr() if dbb is not None else None, 1e-5, out.data_ptr(),
+                      stream_handle())
+        _sync()
+        outs.append(out.view(torch.int32 if dtype == "fp32" else torch.int16).cpu())
+    assert torch.equal(outs[0][torch.from_numpy(pick).long()], outs[1])
 
 
 # ---------------------------------------------------------------- argmax
