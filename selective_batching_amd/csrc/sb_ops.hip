@@ -314,9 +314,9 @@ __global__ __launch_bounds__(256) void norm_stream_kernel(const float* x, const 
 // K/V manager's arenas at the token's slot (k rotated there; qkv's k part is
 // left as it was).  A rotation item is 8 consecutive dims of one half-head with
 // the matching 8 of the other half (q heads with rotation, k heads always):
-// 16-byte accesses in bf16; v moves one element per lane.  Every thread issues
-// the loads of its first items before the token's cos/sin are evaluated, so the
-// double-precision evaluation overlaps the memory latency.
+// 16-byte accesses in bf16.  Every thread issues the loads of its first items
+// before the token's cos/sin are evaluated, so the double-precision evaluation
+// overlaps the memory latency.  V is appended per 8-slot block (below).
 constexpr int kRopeMaxHalf = 64;        // head_dim <= 128
 constexpr int kRopeItemsPerThread = 2;  // items a thread has in flight at once
 
@@ -368,21 +368,17 @@ __global__ __launch_bounds__(256) void rope_append_kernel(void* qkv, long long s
                                                           int D, int rope, double log_theta) {
     using T = typename Store<DT>::T;
     constexpr int IPT = kRopeItemsPerThread;
-    constexpr int VPT = 4;                                  // v elements a thread has in flight at once
     __shared__ float cs[kRopeMaxHalf], sn[kRopeMaxHalf];
-    const int t = blockIdx.x;
+    const int t = blockIdx.x, n_tok = gridDim.x;
     T* row = (T*)qkv + (long long)t * stride;
     T* K = (T*)kplane;
     T* V = (T*)vplane;
     const int half = D / 2, cph = half / 8;                 // 8-dim pieces per half-head
     const int h0 = rope ? 0 : nq;                           // first rotated head (q untouched without rotation)
     const int n_rot = (nq + nkv - h0) * cph;                // rotation items
-    const int n_v = nkv * D;                                // v elements
     const long long s = slot[t];
-    const T* vrow = row + (long long)(nq + nkv) * D;
     Piece8<DT> x1[IPT], x2[IPT];
-    T vv[VPT];
-    auto fetch = [&](int base, int vbase) {
+    auto fetch = [&](int base) {
 #pragma unroll
         for (int j = 0; j < IPT; ++j) {
             const int w = base + j * blockDim.x + threadIdx.x;
@@ -392,13 +388,8 @@ __global__ __launch_bounds__(256) void rope_append_kernel(void* qkv, long long s
                 x2[j] = ld_piece<DT>(p + half);
             }
         }
-#pragma unroll
-        for (int j = 0; j < VPT; ++j) {
-            const int u = vbase + j * blockDim.x + threadIdx.x;
-            if (u < n_v) vv[j] = vrow[u];
-        }
     };
-    auto process = [&](int base, int vbase) {
+    auto process = [&](int base) {
 #pragma unroll
         for (int j = 0; j < IPT; ++j) {
             const int w = base + j * blockDim.x + threadIdx.x;
@@ -421,18 +412,8 @@ __global__ __launch_bounds__(256) void rope_append_kernel(void* qkv, long long s
             st_piece<DT>(p, y1);
             st_piece<DT>(p + half, y2);
         }
-        // v into the blocked layout [slot / 8][dim][slot % 8]: one element per lane, consecutive lanes
-        // on consecutive dims, so a wave's stores fall in 64 consecutive 16-byte rows (8 lines)
-#pragma unroll
-        for (int j = 0; j < VPT; ++j) {
-            const int u = vbase + j * blockDim.x + threadIdx.x;
-            if (u < n_v) {
-                const int g = u / D, e = u % D;
-                V[(long long)g * arena * D + (((s >> 3) * D + e) << 3) + (s & 7)] = vv[j];
-            }
-        }
     };
-    fetch(0, 0);
+    fetch(0);
     if (rope) {
         for (int i = threadIdx.x; i < half; i += blockDim.x) {
             const double inv = exp(-(2.0 * i / D) * log_theta);
@@ -443,11 +424,49 @@ __global__ __launch_bounds__(256) void rope_append_kernel(void* qkv, long long s
         }
         __syncthreads();
     }
-    process(0, 0);
-    for (int base = IPT * blockDim.x, vbase = VPT * blockDim.x; base < n_rot || vbase < n_v;
-         base += IPT * blockDim.x, vbase += VPT * blockDim.x) {
-        fetch(base, vbase);
-        process(base, vbase);
+    process(0);
+    for (int base = IPT * blockDim.x; base < n_rot; base += IPT * blockDim.x) {
+        fetch(base);
+        process(base);
+    }
+
+    // v into the blocked layout [slot / 8][dim][slot % 8].  A request's new tokens sit in consecutive
+    // rows at consecutive slots, and slots are unique, so the rows after t holding slots s + 1, s + 2,
+    // ... are that request's next tokens.  The token opening such a run inside one 8-slot block (its
+    // slot opens the block, or the row before is not the slot before) appends the run's n (<= 8)
+    // tokens: a whole block as one 16-byte piece per (head, dim) -- consecutive lanes on consecutive
+    // dims, so a wave writes 1 KB of whole lines -- a partial one element by element.
+    const int sl = (int)(s & 7);
+    const bool lead = sl == 0 || t == 0 || slot[t - 1] != s - 1;
+    if (!lead) return;
+    int nxt[7];
+#pragma unroll
+    for (int j = 1; j < 8; ++j) nxt[j - 1] = slot[min(t + j, n_tok - 1)];
+    int n = 1;
+#pragma unroll
+    for (int j = 1; j < 8; ++j)
+        if (n == j && sl + j < 8 && t + j < n_tok && nxt[j - 1] == s + j) n = j + 1;
+    const T* vr = row + (long long)(nq + nkv) * D;          // v of row t; of row t + j at + j * stride
+    T* vb = V + ((s >> 3) * D << 3);                         // the block, K/V head 0
+    for (int u = threadIdx.x; u < nkv * D; u += blockDim.x) {
+        const int g = u / D, e = u % D;
+        T* dst = vb + (long long)g * arena * D + (e << 3);
+        if (n == 8) {
+            T v8[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v8[j] = vr[u + j * stride];
+            if constexpr (DT == SB_BF16) {
+                u32x4 w;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) w[c] = (uint32_t)v8[2 * c] | ((uint32_t)v8[2 * c + 1] << 16);
+                *(u32x4*)dst = w;
+            } else {
+                *(float4*)dst = make_float4(v8[0], v8[1], v8[2], v8[3]);
+                *(float4*)(dst + 4) = make_float4(v8[4], v8[5], v8[6], v8[7]);
+            }
+        } else {
+            for (int j = 0; j < n; ++j) dst[sl + j] = vr[u + j * stride];
+        }
     }
 }
 
