@@ -372,8 +372,8 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     const int req = it[ITEM_REQ], kvh = it[ITEM_KVH], mode = it[ITEM_MODE];
     const int row0 = it[ITEM_ROW0], nrows = it[ITEM_NROWS];
     const int kb = it[ITEM_KB], ke = it[ITEM_KE], part0 = it[ITEM_PART];
-    const int tok0 = a.cu[req], ctx = a.ctx[req];
-    const long long kslot0 = (long long)a.tok_slot[tok0] - ctx;   // slot of key 0 of this request
+    const int tok0 = it[ITEM_TOK0], ctx = it[ITEM_CTX];
+    const long long kslot0 = it[ITEM_SLOT0];                      // slot of key 0 of this request
     const T* Kp = (const T*)a.K + (long long)kvh * a.arena * D;
     const T* Vp = (const T*)a.V + (long long)kvh * a.arena * D;
 
@@ -585,7 +585,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, const int
     const int* gp = groups + (long long)blockIdx.x * kGroupInts;
     const int req = gp[GRP_REQ], kvh = gp[GRP_KVH], row0 = gp[GRP_ROW0], nrows = gp[GRP_NROWS];
     const int p0 = gp[GRP_PART0], np = gp[GRP_NPARTS];
-    const int tok0 = a.cu[req];
+    const int tok0 = gp[GRP_TOK0];
     for (int idx = threadIdx.x; idx < 16 * D; idx += 256) {
         const int r = idx / D, e = idx % D;
         if (r >= nrows) break;

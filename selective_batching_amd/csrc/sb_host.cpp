@@ -725,7 +725,8 @@ extern "C" int sb_ragged_build(const sb_model_dims* dims, int32_t n_req, const i
     // request's keys, enough runs keep every CU busy.  Only the grouping depends on the batch.
     const int32_t upr = (int32_t)std::max<int64_t>(1, (n_units + sb::kTargetRuns - 1) / sb::kTargetRuns);
     int32_t n_part = 0;
-    for (int32_t i = 0; i < n_req; ++i) {
+    int32_t tok0 = 0;                               // the request's first row
+    for (int32_t i = 0; i < n_req; tok0 += n_new[i], ++i) {
         const int32_t rows = n_new[i] * G;          // (token, query head of the group) rows
         const int32_t nk = ctx[i] + n_new[i];       // keys visible to the last row
         for (int32_t g = 0; g < nkv; ++g) {
@@ -735,7 +736,7 @@ extern "C" int sb_ragged_build(const sb_model_dims* dims, int32_t n_req, const i
                 const int32_t nu = (nk + sb::kUnitKeys - 1) / sb::kUnitKeys;
                 const int32_t p0 = nu > upr ? n_part : -1;
                 if (p0 >= 0) {
-                    groups.push_back({i, g, 0, rows, p0, nu, 0, 0});
+                    groups.push_back({i, g, 0, rows, p0, nu, tok0, 0});
                     n_part += nu;
                 }
                 for (int32_t u = 0; u < nu; u += upr) {
@@ -748,6 +749,9 @@ extern "C" int sb_ragged_build(const sb_model_dims* dims, int32_t n_req, const i
                     it.v[sb::ITEM_KB] = u * sb::kUnitKeys;
                     it.v[sb::ITEM_KE] = std::min(nk, (u + upr) * sb::kUnitKeys);
                     it.v[sb::ITEM_PART] = p0 >= 0 ? p0 + u : -1;
+                    it.v[sb::ITEM_TOK0] = tok0;
+                    it.v[sb::ITEM_CTX] = ctx[i];
+                    it.v[sb::ITEM_SLOT0] = (int32_t)slot_base[i];
                     it.cost = it.v[sb::ITEM_KE] - it.v[sb::ITEM_KB];
                     items.push_back(it);
                 }
@@ -765,6 +769,9 @@ extern "C" int sb_ragged_build(const sb_model_dims* dims, int32_t n_req, const i
                     it.v[sb::ITEM_KB] = 0;
                     it.v[sb::ITEM_KE] = ctx[i] + last_tok + 1;
                     it.v[sb::ITEM_PART] = -1;
+                    it.v[sb::ITEM_TOK0] = tok0;
+                    it.v[sb::ITEM_CTX] = ctx[i];
+                    it.v[sb::ITEM_SLOT0] = (int32_t)slot_base[i];
                     it.cost = 4 * (int64_t)it.v[sb::ITEM_KE];
                     items.push_back(it);
                 }

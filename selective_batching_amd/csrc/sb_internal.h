@@ -36,11 +36,15 @@ constexpr int kWaves = 4;                 // waves per attention workgroup
 constexpr int kRowsPerTile = kRowsPerWave * kWaves;
 constexpr int kUnitKeys = 512;            // keys per independently reduced unit
 constexpr int kTargetRuns = 1024;         // runs per launch the builder aims at (balance vs. run length)
-constexpr int kItemInts = 8;
+// An item also carries its request's first row, cached-token count and slot base (the
+// request-level metadata a workgroup would otherwise fetch through two more dependent
+// loads before its first q/K/V load); a group carries the request's first row.
+constexpr int kItemInts = 12;
 constexpr int kGroupInts = 8;
-enum { ITEM_REQ = 0, ITEM_KVH, ITEM_MODE, ITEM_ROW0, ITEM_NROWS, ITEM_KB, ITEM_KE, ITEM_PART };
+enum { ITEM_REQ = 0, ITEM_KVH, ITEM_MODE, ITEM_ROW0, ITEM_NROWS, ITEM_KB, ITEM_KE, ITEM_PART,
+       ITEM_TOK0, ITEM_CTX, ITEM_SLOT0 };
 enum { MODE_ROWS = 0, MODE_RUNS = 1 };
-enum { GRP_REQ = 0, GRP_KVH, GRP_ROW0, GRP_NROWS, GRP_PART0, GRP_NPARTS };
+enum { GRP_REQ = 0, GRP_KVH, GRP_ROW0, GRP_NROWS, GRP_PART0, GRP_NPARTS, GRP_TOK0 };
 
 // Upper bound of the units (and so of the partials and runs) of a batch of at most B requests holding
 // `keys` keys in all, per K/V head: every request adds at most one short unit.

@@ -445,6 +445,7 @@ def test_ragged_metadata_pinned_batches(name):
 
 
 UNIT = 512   # keys per independently reduced unit (the library's kUnitKeys)
+ITEM_INTS = 12   # ints per attention work item (the library's kItemInts)
 
 
 def _coverage(m, batch, rg):
@@ -452,10 +453,14 @@ def _coverage(m, batch, rg):
     (mode 0) and runs of whole key units (mode 1); a request split over several runs leaves one partial per
     unit, named in order by one combine group."""
     G = m.nq // m.nkv
-    items = _arr(rg.items, rg.n_items * 8).reshape(-1, 8)
+    items = _arr(rg.items, rg.n_items * ITEM_INTS).reshape(-1, ITEM_INTS)
+    cu = FL.cu_seqlens(batch)
+    slots = _arr(rg.tok_slot, rg.n_tokens)
     spans = {}          # (request, kv head, row) -> key intervals seen by that row
-    for req, kvh, mode, row0, nrows, kb, ke, part in items:
+    for req, kvh, mode, row0, nrows, kb, ke, part, tok0, ctx_i, slot0, _ in items:
         n_new, ctx = batch[req]
+        # the request's first row, cached tokens and slot base, carried by the item
+        assert tok0 == cu[req] and ctx_i == ctx and slot0 == slots[cu[req]] - ctx
         assert 0 <= kb < ke <= n_new + ctx
         if mode == 0:
             assert nrows <= 64 and kb == 0 and part == -1
@@ -478,13 +483,14 @@ def _coverage(m, batch, rg):
     assert not spans
     groups = _arr(rg.groups, rg.n_groups * 8).reshape(-1, 8)
     p0 = {}
-    for req, kvh, row0, nrows, gp0, np_, _, _ in groups:
+    for req, kvh, row0, nrows, gp0, np_, tok0, _ in groups:
         n_new, ctx = batch[req]
+        assert tok0 == cu[req]
         assert np_ == -(-(n_new + ctx) // UNIT) > 1 and row0 == 0 and nrows == n_new * G
         p0[(req, kvh)] = gp0
     assert sorted(int(g[4]) + u for g in groups for u in range(g[5])) == list(range(rg.n_partials))
     runs = items[items[:, 2] == 1]
-    for req, kvh, _, _, _, kb, ke, part in runs:
+    for req, kvh, _, _, _, kb, ke, part in runs[:, :8]:
         if part >= 0:       # one of several runs of the request: partials of its units, in unit order
             assert part == p0[(req, kvh)] + kb // UNIT
         else:               # the run covers all of the request's units
@@ -504,7 +510,7 @@ def test_attention_work_list_llama_mixed_batch_counts():
     rg, buf, _ = host_ragged(LLAMA8B, "bf16", batch)
     assert rg.n_req == 256 and rg.n_tokens == sum(n for n, _ in batch)
     _coverage(LLAMA8B, batch, rg)
-    items = _arr(rg.items, rg.n_items * 8).reshape(-1, 8)
+    items = _arr(rg.items, rg.n_items * ITEM_INTS).reshape(-1, ITEM_INTS)
     cost = np.where(items[:, 2] == 0, 4 * items[:, 6], items[:, 6] - items[:, 5])
     assert np.all(np.diff(cost) <= 0)                       # heaviest first
     # at this size every decode's units fit one run: no partials, no combine
