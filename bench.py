@@ -142,7 +142,7 @@ def kernel_roofline(m, work, brk):
     hbm_bytes = {
         "attention": work["attn_bytes_per_layer"] * L,
         "norm": (2 * L * T + B) * H * (4 + 2),                               # fp32 row in, bf16 row out
-        "rope_append": L * T * ((m.nq + 2 * m.nkv) * m.d * 2 + (m.nq + m.nkv) * m.d * 2 + 2 * m.nkv * m.d * 2),
+        "rope_append": L * T * (m.nq + 2 * m.nkv) * m.d * 2 * 2,            # q, k, v read; q, k, v written
         "embed": T * H * (2 + 4),
         "argmax": B * m.V * 4,
     }
@@ -152,6 +152,61 @@ def kernel_roofline(m, work, brk):
         gbs = byts / (brk[name]["ms_per_step"] * 1e-3) / 1e9
         out[name] = {"bound": "hbm", "gbs": round(gbs, 1), "frac_of_peak": round(gbs * 1e9 / bw, 4)}
     return out
+
+
+def decode_attention(m, batch, seed, launches=20):
+    """The attention kernel alone on the iteration's decodes (one layer: 240 requests, ctx U[128,2048]):
+    algorithmic bytes (every cached K/V row once, q in, o out) over the average launch time, HIP events
+    on the launch stream, K/V arenas random-filled and larger than the caches."""
+    import torch
+    import selective_batching_amd as sb
+    from selective_batching_amd import api as A
+    from selective_batching_amd.runtime import make_dims, stream_handle
+    dec = [(n, c) for n, c in batch if n == 1]
+    one = m.with_layers(1)
+    dims = make_dims(one, "bf16")
+    n_slots = sum(n + c for n, c in dec) + 8 * len(dec)
+    arena = A.sb_kv_arena_slots(n_slots, len(dec))
+    nbytes = A.sb_kv_arena_bytes(arena, 1, m.nkv, m.d, sb.SB_BF16)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed + 7)
+    ka = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda").normal_(generator=g)
+    va = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda").normal_(generator=g)
+    kv = A.sb_kv_create(n_slots, arena, 1, m.nkv, m.d, sb.SB_BF16, ka.data_ptr(), va.data_ptr())
+    try:
+        bases = [A.sb_kv_reserve(kv, i, n + c) for i, (n, c) in enumerate(dec)]
+        T = len(dec)
+        mb = A.sb_ragged_bytes(dims, len(dec), T, n_slots)
+        staging = torch.empty(mb, dtype=torch.uint8, pin_memory=True)
+        meta = torch.empty(mb, dtype=torch.uint8, device="cuda")
+        s = stream_handle()
+        rg = A.sb_ragged_build(dims, [n for n, _ in dec], [c for _, c in dec], bases, None, staging.data_ptr(),
+                               meta.data_ptr(), mb, s)
+        qkv = (torch.randn(T, m.qkv_out, device="cuda", generator=g) * 0.5).to(torch.bfloat16)
+        o = torch.empty(T, m.nq * m.d, dtype=torch.bfloat16, device="cuda")
+        ws = torch.empty(max(rg.n_partials, 1) * 16 * (m.d + 2) * 4, dtype=torch.uint8, device="cuda")
+
+        def run():
+            A.sb_op_attention(dims, rg, kv, 0, qkv.data_ptr(), o.data_ptr(), ws.data_ptr(), ws.numel(), s)
+        for _ in range(5):
+            run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(launches):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / launches
+    finally:
+        A.sb_kv_destroy(kv)
+    kv_bytes = sum((c + 1) * 2 * m.nkv * m.d * 2 for _, c in dec)
+    byts = kv_bytes + T * m.nq * m.d * 2 * 2
+    gbs = byts / (ms * 1e-3) / 1e9
+    return {"workload": f"attention alone over the {T} decodes of the batch (one layer, ctx U[128,2048], bf16)",
+            "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "avg_launch_ms": round(ms, 4), "bytes_per_launch": byts,
+            "launches": launches}
 
 
 def cpu_baseline(m, batch, seed):
@@ -595,6 +650,8 @@ def main():
         "kernels_ms_per_step": {k: round(v["ms_per_step"], 3) for k, v in brk.items()},
         "kernel_roofline": kernel_roofline(m, work, brk),
     }
+    print("[bench] decode attention alone ...", file=sys.stderr, flush=True)
+    out["decode_attention"] = decode_attention(m, batch, args.seed)
     if not args.no_trace:
         print("[bench] serving trace (chained) ...", file=sys.stderr, flush=True)
         out["trace"] = trace_run(W, m, args.seed)
