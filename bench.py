@@ -413,7 +413,9 @@ def trace_run(W, m, seed, iters=600, steady_from=200):
     marks = []
 
     def on_it(res):
-        torch.cuda.synchronize()            # (already settled: its ids are on the host)
+        # settled: its ids are on the host.  No device-wide wait here -- the next iteration is already
+        # queued behind it, and waiting for that one would leave the GPU idle while the host launches
+        # the one after.
         marks.append((time.perf_counter(), int(res["n_new"].sum()), len(res["ids"])))
 
     t0 = time.perf_counter()
