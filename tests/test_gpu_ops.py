@@ -237,6 +237,66 @@ def test_attention_random_ragged(m, dtype, seed):
     _attention_case(m, dtype, batch, seed + 10)
 
 
+# new tokens that start, end and straddle 8-slot blocks of the blocked V layout: decodes sharing a block
+# with their history, prompts filling whole blocks, runs crossing one or two block edges
+BLOCK_EDGES = [(1, 7), (1, 8), (1, 15), (8, 0), (9, 7), (17, 3), (3, 5), (16, 16), (1, 0), (7, 1), (24, 8)]
+
+
+@pytest.mark.parametrize("m,dtype", [(GQA_BF16, "bf16"), (GQA_F32, "fp32"), (TINY_F32, "fp32")])
+def test_attention_append_block_edges(m, dtype):
+    _attention_case(m, dtype, BLOCK_EDGES, 21, rope_check=m.arch == "llama")
+
+
+@pytest.mark.parametrize("m,dtype", [(GQA_BF16, "bf16"), (TINY_F32, "fp32")])
+def test_append_writes_only_its_slots(m, dtype):
+    """RoPE/append writes each new token's K and V at its own slot and nowhere else: every other slot of
+    the arenas (history, reserved but unused, unreserved) keeps its bytes."""
+    print_case("append slots", m.name, dtype)
+    dims = make_dims(m, dtype)
+    batch = BLOCK_EDGES
+    n_slots = sum(n + c + 9 for n, c in batch) + 64
+    arena = sb.sb_kv_arena_slots(n_slots, len(batch))
+    nbytes = sb.sb_kv_arena_bytes(arena, 1, m.nkv, m.d, DT[dtype])
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5)
+    ka = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device="cuda", generator=g)
+    va = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device="cuda", generator=g)
+    ka0, va0 = ka.cpu(), va.cpu()
+    kv = sb.sb_kv_create(n_slots, arena, 1, m.nkv, m.d, DT[dtype], ka.data_ptr(), va.data_ptr())
+    try:
+        bases = [sb.sb_kv_reserve(kv, i, n + c + 9) for i, (n, c) in enumerate(batch)]   # 9 spare slots each
+        T = sum(n for n, _ in batch)
+        qkv = normal(9, "qkv", (T, m.qkv_out), dtype=dtype)
+        mb = sb.sb_ragged_bytes(dims, len(batch), T, n_slots)
+        staging = torch.empty(mb, dtype=torch.uint8, pin_memory=True)
+        meta = torch.empty(mb, dtype=torch.uint8, device="cuda")
+        rg = sb.sb_ragged_build(dims, [n for n, _ in batch], [c for _, c in batch], bases, None, staging.data_ptr(),
+                                meta.data_ptr(), mb, stream_handle())
+        dqkv = dev(qkv, dtype)
+        sb.sb_op_rope_append(dims, rg, kv, 0, dqkv.data_ptr(), stream_handle())
+        _sync()
+        new = set(b + c + j for b, (n, c) in zip(bases, batch) for j in range(n))
+        es = 2 if dtype == "bf16" else 4
+        row = m.d * es                                       # bytes of one slot of one K/V head
+        k1, v1 = ka.cpu(), va.cpu()
+        # K: [kv head][slot][d]; V: [kv head][slot / 8][d][slot % 8]
+        kmask = np.zeros(nbytes, bool)
+        vmask = np.zeros(nbytes, bool)
+        for h in range(m.nkv):
+            for s in new:
+                kmask[(h * arena + s) * row:(h * arena + s + 1) * row] = True
+                blk = (h * arena * m.d + (s // 8) * m.d * 8) * es
+                for e in range(m.d):
+                    o = blk + (e * 8 + s % 8) * es
+                    vmask[o:o + es] = True
+        kchg = (k1.numpy() != ka0.numpy())
+        vchg = (v1.numpy() != va0.numpy())
+        assert not np.any(kchg & ~kmask), "K bytes changed outside the new tokens' slots"
+        assert not np.any(vchg & ~vmask), "V bytes changed outside the new tokens' slots"
+    finally:
+        sb.sb_kv_destroy(kv)
+
+
 def test_attention_decode_only():
     _attention_case(MINI_ATT, "bf16", [(1, 100), (1, 17), (1, 256), (1, 31), (1, 32)], 7)
     _attention_case(MINI_ATT, "fp32", [(1, 100), (1, 17), (1, 256), (1, 31), (1, 32)], 7)
