@@ -124,11 +124,13 @@ __device__ __forceinline__ void softmax_chunk(float (&sc)[8], float& m, float& l
         for (int i = 0; i < 8; ++i) sc[i] = 0.f;
         return;
     }
-    alpha = exp2f(m - mn);               // m == -inf -> 0
+    // the hardware exp2 directly: arguments are <= 0, so results only differ from the library's below
+    // 2^-126, where a probability adds nothing to the sums
+    alpha = __builtin_amdgcn_exp2f(m - mn);       // m == -inf -> 0
     float sum = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        sc[i] = exp2f(sc[i] - mn);       // -inf -> 0
+        sc[i] = __builtin_amdgcn_exp2f(sc[i] - mn);   // -inf -> 0
         sum += sc[i];
     }
     l = l * alpha + sum;
@@ -139,10 +141,17 @@ __device__ __forceinline__ void softmax_chunk(float (&sc)[8], float& m, float& l
 // Keys of a 32-key chunk starting at key cb: S^T block b covers local keys
 // 8*(m/4) + 4*b + (m%4) for MFMA row m, so that lane (g = lane/16) ends up
 // with keys 8g..8g+7 -- exactly the P^T operand layout of the 16x16x32 MFMA.
+// Staged K tile rows keep their 16-byte pieces at position piece ^ k_swz(row): the 16 rows one
+// operand read touches (keys 8(m/4) + 4b + m%4, m < 16) then sit in 16 different bank groups.
+template <int D>
+__device__ __forceinline__ int k_swz(int row) {
+    return ((row & 3) | ((row >> 1) & 12)) & (D / 8 - 1);
+}
+
 template <int D>
 __device__ __forceinline__ void chunk_bf16(const AttnArgs& a, WaveState<D>& st, const bf16x8 (&qf)[D / 32], int cb,
-                                           int key_end, int row_limit, int lane, const uint16_t* ldsK,
-                                           const uint16_t* ldsV) {
+                                           int key_end, int row_limit, int all_visible, int lane,
+                                           const uint16_t* ldsK, const uint16_t* ldsV) {
     const int lr = lane & 15, g = lane >> 4;
     float sc[8];
 #pragma unroll
@@ -151,14 +160,19 @@ __device__ __forceinline__ void chunk_bf16(const AttnArgs& a, WaveState<D>& st, 
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < D / 32; ++s) {
-            const u32x4 kraw = *(const u32x4*)(ldsK + kl * (D + 8) + s * 32 + g * 8);
+            const u32x4 kraw = *(const u32x4*)(ldsK + kl * D + (((4 * s + g) ^ k_swz<D>(kl)) << 3));
             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kraw), qf[s], acc, 0, 0, 0);
         }
-        // acc[r]: key cb + 8g + 4b + r, row lr
+        // acc[r]: key cb + 8g + 4b + r, row lr; a chunk every row of the wave sees whole needs no test
+        if (cb + 32 <= all_visible) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int k = cb + 8 * g + 4 * b + r;
-            sc[4 * b + r] = (k < key_end && k < row_limit) ? acc[r] * a.scale_log2 : kNegInf;
+            for (int r = 0; r < 4; ++r) sc[4 * b + r] = acc[r] * a.scale_log2;
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int k = cb + 8 * g + 4 * b + r;
+                sc[4 * b + r] = (k < key_end && k < row_limit) ? acc[r] * a.scale_log2 : kNegInf;
+            }
         }
     }
     // V^T operand: V[keys cb+8g .. +8][dim 16db + lr] = 16 contiguous bytes of the staged tile
@@ -204,7 +218,8 @@ __device__ __forceinline__ void load_chunk_bf16(ChunkRegs<D>& r, const uint16_t*
 
 template <int D>
 __device__ __forceinline__ void compute_chunk_bf16(const AttnArgs& a, WaveState<D>& st, const bf16x8 (&qf)[D / 32],
-                                                   const ChunkRegs<D>& r, int cb, int key_end, int row_limit, int lane) {
+                                                   const ChunkRegs<D>& r, int cb, int key_end, int row_limit,
+                                                   int all_visible, int lane) {
     const int lr = lane & 15, g = lane >> 4;
     (void)lr;
     float sc[8];
@@ -214,10 +229,15 @@ __device__ __forceinline__ void compute_chunk_bf16(const AttnArgs& a, WaveState<
 #pragma unroll
         for (int s = 0; s < D / 32; ++s)
             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, r.k[b][s]), qf[s], acc, 0, 0, 0);
+        if (cb + 32 <= all_visible) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int k = cb + 8 * g + 4 * b + q;
-            sc[4 * b + q] = (k < key_end && k < row_limit) ? acc[q] * a.scale_log2 : kNegInf;
+            for (int q = 0; q < 4; ++q) sc[4 * b + q] = acc[q] * a.scale_log2;
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int k = cb + 8 * g + 4 * b + q;
+                sc[4 * b + q] = (k < key_end && k < row_limit) ? acc[q] * a.scale_log2 : kNegInf;
+            }
         }
     }
     float alpha;
@@ -358,7 +378,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     constexpr int KT = 64;                                   // keys per LDS stage (MODE_ROWS)
     // MODE_ROWS stages K/V tiles; MODE_RUNS merges wave states: one workgroup
     // uses only one of the two, so they share the LDS allocation.
-    constexpr int LDS_K = (DT == SB_BF16) ? 2 * KT * (D + 8) : 0;
+    constexpr int LDS_K = (DT == SB_BF16) ? 2 * KT * D : 0;
     constexpr int LDS_V = (DT == SB_BF16) ? 2 * (KT / 8) * (D * 8 + 16) : 0;
     constexpr int BYTES_ROWS = (LDS_K + LDS_V) * 2;
     constexpr int BYTES_RED = (kWaves * 16 * (D + 1) + 2 * kWaves * 16) * 4;
@@ -384,6 +404,8 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     const int tok = row_ok ? row / a.G : 0;
     const int head = kvh * a.G + (row_ok ? row % a.G : 0);
     const int row_limit = row_ok ? ctx + tok + 1 : 0;             // keys 0..ctx+tok are visible
+    // keys below this are visible to every row of the wave (its first row has the fewest)
+    const int all_visible = min(ke, ctx + wrow0 / a.G + 1);
     const T* qrow = (const T*)a.qkv + (long long)(tok0 + tok) * a.qkv_stride + (long long)head * D;
 
     WaveState<D> st;
@@ -447,7 +469,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
                     // issued whether or not a next chunk exists (then it re-reads this one): an
                     // unconditional load lets the compiler keep it in flight during the compute
                     load_chunk_bf16<D>(nxt, Kb, Vb, kslot0, nb < ke ? nb : cb, ke, lane);
-                    compute_chunk_bf16<D>(a, st, qf, cur, cb, ke, row_limit, lane);
+                    compute_chunk_bf16<D>(a, st, qf, cur, cb, ke, row_limit, all_visible, lane);
                     cur = nxt;
                     cb = nb;
                 }
@@ -474,7 +496,8 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
         return;
     }
 
-    // MODE_ROWS: stage 32-key tiles of K (row-major, padded rows) and V (8-key blocks, padded) in LDS
+    // MODE_ROWS: stage 64-key tiles of K (row-major, 16-byte pieces swizzled by row) and V (8-key
+    // blocks, padded) in LDS
     if constexpr (DT == SB_BF16) {
         bf16x8 qf[D / 32];
 #pragma unroll
@@ -486,7 +509,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
         const int ntiles = (ke - kb + KT - 1) / KT;
         constexpr int KCH = KT * D / 8;                    // 16-byte chunks per K tile (and per V tile)
         constexpr int PER = (KCH + 255) / 256;
-        constexpr int KSTR = KT * (D + 8), VSTR = (KT / 8) * (D * 8 + 16);   // one LDS buffer
+        constexpr int KSTR = KT * D, VSTR = (KT / 8) * (D * 8 + 16);         // one LDS buffer
         struct Stage { u32x4 k[PER], v[PER]; };
         // global loads of tile t (clamped to the last tile: the loads are issued unconditionally
         // so the compiler keeps them in flight across the compute of the tiles before)
@@ -514,7 +537,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
                 const int c = tid + 256 * q;
                 if (c < KCH) {
                     const int kk = c / (D / 8), dc = (c % (D / 8)) * 8;
-                    *(u32x4*)(ldsK + buf * KSTR + kk * (D + 8) + dc) = r.k[q];
+                    *(u32x4*)(ldsK + buf * KSTR + kk * D + (((dc >> 3) ^ k_swz<D>(kk)) << 3)) = r.k[q];
                     const int vb = c / D, vd = c % D;
                     u32x4 vv = r.v[q];
                     const int kv0 = k0 + vb * 8;
@@ -534,7 +557,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
             for (int h = 0; h < KT / 32; ++h) {
                 const int k0 = kb + t * KT + 32 * h;
                 if (k0 < wave_max_limit)
-                    chunk_bf16<D>(a, st, qf, k0, ke, row_limit, lane, ldsK + buf * KSTR + 32 * h * (D + 8),
+                    chunk_bf16<D>(a, st, qf, k0, ke, row_limit, all_visible, lane, ldsK + buf * KSTR + 32 * h * D,
                                   ldsV + buf * VSTR + 4 * h * (D * 8 + 16));
             }
         };
