@@ -97,8 +97,8 @@ __global__ __launch_bounds__(256) void embed_kernel(const int* ids, const int* p
     }
 }
 
-// Four / eight consecutive elements of a dtype row as one 8- or 16-byte access (bf16) or
-// one / two 16-byte accesses (fp32); the pointer is aligned to the access.
+// Four consecutive elements of a dtype row as one 8-byte access (bf16) or one 16-byte access
+// (fp32); the pointer is aligned to the access.
 template <int DT>
 __device__ __forceinline__ void load4(const typename Store<DT>::T* p, float (&v)[4]) {
     if constexpr (DT == SB_BF16) {
@@ -118,20 +118,6 @@ __device__ __forceinline__ void store4(typename Store<DT>::T* p, const float (&v
     } else {
         *(float4*)p = make_float4(v[0], v[1], v[2], v[3]);
     }
-}
-template <int DT>
-__device__ __forceinline__ void load8(const typename Store<DT>::T* p, float (&v)[8]) {
-    float a[4], b[4];
-    load4<DT>(p, a);
-    load4<DT>(p + 4, b);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) { v[c] = a[c]; v[4 + c] = b[c]; }
-}
-template <int DT>
-__device__ __forceinline__ void store8(typename Store<DT>::T* p, const float (&v)[8]) {
-    const float a[4] = {v[0], v[1], v[2], v[3]}, b[4] = {v[4], v[5], v[6], v[7]};
-    store4<DT>(p, a);
-    store4<DT>(p + 4, b);
 }
 
 // LayerNorm (kind 0) or RMSNorm (kind 1) of fp32 rows into dtype rows; fp32
