@@ -488,6 +488,29 @@ def test_generation_chained_bf16_trace_matches_synchronous():
     assert got == sync
 
 
+def test_llama8b_trace_requests_equal_solo_generation():
+    """The 8B-shaped model (32 layers, GQA 32/8, SwiGLU 14336, vocab 128256; random init, bf16) on a Poisson
+    trace with the serving trace's prompt lengths (U[32,512]) and short outputs, chained: iterations mix
+    prefills over hundreds of rows (the FFN1 GEMM on the big tiles, the norms of more than 1024 rows
+    streamed by waves) with decodes.  Requests generated again alone afterwards -- a prompt, then single
+    rows: the small-problem tiles and a workgroup per norm row -- give bitwise the same ids."""
+    from synth import poisson_trace
+    m = LLAMA8B
+    W = DeviceWeights(m, "bf16", host=None, seed=0)
+    reqs = poisson_trace(seed=12, n=24, rate=2.5, vocab=m.V, plo=32, phi=512, olo=2, ohi=10, reserve_out=10,
+                         with_prompts=True)
+    print_case("8b trace vs solo", len(reqs))
+    n_slots = sum(r.max_tokens for r in reqs) + 8 * len(reqs)
+    got, log = _gpu_generate_chained(m, "bf16", W, reqs, 16, n_slots)
+    rows = [sum(n for _, n, _ in w) for _, w in log]
+    assert max(rows) > 1024                          # some iterations took the large-batch kernels
+    assert all(len(got[r.rid]) == r.out_len and all(0 <= t < m.V for t in got[r.rid]) for r in reqs)
+    for r in (reqs[0], reqs[len(reqs) // 2], reqs[-1]):
+        alone = Req(r.rid, 0.0, r.prompt, r.out_len, r.max_tokens)
+        solo, _ = _gpu_generate_chained(m, "bf16", W, [alone], 1, n_slots)
+        assert solo[r.rid] == got[r.rid], f"request {r.rid}: trace {got[r.rid]} alone {solo[r.rid]}"
+
+
 @pytest.mark.parametrize("chunking", [(4, 2), (6, 3)])
 def test_chunked_prefill_generation_matches_oracle(chunking):
     """Toy fp32 model, Figure-5 requests with prompts fed in chunks under a token budget: the GPU's
