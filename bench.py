@@ -154,25 +154,26 @@ def kernel_roofline(m, work, brk):
     return out
 
 
-def decode_attention(m, batch, seed, launches=20):
-    """The attention kernel alone on the iteration's decodes (one layer: 240 requests, ctx U[128,2048]):
-    algorithmic bytes (every cached K/V row once, q in, o out) over the average launch time, HIP events
-    on the launch stream, K/V arenas random-filled and larger than the caches."""
+def decode_attention(m, batch, seed, launches=20, layers=4):
+    """The attention kernel alone on the iteration's decodes (240 requests, ctx U[128,2048]): algorithmic
+    bytes (every cached K/V row once, q in, o out) over the average launch time, HIP events on the launch
+    stream.  The launches cycle through ``layers`` layers of random-filled K/V arenas (~1.1 GB each), so
+    that, as in the iteration, a launch finds none of its K/V in the caches."""
     import torch
     import selective_batching_amd as sb
     from selective_batching_amd import api as A
     from selective_batching_amd.runtime import make_dims, stream_handle
     dec = [(n, c) for n, c in batch if n == 1]
-    one = m.with_layers(1)
+    one = m.with_layers(layers)
     dims = make_dims(one, "bf16")
     n_slots = sum(n + c for n, c in dec) + 8 * len(dec)
     arena = A.sb_kv_arena_slots(n_slots, len(dec))
-    nbytes = A.sb_kv_arena_bytes(arena, 1, m.nkv, m.d, sb.SB_BF16)
+    nbytes = A.sb_kv_arena_bytes(arena, layers, m.nkv, m.d, sb.SB_BF16)
     g = torch.Generator(device="cuda")
     g.manual_seed(seed + 7)
     ka = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda").normal_(generator=g)
     va = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda").normal_(generator=g)
-    kv = A.sb_kv_create(n_slots, arena, 1, m.nkv, m.d, sb.SB_BF16, ka.data_ptr(), va.data_ptr())
+    kv = A.sb_kv_create(n_slots, arena, layers, m.nkv, m.d, sb.SB_BF16, ka.data_ptr(), va.data_ptr())
     try:
         bases = [A.sb_kv_reserve(kv, i, n + c) for i, (n, c) in enumerate(dec)]
         T = len(dec)
@@ -186,15 +187,15 @@ def decode_attention(m, batch, seed, launches=20):
         o = torch.empty(T, m.nq * m.d, dtype=torch.bfloat16, device="cuda")
         ws = torch.empty(max(rg.n_partials, 1) * 16 * (m.d + 2) * 4, dtype=torch.uint8, device="cuda")
 
-        def run():
-            A.sb_op_attention(dims, rg, kv, 0, qkv.data_ptr(), o.data_ptr(), ws.data_ptr(), ws.numel(), s)
-        for _ in range(5):
-            run()
+        def run(i):
+            A.sb_op_attention(dims, rg, kv, i % layers, qkv.data_ptr(), o.data_ptr(), ws.data_ptr(), ws.numel(), s)
+        for i in range(5):
+            run(i)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        for _ in range(launches):
-            run()
+        for i in range(launches):
+            run(i)
         e1.record()
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / launches
@@ -203,7 +204,8 @@ def decode_attention(m, batch, seed, launches=20):
     kv_bytes = sum((c + 1) * 2 * m.nkv * m.d * 2 for _, c in dec)
     byts = kv_bytes + T * m.nq * m.d * 2 * 2
     gbs = byts / (ms * 1e-3) / 1e9
-    return {"workload": f"attention alone over the {T} decodes of the batch (one layer, ctx U[128,2048], bf16)",
+    return {"workload": (f"attention alone over the {T} decodes of the batch (ctx U[128,2048], bf16), launches "
+                         f"cycling through {layers} layers of K/V"),
             "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(gbs / HBM_PEAK_GBS, 4), "avg_launch_ms": round(ms, 4), "bytes_per_launch": byts,
             "launches": launches}
