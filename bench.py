@@ -55,6 +55,9 @@ def parse():
     ap.add_argument("--op-gemm", default=None, metavar="M,N,K,EPI",
                     help="instead of the iteration: time one bf16 GEMM of this shape (EPI: store, gelu, resid or "
                          "swiglu; N counts output columns) over --steps launches, for kernel-level profiling")
+    ap.add_argument("--gpt175b-layer", action="store_true",
+                    help="instead of the iteration: time one GPT-175B-shaped layer over its 96-decode + 32-prefill "
+                         "batch (per kernel class), --steps layer steps after --warmup")
     return ap.parse_args()
 
 
@@ -91,6 +94,77 @@ def op_gemm(spec, steps, warmup, seed):
     print(json.dumps({"op": "gemm_bf16", "M": M, "N": N, "K": K, "epilogue": epi, "launches": steps,
                       "avg_us": round(ms * 1e3, 2), "tflops": round(2.0 * M * rows * K / ms / 1e9, 1),
                       "weight_gbs": round(rows * K * 2 / ms / 1e6, 1)}), flush=True)
+
+
+def gpt175b_layer(steps, warmup, seed):
+    """One GPT-175B-shaped layer (H 12288, 96 heads x 128, FFN 49152 GeLU; random init, bf16) over its ragged
+    batch of 96 decodes (ctx U[512,2048]) + 32 prefills (prompt U[128,1024]) with random K/V history:
+    the layer step timed with HIP events, then the same steps with every kernel class timed."""
+    import torch
+    import selective_batching_amd as sb
+    from selective_batching_amd import api as A
+    from selective_batching_amd.runtime import DeviceWeights, Engine, stream_handle
+    from synth import GPT175B_LAYER, gpt175b_mixed_batch
+    torch.cuda.set_device(0)
+    m = GPT175B_LAYER
+    batch = gpt175b_mixed_batch(seed=seed)
+    T = sum(n for n, _ in batch)
+    W = DeviceWeights(m, "bf16", host=None, seed=seed, with_head=False)
+    n_slots = sum(n + c for n, c in batch) + 8 * len(batch)
+    eng = Engine(m, "bf16", W, n_slots=n_slots, max_bs=len(batch), max_tokens=T, max_keys_total=n_slots,
+                 zero_arena=False)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed + 1)
+    for a in (eng.k_arena, eng.v_arena):
+        a.view(torch.bfloat16).normal_(0.0, 1.0, generator=g)
+    bases = [A.sb_kv_reserve(eng.kv, i, n + c) for i, (n, c) in enumerate(batch)]
+    rg = eng.build([n for n, _ in batch], [c for _, c in batch], bases, None)
+    xv = eng.x[:T * m.H]
+    xv.copy_(torch.randn(T * m.H, device="cuda", generator=g))
+    s = stream_handle()
+
+    def run():
+        A.sb_layer_step(eng.dims, W.layer_structs[0], rg, eng.kv, 0, xv.data_ptr(), eng.ws.data_ptr(), eng.ws.numel(), s)
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    layer_ms = e0.elapsed_time(e1) / steps
+    A.sb_timing_reset()
+    A.sb_timing_enable(True)
+    for _ in range(steps):
+        run()
+    torch.cuda.synchronize()
+    A.sb_timing_enable(False)
+    cls = {}
+    for k, name in enumerate(sb.KERNEL_CLASSES):
+        ms, n = A.sb_timing_read(k)
+        if n:
+            cls[name] = ms / steps
+    A.sb_timing_reset()
+    eng.close()
+    flops = {"gemm_qkv": 2 * T * m.qkv_out * m.H, "gemm_o": 2 * T * m.H * m.nq * m.d, "gemm_ffn1": 2 * T * m.F * m.H,
+             "gemm_ffn2": 2 * T * m.H * m.F}
+    kv_row = 2 * m.nkv * m.d * 2
+    att_bytes = sum((c + n) * kv_row for n, c in batch) + T * m.nq * m.d * 2 * 2
+    att_flops = 4 * m.d * m.nq * sum(sum(c + j + 1 for j in range(n)) for n, c in batch)
+    gemm_ms = sum(cls[k] for k in flops)
+    print(json.dumps({
+        "workload": ("GPT-175B-shaped layer (hidden 12288, 96 heads x 128, FFN 49152 GeLU), random init, bf16; "
+                     "96 decodes (ctx U[512,2048]) + 32 prefills (prompt U[128,1024])"),
+        "tokens": T, "layer_ms": round(layer_ms, 3), "steps": steps, "warmup": warmup,
+        "classes_ms": {k: round(v, 4) for k, v in cls.items()},
+        "gemm_tflops": {k: round(v / (cls[k] * 1e-3) / 1e12, 1) for k, v in flops.items()},
+        "gemm_all": {"tflops": round(sum(flops.values()) / (gemm_ms * 1e-3) / 1e12, 1),
+                     "frac": round(sum(flops.values()) / (gemm_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)},
+        "attention": {"gbs": round(att_bytes / (cls["attention"] * 1e-3) / 1e9, 1), "bytes": att_bytes,
+                      "tflops": round(att_flops / (cls["attention"] * 1e-3) / 1e12, 1), "flops": att_flops},
+        "tokens_per_s": round(T / (layer_ms * 1e-3), 1)}), flush=True)
 
 
 def algorithmic_work(m, batch, n_layers):
@@ -501,6 +575,9 @@ def main():
 
     if args.op_gemm:
         op_gemm(args.op_gemm, args.steps, args.warmup, args.seed)
+        return
+    if args.gpt175b_layer:
+        gpt175b_layer(args.steps, args.warmup, args.seed)
         return
 
     import numpy as np
