@@ -246,7 +246,8 @@ typedef struct {
     const int32_t* tok_pos;        /* device [T]  position of each row               */
     const int32_t* tok_slot;       /* device [T]  K/V slot of each row               */
     const int32_t* tok_ids;        /* device [T]  token id of each row (or NULL)     */
-    const int32_t* items;          /* device [n_items][12] attention work list       */
+    const int32_t* items;          /* device [n_items][12] attention work list (items
+                                      with n_rows 0 are empty: dispatch-order padding)  */
     const int32_t* groups;         /* device [n_groups][8] unit-combine list         */
 } sb_ragged;
 

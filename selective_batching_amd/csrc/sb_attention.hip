@@ -392,6 +392,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     const int req = it[ITEM_REQ], kvh = it[ITEM_KVH], mode = it[ITEM_MODE];
     const int row0 = it[ITEM_ROW0], nrows = it[ITEM_NROWS];
     const int kb = it[ITEM_KB], ke = it[ITEM_KE], part0 = it[ITEM_PART];
+    if (nrows == 0) return;                      // an empty item (padding of the dispatch order)
     const int tok0 = it[ITEM_TOK0], ctx = it[ITEM_CTX];
     const long long kslot0 = it[ITEM_SLOT0];                      // slot of key 0 of this request
     const T* Kp = (const T*)a.K + (long long)kvh * a.arena * D;

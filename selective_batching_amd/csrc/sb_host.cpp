@@ -663,9 +663,14 @@ Layout layout_for(int64_t B, int64_t T, int64_t n_items, int64_t n_groups) {
 }
 
 // Row tiles: per (request, K/V head) ceil(rows / 64) <= rows / 64 + 1; runs: at most one per unit.
+constexpr int kXcds = 8;                  // XCDs of an MI355X; workgroups are dealt to them round-robin
+constexpr int64_t kItemStartCost = 256;   // start-up of a work item, in keys, for the dispatch order
+
+// Work items of a batch, empty padding items (at most a quarter of the others, plus kXcds) included.
 int64_t max_items_bound(const sb_model_dims* d, int64_t B, int64_t T, int64_t keys) {
     const int64_t g = d->n_heads / d->n_kv_heads, nkv = d->n_kv_heads;
-    return nkv * ((T * g) / sb::kRowsPerTile + B) + sb::max_units_bound(nkv, B, keys);
+    const int64_t n = nkv * ((T * g) / sb::kRowsPerTile + B) + sb::max_units_bound(nkv, B, keys);
+    return n + n / 4 + kXcds;
 }
 }  // namespace
 
@@ -713,7 +718,7 @@ extern "C" int sb_ragged_build(const sb_model_dims* dims, int32_t n_req, const i
     if (T >= (int64_t(1) << 31)) return fail(SB_ERR_INVALID, "too many tokens");
 
     // ---- attention work list (Split as offsets: each item names its request's rows and key range)
-    struct Item { int32_t v[sb::kItemInts]; int64_t cost; };
+    struct Item { int32_t v[sb::kItemInts]; int64_t cost, lane_cost; int32_t grp; };
     std::vector<Item> items;
     std::vector<std::array<int32_t, sb::kGroupInts>> groups;
     // units of the single-tile (request, K/V head) pairs, to size the runs
@@ -725,6 +730,7 @@ extern "C" int sb_ragged_build(const sb_model_dims* dims, int32_t n_req, const i
     // request's keys, enough runs keep every CU busy.  Only the grouping depends on the batch.
     const int32_t upr = (int32_t)std::max<int64_t>(1, (n_units + sb::kTargetRuns - 1) / sb::kTargetRuns);
     int32_t n_part = 0;
+    int32_t n_grp = 0;                              // locality groups: a request-head's row tiles, or one run
     int32_t tok0 = 0;                               // the request's first row
     for (int32_t i = 0; i < n_req; tok0 += n_new[i], ++i) {
         const int32_t rows = n_new[i] * G;          // (token, query head of the group) rows
@@ -753,10 +759,13 @@ extern "C" int sb_ragged_build(const sb_model_dims* dims, int32_t n_req, const i
                     it.v[sb::ITEM_CTX] = ctx[i];
                     it.v[sb::ITEM_SLOT0] = (int32_t)slot_base[i];
                     it.cost = it.v[sb::ITEM_KE] - it.v[sb::ITEM_KB];
+                    it.lane_cost = it.cost + kItemStartCost;
+                    it.grp = n_grp++;
                     items.push_back(it);
                 }
             } else {
                 // 64-row tiles; the four waves take 16 rows each and share K/V tiles through LDS
+                const int32_t rows_grp = n_grp++;
                 for (int32_t r0 = 0; r0 < rows; r0 += sb::kRowsPerTile) {
                     Item it{};
                     const int32_t nr = std::min(sb::kRowsPerTile, rows - r0);
@@ -773,13 +782,72 @@ extern "C" int sb_ragged_build(const sb_model_dims* dims, int32_t n_req, const i
                     it.v[sb::ITEM_CTX] = ctx[i];
                     it.v[sb::ITEM_SLOT0] = (int32_t)slot_base[i];
                     it.cost = 4 * (int64_t)it.v[sb::ITEM_KE];
+                    it.lane_cost = (int64_t)it.v[sb::ITEM_KE] + kItemStartCost;
+                    it.grp = rows_grp;
                     items.push_back(it);
                 }
             }
         }
     }
-    // heaviest items first so the long ones start early (ties keep build order)
-    std::stable_sort(items.begin(), items.end(), [](const Item& a, const Item& b) { return a.cost > b.cost; });
+    // Dispatch order.  By default heaviest items first (a row tile weighted 4 x its keys against a run's
+    // keys), so the long ones start early and the decode runs and prefill tiles interleave.  When the
+    // prefill tiles carry most of the work (long prompts), locality matters more: the row tiles of one
+    // request and K/V head re-read the same keys (each up to its own causal limit); workgroups are dealt to
+    // the kXcds XCDs round-robin by index, and each XCD has its own L2, so such a group is placed at
+    // indices of one residue mod kXcds: its tiles then run side by side on one XCD and share that L2.
+    // Groups go to the XCD lanes heaviest first, each to the least loaded lane (estimated cost: keys plus
+    // a start-up term); a lane runs its groups in that order, a group's tiles heaviest first.  Lanes are
+    // padded to one length with empty items (n_rows 0, skipped by the kernel); if that would take more
+    // than a quarter of the items, the heaviest-first order is kept.
+    int64_t rows_cost = 0, runs_cost = 0;
+    for (const Item& it : items) (it.v[sb::ITEM_MODE] == sb::MODE_ROWS ? rows_cost : runs_cost) += it.lane_cost;
+    bool lanes = rows_cost >= runs_cost && rows_cost > 0;
+    if (lanes) {
+        std::vector<int64_t> gcost(n_grp, 0);
+        for (const Item& it : items) gcost[it.grp] += it.lane_cost;
+        std::vector<int32_t> gorder(n_grp);
+        for (int32_t g = 0; g < n_grp; ++g) gorder[g] = g;
+        std::stable_sort(gorder.begin(), gorder.end(), [&](int32_t a, int32_t b) { return gcost[a] > gcost[b]; });
+        std::vector<int32_t> lane_of(n_grp), rank_of(n_grp);
+        int64_t load[kXcds] = {};
+        for (int32_t r = 0; r < n_grp; ++r) {
+            const int32_t g = gorder[r];
+            int x = 0;
+            for (int y = 1; y < kXcds; ++y)
+                if (load[y] < load[x]) x = y;
+            lane_of[g] = x;
+            rank_of[g] = r;
+            load[x] += gcost[g];
+        }
+        std::stable_sort(items.begin(), items.end(), [&](const Item& a, const Item& b) {
+            if (a.grp != b.grp) return rank_of[a.grp] < rank_of[b.grp];
+            return a.lane_cost > b.lane_cost;
+        });
+        std::vector<std::vector<int32_t>> lane(kXcds);
+        for (int32_t k = 0; k < (int32_t)items.size(); ++k) lane[lane_of[items[k].grp]].push_back(k);
+        size_t len = 0;
+        for (const auto& l : lane) len = std::max(len, l.size());
+        const size_t padded = len * kXcds;
+        if (padded - items.size() <= items.size() / 4 + kXcds) {
+            std::vector<Item> out(padded);
+            for (size_t k = 0; k < len; ++k)
+                for (int x = 0; x < kXcds; ++x) {
+                    Item& o = out[k * kXcds + x];
+                    if (k < lane[x].size()) {
+                        o = items[lane[x][k]];
+                    } else {
+                        o = Item{};
+                        o.v[sb::ITEM_MODE] = sb::MODE_ROWS;          // empty: n_rows 0
+                        o.v[sb::ITEM_PART] = -1;
+                    }
+                }
+            items.swap(out);
+        } else {
+            lanes = false;
+        }
+    }
+    if (!lanes)
+        std::stable_sort(items.begin(), items.end(), [](const Item& a, const Item& b) { return a.cost > b.cost; });
 
     const Layout L = layout_for(n_req, T, (int64_t)items.size(), (int64_t)groups.size());
     if (L.total * sizeof(int32_t) > bytes)

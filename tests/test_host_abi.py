@@ -12,8 +12,8 @@ import selective_batching_amd as sb
 from golden import load
 from oracle import flat as FL
 from oracle import scheduler as OS
-from synth import LLAMA8B, MINI, TOY, figure5_requests, llama_mixed_batch, p4_grid_requests, poisson_trace, \
-    random_ragged_batch
+from synth import GPT175B_LAYER, LLAMA8B, MINI, TOY, figure5_requests, gpt175b_mixed_batch, llama_mixed_batch, \
+    p4_grid_requests, poisson_trace, random_ragged_batch
 from selective_batching_amd.runtime import make_dims
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -457,6 +457,10 @@ def _coverage(m, batch, rg):
     cu = FL.cu_seqlens(batch)
     slots = _arr(rg.tok_slot, rg.n_tokens)
     spans = {}          # (request, kv head, row) -> key intervals seen by that row
+    empty = items[:, 4] == 0                         # padding of the dispatch order: no rows, no keys
+    assert np.all(items[empty][:, [2, 3, 5, 6]] == 0) and np.all(items[empty][:, 7] == -1)
+    assert empty.sum() <= (len(items) - empty.sum()) // 4 + 8
+    items = items[~empty]
     for req, kvh, mode, row0, nrows, kb, ke, part, tok0, ctx_i, slot0, _ in items:
         n_new, ctx = batch[req]
         # the request's first row, cached tokens and slot base, carried by the item
@@ -511,11 +515,36 @@ def test_attention_work_list_llama_mixed_batch_counts():
     assert rg.n_req == 256 and rg.n_tokens == sum(n for n, _ in batch)
     _coverage(LLAMA8B, batch, rg)
     items = _arr(rg.items, rg.n_items * ITEM_INTS).reshape(-1, ITEM_INTS)
+    # decode runs carry most of this batch's work: heaviest first (row tiles weighted 4 x their keys),
+    # no padding
+    assert np.all(items[:, 4] > 0)
     cost = np.where(items[:, 2] == 0, 4 * items[:, 6], items[:, 6] - items[:, 5])
-    assert np.all(np.diff(cost) <= 0)                       # heaviest first
+    assert np.all(np.diff(cost) <= 0)
     # at this size every decode's units fit one run: no partials, no combine
     assert rg.n_partials == 0 and rg.n_groups == 0
     assert FL.useful_pairs(batch) > 0
+
+
+@pytest.mark.parametrize("m,batch", [(LLAMA8B, "llama prefills"), (GPT175B_LAYER, "gpt175b prefills")])
+def test_attention_work_list_prefill_heavy_xcd_lanes(m, batch):
+    """Prefill tiles carry most of the work: the row tiles of one request and K/V head sit at indices of one
+    residue mod 8 (one XCD: workgroups are dealt to the 8 XCDs round-robin), consecutive within that XCD's
+    lane; empty padding items stay within a quarter of the others; every (request, head, row, key) is
+    still covered exactly once."""
+    src = llama_mixed_batch(seed=0) if m is LLAMA8B else gpt175b_mixed_batch(seed=0)
+    b = [x for x in src if x[0] > 1][:8]
+    rg, buf, _ = host_ragged(m, "bf16", b)
+    _coverage(m, b, rg)
+    items = _arr(rg.items, rg.n_items * ITEM_INTS).reshape(-1, ITEM_INTS)
+    assert len(items) % 8 == 0
+    pos = {}
+    for k, (req, kvh, mode, row0, nrows) in enumerate(items[:, :5]):
+        if nrows and mode == 0:
+            pos.setdefault((req, kvh), []).append(k)
+    assert len(pos) == len(b) * m.nkv
+    for ks in pos.values():
+        assert len({k % 8 for k in ks}) == 1
+        assert np.all(np.diff(ks) == 8)
 
 
 def test_attention_work_list_small_batch_one_unit_per_run():
