@@ -373,9 +373,9 @@ __device__ __forceinline__ void merge_unit(WaveState<D>& st, char* smem, RowStat
 }
 
 template <int DT, int D>
-__global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
     using T = typename Store<DT>::T;
-    constexpr int KT = 64;                                   // keys per LDS stage (MODE_ROWS)
+    constexpr int KT = 32;                                   // keys per LDS stage (MODE_ROWS)
     // MODE_ROWS stages K/V tiles; MODE_RUNS merges wave states: one workgroup
     // uses only one of the two, so they share the LDS allocation.
     constexpr int LDS_K = (DT == SB_BF16) ? 2 * KT * D : 0;
@@ -499,14 +499,31 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
 
     // MODE_ROWS: stage 64-key tiles of K (row-major, 16-byte pieces swizzled by row) and V (8-key
     // blocks, padded) in LDS
+    // (bf16: a tile of up to 128 rows; wave w owns rows row0 + 32w .. + 31 as two 16-row blocks, so that
+    // each staged K/V tile serves all 128 rows)
     if constexpr (DT == SB_BF16) {
-        bf16x8 qf[D / 32];
+        constexpr int RB = kRowBlocksBf16;
+        bf16x8 qf2[RB][D / 32];
+        WaveState<D> st2[RB];
+        int rl[RB], av[RB], wml[RB], rtok[RB], rhead[RB];
+        bool rok[RB];
 #pragma unroll
-        for (int s = 0; s < D / 32; ++s) {
-            u32x4 v = row_ok ? *(const u32x4*)(qrow + s * 32 + g * 8) : u32x4{0u, 0u, 0u, 0u};
-            qf[s] = __builtin_bit_cast(bf16x8, v);
+        for (int rb = 0; rb < RB; ++rb) {
+            const int w0 = row0 + wave * 16 * RB + 16 * rb, rrow = w0 + lr;
+            rok[rb] = rrow < row0 + nrows;
+            rtok[rb] = rok[rb] ? rrow / a.G : 0;
+            rhead[rb] = kvh * a.G + (rok[rb] ? rrow % a.G : 0);
+            rl[rb] = rok[rb] ? ctx + rtok[rb] + 1 : 0;
+            av[rb] = min(ke, ctx + w0 / a.G + 1);
+            wml[rb] = w0 < row0 + nrows ? min(ke, ctx + min(w0 + 15, row0 + nrows - 1) / a.G + 1) : 0;
+            const T* q = (const T*)a.qkv + (long long)(tok0 + rtok[rb]) * a.qkv_stride + (long long)rhead[rb] * D;
+#pragma unroll
+            for (int s = 0; s < D / 32; ++s) {
+                u32x4 v = rok[rb] ? *(const u32x4*)(q + s * 32 + g * 8) : u32x4{0u, 0u, 0u, 0u};
+                qf2[rb][s] = __builtin_bit_cast(bf16x8, v);
+            }
+            state_init(st2[rb]);
         }
-        const int wave_max_limit = min(ke, ctx + min(wrow0 + 15, row0 + nrows - 1) / a.G + 1);
         const int ntiles = (ke - kb + KT - 1) / KT;
         constexpr int KCH = KT * D / 8;                    // 16-byte chunks per K tile (and per V tile)
         constexpr int PER = (KCH + 255) / 256;
@@ -557,9 +574,11 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
 #pragma unroll
             for (int h = 0; h < KT / 32; ++h) {
                 const int k0 = kb + t * KT + 32 * h;
-                if (k0 < wave_max_limit)
-                    chunk_bf16<D>(a, st, qf, k0, ke, row_limit, all_visible, lane, ldsK + buf * KSTR + 32 * h * D,
-                                  ldsV + buf * VSTR + 4 * h * (D * 8 + 16));
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb)
+                    if (k0 < wml[rb])
+                        chunk_bf16<D>(a, st2[rb], qf2[rb], k0, ke, rl[rb], av[rb], lane,
+                                      ldsK + buf * KSTR + 32 * h * D, ldsV + buf * VSTR + 4 * h * (D * 8 + 16));
             }
         };
         // registers r0 / r1 hold the even / odd tiles in flight; LDS buffer t & 1 holds tile t
@@ -580,6 +599,20 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
             __syncthreads();
             gload(r0, t + 4);
         }
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+            float l = st2[rb].l;                             // row sum over the 4 lanes of the row
+            l += shfl_xor(l, 16);
+            l += shfl_xor(l, 32);
+            if (!rok[rb]) continue;
+            const float inv = 1.f / l;
+            T* orow = (T*)a.out + (long long)(tok0 + rtok[rb]) * a.out_stride + (long long)rhead[rb] * D;
+#pragma unroll
+            for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) Store<DT>::st(orow + db * 16 + 4 * g + r, st2[rb].o[db][r] * inv);
+        }
+        return;
     } else {
         float qf[D / 4];
 #pragma unroll

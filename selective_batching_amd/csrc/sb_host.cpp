@@ -764,11 +764,13 @@ extern "C" int sb_ragged_build(const sb_model_dims* dims, int32_t n_req, const i
                     items.push_back(it);
                 }
             } else {
-                // 64-row tiles; the four waves take 16 rows each and share K/V tiles through LDS
+                // row tiles (64 rows in fp32, 128 in bf16); the four waves take 16 or 32 rows each and share
+                // the K/V tiles staged in LDS
                 const int32_t rows_grp = n_grp++;
-                for (int32_t r0 = 0; r0 < rows; r0 += sb::kRowsPerTile) {
+                const int32_t rpt = sb::rows_per_tile(dims->dtype);
+                for (int32_t r0 = 0; r0 < rows; r0 += rpt) {
                     Item it{};
-                    const int32_t nr = std::min(sb::kRowsPerTile, rows - r0);
+                    const int32_t nr = std::min(rpt, rows - r0);
                     const int32_t last_tok = (r0 + nr - 1) / G;
                     it.v[sb::ITEM_REQ] = i;
                     it.v[sb::ITEM_KVH] = g;

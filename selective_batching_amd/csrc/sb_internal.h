@@ -33,7 +33,11 @@ inline size_t dtype_size(int dt) { return dt == SB_BF16 ? 2 : 4; }
 //    never on how the builder grouped units into runs.
 constexpr int kRowsPerWave = 16;          // one 16x16 MFMA tile of (token, head) rows
 constexpr int kWaves = 4;                 // waves per attention workgroup
-constexpr int kRowsPerTile = kRowsPerWave * kWaves;
+constexpr int kRowsPerTile = kRowsPerWave * kWaves;       // MODE_ROWS tile (fp32)
+constexpr int kRowBlocksBf16 = 2;                          // 16-row blocks per wave in a bf16 MODE_ROWS tile
+// Rows of one MODE_ROWS work item: in bf16 each wave takes two 16-row blocks, so that a staged K/V tile
+// serves twice the rows.
+inline int rows_per_tile(int dtype) { return dtype == SB_BF16 ? kRowsPerTile * kRowBlocksBf16 : kRowsPerTile; }
 constexpr int kUnitKeys = 512;            // keys per independently reduced unit
 constexpr int kTargetRuns = 1024;         // runs per launch the builder aims at (balance vs. run length)
 // An item also carries its request's first row, cached-token count and slot base (the

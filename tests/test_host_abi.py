@@ -448,7 +448,7 @@ UNIT = 512   # keys per independently reduced unit (the library's kUnitKeys)
 ITEM_INTS = 12   # ints per attention work item (the library's kItemInts)
 
 
-def _coverage(m, batch, rg):
+def _coverage(m, batch, rg, rg_dtype="bf16"):
     """Every (request, kv head, row) must see every visible key exactly once across the work items: row tiles
     (mode 0) and runs of whole key units (mode 1); a request split over several runs leaves one partial per
     unit, named in order by one combine group."""
@@ -467,7 +467,7 @@ def _coverage(m, batch, rg):
         assert tok0 == cu[req] and ctx_i == ctx and slot0 == slots[cu[req]] - ctx
         assert 0 <= kb < ke <= n_new + ctx
         if mode == 0:
-            assert nrows <= 64 and kb == 0 and part == -1
+            assert nrows <= (128 if rg_dtype == "bf16" else 64) and kb == 0 and part == -1
         else:
             assert mode == 1 and row0 == 0 and nrows == n_new * G <= 16
             assert kb % UNIT == 0 and ((ke - kb) % UNIT == 0 or ke == n_new + ctx)
@@ -506,7 +506,7 @@ def _coverage(m, batch, rg):
 def test_attention_work_list_covers_each_pair_once(m, dtype, seed):
     batch = random_ragged_batch(seed, 6, 1100, 40)
     rg, buf, _ = host_ragged(m, dtype, batch)
-    _coverage(m, batch, rg)
+    _coverage(m, batch, rg, dtype)
 
 
 def test_attention_work_list_llama_mixed_batch_counts():
