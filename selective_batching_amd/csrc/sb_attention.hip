@@ -499,23 +499,25 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
 
     // MODE_ROWS: stage 64-key tiles of K (row-major, 16-byte pieces swizzled by row) and V (8-key
     // blocks, padded) in LDS
-    // (bf16: a tile of up to 128 rows; wave w owns rows row0 + 32w .. + 31 as two 16-row blocks, so that
-    // each staged K/V tile serves all 128 rows)
+    // (bf16: a tile of up to 64 x rbn rows; wave w owns rows row0 + 16 rbn w .. as rbn 16-row blocks, so
+    // that each staged K/V tile serves all of them)
     if constexpr (DT == SB_BF16) {
         constexpr int RB = kRowBlocksBf16;
+        const int rbn = it[ITEM_RB];
         bf16x8 qf2[RB][D / 32];
         WaveState<D> st2[RB];
         int rl[RB], av[RB], wml[RB], rtok[RB], rhead[RB];
         bool rok[RB];
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
-            const int w0 = row0 + wave * 16 * RB + 16 * rb, rrow = w0 + lr;
-            rok[rb] = rrow < row0 + nrows;
+            const bool on = rb < rbn;
+            const int w0 = row0 + wave * 16 * rbn + 16 * rb, rrow = w0 + lr;
+            rok[rb] = on && rrow < row0 + nrows;
             rtok[rb] = rok[rb] ? rrow / a.G : 0;
             rhead[rb] = kvh * a.G + (rok[rb] ? rrow % a.G : 0);
             rl[rb] = rok[rb] ? ctx + rtok[rb] + 1 : 0;
             av[rb] = min(ke, ctx + w0 / a.G + 1);
-            wml[rb] = w0 < row0 + nrows ? min(ke, ctx + min(w0 + 15, row0 + nrows - 1) / a.G + 1) : 0;
+            wml[rb] = on && w0 < row0 + nrows ? min(ke, ctx + min(w0 + 15, row0 + nrows - 1) / a.G + 1) : 0;
             const T* q = (const T*)a.qkv + (long long)(tok0 + rtok[rb]) * a.qkv_stride + (long long)rhead[rb] * D;
 #pragma unroll
             for (int s = 0; s < D / 32; ++s) {

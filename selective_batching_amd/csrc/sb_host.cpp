@@ -729,6 +729,13 @@ extern "C" int sb_ragged_build(const sb_model_dims* dims, int32_t n_req, const i
     // units per run: about kTargetRuns runs per launch -- long runs keep a workgroup streaming one
     // request's keys, enough runs keep every CU busy.  Only the grouping depends on the batch.
     const int32_t upr = (int32_t)std::max<int64_t>(1, (n_units + sb::kTargetRuns - 1) / sb::kTargetRuns);
+    // row blocks per wave of the bf16 row tiles: two once the batch has enough 64-row tiles to fill the
+    // GPU twice over, else one (fp32: one)
+    int64_t tiles64 = 0;
+    for (int32_t i = 0; i < n_req; ++i)
+        if (n_new[i] * G > sb::kRowsPerWave)
+            tiles64 += (int64_t)nkv * ((n_new[i] * G + sb::kRowsPerTile - 1) / sb::kRowsPerTile);
+    const int32_t rbn = (dims->dtype == SB_BF16 && tiles64 >= sb::kRowBlocksMinTiles) ? sb::kRowBlocksBf16 : 1;
     int32_t n_part = 0;
     int32_t n_grp = 0;                              // locality groups: a request-head's row tiles, or one run
     int32_t tok0 = 0;                               // the request's first row
@@ -764,10 +771,10 @@ extern "C" int sb_ragged_build(const sb_model_dims* dims, int32_t n_req, const i
                     items.push_back(it);
                 }
             } else {
-                // row tiles (64 rows in fp32, 128 in bf16); the four waves take 16 or 32 rows each and share
-                // the K/V tiles staged in LDS
+                // row tiles of 64 x rbn rows; the four waves take rbn 16-row blocks each and share the K/V
+                // tiles staged in LDS
                 const int32_t rows_grp = n_grp++;
-                const int32_t rpt = sb::rows_per_tile(dims->dtype);
+                const int32_t rpt = sb::kRowsPerTile * rbn;
                 for (int32_t r0 = 0; r0 < rows; r0 += rpt) {
                     Item it{};
                     const int32_t nr = std::min(rpt, rows - r0);
@@ -783,6 +790,7 @@ extern "C" int sb_ragged_build(const sb_model_dims* dims, int32_t n_req, const i
                     it.v[sb::ITEM_TOK0] = tok0;
                     it.v[sb::ITEM_CTX] = ctx[i];
                     it.v[sb::ITEM_SLOT0] = (int32_t)slot_base[i];
+                    it.v[sb::ITEM_RB] = rbn;
                     it.cost = 4 * (int64_t)it.v[sb::ITEM_KE];
                     it.lane_cost = (int64_t)it.v[sb::ITEM_KE] + kItemStartCost;
                     it.grp = rows_grp;

@@ -34,10 +34,10 @@ inline size_t dtype_size(int dt) { return dt == SB_BF16 ? 2 : 4; }
 constexpr int kRowsPerWave = 16;          // one 16x16 MFMA tile of (token, head) rows
 constexpr int kWaves = 4;                 // waves per attention workgroup
 constexpr int kRowsPerTile = kRowsPerWave * kWaves;       // MODE_ROWS tile (fp32)
-constexpr int kRowBlocksBf16 = 2;                          // 16-row blocks per wave in a bf16 MODE_ROWS tile
-// Rows of one MODE_ROWS work item: in bf16 each wave takes two 16-row blocks, so that a staged K/V tile
-// serves twice the rows.
-inline int rows_per_tile(int dtype) { return dtype == SB_BF16 ? kRowsPerTile * kRowBlocksBf16 : kRowsPerTile; }
+constexpr int kRowBlocksBf16 = 2;                          // most 16-row blocks per wave in a bf16 MODE_ROWS tile
+// A batch with at least this many 64-row tiles takes bf16 tiles of kRowBlocksBf16 blocks per wave (each
+// staged K/V tile then serves more rows); fewer tiles keep one block per wave (more, shorter items).
+constexpr int kRowBlocksMinTiles = 1024;
 constexpr int kUnitKeys = 512;            // keys per independently reduced unit
 constexpr int kTargetRuns = 1024;         // runs per launch the builder aims at (balance vs. run length)
 // An item also carries its request's first row, cached-token count and slot base (the
@@ -46,7 +46,7 @@ constexpr int kTargetRuns = 1024;         // runs per launch the builder aims at
 constexpr int kItemInts = 12;
 constexpr int kGroupInts = 8;
 enum { ITEM_REQ = 0, ITEM_KVH, ITEM_MODE, ITEM_ROW0, ITEM_NROWS, ITEM_KB, ITEM_KE, ITEM_PART,
-       ITEM_TOK0, ITEM_CTX, ITEM_SLOT0 };
+       ITEM_TOK0, ITEM_CTX, ITEM_SLOT0, ITEM_RB };
 enum { MODE_ROWS = 0, MODE_RUNS = 1 };
 enum { GRP_REQ = 0, GRP_KVH, GRP_ROW0, GRP_NROWS, GRP_PART0, GRP_NPARTS, GRP_TOK0 };
 

@@ -297,6 +297,51 @@ def test_append_writes_only_its_slots(m, dtype):
         sb.sb_kv_destroy(kv)
 
 
+def test_attention_prefill_tile_shape_invariant():
+    """A prompt's attention alone (few row tiles: one 16-row block per wave, 64-row tiles) and among 32 other
+    prompts (over 1024 tiles of 64 rows: two blocks per wave, 128-row tiles) gives the same bits: a row's
+    arithmetic does not depend on the tile it falls in."""
+    m = GQA_BF16
+    dims = make_dims(m, "bf16")
+    target = (300, 17)
+    others = [(256, 0)] * 32
+    print_case("prefill tile shape invariance", m.name)
+    outs = []
+    for batch in ([target], others + [target]):
+        n_slots = sum(n + c for n, c in batch) + 8 * len(batch)
+        arena = sb.sb_kv_arena_slots(n_slots, len(batch))
+        nbytes = sb.sb_kv_arena_bytes(arena, 1, m.nkv, m.d, sb.SB_BF16)
+        ka = torch.zeros(nbytes // 2, dtype=torch.bfloat16, device="cuda")
+        va = torch.zeros(nbytes // 2, dtype=torch.bfloat16, device="cuda")
+        kv = sb.sb_kv_create(n_slots, arena, 1, m.nkv, m.d, sb.SB_BF16, ka.data_ptr(), va.data_ptr())
+        try:
+            bases = [sb.sb_kv_reserve(kv, i, n + c) for i, (n, c) in enumerate(batch)]
+            ti = len(batch) - 1                              # the target is the last request
+            hk, hv = synthetic_kv(5, "target", target[1], m.nkv, m.d, 1.0, "bf16")
+            slots = torch.arange(bases[ti], bases[ti] + target[1], dtype=torch.int32, device="cuda")
+            dk, dv = dev(hk, "bf16"), dev(hv, "bf16")
+            sb.sb_kv_write(kv, 0, target[1], slots.data_ptr(), dk.data_ptr(), dv.data_ptr(), stream_handle())
+            T = sum(n for n, _ in batch)
+            qkv = np.concatenate([normal(6 + i, "qkv", (n, m.qkv_out), dtype="bf16") for i, (n, _) in enumerate(batch[:-1])]
+                                 + [normal(99, "qkv-target", (target[0], m.qkv_out), dtype="bf16")])
+            mb = sb.sb_ragged_bytes(dims, len(batch), T, n_slots)
+            staging = torch.empty(mb, dtype=torch.uint8, pin_memory=True)
+            meta = torch.empty(mb, dtype=torch.uint8, device="cuda")
+            rg = sb.sb_ragged_build(dims, [n for n, _ in batch], [c for _, c in batch], bases, None,
+                                    staging.data_ptr(), meta.data_ptr(), mb, stream_handle())
+            dqkv = dev(qkv, "bf16")
+            sb.sb_op_rope_append(dims, rg, kv, 0, dqkv.data_ptr(), stream_handle())
+            o = torch.zeros((T, m.nq * m.d), dtype=torch.bfloat16, device="cuda")
+            ws = torch.empty(max(rg.n_partials, 1) * 16 * (m.d + 2) * 4, dtype=torch.uint8, device="cuda")
+            sb.sb_op_attention(dims, rg, kv, 0, dqkv.data_ptr(), o.data_ptr(), ws.data_ptr(), ws.numel(),
+                               stream_handle())
+            _sync()
+            outs.append(o[T - target[0]:].view(torch.int16).cpu())
+        finally:
+            sb.sb_kv_destroy(kv)
+    assert torch.equal(outs[0], outs[1])
+
+
 def test_attention_decode_only():
     _attention_case(MINI_ATT, "bf16", [(1, 100), (1, 17), (1, 256), (1, 31), (1, 32)], 7)
     _attention_case(MINI_ATT, "fp32", [(1, 100), (1, 17), (1, 256), (1, 31), (1, 32)], 7)

@@ -461,13 +461,17 @@ def _coverage(m, batch, rg, rg_dtype="bf16"):
     assert np.all(items[empty][:, [2, 3, 5, 6]] == 0) and np.all(items[empty][:, 7] == -1)
     assert empty.sum() <= (len(items) - empty.sum()) // 4 + 8
     items = items[~empty]
-    for req, kvh, mode, row0, nrows, kb, ke, part, tok0, ctx_i, slot0, _ in items:
+    rbs = set()
+    for req, kvh, mode, row0, nrows, kb, ke, part, tok0, ctx_i, slot0, rb in items:
         n_new, ctx = batch[req]
         # the request's first row, cached tokens and slot base, carried by the item
         assert tok0 == cu[req] and ctx_i == ctx and slot0 == slots[cu[req]] - ctx
         assert 0 <= kb < ke <= n_new + ctx
         if mode == 0:
-            assert nrows <= (128 if rg_dtype == "bf16" else 64) and kb == 0 and part == -1
+            # row tiles of rb 16-row blocks per wave (two only in bf16), one choice for the whole batch
+            assert rb in ((1, 2) if rg_dtype == "bf16" else (1,))
+            rbs.add(int(rb))
+            assert nrows <= 64 * rb and row0 % (64 * rb) == 0 and kb == 0 and part == -1
         else:
             assert mode == 1 and row0 == 0 and nrows == n_new * G <= 16
             assert kb % UNIT == 0 and ((ke - kb) % UNIT == 0 or ke == n_new + ctx)
@@ -485,6 +489,7 @@ def _coverage(m, batch, rg, rg_dtype="bf16"):
                 assert iv[0][0] == 0 and iv[-1][1] == ctx + r // G + 1
                 assert all(a[1] == b[0] for a, b in zip(iv, iv[1:]))
     assert not spans
+    assert len(rbs) <= 1
     groups = _arr(rg.groups, rg.n_groups * 8).reshape(-1, 8)
     p0 = {}
     for req, kvh, row0, nrows, gp0, np_, tok0, _ in groups:
@@ -515,6 +520,8 @@ def test_attention_work_list_llama_mixed_batch_counts():
     assert rg.n_req == 256 and rg.n_tokens == sum(n for n, _ in batch)
     _coverage(LLAMA8B, batch, rg)
     items = _arr(rg.items, rg.n_items * ITEM_INTS).reshape(-1, ITEM_INTS)
+    # 1816 tiles of 64 rows: the row tiles take two 16-row blocks per wave (128 rows)
+    assert set(items[items[:, 2] == 0][:, 11]) == {2}
     # decode runs carry most of this batch's work: heaviest first (row tiles weighted 4 x their keys),
     # no padding
     assert np.all(items[:, 4] > 0)
