@@ -22,9 +22,17 @@ processed tokens per second (sum of n_new over the batch / step time).
 Also reported: HIP-event timing, on the launch stream during the timed steps,
 of the FFN1 GEMM and attention launches (only those two classes are timed
 there: every recorded event pair costs time); the roofline of the dominant
-kernel (the FFN1 SwiGLU GEMM, MFMA-bound); decode-attention HBM bandwidth; a
-per-class breakdown from three extra steps with every class timed; and the
-CPU oracle timed on a bounded sample of the same workload.
+kernel (the FFN1 SwiGLU GEMM, MFMA-bound); the attention's HBM bandwidth over
+the mixed batch and, launched alone, over its decodes (``decode_attention``,
+the launches cycling through four layers of K/V so that none is served from
+the caches); a per-class breakdown from three extra steps with every class
+timed; the serving trace, the reservation-policy replay, iteration- against
+request-level scheduling and the mini-model decode loop; and the CPU oracle
+timed on a bounded sample of the same workload.
+
+Other modes (each prints its own JSON line instead): ``--op-gemm M,N,K,EPI``
+times one GEMM shape; ``--gpt175b-layer`` times one GPT-175B-shaped layer over
+its 96-decode + 32-prefill batch, per kernel class.
 """
 import argparse
 import json
