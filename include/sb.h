@@ -122,7 +122,8 @@ int sb_kv_stats(const sb_kv* kv, int64_t* n_rsrv, int64_t* n_slots, int64_t* n_l
 /* Device pointers of layer `layer`'s K and V planes (for the kernels). */
 int sb_kv_layer_ptrs(const sb_kv* kv, int32_t layer, void** k, void** v);
 /* Scatter n rows of K and V ([n][n_kv_heads][head_dim], device, model dtype)
- * of layer `layer` to the slots slots[0..n) (device int32). */
+ * of layer `layer` to the slots slots[0..n) (device int32).  A slot outside
+ * [0, arena_slots) is skipped (its row is neither written nor read). */
 int sb_kv_write(const sb_kv* kv, int32_t layer, int32_t n, const int32_t* slots, const void* k,
                 const void* v, void* stream);
 /* Gather the rows of slots[0..n) back into [n][n_kv_heads][head_dim] (device). */
@@ -172,7 +173,11 @@ int sb_sched_set_chunking(sb_sched* s, int32_t token_budget, int32_t chunk);
 int sb_sched_set_request_level(sb_sched* s, int32_t on);
 /* Select the next batch (host arrays of capacity cap).  For member i:
  * n_new[i] = tokens fed this iteration (the prompt or a chunk of it, or 1),
- * ctx[i] = tokens already cached, slot_base[i] = first slot of its reservation.
+ * ctx[i] = tokens already cached, slot_base[i] = first slot of its reservation
+ * as the K/V manager holds it once the whole batch is admitted (a reservation
+ * made during this Select may compact the arena and move members admitted
+ * before it: their histories are copied on the manager's stream, and only
+ * these bases are valid for this iteration and after).
  * *n_out == 0 is legal (empty pool). */
 int sb_select_batch(sb_sched* s, int32_t cap, int64_t* ids, int32_t* n_new, int32_t* ctx,
                     int64_t* slot_base, int32_t* n_out);
@@ -272,10 +277,23 @@ int sb_ragged_build(const sb_model_dims* dims, int32_t n_req, const int32_t* n_n
 size_t sb_layer_workspace_bytes(const sb_model_dims* dims, int32_t max_tokens, int32_t max_req,
                                 int32_t max_partials);
 
-/* Token embedding (+ learned position for GPT) of every row: x[t] = E[id_t] (+ P[pos_t]). */
+/* Token embedding (+ learned position for GPT) of every row: x[t] = E[id_t] (+ P[pos_t]).
+ * The rows are the flattened [sum L_i, H] input of [W] Figure 5 (request i's
+ * new tokens at rows cu_seqlens[i] ..); each is the token the request feeds
+ * this iteration: prompt tokens in the initiation phase, else the token the
+ * previous iteration generated ([W] 为什么这对生成式模型是灾难: an iteration's
+ * input is the previous iteration's output; Figure 3).  The pages do not fix
+ * the position scheme: GPT-style models use learned absolute positions
+ * ctx_i + j, Llama-style models none here (RoPE is applied inside the layer).
+ * rg->tok_ids must be set; ids outside [0, vocab) are refused by
+ * sb_ragged_build.  x: device fp32 [T, hidden], written entirely. */
 int sb_embed(const sb_model_dims* dims, const sb_model_weights* w, const sb_ragged* rg, float* x,
              void* stream);
-/* The same, resolving token references -(1 + j) to prev_ids[j] (device int32
+/* sb_embed for chained iterations ([W] 控制面与数据面分离: keep the host's
+ * control path free of per-iteration GPU waits -- here the host schedules
+ * the next iteration without waiting for the device's tokens; "CS349D
+ * Lecture 2" section 7, CPU-side scheduling as the bottleneck):
+ * resolves token references -(1 + j) to prev_ids[j] (device int32
  * [prev_n]: the previous iteration's sb_lm_argmax output, read in stream order,
  * so it is never copied through the host).  A reference with j >= prev_n, or
  * any id outside [0, vocab), embeds a clamped id: it cannot read outside the
@@ -293,13 +311,22 @@ int sb_layer_step(const sb_model_dims* dims, const sb_layer_weights* w, const sb
                   void* stream);
 
 /* Final norm of each request's last row, LM head, greedy argmax (lowest index
- * on ties).  logits: device fp32 [B, vocab] (may be NULL); out_ids: device int32 [B]. */
+ * on ties).  Each iteration yields one token per request from the last of its
+ * rows ([W] Figure 3: every iteration of an autoregressive model emits one
+ * token, the initiation iteration its first one; "CS349D Lecture 2" 4.2:
+ * greedy decoding, batched ids equal one-by-one ids).  Row r = last_row[r]
+ * of x (device fp32 [T, hidden]); logits: device fp32 [B, vocab] (may be
+ * NULL: then held in the workspace); out_ids: device int32 [B], request order.
+ * SB_ERR_WORKSPACE if ws_bytes < sb_layer_workspace_bytes for this batch. */
 int sb_lm_argmax(const sb_model_dims* dims, const sb_model_weights* w, const sb_ragged* rg,
                  const float* x, float* logits, int32_t* out_ids, void* workspace, size_t ws_bytes,
                  void* stream);
 
-/* One iteration's whole device side in one call (one host call instead of
- * 2 + n_layers): sb_embed_chained (prev_ids may be NULL), sb_layer_step for
+/* One iteration's whole device side in one call -- the engine's "run one
+ * iteration for the batch" of [W] Algorithm 1 (the scheduler hands the engine
+ * a batch, the engine runs exactly one iteration and returns one token per
+ * request) over the Figure-5 data flow of every layer.  One host call instead
+ * of 2 + n_layers: sb_embed_chained (prev_ids may be NULL), sb_layer_step for
  * layers 0 .. n_layers-1 with layers[l] (host array of n_layers structs),
  * then sb_lm_argmax.  Arguments, ownership and errors as for those calls; the
  * first failing step's status is returned and nothing after it is enqueued.

@@ -834,6 +834,12 @@ int num_cus() {
 int launch_gemm(int dtype, int epi, const GemmArgs& a, hipStream_t s) {
     if (a.M <= 0) return SB_OK;
     if (a.N <= 0 || a.K <= 0 || !a.A || !a.W || !a.C) return fail(SB_ERR_INVALID, "gemm: bad arguments");
+    // the kernels index every operand with 32-bit element offsets
+    const long long w_rows = epi == EPI_SWIGLU ? 2LL * a.F : (long long)a.N;
+    const long long lim = 1LL << 31;
+    if ((long long)a.M * a.lda >= lim || w_rows * a.ldw >= lim || (long long)a.M * a.ldc >= lim)
+        return fail(SB_ERR_INVALID, "gemm: an operand spans 2^31 elements or more (M %d, lda %lld, W rows %lld, ldw %lld, ldc %lld)",
+                    a.M, (long long)a.lda, w_rows, (long long)a.ldw, (long long)a.ldc);
     if (dtype == SB_BF16) {
         if (a.K % 64 || a.lda % 8 || a.ldw % 8) return fail(SB_ERR_INVALID, "bf16 gemm needs K %% 64 == 0 and 16-byte aligned rows");
         switch (epi) {

@@ -41,10 +41,12 @@ int validate_dims(const sb_model_dims* d) {
     if (kRowsPerWave % g) return fail(SB_ERR_INVALID, "query heads per K/V head (%d) must divide 16", g);
     if (d->hidden % 64 || d->ffn % 64 || (d->n_heads * d->head_dim) % 64)
         return fail(SB_ERR_INVALID, "hidden, ffn and n_heads*head_dim must be multiples of 64");
-    if (d->dtype == SB_BF16 && (d->head_dim % 32 || d->head_dim > 128))
-        return fail(SB_ERR_INVALID, "bf16 head_dim must be 32, 64, 96 or 128");
-    if (d->dtype == SB_F32 && (d->head_dim % 16 || d->head_dim > 128))
-        return fail(SB_ERR_INVALID, "fp32 head_dim must be a multiple of 16 up to 128");
+    // exactly the head dims the attention kernel is instantiated for
+    const int hd = d->head_dim;
+    if (d->dtype == SB_BF16 && hd != 32 && hd != 64 && hd != 128)
+        return fail(SB_ERR_INVALID, "bf16 head_dim must be 32, 64 or 128 (got %d)", hd);
+    if (d->dtype == SB_F32 && hd != 16 && hd != 32 && hd != 64 && hd != 128)
+        return fail(SB_ERR_INVALID, "fp32 head_dim must be 16, 32, 64 or 128 (got %d)", hd);
     if (d->arch == SB_ARCH_LLAMA && d->head_dim % 2) return fail(SB_ERR_INVALID, "RoPE needs an even head_dim");
     return SB_OK;
 }
@@ -232,7 +234,6 @@ struct Req {
     int32_t prompt_len, out_len, max_tokens;
     int32_t state;
     int32_t generated;
-    int64_t slot_base;
     std::vector<int32_t> prompt;
     std::vector<int32_t> out;
     int32_t prefilled = 0;                          // prompt tokens already processed (K/V cached)
@@ -309,7 +310,6 @@ extern "C" int sb_sched_add(sb_sched* s, int64_t req_id, double arrival, int32_t
     r->max_tokens = max_tokens;
     r->state = ST_INITIATION;
     r->generated = 0;
-    r->slot_base = -1;
     r->prompt.assign(prompt_len, 0);
     if (prompt_tokens) std::memcpy(r->prompt.data(), prompt_tokens, sizeof(int32_t) * prompt_len);
     return insert_req(s, std::move(r));
@@ -322,8 +322,7 @@ extern "C" int sb_sched_add_running(sb_sched* s, int64_t req_id, double arrival,
     if (st) return st;
     if (generated < 1 || generated >= out_len)
         return fail(SB_ERR_INVALID, "generated must be in [1, out_len)");
-    int64_t base = -1;
-    st = sb_kv_reserve(s->kv, req_id, max_tokens, &base);
+    st = sb_kv_reserve(s->kv, req_id, max_tokens, nullptr);
     if (st) return st;
     auto r = std::make_unique<Req>();
     r->id = req_id;
@@ -335,7 +334,6 @@ extern "C" int sb_sched_add_running(sb_sched* s, int64_t req_id, double arrival,
     r->state = ST_INCREMENT;
     r->generated = generated;
     r->prefilled = prompt_len;
-    r->slot_base = base;
     r->prompt.assign(prompt_len, 0);
     if (prompt_tokens) std::memcpy(r->prompt.data(), prompt_tokens, sizeof(int32_t) * prompt_len);
     r->out.assign(generated, 0);
@@ -371,15 +369,12 @@ extern "C" int sb_select_batch(sb_sched* s, int32_t cap, int64_t* ids, int32_t* 
     auto admit = [&](Req* r, int* st) {             // first scheduling: reserve max_tokens (stop on failure)
         *st = SB_OK;
         if (r->state != ST_INITIATION) return true;
-        int64_t base = -1;
-        *st = sb_kv_reserve(s->kv, r->id, r->max_tokens, &base);
+        *st = sb_kv_reserve(s->kv, r->id, r->max_tokens, nullptr);
         if (*st == SB_ERR_NO_SLOTS) {
             *st = SB_OK;
             return false;
         }
-        if (*st) return false;
-        r->slot_base = base;
-        return true;
+        return *st == SB_OK;
     };
     int st = SB_OK;
     if (s->request_level && !s->seated.empty()) {
@@ -419,7 +414,9 @@ extern "C" int sb_select_batch(sb_sched* s, int32_t cap, int64_t* ids, int32_t* 
         const bool prompt = r->prefilled < r->prompt_len;
         if (n_new) n_new[i] = r->cur_new;
         if (ctx) ctx[i] = prompt ? r->prefilled : r->prompt_len + r->generated - 1;
-        if (slot_base) slot_base[i] = r->slot_base;
+        // The manager's base, read after the whole batch is admitted: a later member's reservation may
+        // have compacted the arena and moved the ranges of members admitted before it.
+        if (slot_base) slot_base[i] = s->kv->live.at(r->id).base;
     }
     *n_out = (int32_t)batch.size();
     return SB_OK;

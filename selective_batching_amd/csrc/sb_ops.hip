@@ -463,6 +463,7 @@ __global__ __launch_bounds__(256) void kv_copy_kernel(const int* slots, void* kp
     using T = typename Store<DT>::T;
     const int t = blockIdx.x;
     const long long s = slots[t];
+    if (s < 0 || s >= arena) return;          // a slot outside the arena is skipped, never dereferenced
     T* K = (T*)kplane;
     T* V = (T*)vplane;
     T* kr = (T*)k + (long long)t * nkv * D;

@@ -202,6 +202,13 @@ static void sched_random(uint32_t seed, Mode mode, const sb_model_dims& d) {
         CHECK(n <= max_bs);
         if (n == 0) break;
         ++iters;
+        // every base handed out is the manager's current one (a reservation made during this Select may
+        // have compacted the arena and moved the members admitted before it)
+        for (int32_t i = 0; i < n; ++i) {
+            int64_t lb = -1;
+            OK(sb_kv_lookup(kv, ids[i], &lb, nullptr));
+            CHECK(lb == base[i]);
+        }
         int64_t reserved = 0, stored = 0;
         OK(sb_kv_usage(s, &reserved, &stored));
         CHECK(reserved <= n_slots && stored <= reserved);

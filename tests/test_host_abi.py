@@ -94,6 +94,71 @@ def test_kv_placement_disjoint_aligned_and_compacts(seed):
     sb.sb_kv_destroy(kv)
 
 
+def test_select_reports_bases_after_compaction():
+    """A reservation that compacts the arena moves the ranges of requests admitted before it: Select must
+    hand out the bases the K/V manager holds after the move.  48 slots: A8 B16 C8 D16 fill the arena; A and
+    C finish, leaving two 8-slot holes; E16 fits the counter (32 + 16 = 48) but no hole, so B and D are
+    packed to 0 and 16 and E lands at 32."""
+    kv = sb.sb_kv_create(48, 48, 1, 1, 8, sb.SB_F32)
+    s = sb.sb_sched_create(4, kv)
+    for rid, (mt, out) in enumerate(((8, 1), (16, 9), (8, 1), (16, 9))):
+        sb.sb_sched_add(s, rid, 0.0, [1, 2, 3, 4], out, mt)
+    ids, _, _, base = sb.sb_select_batch(s, 4)
+    assert list(ids) == [0, 1, 2, 3] and list(base) == [0, 8, 24, 32]
+    assert list(sb.sb_sched_complete(s, ids, np.zeros(4, np.int32))) == [0, 2]
+    sb.sb_sched_add(s, 4, 1.0, [1, 2, 3, 4], 2, 16)
+    ids, _, _, base = sb.sb_select_batch(s, 4)
+    assert list(ids) == [1, 3, 4]
+    assert sb.sb_kv_stats(kv)["n_compactions"] == 1
+    assert list(base) == [sb.sb_kv_lookup(kv, int(r))[0] for r in ids] == [0, 16, 32]
+    sb.sb_sched_destroy(s)
+    sb.sb_kv_destroy(kv)
+
+
+@pytest.mark.parametrize("policy", ["pow2", "oracle"])
+@pytest.mark.parametrize("chunking", [None, (24, 8)])
+def test_select_bases_match_manager_under_binding_reservations(policy, chunking):
+    """A trace whose reservations bind (Pow2 / Oracle policies, few slots): on every iteration each member's
+    base from Select equals the manager's, the members' ranges are disjoint, 8-aligned, inside the arena and
+    hold the member's history plus this iteration's tokens; compaction happens many times."""
+    code = {"pow2": sb.SB_RESERVE_POW2, "oracle": sb.SB_RESERVE_ORACLE}[policy]
+    reqs = poisson_trace(seed=41, n=300, rate=0.9, plo=1, phi=60, olo=1, ohi=40, reserve_out=40)
+    for r in reqs:
+        r.max_tokens = sb.sb_reservation_tokens(code, len(r.prompt), r.out_len, 40)
+    n_slots, max_bs = 400, 12
+    arena = sb.sb_kv_arena_slots(n_slots, max_bs)
+    kv = sb.sb_kv_create(n_slots, arena, 1, 1, 8, sb.SB_F32)
+    s = sb.sb_sched_create(max_bs, kv)
+    if chunking:
+        sb.sb_sched_set_chunking(s, *chunking)
+    pending = sorted(reqs, key=lambda r: (r.arrival, r.rid))
+    mt = {r.rid: r.max_tokens for r in reqs}
+    i, t, iters = 0, 0, 0
+    while i < len(pending) or sb.sb_sched_stats(s)["pool"]:
+        while i < len(pending) and pending[i].arrival <= t:
+            r = pending[i]
+            sb.sb_sched_add(s, r.rid, r.arrival, r.prompt, r.out_len, r.max_tokens)
+            i += 1
+        if not sb.sb_sched_stats(s)["pool"]:
+            t = int(math.ceil(pending[i].arrival))
+            continue
+        ids, n_new, ctx, base = sb.sb_select_batch(s, max_bs)
+        spans = []
+        for rid, n, c, b in zip(ids, n_new, ctx, base):
+            lb, lmt = sb.sb_kv_lookup(kv, int(rid))
+            assert b == lb and lmt == mt[int(rid)]
+            assert b % 8 == 0 and c + n <= lmt
+            spans.append((int(b), int(b) + lmt))
+        spans.sort()
+        assert all(a[1] <= b[0] for a, b in zip(spans, spans[1:])) and (not spans or spans[-1][1] <= arena)
+        sb.sb_sched_complete(s, ids, np.zeros(len(ids), np.int32))
+        t += 1
+        iters += 1
+    assert sb.sb_kv_stats(kv)["n_compactions"] >= 10, sb.sb_kv_stats(kv)
+    sb.sb_sched_destroy(s)
+    sb.sb_kv_destroy(kv)
+
+
 # ---------------------------------------------------------------- scheduler vs oracle
 def native_replay(reqs, max_bs, n_slots, budget=None, chunk=None, usage=None, static=False):
     """The oracle's logical-clock loop, with the scheduling decisions made by libsb."""
@@ -576,3 +641,42 @@ def test_ragged_rejects_bad_input():
     with pytest.raises(sb.SBError) as e:
         sb.sb_ragged_build(dims, [5] * 300, [0] * 300, [0] * 300, None, buf.ctypes.data, None, 64)
     assert e.value.status in (sb.SB_ERR_WORKSPACE, sb.SB_ERR_INVALID)
+
+
+@pytest.mark.parametrize("dtype,head_dim", [("bf16", 96), ("bf16", 16), ("fp32", 48), ("fp32", 80), ("fp32", 96),
+                                            ("fp32", 112)])
+def test_ragged_rejects_head_dims_attention_lacks(dtype, head_dim):
+    """Only the head dims the attention kernel is built for pass validation (bf16 32/64/128, fp32
+    16/32/64/128): any other is refused at the first call that takes the shape, before any launch."""
+    from synth import ModelDims
+    nq = 4 if head_dim != 112 else 8
+    m = ModelDims("hd", "llama", n_layers=1, H=nq * head_dim, nq=nq, nkv=nq, d=head_dim, F=256, V=64, max_pos=0)
+    dims = make_dims(m, dtype)
+    buf = np.zeros(4096, np.int32)
+    with pytest.raises(sb.SBError) as e:
+        sb.sb_ragged_build(dims, [1], [0], [0], None, buf.ctypes.data, None, buf.nbytes)
+    assert e.value.status == sb.SB_ERR_INVALID and "head_dim" in str(e.value)
+    assert sb.sb_ragged_bytes(dims, 4, 16, 64) == 0
+    for ok in ((("bf16", d) for d in (32, 64, 128)), (("fp32", d) for d in (16, 32, 64, 128))):
+        for dt, d in ok:
+            mm = ModelDims("hd", "llama", n_layers=1, H=4 * d, nq=4, nkv=4, d=d, F=256, V=64, max_pos=0)
+            sb.sb_ragged_build(make_dims(mm, dt), [1], [0], [0], None, buf.ctypes.data, None, buf.nbytes)
+
+
+@pytest.mark.parametrize("epi", ["store", "resid", "swiglu"])
+def test_gemm_rejects_operands_past_32bit_offsets(epi):
+    """The GEMM kernels index operands with 32-bit element offsets: an operand of 2^31 elements or more is
+    refused on the host, before any launch (the pointers here are never touched).  A GPT-175B-shaped FFN2
+    at 43,691 rows has an A operand of 43,691 x 49152 > 2^31 elements."""
+    code = {"store": sb.SB_EPI_STORE, "resid": sb.SB_EPI_RESID, "swiglu": sb.SB_EPI_SWIGLU}[epi]
+    fake = 1 << 20
+    K, F = 49152, 12288
+    cases = [(43691, 12288, K, K, K, 12288, F)]                 # M * lda >= 2^31
+    cases.append((16, 12288, 4096, 4096, 1 << 18, 12288, F))     # weight rows * ldw >= 2^31
+    cases.append((1 << 17, 64, 64, 64, 64, 1 << 14, 64))         # M * ldc >= 2^31
+    if epi == "swiglu":
+        cases.append((16, 64, 4096, 4096, 4096, 64, 1 << 18))   # 2F weight rows * ldw >= 2^31
+    for M, N, Kk, lda, ldw, ldc, FF in cases:
+        with pytest.raises(sb.SBError) as e:
+            sb.sb_op_gemm(sb.SB_BF16, code, M, N, Kk, fake, lda, fake, ldw, None, fake, ldc, 0, FF)
+        assert e.value.status == sb.SB_ERR_INVALID and "2^31" in str(e.value)
