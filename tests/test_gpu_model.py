@@ -4,7 +4,7 @@ import pytest
 import torch
 
 import selective_batching_amd as sb
-from gpu_util import TOL, assert_close_elem, assert_close_rms, dev, host, print_case
+from gpu_util import TDT, TOL, assert_close_elem, assert_close_rms, dev, host, print_case
 from oracle import flat as FL
 from oracle import generate as OG
 from oracle import model as M
@@ -250,7 +250,8 @@ def test_llama8b_shape_layer_stepwise():
         sb.sb_kv_destroy(kv)
 
 
-def _gpu_generate(m, dtype, W, reqs, max_bs, n_slots, chunking=None, request_level=False, graphs=False):
+def _gpu_generate(m, dtype, W, reqs, max_bs, n_slots, chunking=None, request_level=False, graphs=False,
+                  stats=None):
     eng = Engine(m, dtype, W, n_slots=n_slots, max_bs=max_bs, max_tokens=sum(len(r.prompt) for r in reqs) + max_bs,
                  max_keys_total=sum(r.max_tokens for r in reqs), chunking=chunking, request_level=request_level,
                  graphs=graphs)
@@ -271,6 +272,8 @@ def _gpu_generate(m, dtype, W, reqs, max_bs, n_slots, chunking=None, request_lev
                 continue
             log.append((t, [(int(a), int(b), int(c)) for a, b, c in zip(res["ids"], res["n_new"], res["ctx"])]))
             t += 1
+        if stats is not None:
+            stats.update(sb.sb_kv_stats(eng.kv))
         return {r.rid: list(eng.output(r.rid)) for r in reqs}, log
     finally:
         eng.close()
@@ -441,7 +444,8 @@ def test_pipelined_launches_match_sequential_steps():
         eng.close()
 
 
-def _gpu_generate_chained(m, dtype, W, reqs, max_bs, n_slots, chunking=None, request_level=False, graphs=False):
+def _gpu_generate_chained(m, dtype, W, reqs, max_bs, n_slots, chunking=None, request_level=False, graphs=False,
+                          stats=None):
     """As _gpu_generate, but one iteration ahead of the host (Engine.run_chained): decodes embed the
     previous iteration's ids straight from its device buffer."""
     eng = Engine(m, dtype, W, n_slots=n_slots, max_bs=max_bs, max_tokens=sum(len(r.prompt) for r in reqs) + max_bs,
@@ -451,6 +455,8 @@ def _gpu_generate_chained(m, dtype, W, reqs, max_bs, n_slots, chunking=None, req
         log = []
         eng.run_chained(reqs, on_iteration=lambda res: log.append(
             (res["t"], [(int(a), int(b), int(c)) for a, b, c in zip(res["ids"], res["n_new"], res["ctx"])])))
+        if stats is not None:
+            stats.update(sb.sb_kv_stats(eng.kv))
         return {r.rid: list(eng.output(r.rid)) for r in reqs}, log
     finally:
         eng.close()
@@ -482,8 +488,123 @@ def test_generation_chained_bf16_trace_matches_synchronous():
     reqs = poisson_trace(seed=3, n=40, rate=0.4, vocab=m.V, plo=1, phi=40, olo=1, ohi=24, reserve_out=24,
                          with_prompts=True)
     n_slots = 300
-    got, log = _gpu_generate_chained(m, "bf16", W, reqs, 6, n_slots)
+    st = {}
+    got, log = _gpu_generate_chained(m, "bf16", W, reqs, 6, n_slots, stats=st)
     sync, slog = _gpu_generate(m, "bf16", W, reqs, 6, n_slots)
+    assert log == slog
+    assert got == sync
+    print(f"[case] K/V compactions: {st['n_compactions']}", flush=True)
+
+
+# ---------------------------------------------------------------- binding reservations: K/V compaction
+# Traces whose reservations bind (the lecture's Pow2 and Oracle policies, few slots), chosen so that the
+# K/V manager has to compact live ranges several times in mid-generation: a request admitted then finds no
+# hole, and the histories of requests still decoding are moved to lower slots between two iterations.
+BINDING = {"pow2": dict(seed=61, max_bs=10, n_slots=260), "oracle": dict(seed=63, max_bs=12, n_slots=300)}
+
+
+def _binding_trace(policy, vocab):
+    from synth import poisson_trace
+    from oracle import scheduler as OS
+    code = {"pow2": sb.SB_RESERVE_POW2, "oracle": sb.SB_RESERVE_ORACLE}[policy]
+    reqs = poisson_trace(seed=BINDING[policy]["seed"], n=100, rate=1.0, vocab=vocab, plo=1, phi=48, olo=1, ohi=24,
+                         reserve_out=24, with_prompts=True)
+    for r in reqs:
+        r.max_tokens = sb.sb_reservation_tokens(code, len(r.prompt), r.out_len, 24)
+        assert r.max_tokens == OS.reservation(policy, len(r.prompt), r.out_len, 24)
+    return reqs
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_kv_compaction_moves_history_bitwise(dtype):
+    """The manager's device copies: four requests fill a 3-layer arena with distinct K/V rows, two are
+    freed, and a reservation that fits the counter but no hole compacts the arena.  Every surviving row,
+    read back at the request's new base, equals what was written (K rows and the 8-slot V blocks)."""
+    nl, nkv, d = 3, 2, 32
+    es = 2 if dtype == "bf16" else 4
+    n_slots = 96
+    arena = n_slots
+    nb = sb.sb_kv_arena_bytes(arena, nl, nkv, d, sb.SB_BF16 if dtype == "bf16" else sb.SB_F32)
+    assert nb == arena * nl * nkv * d * es
+    ka = torch.zeros(nb, dtype=torch.uint8, device="cuda")
+    va = torch.zeros(nb, dtype=torch.uint8, device="cuda")
+    kv = sb.sb_kv_create(n_slots, arena, nl, nkv, d, sb.SB_BF16 if dtype == "bf16" else sb.SB_F32,
+                         ka.data_ptr(), va.data_ptr())
+    sb.sb_kv_set_stream(kv, stream_handle())
+    try:
+        sizes = {0: 16, 1: 29, 2: 8, 3: 40}          # 16 + 32 + 8 + 40 physical slots = 96
+        base = {r: sb.sb_kv_reserve(kv, r, n) for r, n in sizes.items()}
+        assert base == {0: 0, 1: 16, 2: 48, 3: 56}
+        rows = {}
+        keep = []
+        for r, n in sizes.items():
+            for l in range(nl):
+                k = normal(7, f"cmp.k{r}.{l}", (n, nkv, d), dtype=dtype)
+                v = normal(7, f"cmp.v{r}.{l}", (n, nkv, d), dtype=dtype)
+                rows[r, l] = (k, v)
+                slots = torch.arange(base[r], base[r] + n, dtype=torch.int32, device="cuda")
+                dk, dv = dev(k, dtype), dev(v, dtype)
+                keep += [slots, dk, dv]
+                sb.sb_kv_write(kv, l, n, slots.data_ptr(), dk.data_ptr(), dv.data_ptr(), stream_handle())
+        sb.sb_kv_free(kv, 0)
+        sb.sb_kv_free(kv, 2)                          # holes of 16 and 8 slots; 69 reserved
+        sb.sb_kv_reserve(kv, 4, 24)                   # 69 + 24 <= 96, but no hole holds 24
+        st = sb.sb_kv_stats(kv)
+        assert st["n_compactions"] == 1
+        moved = {r: sb.sb_kv_lookup(kv, r)[0] for r in (1, 3)}
+        assert moved == {1: 0, 3: 32} and sb.sb_kv_lookup(kv, 4)[0] == 72
+        for r in (1, 3):
+            n = sizes[r]
+            slots = torch.arange(moved[r], moved[r] + n, dtype=torch.int32, device="cuda")
+            for l in range(nl):
+                gk = torch.empty((n, nkv * d), dtype=TDT[dtype], device="cuda")
+                gv = torch.empty((n, nkv * d), dtype=TDT[dtype], device="cuda")
+                sb.sb_kv_read(kv, l, n, slots.data_ptr(), gk.data_ptr(), gv.data_ptr(), stream_handle())
+                torch.cuda.synchronize()
+                k, v = rows[r, l]
+                assert np.array_equal(host(gk), k.reshape(n, nkv * d)), f"request {r} layer {l}: K rows"
+                assert np.array_equal(host(gv), v.reshape(n, nkv * d)), f"request {r} layer {l}: V rows"
+    finally:
+        sb.sb_kv_destroy(kv)
+
+
+@pytest.mark.parametrize("policy", ["pow2", "oracle"])
+def test_generation_binding_reservations_matches_oracle(policy):
+    """Toy fp32 model on a 100-request Poisson trace under the Pow2 / Oracle reservation policy with few
+    slots: compaction moves live K/V several times during generation.  Synchronous and chained loops
+    schedule exactly as the oracle's replay and generate the oracle's ids, bit-exact."""
+    from oracle import scheduler as OS
+    m = TOY
+    Wh = make_weights(m, 0, "fp32")
+    W = DeviceWeights(m, "fp32", host=Wh)
+    reqs = _binding_trace(policy, m.V)
+    cfg = BINDING[policy]
+    print_case("binding reservations", policy, cfg)
+    want, olog = OG.generate_continuous(m, Wh, reqs, max_bs=cfg["max_bs"], n_slots=cfg["n_slots"])
+    assert [w for _, w, _ in olog] == [w for _, w, _ in OS.replay(reqs, cfg["max_bs"], cfg["n_slots"])]
+    for gen in (_gpu_generate, _gpu_generate_chained):
+        st = {}
+        got, log = gen(m, "fp32", W, reqs, cfg["max_bs"], cfg["n_slots"], stats=st)
+        print(f"[case] {gen.__name__}: {len(log)} iterations, {st['n_compactions']} compactions", flush=True)
+        assert st["n_compactions"] >= 3
+        assert log == [(t, w) for t, w, _ in olog]
+        bad = [r.rid for r in reqs if got[r.rid] != want[r.rid]]
+        assert not bad, f"requests {bad[:5]}: gpu {got[bad[0]]} oracle {want[bad[0]]}"
+
+
+@pytest.mark.parametrize("policy", ["pow2", "oracle"])
+def test_generation_binding_reservations_bf16_chained_equals_synchronous(policy):
+    """GQA + RoPE bf16 model on the same binding traces: chained and synchronous generation compact the
+    K/V arena several times and still give identical schedules and identical ids (bitwise)."""
+    m = TINY_LLAMA
+    W = DeviceWeights(m, "bf16", host=make_weights(m, 4, "bf16"))
+    reqs = _binding_trace(policy, m.V)
+    cfg = BINDING[policy]
+    print_case("binding reservations bf16", policy, cfg)
+    s1, s2 = {}, {}
+    got, log = _gpu_generate_chained(m, "bf16", W, reqs, cfg["max_bs"], cfg["n_slots"], stats=s1)
+    sync, slog = _gpu_generate(m, "bf16", W, reqs, cfg["max_bs"], cfg["n_slots"], stats=s2)
+    assert s1["n_compactions"] >= 3 and s2["n_compactions"] == s1["n_compactions"]
     assert log == slog
     assert got == sync
 
