@@ -53,3 +53,24 @@ def assert_close_elem(got, want, dtype, what=""):
     bound = u * np.abs(want) + 1e-5 * rms(want)     # absolute term: fp32 sums with cancellation
     bad = np.abs(got - want) > bound
     assert not bad.any(), f"{what}: {int(bad.sum())} elements off; worst {float(np.max(np.abs(got - want) - bound)):.3e}"
+
+
+def assert_close_attention(got, want, want_abs, dtype, what=""):
+    """Element-wise bound for the attention kernel's output.
+
+    bf16: one rounding of the result (as ``assert_close_elem``) plus the error of the probabilities.  The
+    kernel feeds each probability p_k to the P.V product as a hi + lo pair of bf16 values, 16 significant
+    bits, so p_k carries a relative error of at most 2^-17 (scores and exp2 add far less).  The output error
+    is then at most eps * sum_k p_k |v_k| / sum_k p_k, which is the attention of the same q and K over |V|
+    (``want_abs``); eps = 2^-15 leaves a factor of 4.  Against the row's RMS this term is not small for a
+    prompt row spread over hundreds of keys, whose output (a mean of many values) is much smaller than the
+    values themselves.  fp32 rows: ``assert_close_elem``."""
+    if dtype != "bf16":
+        return assert_close_elem(got, want, dtype, what)
+    got = np.asarray(got, np.float64)
+    want = np.asarray(want, np.float64)
+    want_abs = np.asarray(want_abs, np.float64)
+    assert got.shape == want.shape == want_abs.shape, (what, got.shape, want.shape, want_abs.shape)
+    bound = 2.0 ** -7 * np.abs(want) + 2.0 ** -15 * want_abs + 1e-6 * rms(want)
+    bad = np.abs(got - want) > bound
+    assert not bad.any(), f"{what}: {int(bad.sum())} elements off; worst {float(np.max(np.abs(got - want) - bound)):.3e}"

@@ -4,7 +4,7 @@ import pytest
 import torch
 
 import selective_batching_amd as sb
-from gpu_util import TDT, TOL, assert_close_elem, assert_close_rms, dev, host, print_case
+from gpu_util import TDT, TOL, assert_close_attention, assert_close_elem, assert_close_rms, dev, host, print_case
 from oracle import flat as FL
 from oracle import generate as OG
 from oracle import model as M
@@ -149,7 +149,8 @@ def test_llama8b_shape_layer_stepwise():
     entry points; every intermediate of sampled requests is checked against the oracle."""
     m, dtype = LLAMA8B, "bf16"
     batch = llama_mixed_batch(seed=0)
-    sample = [0, 57, 239] + sorted(range(240, 256), key=lambda i: batch[i][0])[:1]
+    pre = sorted(range(240, 256), key=lambda i: batch[i][0])
+    sample = [0, 57, 239] + [pre[0], pre[-1]]             # the shortest and the longest prompt
     print_case("8b stepwise", sample)
     from selective_batching_amd.runtime import make_dims
     wl = make_layer_weights(m, 3, 0, dtype)
@@ -238,7 +239,8 @@ def test_llama8b_shape_layer_stepwise():
             v = qkv_pre[r, nq_d + nkv_d:].reshape(n, m.nkv, m.d)
             K = np.concatenate([caches[i][0], kg]); V = np.concatenate([caches[i][1], v])
             att = M.attention(qg, K, V, c, m.group).reshape(n, nq_d)
-            assert_close_elem(o1[r], att, dtype, f"req {i} (n {n}, ctx {c}) attention")
+            att_abs = M.attention(qg, K, np.abs(V), c, m.group).reshape(n, nq_d)
+            assert_close_attention(o1[r], att, att_abs, dtype, f"req {i} (n {n}, ctx {c}) attention")
             ra = float(np.max(np.abs(o1[r] - att)) / np.sqrt(np.mean(att ** 2)))
             assert_close_rms(x1[r], xi + M.linear(o1[r], w64["w_o"]), 1e-5, f"req {i} x after attention")
             assert_close_elem(h2[r], M.rms_norm(x1[r], w64["ln2_g"], m.eps), dtype, f"req {i} norm2")
@@ -346,12 +348,15 @@ def _sampled_layer_parity(m, dtype, batch, sample, seed, kv_std):
         for i in sample:
             n, c = batch[i]
             got = host(got_all[cu[i]:cu[i + 1]])
-            want_store = M.layer_forward(m, wl, x_in[cu[i]:cu[i + 1]], c, copy.deepcopy(caches[i]), store=dtype)
-            want = M.layer_forward(m, wl, x_in[cu[i]:cu[i + 1]], c, caches[i])
+            # layer_forward extends the cache it is given: each call takes its own copy
+            want = M.layer_forward(m, wl, x_in[cu[i]:cu[i + 1]], c, copy.deepcopy(caches[i]))
             tol_exact = TOL[dtype]
-            r1 = float(np.max(np.abs(got - want_store)) / np.sqrt(np.mean(want_store ** 2)))
             r2 = assert_close_rms(got, want, tol_exact, f"{m.name} request {i} (n_new {n}, ctx {c}) exact")
-            print(f"[parity] {m.name} request {i} (n_new {n}, ctx {c}): {r1:.2e} (storage oracle), "
+            note = ""
+            if n <= 64:          # the storage-precision oracle (reported only) for the short ones: host time
+                want_store = M.layer_forward(m, wl, x_in[cu[i]:cu[i + 1]], c, copy.deepcopy(caches[i]), store=dtype)
+                note = f"{float(np.max(np.abs(got - want_store)) / np.sqrt(np.mean(want_store ** 2))):.2e} (storage oracle), "
+            print(f"[parity] {m.name} request {i} (n_new {n}, ctx {c}): {note}"
                   f"{r2:.2e} (exact oracle, bar {tol_exact})", flush=True)
     finally:
         eng.close()
@@ -361,8 +366,9 @@ def test_llama8b_shape_layer_sampled():
     """Llama-3-8B-shaped layer over the 256-request mixed batch (240 decodes + 16 prefills); sampled requests."""
     batch = llama_mixed_batch(seed=0)
     dec = [0, 1, 57, 119, 200, 239]
-    pre = sorted(range(240, 256), key=lambda i: batch[i][0])[:2]
-    _sampled_layer_parity(LLAMA8B, "bf16", batch, dec + pre, 0, kv_std(LLAMA8B))
+    pre = sorted(range(240, 256), key=lambda i: batch[i][0])
+    # the two shortest prompts, a median one and the longest: the row tiles far past the causal diagonal
+    _sampled_layer_parity(LLAMA8B, "bf16", batch, dec + pre[:2] + [pre[len(pre) // 2], pre[-1]], 0, kv_std(LLAMA8B))
 
 
 def test_llama8b_shape_lm_head_sampled():
@@ -396,8 +402,10 @@ def test_llama8b_shape_lm_head_sampled():
 def test_gpt175b_shape_layer_sampled():
     """GPT-175B-shaped layer (H 12288, 96 heads, FFN 49152) over 96 decodes + 32 prefills; sampled requests."""
     batch = gpt175b_mixed_batch(seed=0)
-    pre = sorted(range(96, 128), key=lambda i: batch[i][0])[:1]
-    _sampled_layer_parity(GPT175B_LAYER, "bf16", batch, [0, 50, 95] + pre, 0, kv_std(GPT175B_LAYER))
+    pre = sorted(range(96, 128), key=lambda i: batch[i][0])
+    # the shortest, a median and the longest prompt (1012 tokens: 16 row tiles of 128 past the diagonal)
+    _sampled_layer_parity(GPT175B_LAYER, "bf16", batch, [0, 50, 95] + [pre[0], pre[len(pre) // 2], pre[-1]], 0,
+                          kv_std(GPT175B_LAYER))
 
 
 def test_pipelined_launches_match_sequential_steps():

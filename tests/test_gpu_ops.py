@@ -6,7 +6,7 @@ import pytest
 import torch
 
 import selective_batching_amd as sb
-from gpu_util import TOL, assert_close_elem, assert_close_rms, dev, host, print_case
+from gpu_util import TOL, assert_close_attention, assert_close_elem, assert_close_rms, dev, host, print_case
 from oracle import model as OM
 from synth import ModelDims, bf16_round, normal, random_ragged_batch, synthetic_kv
 from selective_batching_amd.runtime import make_dims, stream_handle
@@ -188,6 +188,7 @@ def _attention_case(m: ModelDims, dtype, batch, seed, rope_check=False):
         got = host(o)
         got_qkv = host(dqkv)
         want = np.zeros_like(got)
+        want_abs = np.zeros_like(got)
         t0 = 0
         nq_d, nkv_d = m.nq * m.d, m.nkv * m.d
         for i, (n, c) in enumerate(batch):
@@ -206,9 +207,11 @@ def _attention_case(m: ModelDims, dtype, batch, seed, rope_check=False):
             K = np.concatenate([hist[i][0].astype(np.float64), k], axis=0)
             V = np.concatenate([hist[i][1].astype(np.float64), v], axis=0)
             want[rows] = OM.attention(q, K, V, c, G).reshape(n, nq_d)
+            want_abs[rows] = OM.attention(q, K, np.abs(V), c, G).reshape(n, nq_d)
             t0 += n
-        # one rounding of the exact attention of the stored q, k, v (fp32: a few fp32 operations)
-        assert_close_elem(got, want, dtype, f"attention {m.name} {dtype}")
+        # one rounding of the exact attention of the stored q, k, v (fp32: a few fp32 operations; bf16: plus
+        # the probabilities' 16-bit hi + lo representation)
+        assert_close_attention(got, want, want_abs, dtype, f"attention {m.name} {dtype}")
         # the appended rows landed in their slots (V is copied as is; K too unless rotated)
         np.testing.assert_array_equal(host(vv_new).reshape(T, -1), qkv[:, nq_d + nkv_d:])
         if m.arch == "gpt":
@@ -495,7 +498,8 @@ def test_attention_unit_merge_is_batch_invariant():
         _sync()
         q = host(qkv_all[0:1, :m.nq * m.d]).reshape(1, m.nq, m.d)
         want = OM.attention(q, host(kk), host(vv), c, G).reshape(1, -1)
-        assert_close_elem(host(o_big[0:1]), want, "bf16", "attention of a merged request")
+        want_abs = OM.attention(q, host(kk), np.abs(host(vv)), c, G).reshape(1, -1)
+        assert_close_attention(host(o_big[0:1]), want, want_abs, "bf16", "attention of a merged request")
     finally:
         sb.sb_kv_destroy(kv)
 
