@@ -48,6 +48,22 @@ int sb_op_rope_append(const sb_model_dims* dims, const sb_ragged* rg, const sb_k
 int sb_op_attention(const sb_model_dims* dims, const sb_ragged* rg, const sb_kv* kv, int32_t layer, const void* qkv,
                     void* o, void* workspace, size_t ws_bytes, void* stream);
 
+/* sb_op_attention without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  The split-attention unit partials go to
+ * a static device array of SB_ATTN_NOALLOC_SCRATCH_BYTES that the library
+ * holds on every GPU it runs on until the process ends (its address is taken
+ * on the first call on each device).  The call allocates nothing and frees
+ * nothing.  Every call on one GPU shares that GPU's array: calls that overlap
+ * on one GPU (two streams, or two threads) race and give undefined results.
+ * Each partial a call reads is written earlier in the same call, so nothing
+ * carries over from the previous call.  SB_ERR_WORKSPACE if the batch needs
+ * more than the array holds (n_partials * 16 * (head_dim + 2) * 4 bytes);
+ * other arguments and errors as sb_op_attention. */
+#define SB_ATTN_NOALLOC_SCRATCH_BYTES (64u << 20)
+int sb_op_attention_noalloc(const sb_model_dims* dims, const sb_ragged* rg, const sb_kv* kv, int32_t layer,
+                            const void* qkv, void* o, void* stream);
+
 /* out[r] = index of the largest of logits[r, 0..V) (lowest index on ties). */
 int sb_op_argmax(int32_t rows, int32_t V, const float* logits, int32_t* out, void* stream);
 

@@ -13,6 +13,7 @@ from ._lib import (  # noqa: F401
     SB_F32, SB_BF16, SB_ARCH_GPT, SB_ARCH_LLAMA,
     SB_EPI_STORE, SB_EPI_GELU, SB_EPI_RESID, SB_EPI_SWIGLU,
     SB_RESERVE_MAX, SB_RESERVE_POW2, SB_RESERVE_ORACLE,
+    SB_ATTN_NOALLOC_SCRATCH_BYTES,
     KERNEL_CLASSES,
     sb_model_dims, sb_layer_weights, sb_model_weights, sb_ragged,
 )

@@ -16,6 +16,7 @@ SB_F32, SB_BF16 = 0, 1
 SB_ARCH_GPT, SB_ARCH_LLAMA = 0, 1
 SB_EPI_STORE, SB_EPI_GELU, SB_EPI_RESID, SB_EPI_SWIGLU = 0, 1, 2, 3
 SB_RESERVE_MAX, SB_RESERVE_POW2, SB_RESERVE_ORACLE = 0, 1, 2
+SB_ATTN_NOALLOC_SCRATCH_BYTES = 64 << 20
 (SB_K_GEMM_QKV, SB_K_GEMM_O, SB_K_GEMM_FFN1, SB_K_GEMM_FFN2, SB_K_GEMM_LM, SB_K_ATTN, SB_K_ATTN_COMBINE,
  SB_K_NORM, SB_K_ROPE_APPEND, SB_K_EMBED, SB_K_ARGMAX, SB_K_COUNT) = range(12)
 KERNEL_CLASSES = ["gemm_qkv", "gemm_o", "gemm_ffn1", "gemm_ffn2", "gemm_lm", "attention", "attention_combine",
@@ -115,6 +116,7 @@ _PROTOS = {
     "sb_op_norm": (C.c_int, [i32, i32, i32, i32, vp, vp, vp, vp, f32, vp, vp]),
     "sb_op_rope_append": (C.c_int, [P(sb_model_dims), P(sb_ragged), vp, i32, vp, vp]),
     "sb_op_attention": (C.c_int, [P(sb_model_dims), P(sb_ragged), vp, i32, vp, vp, vp, sz, vp]),
+    "sb_op_attention_noalloc": (C.c_int, [P(sb_model_dims), P(sb_ragged), vp, i32, vp, vp, vp]),
     "sb_op_argmax": (C.c_int, [i32, i32, vp, vp, vp]),
 }
 

@@ -279,5 +279,9 @@ def sb_op_attention(dims, rg, kv, layer, qkv, o, ws, ws_bytes, stream=None):
     call("sb_op_attention", C.byref(dims), C.byref(rg), kv, layer, qkv, o, ws, ws_bytes, stream)
 
 
+def sb_op_attention_noalloc(dims, rg, kv, layer, qkv, o, stream=None):
+    call("sb_op_attention_noalloc", C.byref(dims), C.byref(rg), kv, layer, qkv, o, stream)
+
+
 def sb_op_argmax(rows, V, logits, out, stream=None):
     call("sb_op_argmax", rows, V, logits, out, stream)

@@ -34,8 +34,10 @@
 //     waves share every K/V byte, with the global loads of the next two tiles
 //     in flight in registers while a tile computes.
 #include <cfloat>
+#include <mutex>
 
 #include "sb_device.h"
+#include "sb_ops.h"
 
 namespace sb {
 namespace {
@@ -720,3 +722,56 @@ int launch_attention(const sb_model_dims* dims, const sb_ragged* rg, const void*
 }
 
 }  // namespace sb
+
+// ------------------------------------------------------------------ allocation-free attention
+// A variant of sb_op_attention whose unit partials live in a file-scope device array instead of a
+// caller-provided workspace.  Host code must never pass `scratch` itself to a kernel: in host code
+// the name is a stand-in, not a device address.  Its address on each device comes from
+// hipGetSymbolAddress, taken once per device with that device current and kept in g_scratch_dev.
+static __device__ __align__(256) unsigned char scratch[SB_ATTN_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (taken on the first call on that device).
+int scratch_address(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return sb::fail(SB_ERR_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return sb::fail(SB_ERR_DEVICE, "device %d out of range", dev);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return sb::fail(SB_ERR_DEVICE, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+        g_scratch_dev[dev] = p;
+    }
+    *out = g_scratch_dev[dev];
+    return SB_OK;
+}
+}  // namespace
+
+extern "C" int sb_op_attention_noalloc(const sb_model_dims* dims, const sb_ragged* rg, const sb_kv* kv, int32_t layer,
+                                       const void* qkv, void* o, void* stream) {
+    int st = sb::validate_dims(dims);
+    if (st) return st;
+    if (!rg || !kv || !qkv || !o) return sb::fail(SB_ERR_INVALID, "sb_op_attention_noalloc: NULL argument");
+    const size_t need = (size_t)rg->n_partials * 16 * (dims->head_dim + 2) * 4;
+    if (need > (size_t)SB_ATTN_NOALLOC_SCRATCH_BYTES)
+        return sb::fail(SB_ERR_WORKSPACE, "attention partials need %zu bytes, the static scratch holds %zu", need,
+                        (size_t)SB_ATTN_NOALLOC_SCRATCH_BYTES);
+    void *kp, *vp;
+    if ((st = sb_kv_layer_ptrs(kv, layer, &kp, &vp))) return st;
+    float* po = nullptr;
+    float* pm = nullptr;
+    if (rg->n_partials > 0) {
+        void* base = nullptr;
+        if ((st = scratch_address(&base))) return st;
+        po = (float*)base;
+        pm = po + (size_t)rg->n_partials * 16 * dims->head_dim;
+    }
+    return sb::launch_attention(dims, rg, kp, vp, kv->arena_slots, qkv, o, po, pm, (hipStream_t)stream);
+}
