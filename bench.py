@@ -26,9 +26,13 @@ kernel (the FFN1 SwiGLU GEMM, MFMA-bound); the attention's HBM bandwidth over
 the mixed batch and, launched alone, over its decodes (``decode_attention``,
 the launches cycling through four layers of K/V so that none is served from
 the caches); a per-class breakdown from three extra steps with every class
-timed; the serving trace, the reservation-policy replay, iteration- against
-request-level scheduling and the mini-model decode loop; and the CPU oracle
-timed on a bounded sample of the same workload.
+timed; one GPT-175B-shaped layer over its 96-decode + 32-prefill batch
+(``gpt175b_layer``); the whole 2000-request serving trace on the 8B-shaped
+model with its K/V pool at 60% of the free HBM, overall and steady-state
+throughput and a per-iteration JSONL log (``trace``); the reservation-policy
+replay, iteration- against request-level scheduling and the mini-model decode
+loop; and the CPU oracle timed on one layer over the whole batch, per request
+and flattened, extrapolated to the iteration.
 
 Other modes (each prints its own JSON line instead): ``--op-gemm M,N,K,EPI``
 times one GEMM shape; ``--gpt175b-layer`` times one GPT-175B-shaped layer over
@@ -58,6 +62,9 @@ def parse():
     ap.add_argument("--no-decode-loop", action="store_true", help="skip the mini-model generation loop")
     ap.add_argument("--no-trace", action="store_true", help="skip the serving-trace window and the policy replay")
     ap.add_argument("--layers", type=int, default=32, help="decoder layers (the workload has 32)")
+    ap.add_argument("--log-dir", default=os.path.join(ROOT, "gpurun_out"),
+                    help="directory of the serving trace's per-iteration JSONL log ('' for none)")
+    ap.add_argument("--no-gpt175b", action="store_true", help="skip the GPT-175B-shaped layer figures")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one 1 GiB device-to-device copy before the steps (calibrates HBM counters)")
     ap.add_argument("--op-gemm", default=None, metavar="M,N,K,EPI",
@@ -107,7 +114,8 @@ def op_gemm(spec, steps, warmup, seed):
 def gpt175b_layer(steps, warmup, seed):
     """One GPT-175B-shaped layer (H 12288, 96 heads x 128, FFN 49152 GeLU; random init, bf16) over its ragged
     batch of 96 decodes (ctx U[512,2048]) + 32 prefills (prompt U[128,1024]) with random K/V history:
-    the layer step timed with HIP events, then the same steps with every kernel class timed."""
+    the layer step timed with HIP events, then the same steps with every kernel class timed.  Returns the
+    figures as a dict."""
     import torch
     import selective_batching_amd as sb
     from selective_batching_amd import api as A
@@ -162,7 +170,9 @@ def gpt175b_layer(steps, warmup, seed):
     att_bytes = sum((c + n) * kv_row for n, c in batch) + T * m.nq * m.d * 2 * 2
     att_flops = 4 * m.d * m.nq * sum(sum(c + j + 1 for j in range(n)) for n, c in batch)
     gemm_ms = sum(cls[k] for k in flops)
-    print(json.dumps({
+    del eng, W, xv
+    torch.cuda.empty_cache()
+    return {
         "workload": ("GPT-175B-shaped layer (hidden 12288, 96 heads x 128, FFN 49152 GeLU), random init, bf16; "
                      "96 decodes (ctx U[512,2048]) + 32 prefills (prompt U[128,1024])"),
         "tokens": T, "layer_ms": round(layer_ms, 3), "steps": steps, "warmup": warmup,
@@ -172,7 +182,7 @@ def gpt175b_layer(steps, warmup, seed):
                      "frac": round(sum(flops.values()) / (gemm_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)},
         "attention": {"gbs": round(att_bytes / (cls["attention"] * 1e-3) / 1e9, 1), "bytes": att_bytes,
                       "tflops": round(att_flops / (cls["attention"] * 1e-3) / 1e12, 1), "flops": att_flops},
-        "tokens_per_s": round(T / (layer_ms * 1e-3), 1)}), flush=True)
+        "tokens_per_s": round(T / (layer_ms * 1e-3), 1)}
 
 
 def algorithmic_work(m, batch, n_layers):
@@ -293,39 +303,58 @@ def decode_attention(m, batch, seed, launches=20, layers=4):
             "launches": launches}
 
 
-def cpu_baseline(m, batch, seed):
-    """The oracle (fp64 numpy, per-request plain definition) on a bounded sample of the workload."""
+def cpu_baseline(m, batch, seed, lm_sample=8):
+    """The oracle (fp64 numpy, as it stands) on one decoder layer over the whole batch -- the 240 decodes
+    with their synthetic K/V history and the 16 prompts, 3741 rows at seed 0 -- timed two ways: per request
+    (the plain definition: each request's rows through the layer on their own) and flattened (the
+    oracle's [T, H] self-check: token-wise operators on all rows at once, attention split by request).
+    The iteration is then extrapolated: the layer x 32 plus the LM head (final norm, 128256-way product,
+    argmax) of each request's last row, timed on ``lm_sample`` rows one at a time (per request) and on all
+    rows at once (flattened).  BLAS uses every host thread."""
     import numpy as np
+    from oracle import flat as FL
     from oracle import model as OM
     from synth import kv_std, make_layer_weights, normal, synthetic_kv, init_std
     cores = len(os.sched_getaffinity(0))
-    wl = make_layer_weights(m, seed, 0, "bf16")
-    dec_idx = [i for i, (n, _) in enumerate(batch) if n == 1][:6]
-    pre_idx = sorted([i for i, (n, _) in enumerate(batch) if n > 1], key=lambda i: batch[i][0])[:1]
-    sample = dec_idx + pre_idx
-    inputs = []
-    for i in sample:
-        n, c = batch[i]
+    wl = {k: np.asarray(v, np.float64) for k, v in make_layer_weights(m, seed, 0, "bf16").items()}
+    T = sum(n for n, _ in batch)
+    B = len(batch)
+    caches = []
+    for i, (n, c) in enumerate(batch):
         hk, hv = synthetic_kv(seed, f"cpu{i}", c, m.nkv, m.d, kv_std(m), "bf16")
-        x = normal(seed, f"cpu.x{i}", (n, m.H))
-        inputs.append((x, c, {"k": hk.astype(np.float64), "v": hv.astype(np.float64)}))
+        caches.append({"k": hk.astype(np.float64), "v": hv.astype(np.float64)})
+    x = normal(seed, "cpu.x", (T, m.H)).astype(np.float64)
+    cu = np.concatenate([[0], np.cumsum([n for n, _ in batch])])
     t0 = time.perf_counter()
-    for x, c, cache in inputs:
-        OM.layer_forward(m, wl, x, c, cache)
-    t_layer = time.perf_counter() - t0
-    del wl
-    w_lm = normal(seed, "cpu.w_lm", (m.V, m.H), std=init_std(m.H), dtype="bf16")
-    W = {"lnf_g": np.ones(m.H, np.float32), "w_lm": w_lm}
+    for i, (n, c) in enumerate(batch):
+        OM.layer_forward(m, wl, x[cu[i]:cu[i + 1]], c, dict(caches[i]))
+    t_req = time.perf_counter() - t0
     t0 = time.perf_counter()
-    for x, _, _ in inputs:
-        OM.lm_logits(m, W, x[-1])
-    t_lm = time.perf_counter() - t0
-    tokens = sum(batch[i][0] for i in sample)
-    est = t_layer * m.n_layers + t_lm
-    return {"value": tokens / est, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": (f"{len(dec_idx)} decodes + {len(pre_idx)} prefill of the same batch ({tokens} tokens), "
-                       f"one decoder layer timed ({t_layer:.2f} s) x {m.n_layers} layers + LM head "
-                       f"({t_lm:.2f} s); fp64 numpy, BLAS threads = {cores}")}
+    FL.layer_forward_flat(m, wl, x, batch, [dict(c) for c in caches])
+    t_flat = time.perf_counter() - t0
+    del wl, caches
+    W = {"lnf_g": np.ones(m.H), "w_lm": normal(seed, "cpu.w_lm", (m.V, m.H), std=init_std(m.H),
+                                               dtype="bf16").astype(np.float64)}
+    last = x[cu[1:] - 1]
+    t0 = time.perf_counter()
+    for r in range(lm_sample):
+        OM.greedy(OM.lm_logits(m, W, last[r]))
+    t_lm_req = (time.perf_counter() - t0) * B / lm_sample
+    t0 = time.perf_counter()
+    np.argmax(OM.linear(OM.final_norm(m, W, last), W["w_lm"]), axis=1)
+    t_lm_flat = time.perf_counter() - t0
+    est_req = t_req * m.n_layers + t_lm_req
+    est_flat = t_flat * m.n_layers + t_lm_flat
+    return {"value": round(T / est_req, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": (f"one decoder layer over the whole batch ({B} requests, {T} rows), per request: "
+                       f"{t_req:.2f} s; x {m.n_layers} layers + the LM head of each request's last row "
+                       f"({lm_sample} rows timed, x {B // lm_sample}: {t_lm_req:.2f} s) = {est_req:.1f} s per iteration, "
+                       f"extrapolated; fp64 numpy, BLAS threads = {cores}"),
+            "flattened": {"value": round(T / est_flat, 3), "unit": "tokens/s",
+                          "layer_s": round(t_flat, 3), "lm_head_s": round(t_lm_flat, 3),
+                          "iteration_s_extrapolated": round(est_flat, 2)},
+            "per_request_layer_s": round(t_req, 3), "iteration_s_extrapolated": round(est_req, 2),
+            "batched_speedup": round(est_req / est_flat, 2)}
 
 
 def cpu_mini(seed):
@@ -481,43 +510,80 @@ def reservation_policies(seed, n_slots=20000):
     return out
 
 
-def trace_run(W, m, seed, iters=600, steady_from=200):
-    """The first ``iters`` iterations of the 8B-shaped serving trace on the GPU (Poisson arrivals at 0.5 per
-    iteration, prompt U[32,512], output U[1,512], max_tokens = prompt + 512, max_bs 64, K/V pool not
-    binding), run chained (iteration t+1 launched before t's ids reach the host).  Reports processed
-    (prompt + decode) and generated tokens per second over the window and over its steady part (from
-    iteration ``steady_from``, once the batch is full)."""
+SLOT_BYTES_8B = 2 * 32 * 8 * 128 * 2     # one K/V slot of the 8B-shaped model: K and V, 32 layers, 8 heads x 128, bf16
+
+
+def trace_slots(frac=0.6):
+    """K/V slots of the serving trace by its rule: 60% of the HBM free now, over the bytes one slot takes
+    (K and V of one token in every layer)."""
+    import torch
+    free, _ = torch.cuda.mem_get_info()
+    return int(frac * free) // SLOT_BYTES_8B, int(free)
+
+
+def trace_run(W, m, seed, log_path=None, iters=None):
+    """The 8B-shaped serving trace on the GPU, run to the end: 2000 requests, Poisson arrivals at 0.5 per
+    iteration, prompt U[32,512], output U[1,512], max_tokens = prompt + 512, max_bs 64, K/V slots 60% of
+    the free HBM (1M+ slots: the pool never binds, since at most 64 x 1024 are ever reserved), chained
+    (iteration t+1 launched before t's ids reach the host).
+
+    Throughput is reported two ways ("CS349D Lecture 2", section 5.4): overall, over the whole run, and
+    steady-state, counting only up to the iteration in which the last request starts producing tokens
+    (its prefill): after that only the drain remains, a few long requests in ever smaller batches, whose
+    length depends on the longest output rather than on the scheduler.  Processed tokens count every
+    row (prompt tokens + decodes), generated tokens one per member.  Each iteration is logged as one JSON
+    line: clock t, batch ids, rows T, prefill / decode members, reserved slots after Select, device ms
+    (HIP events around its work on the stream) and host ms (Select, metadata and launches)."""
     import torch
     from selective_batching_amd.runtime import Engine
     from synth import poisson_trace
     reqs = poisson_trace(seed=seed, n=2000, rate=0.5, vocab=m.V, with_prompts=True)
-    n_slots = 64 * 1024 + 64 * 8
-    eng = Engine(m, "bf16", W, n_slots=n_slots, max_bs=64, max_tokens=64 * 512, max_keys_total=n_slots,
+    n_slots, free = trace_slots()
+    eng = Engine(m, "bf16", W, n_slots=n_slots, max_bs=64, max_tokens=64 * 512, max_keys_total=64 * 1024,
                  zero_arena=False)
+    eng.record_events = True
     marks = []
+    log = open(log_path, "w") if log_path else None
 
     def on_it(res):
         # settled: its ids are on the host.  No device-wide wait here -- the next iteration is already
         # queued behind it, and waiting for that one would leave the GPU idle while the host launches
         # the one after.
-        marks.append((time.perf_counter(), int(res["n_new"].sum()), len(res["ids"])))
+        n_pre = int((res["ctx"] == 0).sum())
+        marks.append((time.perf_counter(), int(res["n_new"].sum()), len(res["ids"]), n_pre))
+        if log is not None:
+            log.write(json.dumps({"t": res["t"], "ids": [int(i) for i in res["ids"]], "T": int(res["n_new"].sum()),
+                                  "n_prefill": n_pre, "n_decode": len(res["ids"]) - n_pre, "n_rsrv": res["n_rsrv"],
+                                  "gpu_ms": round(res["gpu_ms"], 4), "host_ms": round(res["host_ms"], 4)}) + "\n")
 
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
     n = eng.run_chained(reqs, on_iteration=on_it, max_iters=iters)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     eng.close()
-    proc = sum(p for _, p, _ in marks)
-    gen = sum(g for _, _, g in marks)
-    st = marks[steady_from:]
-    dt = st[-1][0] - marks[steady_from - 1][0]
+    del eng
+    if log is not None:
+        log.close()
+    proc = sum(p for _, p, _, _ in marks)
+    gen = sum(g for _, _, g, _ in marks)
+    last_start = max(k for k, mk in enumerate(marks) if mk[3] > 0)       # the last request's prefill
+    st = marks[:last_start + 1]
+    st_s = st[-1][0] - t0
     return {"workload": ("8B-shaped decoder on the 2000-request Poisson trace (rate 0.5/iteration, prompt U[32,512], "
-                         f"output U[1,512], max_tokens = prompt + 512, max_bs 64): first {n} iterations, chained"),
-            "iterations": n, "processed_tokens_per_s": round(proc / wall, 1), "generated_tokens_per_s": round(gen / wall, 1),
-            "steady": {"from_iteration": steady_from, "processed_tokens_per_s": round(sum(p for _, p, _ in st) / dt, 1),
-                       "generated_tokens_per_s": round(sum(g for _, _, g in st) / dt, 1),
-                       "mean_batch": round(sum(g for _, _, g in st) / len(st), 2),
-                       "ms_per_iteration": round(1e3 * dt / len(st), 3)}}
+                         "output U[1,512], max_tokens = prompt + 512, max_bs 64), run to the end, chained"),
+            "n_slots": n_slots, "n_slots_rule": (f"floor(0.6 x {free} free HBM bytes / {SLOT_BYTES_8B} bytes per slot "
+                                                 "(K+V, 32 layers, 8 x 128, bf16)); never binding (at most 64 x 1024 "
+                                                 "reserved)"),
+            "iterations": n, "wall_s": round(wall, 3),
+            "overall": {"processed_tokens_per_s": round(proc / wall, 1), "generated_tokens_per_s": round(gen / wall, 1),
+                        "mean_batch": round(gen / len(marks), 2), "ms_per_iteration": round(1e3 * wall / len(marks), 3)},
+            "steady": {"definition": "up to the iteration in which the last request produces its first token",
+                       "iterations": len(st), "processed_tokens_per_s": round(sum(p for _, p, _, _ in st) / st_s, 1),
+                       "generated_tokens_per_s": round(sum(g for _, _, g, _ in st) / st_s, 1),
+                       "mean_batch": round(sum(g for _, _, g, _ in st) / len(st), 2),
+                       "ms_per_iteration": round(1e3 * st_s / len(st), 3)},
+            "iteration_log": os.path.relpath(log_path, ROOT) if log_path else None}
 
 
 def scheduling_compare(W, m, seed, n=96):
@@ -585,7 +651,7 @@ def main():
         op_gemm(args.op_gemm, args.steps, args.warmup, args.seed)
         return
     if args.gpt175b_layer:
-        gpt175b_layer(args.steps, args.warmup, args.seed)
+        print(json.dumps(gpt175b_layer(args.steps, args.warmup, args.seed)), flush=True)
         return
 
     import numpy as np
@@ -741,9 +807,24 @@ def main():
     }
     print("[bench] decode attention alone ...", file=sys.stderr, flush=True)
     out["decode_attention"] = decode_attention(m, batch, args.seed)
+    for pool in pools:
+        if pool is not None:
+            A.sb_sched_destroy(pool[1])
+            A.sb_kv_destroy(pool[0])
+    eng.close()
+    del eng
+    torch.cuda.empty_cache()
+    if not args.no_gpt175b:
+        print("[bench] GPT-175B-shaped layer ...", file=sys.stderr, flush=True)
+        out["gpt175b_layer"] = gpt175b_layer(10, 3, args.seed)
     if not args.no_trace:
-        print("[bench] serving trace (chained) ...", file=sys.stderr, flush=True)
-        out["trace"] = trace_run(W, m, args.seed)
+        print("[bench] serving trace, whole (chained) ...", file=sys.stderr, flush=True)
+        log_path = None
+        if args.log_dir:
+            os.makedirs(args.log_dir, exist_ok=True)
+            log_path = os.path.join(args.log_dir, "trace_iterations.jsonl")
+        out["trace"] = trace_run(W, m, args.seed, log_path=log_path)
+        torch.cuda.empty_cache()
         out["reservation_policies"] = reservation_policies(args.seed)
         print("[bench] iteration-level vs request-level scheduling ...", file=sys.stderr, flush=True)
         out["scheduling"] = scheduling_compare(W, m, args.seed)
@@ -754,11 +835,6 @@ def main():
         print("[bench] timing the CPU oracle on a sample ...", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(m.with_layers(args.layers), batch, args.seed)
         out["cpu_mini_iteration"] = cpu_mini(args.seed)
-    for pool in pools:
-        if pool is not None:
-            A.sb_sched_destroy(pool[1])
-            A.sb_kv_destroy(pool[0])
-    eng.close()
     print(json.dumps(out), flush=True)
 
 

@@ -8,6 +8,7 @@ batch, build the ragged metadata, run embed -> layers -> LM head/argmax on the
 flattened batch, bring the B new token ids back, complete the iteration.
 """
 import ctypes as C
+import time
 
 import numpy as np
 import torch
@@ -109,6 +110,9 @@ class Engine:
         shape has run before (see ``forward``)."""
         self.m, self.dtype, self.w = m, dtype, weights
         self.graphs = graphs
+        # per-iteration timing for logs: host time of each launch (Select, metadata, enqueue) and, when
+        # record_events is set, the device time of its work from a pair of HIP events on the stream
+        self.record_events = False
         self._graph_seen = {}          # iteration shape -> times seen (captured on the second)
         self._graph_cache = {}         # iteration shape -> captured torch.cuda.CUDAGraph
         self.dims = make_dims(m, dtype)
@@ -252,9 +256,11 @@ class Engine:
         values may still be on the device: members that continue from it embed its ids straight from
         its device buffer (the other ``buf``), so this launch never waits for them."""
         sched = self.sched if sched is None else sched
+        h0 = time.perf_counter()
         ids, n_new, ctx, base = A.sb_select_batch(sched, self.max_bs)
         if len(ids) == 0:
             return None
+        n_rsrv = A.sb_sched_stats(sched)["n_rsrv"]
         prev = None
         if chain is not None:
             toks, ticket = A.sb_batch_token_refs(sched, ids, self.max_tokens)
@@ -265,17 +271,24 @@ class Engine:
             toks = A.sb_batch_tokens(sched, ids, self.max_tokens)
         rg = self.build(n_new, ctx, base, toks, buf)
         outs = [] if keep else None
+        start = None
+        if self.record_events:
+            start = torch.cuda.Event(enable_timing=True)
+            start.record()
         ids_dev = self.forward(rg, layer_outputs=outs, buf=buf, prev=prev)
         B = len(ids)
         self.ids_host_bufs[buf][:B].copy_(ids_dev[:B], non_blocking=True)
-        done = torch.cuda.Event()
+        done = torch.cuda.Event(enable_timing=self.record_events)
         done.record()
         return {"sched": sched, "buf": buf, "ids": ids, "n_new": n_new, "ctx": ctx, "slot_base": base,
-                "event": done, "outs": outs, "ticket": None}
+                "event": done, "start": start, "outs": outs, "ticket": None, "n_rsrv": n_rsrv,
+                "host_ms": 1e3 * (time.perf_counter() - h0)}
 
     def _result(self, p, new):
         res = {"ids": p["ids"], "n_new": p["n_new"], "ctx": p["ctx"], "slot_base": p["slot_base"], "tokens": new,
-               "finished": p.get("finished")}
+               "finished": p.get("finished"), "n_rsrv": p["n_rsrv"], "host_ms": p["host_ms"]}
+        if p.get("start") is not None:
+            res["gpu_ms"] = p["start"].elapsed_time(p["event"])
         if p["outs"] is not None:
             B = len(p["ids"])
             res["layer_outputs"] = [o.cpu() for o in p["outs"]]
