@@ -406,24 +406,25 @@ def cpu_mini(seed):
     return out
 
 
-def decode_loop(seed, steps=64, reps=3):
-    """Generation loop on the mini model (4 layers, hidden 256, 8 heads, FFN 1024, vocab 4096, bf16):
+def decode_loop(seed, steps=64, reps=3, dtype="bf16"):
+    """Generation loop on the mini model (4 layers, hidden 256, 8 heads, FFN 1024, vocab 4096, ``dtype``):
     64 requests in decode with cached context U[16, 256] (random K/V history), each generating ``steps``
     more tokens.  Timed three ways: the synchronous loop (each iteration waits for its ids before the
     next Select), the chained one (iteration t+1 selected and launched before t's ids reach the host),
     and the chained one with each iteration's device side replayed from a HIP graph (one launch per
     iteration instead of one per kernel).  Best of ``reps`` runs of each."""
     import torch
-    from selective_batching_amd.runtime import DeviceWeights, Engine
+    from selective_batching_amd.runtime import TORCH_DT, DeviceWeights, Engine, make_dims
     from synth import MINI, mini_decode_batch, uniform_int
     m = MINI
     batch = mini_decode_batch(seed=seed)
     B = len(batch)
-    W = DeviceWeights(m, "bf16", host=None, seed=seed)
+    W = DeviceWeights(m, dtype, host=None, seed=seed)
     n_slots = sum(c + steps + 1 for _, c in batch) + 8 * B
-    eng = Engine(m, "bf16", W, n_slots=n_slots, max_bs=B, max_tokens=B, max_keys_total=n_slots, zero_arena=False)
+    eng = Engine(m, dtype, W, n_slots=n_slots, max_bs=B, max_tokens=B, max_keys_total=n_slots, zero_arena=False)
+    tdt = TORCH_DT[make_dims(m, dtype).dtype]
     for a in (eng.k_arena, eng.v_arena):
-        a.view(torch.bfloat16).normal_(0.0, 1.0)
+        a.view(tdt).normal_(0.0, 1.0)
     last = uniform_int(seed, "decode.last", 0, m.V - 1, B).tolist()
     rid = [0]
 
@@ -459,7 +460,7 @@ def decode_loop(seed, steps=64, reps=3):
             best = dt if best is None else min(best, dt)
         out[name] = {"ms_per_step": round(1e3 * best / steps, 4), "tokens_per_s": round(B * steps / best, 1)}
     eng.close()
-    return {"workload": (f"mini GPT (4 layers, hidden 256, 8 heads, FFN 1024, vocab 4096) bf16, random init; {B} "
+    return {"workload": (f"mini GPT (4 layers, hidden 256, 8 heads, FFN 1024, vocab 4096) {dtype}, random init; {B} "
                          f"requests in decode, cached context U[16,256], {steps} generated tokens each"),
             **out, "chained_speedup": round(out["synchronous"]["ms_per_step"] / out["chained"]["ms_per_step"], 3),
             "chained_graphs_speedup": round(out["synchronous"]["ms_per_step"] / out["chained_graphs"]["ms_per_step"], 3)}
@@ -831,6 +832,7 @@ def main():
     if not args.no_decode_loop:
         print("[bench] mini-model decode loop ...", file=sys.stderr, flush=True)
         out["decode_loop"] = decode_loop(args.seed)
+        out["decode_loop_fp32"] = decode_loop(args.seed, dtype="fp32")
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample ...", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(m.with_layers(args.layers), batch, args.seed)

@@ -11,7 +11,7 @@
 // XOR-swizzled rows: no bank conflicts on the operand reads), XCD-aware grouped
 // tile order.  Small GEMMs (decode-heavy batches): 128 x 128 register-staged
 // tiles or 64-row tiles with deep K rings, by a cost model.
-// fp32: a plain LDS-tiled FMA kernel with a fixed, sequential K order.
+// fp32: 16x16x4 fp32 MFMA tiles with a fixed, ascending K order.
 // Epilogues fuse bias, exact GeLU, SwiGLU (SiLU(gate) * up) or the residual
 // add into the fp32 stream x.
 #include <algorithm>
@@ -578,69 +578,88 @@ __global__ __launch_bounds__(64 * WAVES_M_ * WAVES_N_, MINW) void gemm_bf16_dma_
     tile_epilogue<MI, NI, EPI>(a, acc, m0 + wm * WM + lr, n_lane);
 }
 
-// ================================================================== fp32 FMA
-// 64 x 64 tile (for SwiGLU: 32 gate + 32 up columns), 4 x 4 outputs per
-// thread, K in steps of 16 through LDS.  Each output's K sum runs in
-// ascending k, independent of M and of the tile a row falls in.
+// ================================================================== fp32 MFMA
+// 64 x 64 tile (64 A rows x 64 W rows), 4 waves of 32 x 32 outputs (2 x 2 blocks of the 16x16x4 fp32
+// MFMA), K in steps of 16 through LDS with the next step's global loads in flight in registers.  As in
+// the bf16 kernels the W fragment is the MFMA's first operand, so lane (lr = lane % 16, g = lane / 16)
+// of block (i, j) holds output row m0 + 16 i + lr and the four consecutive columns 16 j + 4 g + {0..3}.
+// Each output is one MFMA chain over ascending K (4 at a time), whatever M and the tile a row falls in.
+// SwiGLU: wave wn's 32 W rows are 16 gate rows and the matching 16 up rows, so block j = 0 holds gate
+// and j = 1 up values of the same 16 output columns (a tile covers 32 output columns).
 template <int EPI>
-__global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
-    __shared__ float As[16][64 + 4];
-    __shared__ float Bs[16][64 + 4];
-    const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+__global__ __launch_bounds__(256) void gemm_f32_mfma_kernel(GemmArgs a) {
+    constexpr int BK = 16, LDK = BK + 4;            // 80-byte rows: 16-byte aligned stores
+    __shared__ __attribute__((aligned(16))) float As[2][64 * LDK];
+    __shared__ __attribute__((aligned(16))) float Ws[2][64 * LDK];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int wm = wave >> 1, wn = wave & 1, lr = lane & 15, g = lane >> 4;
     const int out_cols = (EPI == EPI_SWIGLU) ? 32 : 64;
     const int tiles_n = (a.N + out_cols - 1) / out_cols;
     const int tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
     const int m0 = tm * 64;
     const float* A = (const float*)a.A;
     const float* W = (const float*)a.W;
-    const int lr = tid >> 2, lk = (tid & 3) * 4;
-    const float* pa = A + (long long)min(m0 + lr, a.M - 1) * a.lda + lk;
-    int br;
+    // this thread copies 4 consecutive k of one A row and one W row per step
+    const int cr = tid >> 2, ck = (tid & 3) * 4;
+    const float* pa = A + (long long)min(m0 + cr, a.M - 1) * a.lda + ck;
+    int wr;
     if (EPI == EPI_SWIGLU) {
-        const int j = lr & 3, f = tn * 32 + (lr >> 2) * 2 + (j & 1);
-        br = min(f, a.N - 1) + (j >= 2 ? a.F : 0);
+        const int w = cr >> 5, cc = cr & 31;          // W tile row cr: wave w, gate (cc < 16) or up
+        const int f = tn * 32 + w * 16 + (cc & 15);
+        wr = min(f, a.N - 1) + (cc >= 16 ? a.F : 0);
     } else {
-        br = min(tn * 64 + lr, a.N - 1);
+        wr = min(tn * 64 + cr, a.N - 1);
     }
-    const float* pb = W + (long long)br * a.ldw + lk;
-    float acc[4][4] = {};
-    for (int k0 = 0; k0 < a.K; k0 += 16) {
-        const float4 va = *(const float4*)(pa + k0);
-        const float4 vb = *(const float4*)(pb + k0);
-        As[lk + 0][lr] = va.x; As[lk + 1][lr] = va.y; As[lk + 2][lr] = va.z; As[lk + 3][lr] = va.w;
-        Bs[lk + 0][lr] = vb.x; Bs[lk + 1][lr] = vb.y; Bs[lk + 2][lr] = vb.z; Bs[lk + 3][lr] = vb.w;
+    const float* pw = W + (long long)wr * a.ldw + ck;
+    f32x4 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int nk = a.K / BK;
+    f32x4 ra = *(const f32x4*)pa, rw = *(const f32x4*)pw;
+    for (int kt = 0; kt < nk; ++kt) {
+        const int buf = kt & 1;
+        *(f32x4*)&As[buf][cr * LDK + ck] = ra;
+        *(f32x4*)&Ws[buf][cr * LDK + ck] = rw;
         __syncthreads();
-#pragma unroll
-        for (int kk = 0; kk < 16; ++kk) {
-            float av[4], bv[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) av[i] = As[kk][ty * 4 + i];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) bv[j] = Bs[kk][tx * 4 + j];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
+        if (kt + 1 < nk) {
+            ra = *(const f32x4*)(pa + (kt + 1) * BK);
+            rw = *(const f32x4*)(pw + (kt + 1) * BK);
         }
-        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < BK; kk += 4) {
+            float av[2], wv[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) av[i] = As[buf][(wm * 32 + i * 16 + lr) * LDK + kk + g];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) wv[j] = Ws[buf][(wn * 32 + j * 16 + lr) * LDK + kk + g];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(wv[j], av[i], acc[i][j], 0, 0, 0);
+        }
+        // the other buffer is written next step: every wave has finished reading it (it was read one
+        // step ago, before this step's barrier)
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int m = m0 + ty * 4 + i;
+    for (int i = 0; i < 2; ++i) {
+        const int m = m0 + wm * 32 + i * 16 + lr;
         if (m >= a.M) continue;
         if (EPI == EPI_SWIGLU) {
-            // columns tx*4 + {0,1} are gate, tx*4 + {2,3} the matching up values
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int f = tn * 32 + tx * 2 + j;
-                if (f < a.N) swiglu_store<SB_F32>(a, m, f, acc[i][j], acc[i][j + 2]);
+            for (int r = 0; r < 4; ++r) {
+                const int f = tn * 32 + wn * 16 + 4 * g + r;
+                if (f < a.N) swiglu_store<SB_F32>(a, m, f, acc[i][0][r], acc[i][1][r]);
             }
         } else {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int n = tn * 64 + tx * 4 + j;
-                if (n < a.N) epi_store<SB_F32, EPI>(a, m, n, acc[i][j]);
-            }
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int n = tn * 64 + wn * 32 + j * 16 + 4 * g + r;
+                    if (n < a.N) epi_store<SB_F32, EPI>(a, m, n, acc[i][j][r]);
+                }
         }
     }
 }
@@ -812,7 +831,7 @@ template <int EPI>
 int launch_f32(const GemmArgs& a, hipStream_t s) {
     const int out_cols = (EPI == EPI_SWIGLU) ? 32 : 64;
     const long long tiles = (long long)((a.M + 63) / 64) * ((a.N + out_cols - 1) / out_cols);
-    hipLaunchKernelGGL((gemm_f32_kernel<EPI>), dim3((unsigned)tiles), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((gemm_f32_mfma_kernel<EPI>), dim3((unsigned)tiles), dim3(256), 0, s, a);
     return check_launch("gemm_f32");
 }
 
