@@ -150,51 +150,6 @@ __device__ __forceinline__ int k_swz(int row) {
     return ((row & 3) | ((row >> 1) & 12)) & (D / 8 - 1);
 }
 
-template <int D>
-__device__ __forceinline__ void chunk_bf16(const AttnArgs& a, WaveState<D>& st, const bf16x8 (&qf)[D / 32], int cb,
-                                           int key_end, int row_limit, int all_visible, int lane,
-                                           const uint16_t* ldsK, const uint16_t* ldsV) {
-    const int lr = lane & 15, g = lane >> 4;
-    float sc[8];
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-        const int kl = 8 * (lr >> 2) + 4 * b + (lr & 3);          // local key of MFMA row lr
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < D / 32; ++s) {
-            const u32x4 kraw = *(const u32x4*)(ldsK + kl * D + (((4 * s + g) ^ k_swz<D>(kl)) << 3));
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kraw), qf[s], acc, 0, 0, 0);
-        }
-        // acc[r]: key cb + 8g + 4b + r, row lr; a chunk every row of the wave sees whole needs no test
-        if (cb + 32 <= all_visible) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sc[4 * b + r] = acc[r] * a.scale_log2;
-        } else {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int k = cb + 8 * g + 4 * b + r;
-                sc[4 * b + r] = (k < key_end && k < row_limit) ? acc[r] * a.scale_log2 : kNegInf;
-            }
-        }
-    }
-    // V^T operand: V[keys cb+8g .. +8][dim 16db + lr] = 16 contiguous bytes of the staged tile
-    // (keys at or past key_end were zeroed when the tile was staged)
-    u32x4 vr[D / 16];
-#pragma unroll
-    for (int db = 0; db < D / 16; ++db) vr[db] = *(const u32x4*)(ldsV + g * (D * 8 + 16) + (db * 16 + lr) * 8);
-    float alpha;
-    softmax_chunk(sc, st.m, st.l, alpha);
-    rescale(st.o, alpha);
-    bf16x8 ph, pl;
-    split_p(sc, ph, pl);
-#pragma unroll
-    for (int db = 0; db < D / 16; ++db) {
-        const bf16x8 vv8 = __builtin_bit_cast(bf16x8, vr[db]);
-        st.o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv8, ph, st.o[db], 0, 0, 0);
-        st.o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv8, pl, st.o[db], 0, 0, 0);
-    }
-}
-
 // K/V registers of one 32-key chunk for the direct-from-HBM path (MODE_RUNS):
 // K operands of the two S^T blocks and V^T operands of every 16-dim block.
 template <int D>
@@ -379,14 +334,20 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
     using T = typename Store<DT>::T;
     constexpr int KT = 32;                                   // keys per LDS stage (MODE_ROWS)
     // MODE_ROWS stages K/V tiles; MODE_RUNS merges wave states: one workgroup
-    // uses only one of the two, so they share the LDS allocation.
-    constexpr int LDS_K = (DT == SB_BF16) ? 2 * KT * D : 0;
-    constexpr int LDS_V = (DT == SB_BF16) ? 2 * (KT / 8) * (D * 8 + 16) : 0;
-    constexpr int BYTES_ROWS = (LDS_K + LDS_V) * 2;
+    // uses only one of the two, so they share the LDS allocation.  A MODE_ROWS stage holds a K tile
+    // [KT][D] then KT / 8 V blocks of [D][8] (rows of 16 extra elements between blocks when a block
+    // is a whole number of 1 KB copies).
+    constexpr int ROWS_NS = 4;                               // stages of the copy ring
+    constexpr int ROWS_VBS = (D >= 64) ? D * 8 + 16 : D * 8; // elements from one V block to the next
+    constexpr int ROWS_STAGE = KT * D + (KT / 8) * ROWS_VBS;  // elements per stage
+    constexpr int ROWS_KI = KT * D * 2 / 1024;               // copy instructions of a K tile (= of a V tile)
+    constexpr int ROWS_PERW = 2 * ROWS_KI / kWaves;          // per wave per stage
+    static_assert(DT != SB_BF16 || ROWS_PERW * kWaves == 2 * ROWS_KI, "copies must split evenly over the waves");
+    static_assert(ROWS_NS - 2 <= 2, "the wait ladder covers at most two tiles in flight");
+    constexpr int BYTES_ROWS = (DT == SB_BF16) ? ROWS_NS * ROWS_STAGE * 2 : 0;
     constexpr int BYTES_RED = (kWaves * 16 * (D + 1) + 2 * kWaves * 16) * 4;
-    __shared__ __attribute__((aligned(16))) char smem[BYTES_ROWS > BYTES_RED ? BYTES_ROWS : BYTES_RED];
-    uint16_t* ldsK = (uint16_t*)smem;
-    uint16_t* ldsV = ldsK + LDS_K;
+    __shared__ __attribute__((aligned(1024))) char smem[BYTES_ROWS > BYTES_RED ? BYTES_ROWS : BYTES_RED];
+    const uint16_t* smem_u16 = (const uint16_t*)smem;
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int lr = lane & 15, g = lane >> 4;
@@ -499,10 +460,10 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
         return;
     }
 
-    // MODE_ROWS: stage 64-key tiles of K (row-major, 16-byte pieces swizzled by row) and V (8-key
-    // blocks, padded) in LDS
-    // (bf16: a tile of up to 64 x rbn rows; wave w owns rows row0 + 16 rbn w .. as rbn 16-row blocks, so
-    // that each staged K/V tile serves all of them)
+    // MODE_ROWS (bf16): a tile of up to 64 x rbn rows; wave w owns rows row0 + 16 rbn w .. as rbn 16-row
+    // blocks.  32-key K/V tiles are copied global -> LDS directly (global_load_lds_dwordx4) into a ring of
+    // NS stages, NS - 1 tiles ahead of the one being computed; each wave reads a chunk's K and V operands
+    // from LDS once and applies them to all of its row blocks.
     if constexpr (DT == SB_BF16) {
         constexpr int RB = kRowBlocksBf16;
         const int rbn = it[ITEM_RB];
@@ -510,6 +471,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
         WaveState<D> st2[RB];
         int rl[RB], av[RB], wml[RB], rtok[RB], rhead[RB];
         bool rok[RB];
+        int wmax = 0;                                  // keys past this are seen by no row of the wave
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
             const bool on = rb < rbn;
@@ -520,6 +482,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
             rl[rb] = rok[rb] ? ctx + rtok[rb] + 1 : 0;
             av[rb] = min(ke, ctx + w0 / a.G + 1);
             wml[rb] = on && w0 < row0 + nrows ? min(ke, ctx + min(w0 + 15, row0 + nrows - 1) / a.G + 1) : 0;
+            wmax = max(wmax, wml[rb]);
             const T* q = (const T*)a.qkv + (long long)(tok0 + rtok[rb]) * a.qkv_stride + (long long)rhead[rb] * D;
 #pragma unroll
             for (int s = 0; s < D / 32; ++s) {
@@ -528,80 +491,124 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
             }
             state_init(st2[rb]);
         }
+        // the q loads are the only loads the compiler sees: complete them before any copy is in flight,
+        // so that no wait it inserts later also waits for the copies
+        wait_vmcnt<0>();
         const int ntiles = (ke - kb + KT - 1) / KT;
-        constexpr int KCH = KT * D / 8;                    // 16-byte chunks per K tile (and per V tile)
-        constexpr int PER = (KCH + 255) / 256;
-        constexpr int KSTR = KT * D, VSTR = (KT / 8) * (D * 8 + 16);         // one LDS buffer
-        struct Stage { u32x4 k[PER], v[PER]; };
-        // global loads of tile t (clamped to the last tile: the loads are issued unconditionally
-        // so the compiler keeps them in flight across the compute of the tiles before)
-        auto gload = [&](Stage& r, int t) {
-            const int k0 = kb + min(t, ntiles - 1) * KT;
-#pragma unroll
-            for (int q = 0; q < PER; ++q) {
-                const int c = tid + 256 * q;
-                if (c < KCH) {
-                    const int kk = c / (D / 8), dc = (c % (D / 8)) * 8;
-                    const long long slot = kslot0 + min(k0 + kk, ke - 1);
-                    r.k[q] = *(const u32x4*)((const uint16_t*)Kp + slot * D + dc);
-                    // V: chunk c covers block c / D of 8 keys, dim c % D
-                    const int vb = c / D, vd = c % D;
-                    const long long vslot = kslot0 + min(k0 + vb * 8, ((ke - 1) & ~7));
-                    r.v[q] = *(const u32x4*)((const uint16_t*)Vp + ((vslot >> 3) * D + vd) * 8);
+        const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(smem));
+        // copy instruction q of the tile starting at key k0 into stage `stage`: K rows first (R rows of D
+        // elements per instruction; lane L fills position L % (D/8) of row L / (D/8) with the source piece
+        // that belongs there, (L % (D/8)) ^ k_swz(row)), then the V blocks (8 keys x D dims each, as in the
+        // arena; a block of D = 32 is half an instruction).  Keys at or past ke read key ke - 1 (K) or the
+        // block holding it (V): finite values, masked in the compute.
+        auto copy = [&](int stage, int k0, int q) {
+            const uint32_t sbase = lds0 + (uint32_t)(stage * ROWS_STAGE * 2);
+            if (q < ROWS_KI) {
+                constexpr int R = 1024 / (D * 2);
+                const int row = q * R + lane / (D / 8), p = lane % (D / 8);
+                const long long slot = kslot0 + min(k0 + row, ke - 1);
+                dma16((const uint16_t*)Kp + slot * D + ((p ^ k_swz<D>(row)) << 3), sbase + q * 1024);
+            } else {
+                const int j = q - ROWS_KI;
+                const long long last = (kslot0 + ke - 1) >> 3;
+                if constexpr (D >= 64) {
+                    constexpr int PB = D * 16 / 1024;          // instructions per V block
+                    const int vb = j / PB, h = j % PB;
+                    const long long blk = min(((kslot0 + k0) >> 3) + vb, last);
+                    dma16((const uint16_t*)Vp + blk * D * 8 + h * 512 + lane * 8,
+                          sbase + KT * D * 2 + vb * ROWS_VBS * 2 + h * 1024);
+                } else {
+                    const int vb = 2 * j + lane / 32;           // two 512-byte blocks per instruction
+                    const long long blk = min(((kslot0 + k0) >> 3) + vb, last);
+                    dma16((const uint16_t*)Vp + blk * D * 8 + (lane % 32) * 8, sbase + KT * D * 2 + j * 1024);
                 }
             }
         };
-        // stage tile t; V of keys at or past ke is zeroed (a P of 0 times stale memory could be NaN)
-        auto lstore = [&](const Stage& r, int buf, int t) {
-            const int k0 = kb + t * KT;
+        const int wave_u = __builtin_amdgcn_readfirstlane(wave);      // wave-uniform, for the copies' LDS base
+        auto issue = [&](int stage, int t) {
 #pragma unroll
-            for (int q = 0; q < PER; ++q) {
-                const int c = tid + 256 * q;
-                if (c < KCH) {
-                    const int kk = c / (D / 8), dc = (c % (D / 8)) * 8;
-                    *(u32x4*)(ldsK + buf * KSTR + kk * D + (((dc >> 3) ^ k_swz<D>(kk)) << 3)) = r.k[q];
-                    const int vb = c / D, vd = c % D;
-                    u32x4 vv = r.v[q];
-                    const int kv0 = k0 + vb * 8;
-                    if (kv0 + 8 > ke) {
+            for (int i = 0; i < ROWS_PERW; ++i) copy(stage, kb + t * KT, wave_u * ROWS_PERW + i);
+        };
+        auto compute = [&](int t, int stage) {
+            const int cb = kb + t * KT;
+            if (cb >= wmax) return;                      // no row of this wave sees these keys
+            const uint16_t* lk = smem_u16 + stage * ROWS_STAGE;
+            const uint16_t* lv = lk + KT * D;
+            // K operands of the chunk (both S^T blocks), read once for every row block
+            u32x4 kr[2][D / 32];
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const uint32_t keep = (kv0 + 2 * e < ke ? 0xffffu : 0u) | (kv0 + 2 * e + 1 < ke ? 0xffff0000u : 0u);
-                            vv[e] &= keep;
+            for (int b = 0; b < 2; ++b) {
+                const int kl = 8 * (lr >> 2) + 4 * b + (lr & 3);      // local key of MFMA row lr
+#pragma unroll
+                for (int s = 0; s < D / 32; ++s) kr[b][s] = *(const u32x4*)(lk + kl * D + (((4 * s + g) ^ k_swz<D>(kl)) << 3));
+            }
+            float sc[RB][8];
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+                if (cb >= wml[rb]) continue;
+#pragma unroll
+                for (int b = 0; b < 2; ++b) {
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int s = 0; s < D / 32; ++s)
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[b][s]), qf2[rb][s], acc, 0, 0, 0);
+                    if (cb + 32 <= av[rb]) {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) sc[rb][4 * b + r] = acc[r] * a.scale_log2;
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int k = cb + 8 * g + 4 * b + r;
+                            sc[rb][4 * b + r] = (k < ke && k < rl[rb]) ? acc[r] * a.scale_log2 : kNegInf;
                         }
                     }
-                    *(u32x4*)(ldsV + buf * VSTR + vb * (D * 8 + 16) + vd * 8) = vv;
+                }
+            }
+            // V^T operands: V[keys cb+8g .. +8][dim 16db + lr], 16 contiguous bytes of the staged block;
+            // entries of keys at or past ke are zeroed (a probability of 0 times stale memory could be NaN)
+            u32x4 vr[D / 16];
+            const int k8 = cb + 8 * g;
+#pragma unroll
+            for (int db = 0; db < D / 16; ++db) vr[db] = *(const u32x4*)(lv + g * ROWS_VBS + (db * 16 + lr) * 8);
+            if (k8 + 8 > ke) {
+#pragma unroll
+                for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const uint32_t keep = (k8 + 2 * e < ke ? 0xffffu : 0u) | (k8 + 2 * e + 1 < ke ? 0xffff0000u : 0u);
+                        vr[db][e] &= keep;
+                    }
+            }
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+                if (cb >= wml[rb]) continue;
+                float alpha;
+                softmax_chunk(sc[rb], st2[rb].m, st2[rb].l, alpha);
+                rescale(st2[rb].o, alpha);
+                bf16x8 ph, pl;
+                split_p(sc[rb], ph, pl);
+#pragma unroll
+                for (int db = 0; db < D / 16; ++db) {
+                    const bf16x8 vv8 = __builtin_bit_cast(bf16x8, vr[db]);
+                    st2[rb].o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv8, ph, st2[rb].o[db], 0, 0, 0);
+                    st2[rb].o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv8, pl, st2[rb].o[db], 0, 0, 0);
                 }
             }
         };
-        auto compute = [&](int t, int buf) {
+        // ring: tile t in stage t % NS; step t waits for its own copies of tile t, then the barrier (every
+        // wave's copies of tile t landed; every wave finished tile t - 1), then issues tile t + NS - 1 into
+        // the stage tile t - 1 used, then computes tile t
 #pragma unroll
-            for (int h = 0; h < KT / 32; ++h) {
-                const int k0 = kb + t * KT + 32 * h;
-#pragma unroll
-                for (int rb = 0; rb < RB; ++rb)
-                    if (k0 < wml[rb])
-                        chunk_bf16<D>(a, st2[rb], qf2[rb], k0, ke, rl[rb], av[rb], lane,
-                                      ldsK + buf * KSTR + 32 * h * D, ldsV + buf * VSTR + 4 * h * (D * 8 + 16));
-            }
-        };
-        // registers r0 / r1 hold the even / odd tiles in flight; LDS buffer t & 1 holds tile t
-        Stage r0, r1;
-        gload(r0, 0);
-        gload(r1, 1);
-        lstore(r0, 0, 0);
-        __syncthreads();
-        gload(r0, 2);
-        for (int t = 0; t < ntiles; t += 2) {
-            compute(t, 0);
-            if (t + 1 < ntiles) lstore(r1, 1, t + 1);      // buffer 1 was last read before the previous barrier
-            __syncthreads();
-            if (t + 1 >= ntiles) break;
-            gload(r1, t + 3);
-            compute(t + 1, 1);
-            if (t + 2 < ntiles) lstore(r0, 0, t + 2);
-            __syncthreads();
-            gload(r0, t + 4);
+        for (int t = 0; t < ROWS_NS - 1; ++t)
+            if (t < ntiles) issue(t, t);
+        for (int t = 0; t < ntiles; ++t) {
+            const int later = min(ROWS_NS - 2, ntiles - 1 - t);     // tiles issued after t, still in flight
+            if (later >= 2) wait_vmcnt<2 * ROWS_PERW>();
+            else if (later == 1) wait_vmcnt<ROWS_PERW>();
+            else wait_vmcnt<0>();
+            lds_barrier();
+            if (t + ROWS_NS - 1 < ntiles) issue((t + ROWS_NS - 1) % ROWS_NS, t + ROWS_NS - 1);
+            compute(t, t % ROWS_NS);
         }
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {

@@ -43,6 +43,31 @@ __device__ __forceinline__ int xcd_remap(int pid, int total) {
     return x * per + (x < rem ? x : rem) + local;
 }
 
+// ------------------------------------------------------------------ global -> LDS copies
+typedef __attribute__((address_space(3))) void lds_void;
+
+// vmcnt <= n (other counters untouched): gfx9 encoding, vmcnt in bits 3:0 and 15:14
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// One 16-byte-per-lane global -> LDS transfer (global_load_lds_dwordx4): lane i
+// of the wave writes LDS bytes [lds_base + 16 i, +16).  Issued from inline
+// assembly so that the compiler's wait insertion does not see it: the caller
+// orders it with its own vmcnt waits and barriers.  lds_base is wave-uniform.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(src), "s"(lds_base)
+                 : "memory", "m0");
+}
+
+// Workgroup barrier that is also a compiler memory barrier (no LDS access moves across it).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(lds_void*)p; }
+
 // ------------------------------------------------------------------ GEMM
 enum { EPI_STORE = 0, EPI_GELU = 1, EPI_RESID = 2, EPI_SWIGLU = 3 };
 
