@@ -65,6 +65,8 @@ def parse():
     ap.add_argument("--log-dir", default=os.path.join(ROOT, "gpurun_out"),
                     help="directory of the serving trace's per-iteration JSONL log ('' for none)")
     ap.add_argument("--no-gpt175b", action="store_true", help="skip the GPT-175B-shaped layer figures")
+    ap.add_argument("--trace-iters", type=int, default=None,
+                    help="stop the serving trace after this many iterations (for profiling; default: the whole trace)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one 1 GiB device-to-device copy before the steps (calibrates HBM counters)")
     ap.add_argument("--op-gemm", default=None, metavar="M,N,K,EPI",
@@ -824,7 +826,7 @@ def main():
         if args.log_dir:
             os.makedirs(args.log_dir, exist_ok=True)
             log_path = os.path.join(args.log_dir, "trace_iterations.jsonl")
-        out["trace"] = trace_run(W, m, args.seed, log_path=log_path)
+        out["trace"] = trace_run(W, m, args.seed, log_path=log_path, iters=args.trace_iters)
         torch.cuda.empty_cache()
         out["reservation_policies"] = reservation_policies(args.seed)
         print("[bench] iteration-level vs request-level scheduling ...", file=sys.stderr, flush=True)
