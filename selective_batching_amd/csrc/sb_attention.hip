@@ -14,13 +14,14 @@
 // request's keys 0..ctx_i + j of q.k / sqrt(d), times V.  Scores and the
 // running max / sum live in fp32 (log2 domain).
 //
-// Tiling (CDNA4, 64-wide waves): S^T = K Q^T and O^T = V^T P^T on 16x16
-// MFMA tiles, so that a query row lives in lane % 16 for both products and
-// the softmax rescale needs no cross-lane moves.  The 32-key chunk is
+// Tiling (CDNA4, 64-wide waves): S^T = K Q^T and O^T = V^T P^T, so that a
+// query row's scores and outputs sit in the same lanes for both products and
+// the softmax rescale needs no cross-lane moves.  The keys of a chunk are
 // ordered so the S^T accumulators are directly the bf16 P^T operand; P is
 // fed as a hi + lo pair of bf16 values (two MFMAs), which keeps P.V at about
-// fp32 accuracy -- decode is HBM-bound, so the extra MFMA is free there.
-//   MODE_RUNS (<= 16 rows per request and K/V head: decodes, small chunks):
+// fp32 accuracy.
+//   MODE_RUNS (<= 16 rows per request and K/V head: decodes, small chunks;
+//     16x16x32 MFMAs, a row in lane % 16):
 //     the 4 waves take interleaved 32-key chunks of a run of 512-key units;
 //     K/V go straight from HBM into MFMA operand registers (16-byte loads,
 //     the next chunk's loads in flight while the current one computes, also
@@ -29,12 +30,15 @@
 //     the unit states in unit order itself; otherwise each unit leaves a
 //     partial state, merged by attn_combine in unit order with the same
 //     two-state merge, so the result does not depend on the rest of the batch.
-//   MODE_ROWS (prefill tiles of 64 rows): each wave owns 16 rows; the
-//     workgroup stages 64-key K/V tiles through LDS (two buffers) so the 4
-//     waves share every K/V byte, with the global loads of the next two tiles
-//     in flight in registers while a tile computes.
+//   MODE_ROWS (prefill tiles of 64 or 128 rows; 32x32x16 MFMAs): each wave
+//     owns one 32-column block of rows (16 or 32 of them real); the workgroup
+//     copies 64-key K/V tiles global -> LDS directly, the next tile in flight
+//     while a tile computes, so the 4 waves share every K/V byte.  A row's
+//     reference max moves only when a chunk's max exceeds it by more than
+//     kLazyLog2, so the output accumulators are rarely rescaled.
 #include <cfloat>
 #include <mutex>
+#include <type_traits>
 
 #include "sb_device.h"
 #include "sb_ops.h"
@@ -85,6 +89,42 @@ __device__ __forceinline__ void split_p(const float (&p)[8], bf16x8& hi, bf16x8&
     hi = __builtin_bit_cast(bf16x8, h);
     lo = __builtin_bit_cast(bf16x8, l);
 }
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// The value of lane l ^ 32 (v_permlane32_swap: lanes 32..63 of the first operand trade places with
+// lanes 0..31 of the second; with both operands v, the two results hold v of lanes 0..31 and of
+// lanes 32..63, each in every lane).
+__device__ __forceinline__ float swap32(float v) {
+    const uint32_t u = __float_as_uint(v);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
+
+// values i0 .. i0 + 7 of a 32x32 MFMA accumulator as a hi + lo pair of bf16 operands (as split_p)
+__device__ __forceinline__ void split_p8(const f32x16& p, int i0, bf16x8& hi, bf16x8& lo) {
+    u32x4 hh, ll;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float a = p[i0 + 2 * i], b = p[i0 + 2 * i + 1];
+        hh[i] = pack_bf16x2(a, b);
+        ll[i] = pack_bf16x2(a - __uint_as_float(hh[i] << 16), b - __uint_as_float(hh[i] & 0xffff0000u));
+    }
+    hi = __builtin_bit_cast(bf16x8, hh);
+    lo = __builtin_bit_cast(bf16x8, ll);
+}
+
+// Swizzle of the staged K tile of a prefill tile: the 16-byte piece p of local row r sits at position
+// p ^ kt_swz(r).  The 16 lanes of a quarter-wave read 16 rows at one piece index; their positions then
+// spread over all 64 banks.
+template <int D>
+__device__ __forceinline__ int kt_swz(int row) {
+    constexpr int SH = D >= 128 ? 0 : (D == 64 ? 1 : 2);
+    return (row >> SH) & (D / 8 - 1);
+}
+
+// A prefill row's reference max moves only when a chunk's max exceeds it by more than this (log2 units).
+constexpr float kLazyLog2 = 8.f;
 
 // o *= alpha, skipped when no row of the wave changed its max (alpha == 1 exactly)
 template <int N>
@@ -143,13 +183,6 @@ __device__ __forceinline__ void softmax_chunk(float (&sc)[8], float& m, float& l
 // Keys of a 32-key chunk starting at key cb: S^T block b covers local keys
 // 8*(m/4) + 4*b + (m%4) for MFMA row m, so that lane (g = lane/16) ends up
 // with keys 8g..8g+7 -- exactly the P^T operand layout of the 16x16x32 MFMA.
-// Staged K tile rows keep their 16-byte pieces at position piece ^ k_swz(row): the 16 rows one
-// operand read touches (keys 8(m/4) + 4b + m%4, m < 16) then sit in 16 different bank groups.
-template <int D>
-__device__ __forceinline__ int k_swz(int row) {
-    return ((row & 3) | ((row >> 1) & 12)) & (D / 8 - 1);
-}
-
 // K/V registers of one 32-key chunk for the direct-from-HBM path (MODE_RUNS):
 // K operands of the two S^T blocks and V^T operands of every 16-dim block.
 template <int D>
@@ -332,14 +365,12 @@ __device__ __forceinline__ void merge_unit(WaveState<D>& st, char* smem, RowStat
 template <int DT, int D>
 __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
     using T = typename Store<DT>::T;
-    constexpr int KT = 32;                                   // keys per LDS stage (MODE_ROWS)
-    // MODE_ROWS stages K/V tiles; MODE_RUNS merges wave states: one workgroup
-    // uses only one of the two, so they share the LDS allocation.  A MODE_ROWS stage holds a K tile
-    // [KT][D] then KT / 8 V blocks of [D][8] (rows of 16 extra elements between blocks when a block
-    // is a whole number of 1 KB copies).
-    constexpr int ROWS_NS = 4;                               // stages of the copy ring
-    constexpr int ROWS_VBS = (D >= 64) ? D * 8 + 16 : D * 8; // elements from one V block to the next
-    constexpr int ROWS_STAGE = KT * D + (KT / 8) * ROWS_VBS;  // elements per stage
+    constexpr int KT = 64;                                   // keys per LDS stage (MODE_ROWS)
+    // MODE_ROWS stages K/V tiles; MODE_RUNS merges wave states: one workgroup uses only one of the two,
+    // so they share the LDS allocation.  A MODE_ROWS stage holds a K tile [KT][D] then the KT / 8 V
+    // blocks [D][8] of the same keys.
+    constexpr int ROWS_NS = 2;                               // stages of the copy ring
+    constexpr int ROWS_STAGE = 2 * KT * D;                   // elements per stage
     constexpr int ROWS_KI = KT * D * 2 / 1024;               // copy instructions of a K tile (= of a V tile)
     constexpr int ROWS_PERW = 2 * ROWS_KI / kWaves;          // per wave per stage
     static_assert(DT != SB_BF16 || ROWS_PERW * kWaves == 2 * ROWS_KI, "copies must split evenly over the waves");
@@ -460,138 +491,178 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
         return;
     }
 
-    // MODE_ROWS (bf16): a tile of up to 64 x rbn rows; wave w owns rows row0 + 16 rbn w .. as rbn 16-row
-    // blocks.  32-key K/V tiles are copied global -> LDS directly (global_load_lds_dwordx4) into a ring of
-    // NS stages, NS - 1 tiles ahead of the one being computed; each wave reads a chunk's K and V operands
-    // from LDS once and applies them to all of its row blocks.
+    // MODE_ROWS (bf16): a tile of up to 64 x rbn rows; wave w owns rows row0 + 16 rbn w + c for the
+    // columns c < 16 rbn of one 32-column block (lane c and lane c + 32 share row c; other columns are
+    // padding: q = 0, every key visible, never stored).  KT-key K/V tiles are copied global -> LDS
+    // directly (global_load_lds_dwordx4) into a ring of NS stages, one tile ahead of the one being
+    // computed.  Per tile and wave: S^T = K Q^T as two 32-key blocks of 32x32x16 MFMAs, the softmax
+    // update in registers, then O^T += V^T P^T as 16-key steps.
     if constexpr (DT == SB_BF16) {
-        constexpr int RB = kRowBlocksBf16;
+        constexpr int NP = D / 8;                      // 16-byte pieces of a K row
         const int rbn = it[ITEM_RB];
-        bf16x8 qf2[RB][D / 32];
-        WaveState<D> st2[RB];
-        int rl[RB], av[RB], wml[RB], rtok[RB], rhead[RB];
-        bool rok[RB];
-        int wmax = 0;                                  // keys past this are seen by no row of the wave
+        const int c = lane & 31, h = lane >> 5;
+        const int wr0 = row0 + wave * 16 * rbn;        // first row of the wave
+        const int wend = min(wr0 + 16 * rbn, row0 + nrows);
+        const int rrow = wr0 + c;
+        const bool ok = c < 16 * rbn && rrow < wend;
+        const int rtok = ok ? rrow / a.G : 0;
+        const int rhead = kvh * a.G + (ok ? rrow % a.G : 0);
+        const int rl = ok ? ctx + rtok + 1 : ke;      // keys below rl are visible to this column
+        // keys below all_vis are visible to every row of the wave (its first row sees the fewest); keys at
+        // or past wmax to none
+        const int all_vis = min(ke, ctx + wr0 / a.G + 1);
+        const int wmax = wr0 < wend ? min(ke, ctx + (wend - 1) / a.G + 1) : 0;
+        // S^T row m of a 32-key block holds local key pi(m) (bits 2 and 3 of m swapped): the accumulator
+        // values of a lane are then, eight at a time, the P^T operand of one 16-key step of O^T += V^T P^T
+        const int pic = (c & ~12) | ((c & 4) << 1) | ((c & 8) >> 1);
+        bf16x8 qf[D / 16];                             // Q^T operand: dims 16 s + 8 h .. + 8 of row c
+        {
+            const T* q = (const T*)a.qkv + (long long)(tok0 + rtok) * a.qkv_stride + (long long)rhead * D;
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-            const bool on = rb < rbn;
-            const int w0 = row0 + wave * 16 * rbn + 16 * rb, rrow = w0 + lr;
-            rok[rb] = on && rrow < row0 + nrows;
-            rtok[rb] = rok[rb] ? rrow / a.G : 0;
-            rhead[rb] = kvh * a.G + (rok[rb] ? rrow % a.G : 0);
-            rl[rb] = rok[rb] ? ctx + rtok[rb] + 1 : 0;
-            av[rb] = min(ke, ctx + w0 / a.G + 1);
-            wml[rb] = on && w0 < row0 + nrows ? min(ke, ctx + min(w0 + 15, row0 + nrows - 1) / a.G + 1) : 0;
-            wmax = max(wmax, wml[rb]);
-            const T* q = (const T*)a.qkv + (long long)(tok0 + rtok[rb]) * a.qkv_stride + (long long)rhead[rb] * D;
-#pragma unroll
-            for (int s = 0; s < D / 32; ++s) {
-                u32x4 v = rok[rb] ? *(const u32x4*)(q + s * 32 + g * 8) : u32x4{0u, 0u, 0u, 0u};
-                qf2[rb][s] = __builtin_bit_cast(bf16x8, v);
+            for (int s = 0; s < D / 16; ++s) {
+                u32x4 v = ok ? *(const u32x4*)(q + 16 * s + 8 * h) : u32x4{0u, 0u, 0u, 0u};
+                qf[s] = __builtin_bit_cast(bf16x8, v);
             }
-            state_init(st2[rb]);
         }
+        f32x16 oacc[D / 32];                           // O^T: dims 32 db + 8 (i / 4) + 4 h + i % 4 of row c
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
+        float m = kNegInf, l = 0.f;                    // reference max (log2 units) and this lane's sum
         // the q loads are the only loads the compiler sees: complete them before any copy is in flight,
         // so that no wait it inserts later also waits for the copies
         wait_vmcnt<0>();
         const int ntiles = (ke - kb + KT - 1) / KT;
         const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(smem));
+        const long long vlast = (kslot0 + ke - 1) >> 3;
         // copy instruction q of the tile starting at key k0 into stage `stage`: K rows first (R rows of D
-        // elements per instruction; lane L fills position L % (D/8) of row L / (D/8) with the source piece
-        // that belongs there, (L % (D/8)) ^ k_swz(row)), then the V blocks (8 keys x D dims each, as in the
-        // arena; a block of D = 32 is half an instruction).  Keys at or past ke read key ke - 1 (K) or the
-        // block holding it (V): finite values, masked in the compute.
+        // elements per instruction; lane L fills position L % NP of row L / NP with the source piece that
+        // belongs there, (L % NP) ^ kt_swz(row)), then the V blocks (8 keys x D dims each, as in the arena;
+        // a block of D = 32 is half an instruction).  Keys at or past ke read key ke - 1 (K) or the block
+        // holding it (V): finite values, masked in the compute.
         auto copy = [&](int stage, int k0, int q) {
             const uint32_t sbase = lds0 + (uint32_t)(stage * ROWS_STAGE * 2);
             if (q < ROWS_KI) {
                 constexpr int R = 1024 / (D * 2);
-                const int row = q * R + lane / (D / 8), p = lane % (D / 8);
+                const int row = q * R + lane / NP, p = lane % NP;
                 const long long slot = kslot0 + min(k0 + row, ke - 1);
-                dma16((const uint16_t*)Kp + slot * D + ((p ^ k_swz<D>(row)) << 3), sbase + q * 1024);
+                dma16((const uint16_t*)Kp + slot * D + ((p ^ kt_swz<D>(row)) << 3), sbase + q * 1024);
             } else {
                 const int j = q - ROWS_KI;
-                const long long last = (kslot0 + ke - 1) >> 3;
                 if constexpr (D >= 64) {
                     constexpr int PB = D * 16 / 1024;          // instructions per V block
-                    const int vb = j / PB, h = j % PB;
-                    const long long blk = min(((kslot0 + k0) >> 3) + vb, last);
-                    dma16((const uint16_t*)Vp + blk * D * 8 + h * 512 + lane * 8,
-                          sbase + KT * D * 2 + vb * ROWS_VBS * 2 + h * 1024);
+                    const int vb = j / PB, hh = j % PB;
+                    const long long blk = min(((kslot0 + k0) >> 3) + vb, vlast);
+                    dma16((const uint16_t*)Vp + blk * D * 8 + hh * 512 + lane * 8, sbase + KT * D * 2 + j * 1024);
                 } else {
                     const int vb = 2 * j + lane / 32;           // two 512-byte blocks per instruction
-                    const long long blk = min(((kslot0 + k0) >> 3) + vb, last);
+                    const long long blk = min(((kslot0 + k0) >> 3) + vb, vlast);
                     dma16((const uint16_t*)Vp + blk * D * 8 + (lane % 32) * 8, sbase + KT * D * 2 + j * 1024);
                 }
             }
         };
         const int wave_u = __builtin_amdgcn_readfirstlane(wave);      // wave-uniform, for the copies' LDS base
-        auto issue = [&](int stage, int t) {
+        // Copies of a tile whose keys all lie below ke need no clamping: this wave's copy i then reads
+        // cbase + (kslot0 + k0) D + src_off[i] (waves 0 and 1 copy K rows, waves 2 and 3 V blocks).
+        const uint16_t* cbase = (const uint16_t*)(wave_u * ROWS_PERW < ROWS_KI ? Kp : Vp);
+        int src_off[ROWS_PERW];
 #pragma unroll
-            for (int i = 0; i < ROWS_PERW; ++i) copy(stage, kb + t * KT, wave_u * ROWS_PERW + i);
+        for (int i = 0; i < ROWS_PERW; ++i) {
+            const int q = wave_u * ROWS_PERW + i;
+            if (q < ROWS_KI) {
+                constexpr int R = 1024 / (D * 2);
+                const int row = q * R + lane / NP, p = lane % NP;
+                src_off[i] = row * D + ((p ^ kt_swz<D>(row)) << 3);
+            } else if constexpr (D >= 64) {
+                constexpr int PB = D * 16 / 1024;
+                const int j = q - ROWS_KI;
+                src_off[i] = (j / PB) * D * 8 + (j % PB) * 512 + lane * 8;
+            } else {
+                const int j = q - ROWS_KI;
+                src_off[i] = (2 * j + lane / 32) * D * 8 + (lane % 32) * 8;
+            }
+        }
+        auto issue = [&](int stage, int t) {
+            const int k0 = kb + t * KT;
+            if (k0 + KT <= ke) {
+                const uint16_t* src = cbase + (kslot0 + k0) * D;
+                const uint32_t sbase = lds0 + (uint32_t)(stage * ROWS_STAGE * 2) + (uint32_t)(wave_u * ROWS_PERW * 1024);
+#pragma unroll
+                for (int i = 0; i < ROWS_PERW; ++i) dma16(src + src_off[i], sbase + i * 1024);
+            } else {
+#pragma unroll
+                for (int i = 0; i < ROWS_PERW; ++i) copy(stage, k0, wave_u * ROWS_PERW + i);
+            }
         };
         auto compute = [&](int t, int stage) {
             const int cb = kb + t * KT;
             if (cb >= wmax) return;                      // no row of this wave sees these keys
             const uint16_t* lk = smem_u16 + stage * ROWS_STAGE;
             const uint16_t* lv = lk + KT * D;
-            // K operands of the chunk (both S^T blocks), read once for every row block
-            u32x4 kr[2][D / 32];
-#pragma unroll
-            for (int b = 0; b < 2; ++b) {
-                const int kl = 8 * (lr >> 2) + 4 * b + (lr & 3);      // local key of MFMA row lr
-#pragma unroll
-                for (int s = 0; s < D / 32; ++s) kr[b][s] = *(const u32x4*)(lk + kl * D + (((4 * s + g) ^ k_swz<D>(kl)) << 3));
-            }
-            float sc[RB][8];
-#pragma unroll
-            for (int rb = 0; rb < RB; ++rb) {
-                if (cb >= wml[rb]) continue;
+            f32x16 sacc[2];
+            {
+                bf16x8 kf[2][D / 16];
 #pragma unroll
                 for (int b = 0; b < 2; ++b) {
-                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                    const int r = 32 * b + pic;
+                    const int sw = kt_swz<D>(r);
 #pragma unroll
-                    for (int s = 0; s < D / 32; ++s)
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[b][s]), qf2[rb][s], acc, 0, 0, 0);
-                    if (cb + 32 <= av[rb]) {
+                    for (int s = 0; s < D / 16; ++s) kf[b][s] = *(const bf16x8*)(lk + r * D + (((2 * s + h) ^ sw) << 3));
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) sc[rb][4 * b + r] = acc[r] * a.scale_log2;
-                    } else {
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const int k = cb + 8 * g + 4 * b + r;
-                            sc[rb][4 * b + r] = (k < ke && k < rl[rb]) ? acc[r] * a.scale_log2 : kNegInf;
-                        }
-                    }
+                    for (int i = 0; i < 16; ++i) sacc[b][i] = 0.f;
                 }
+#pragma unroll
+                for (int s = 0; s < D / 16; ++s)
+#pragma unroll
+                    for (int b = 0; b < 2; ++b) sacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[b][s], qf[s], sacc[b], 0, 0, 0);
             }
-            // V^T operands: V[keys cb+8g .. +8][dim 16db + lr], 16 contiguous bytes of the staged block;
-            // entries of keys at or past ke are zeroed (a probability of 0 times stale memory could be NaN)
-            u32x4 vr[D / 16];
-            const int k8 = cb + 8 * g;
+            // value i of block b is the score of key cb + 32 b + 16 (i / 8) + 8 h + i % 8
+            if (cb + KT > all_vis) {
 #pragma unroll
-            for (int db = 0; db < D / 16; ++db) vr[db] = *(const u32x4*)(lv + g * ROWS_VBS + (db * 16 + lr) * 8);
-            if (k8 + 8 > ke) {
+                for (int b = 0; b < 2; ++b)
 #pragma unroll
-                for (int db = 0; db < D / 16; ++db)
+                    for (int i = 0; i < 16; ++i)
+                        if (cb + 32 * b + 16 * (i / 8) + 8 * h + (i % 8) >= rl) sacc[b][i] = kNegInf;
+            }
+            float mx = sacc[0][0];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const uint32_t keep = (k8 + 2 * e < ke ? 0xffffu : 0u) | (k8 + 2 * e + 1 < ke ? 0xffff0000u : 0u);
-                        vr[db][e] &= keep;
-                    }
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[b][i]);
+            mx = fmaxf(mx, swap32(mx));                  // the row's other 32 keys sit in lane c ^ 32
+            // lazy reference max: moved only when the chunk's max exceeds it by more than kLazyLog2, so the
+            // accumulators are rarely rescaled; probabilities stay below 2^kLazyLog2
+            const float mxs = mx * a.scale_log2;
+            const bool up = mxs > m + kLazyLog2;
+            const float mn = up ? mxs : m;
+            const float alpha = up ? __builtin_amdgcn_exp2f(m - mn) : 1.f;   // m == -inf -> 0
+            m = mn;
+            const float nm = (mn == kNegInf) ? 0.f : -mn;
+            float ps[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    sacc[b][i] = __builtin_amdgcn_exp2f(fmaf(sacc[b][i], a.scale_log2, nm));   // -inf -> 0
+                    ps[i % 4] += sacc[b][i];
+                }
+            const float sum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
+            l = l * alpha + sum;
+            if (__ballot(alpha != 1.f) != 0) {
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
             }
 #pragma unroll
-            for (int rb = 0; rb < RB; ++rb) {
-                if (cb >= wml[rb]) continue;
-                float alpha;
-                softmax_chunk(sc[rb], st2[rb].m, st2[rb].l, alpha);
-                rescale(st2[rb].o, alpha);
+            for (int j = 0; j < KT / 16; ++j) {
                 bf16x8 ph, pl;
-                split_p(sc[rb], ph, pl);
+                split_p8(sacc[j / 2], 8 * (j % 2), ph, pl);
 #pragma unroll
-                for (int db = 0; db < D / 16; ++db) {
-                    const bf16x8 vv8 = __builtin_bit_cast(bf16x8, vr[db]);
-                    st2[rb].o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv8, ph, st2[rb].o[db], 0, 0, 0);
-                    st2[rb].o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv8, pl, st2[rb].o[db], 0, 0, 0);
+                for (int db = 0; db < D / 32; ++db) {
+                    // V^T operand: keys cb + 16 j + 8 h .. + 8 at dim 32 db + c, 16 contiguous bytes of a block
+                    const bf16x8 vv = *(const bf16x8*)(lv + (2 * j + h) * 8 * D + (32 * db + c) * 8);
+                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, ph, oacc[db], 0, 0, 0);
+                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, pl, oacc[db], 0, 0, 0);
                 }
             }
         };
@@ -608,20 +679,32 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
             else wait_vmcnt<0>();
             lds_barrier();
             if (t + ROWS_NS - 1 < ntiles) issue((t + ROWS_NS - 1) % ROWS_NS, t + ROWS_NS - 1);
+            if (t == ntiles - 1 && kb + (t + 1) * KT > ke) {
+                // the last tile holds keys at or past ke: zero their V entries (a probability of 0 times
+                // stale memory could be NaN); K rows there are copies of key ke - 1, masked in the scores
+                const int nvalid = ke - (kb + t * KT);
+                uint16_t* lvw = (uint16_t*)smem + (t % ROWS_NS) * ROWS_STAGE + KT * D;
+                for (int idx = tid; idx < (KT - nvalid) * D; idx += 256) {
+                    const int kk = nvalid + idx / D, d = idx % D;
+                    lvw[(kk >> 3) * 8 * D + d * 8 + (kk & 7)] = 0;
+                }
+                __syncthreads();
+            }
             compute(t, t % ROWS_NS);
         }
+        const float lt = l + swap32(l);                  // l of lane c plus that of lane c ^ 32 (the same in both lanes)
+        if (ok) {
+            const float inv = 1.f / lt;
+            T* orow = (T*)a.out + (long long)(tok0 + rtok) * a.out_stride + (long long)rhead * D;
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-            float l = st2[rb].l;                             // row sum over the 4 lanes of the row
-            l += shfl_xor(l, 16);
-            l += shfl_xor(l, 32);
-            if (!rok[rb]) continue;
-            const float inv = 1.f / l;
-            T* orow = (T*)a.out + (long long)(tok0 + rtok[rb]) * a.out_stride + (long long)rhead[rb] * D;
+            for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-            for (int db = 0; db < D / 16; ++db)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) Store<DT>::st(orow + db * 16 + 4 * g + r, st2[rb].o[db][r] * inv);
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    u32x2 v;
+                    v[0] = pack_bf16x2(oacc[db][4 * g4] * inv, oacc[db][4 * g4 + 1] * inv);
+                    v[1] = pack_bf16x2(oacc[db][4 * g4 + 2] * inv, oacc[db][4 * g4 + 3] * inv);
+                    *(u32x2*)(orow + 32 * db + 8 * g4 + 4 * h) = v;
+                }
         }
         return;
     } else {
