@@ -34,8 +34,12 @@ Pins (tests marked ``not gpu``) tie each part to facts the pages fix: the
 lecture's continuous-batching timeline, the Figure-3 and Figure-5 counts, the
 exercise-4 token and (query, key)-pair counts, closed forms of the scalar
 functions, brute-force attention, and the continuous == one-at-a-time
-invariant.  The pages' worked numbers for the lecture's mini model (max logit
-difference 1.1e-6, 4.88x fewer weight bytes) need that model's code, which the
-pages do not include: parity unpinned for those two figures.
+invariant.  Every function here has such a pin.  The pages also print two
+measurements of the lecture's own program (a largest logit difference of
+1.1e-6 between batched and one-at-a-time computation, and 4.88x fewer weight
+bytes read); no function here computes either figure -- they depend on that
+program's model and byte accounting, which the pages do not give.  The
+property behind the first (batched equals one-at-a-time up to rounding) is
+pinned by the flat == per-request and continuous == one-at-a-time tests.
 """
 from . import scheduler, model, flat, brute, generate, precision  # noqa: F401
