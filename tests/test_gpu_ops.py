@@ -224,16 +224,18 @@ TINY_F32 = ModelDims("attn-f32", "gpt", 1, H=64, nq=4, nkv=4, d=16, F=64, V=0)
 MINI_ATT = ModelDims("attn-mini", "gpt", 1, H=256, nq=8, nkv=8, d=32, F=64, V=0)
 GQA_BF16 = ModelDims("attn-gqa", "llama", 1, H=1024, nq=8, nkv=2, d=128, F=64, V=0, rope_theta=500000.0)
 GQA_F32 = ModelDims("attn-gqa32", "llama", 1, H=512, nq=8, nkv=2, d=64, F=64, V=0, rope_theta=10000.0)
+GQA64_BF16 = ModelDims("attn-gqa64", "llama", 1, H=512, nq=8, nkv=2, d=64, F=64, V=0, rope_theta=10000.0)
 
 
 @pytest.mark.parametrize("m,dtype", [(TINY_F32, "fp32"), (MINI_ATT, "bf16"), (MINI_ATT, "fp32"), (GQA_BF16, "bf16"),
-                                     (GQA_F32, "fp32")])
+                                     (GQA_F32, "fp32"), (GQA64_BF16, "bf16")])
 def test_attention_figure5_and_exercise4(m, dtype):
     _attention_case(m, dtype, [(1, 3), (1, 1), (2, 0), (3, 0)], 1, rope_check=True)
     _attention_case(m, dtype, [(37, 0), (9, 0), (1, 120), (1, 15), (1, 64)], 2)
 
 
-@pytest.mark.parametrize("m,dtype", [(MINI_ATT, "bf16"), (GQA_BF16, "bf16"), (GQA_F32, "fp32"), (TINY_F32, "fp32")])
+@pytest.mark.parametrize("m,dtype", [(MINI_ATT, "bf16"), (GQA_BF16, "bf16"), (GQA_F32, "fp32"), (TINY_F32, "fp32"),
+                                     (GQA64_BF16, "bf16")])
 @pytest.mark.parametrize("seed", range(3))
 def test_attention_random_ragged(m, dtype, seed):
     batch = random_ragged_batch(seed, 7, 1500, 90)     # long histories -> split items; big prefills -> row tiles
@@ -300,11 +302,12 @@ def test_append_writes_only_its_slots(m, dtype):
         sb.sb_kv_destroy(kv)
 
 
-def test_attention_prefill_tile_shape_invariant():
-    """A prompt's attention alone (few row tiles: one 16-row block per wave, 64-row tiles) and among 32 other
-    prompts (over 1024 tiles of 64 rows: two blocks per wave, 128-row tiles) gives the same bits: a row's
+@pytest.mark.parametrize("m", [GQA_BF16, GQA64_BF16, ModelDims("attn-gqa-d32", "llama", 1, H=256, nq=8, nkv=2, d=32,
+                                                              F=64, V=0, rope_theta=10000.0)])
+def test_attention_prefill_tile_shape_invariant(m):
+    """A prompt's attention alone (few row tiles: 64-row tiles, 16 real rows per wave) and among 32 other
+    prompts (over 1024 tiles of 64 rows: 128-row tiles, 32 real rows per wave) gives the same bits: a row's
     arithmetic does not depend on the tile it falls in."""
-    m = GQA_BF16
     dims = make_dims(m, "bf16")
     target = (300, 17)
     others = [(256, 0)] * 32
