@@ -256,18 +256,22 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_bf16_kernel(GemmA
 }
 
 // ================================================================== bf16 MFMA, register ring
-// Small problems (decode-heavy batches): few workgroups, each walking all of K,
-// so what bounds them is the bytes one workgroup keeps in flight.  Loads go to
-// registers first -- a ring of PF 64-deep K tiles per thread, each load issued
-// PF steps before its tile is used -- and each tile is copied to LDS (two
-// buffers, padded rows) one step before its MFMAs.  Same operand layout, MFMA
-// and K order as gemm_bf16_kernel, so results are bitwise those of every other
-// configuration.
-template <int BM, int BN, int WAVES_M, int WAVES_N, int PF, int EPI>
+// Small problems (decode-heavy batches): few workgroups, each walking all of K.
+// Loads go to registers first -- a ring of PF BK-deep K tiles per thread, each
+// load issued PF steps before its tile is used -- and each tile is copied to LDS
+// (two buffers, padded rows) one step before its MFMAs.  A step costs a fixed
+// latency (copy to LDS, barrier, operand reads, MFMA chain) besides its bytes, so
+// deeper steps move more bytes per step: 128-deep steps with 4 in flight take the
+// 8B-shaped FFN2 at 64 rows from 46 to 37 us against 64-deep steps with 8 in
+// flight (same bytes in flight).  Same operand layout, MFMA and K order (32-wide
+// MFMA steps, ascending) as gemm_bf16_kernel, so results are bitwise those of
+// every other configuration.
+template <int BM, int BN, int WAVES_M, int WAVES_N, int PF, int EPI, int BK>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_bf16_ring_kernel(GemmArgs a) {
     static_assert(PF % 2 == 0, "ring slot parity selects the LDS buffer");
+    static_assert(BK % 64 == 0, "K depth of a step");
     constexpr int THREADS = 64 * WAVES_M * WAVES_N;
-    constexpr int BK = 64, LDSK = BK + 8;            // 144-byte rows: conflict-free 16-byte reads
+    constexpr int LDSK = BK + 8;                     // rows padded by 16 bytes: conflict-free 16-byte reads
     constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
     constexpr int MI = WM / 16, NI = WN / 16;
     constexpr int CH = BK / 8;                       // 16-byte chunks per row
@@ -649,7 +653,7 @@ enum {
     CFG_DMA_256x192_8W_K64_S2_SPREAD, CFG_DMA_192x256_8W_K64_S2_SPREAD,                       // fewer-tile shapes
     CFG_DMA_64x32_4W_K64_S8, CFG_DMA_64x16_2W_K64_S6, CFG_DMA_64x64_4W_K64_S6,                // skinny: deep K pipelines
     CFG_DMA_256x384_8W_K64_S2_SPREAD,                                                         // all of LDS
-    CFG_RING_64x32_PF8, CFG_RING_64x64_PF6, CFG_RING_32x32_PF8, CFG_RING_32x64_PF8,          // register rings
+    CFG_RING_64x32, CFG_RING_64x64, CFG_RING_32x32, CFG_RING_32x64,                          // register rings
     CFG_COUNT
 };
 
@@ -675,15 +679,21 @@ int launch_dma(const GemmArgs& a, hipStream_t s) {
     }
 }
 
-template <int BM, int BN, int WMW, int WNW, int PF, int EPI>
+// Register rings take 128-deep K steps, 4 in flight; a K that is not a multiple of 128 takes 64-deep steps,
+// 8 in flight (the same MFMA sequence either way).
+template <int BM, int BN, int WMW, int WNW, int EPI>
 int launch_ring(const GemmArgs& a, hipStream_t s) {
     if constexpr (EPI == EPI_SWIGLU && (BN / WNW / 2) % 16 != 0) {
-        return launch_ring<BM, 2 * BN, WMW, WNW, PF, EPI>(a, s);      // gate/up need 16-wide halves per wave
+        return launch_ring<BM, 2 * BN, WMW, WNW, EPI>(a, s);      // gate/up need 16-wide halves per wave
     } else {
         const int out_cols = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
         const long long tiles = (long long)((a.M + BM - 1) / BM) * ((a.N + out_cols - 1) / out_cols);
-        hipLaunchKernelGGL((gemm_bf16_ring_kernel<BM, BN, WMW, WNW, PF, EPI>), dim3((unsigned)tiles),
-                           dim3(64 * WMW * WNW), 0, s, a);
+        if (a.K % 128 == 0)
+            hipLaunchKernelGGL((gemm_bf16_ring_kernel<BM, BN, WMW, WNW, 4, EPI, 128>), dim3((unsigned)tiles),
+                               dim3(64 * WMW * WNW), 0, s, a);
+        else
+            hipLaunchKernelGGL((gemm_bf16_ring_kernel<BM, BN, WMW, WNW, 8, EPI, 64>), dim3((unsigned)tiles),
+                               dim3(64 * WMW * WNW), 0, s, a);
         return check_launch("gemm_bf16_ring");
     }
 }
@@ -697,22 +707,22 @@ int launch_ring(const GemmArgs& a, hipStream_t s) {
 // cu_rate (the CU's ceiling with several) are measured on MI355X, in GB/s: 128 x
 // 128 register-staged 42 / 55; 64 x 32 and 64 x 64 DMA-fed with 8 and 6 stages 40
 // and 44, 256 x 256 DMA-fed 40 (one per CU: their rings fill LDS); the
-// register-ring tiles 45 / 60.  Up to 256 rows the big tile competes here too (an
+// register-ring tiles (128-deep steps) 50 / 60.  Up to 256 rows the big tile competes here too (an
 // LM head over 64 rows streams its 1 GB of weights faster from 64 x 64 rings).  A
 // 64-deep K tile of a BM x BN workgroup is (BM + BN) x 128 bytes.  SwiGLU needs
 // 16-wide gate and up halves per wave, which the 32-column tiles do not have.
 // E.g. the 8B-shaped FFN2 (N 4096, K 14336) at M 64 takes the 32 x 32 ring: 256
-// tiles, one per CU, 1.84 MB each: ~44 us instead of 66 us with 64 x 32 tiles.
+// tiles, one per CU, 1.84 MB each: ~37 us instead of 53 us with 64 x 32 tiles.
 int pick_small(const GemmArgs& a, int epi) {
     struct Cand { int cfg, bm, bn; double wg_gbs, cu_gbs; };
     const Cand cands[8] = {{CFG_128x128_4W, 128, 128, 42.0, 55.0},
                            {CFG_DMA_256x256_8W_K64_S2, 256, 256, 40.0, 40.0},
                            {CFG_DMA_64x32_4W_K64_S8, 64, 32, 40.0, 40.0},
                            {CFG_DMA_64x64_4W_K64_S6, 64, 64, 44.0, 44.0},
-                           {CFG_RING_64x32_PF8, 64, 32, 45.0, 60.0},
-                           {CFG_RING_64x64_PF6, 64, 64, 45.0, 60.0},
-                           {CFG_RING_32x32_PF8, 32, 32, 45.0, 60.0},
-                           {CFG_RING_32x64_PF8, 32, 64, 45.0, 60.0}};
+                           {CFG_RING_64x32, 64, 32, 50.0, 60.0},
+                           {CFG_RING_64x64, 64, 64, 50.0, 60.0},
+                           {CFG_RING_32x32, 32, 32, 50.0, 60.0},
+                           {CFG_RING_32x64, 32, 64, 50.0, 60.0}};
     const int cus = num_cus();
     const double nk = (double)a.K / 64.0;
     const double wbytes = (double)(epi == EPI_SWIGLU ? 2 * a.N : a.N) * a.K * 2.0;
@@ -795,10 +805,10 @@ int launch_bf16(const GemmArgs& a, hipStream_t s) {
         case CFG_DMA_64x16_2W_K64_S6: return launch_dma<64, 16, 2, 1, 64, 6, 2, 0, EPI>(a, s);
         case CFG_DMA_64x64_4W_K64_S6: return launch_dma<64, 64, 2, 2, 64, 6, 2, 0, EPI>(a, s);
         case CFG_DMA_256x384_8W_K64_S2_SPREAD: return launch_dma<256, 384, 2, 4, 64, 2, 2, 1, EPI>(a, s);
-        case CFG_RING_64x32_PF8: return launch_ring<64, 32, 2, 2, 8, EPI>(a, s);
-        case CFG_RING_64x64_PF6: return launch_ring<64, 64, 2, 2, 6, EPI>(a, s);
-        case CFG_RING_32x32_PF8: return launch_ring<32, 32, 2, 2, 8, EPI>(a, s);
-        case CFG_RING_32x64_PF8: return launch_ring<32, 64, 2, 2, 8, EPI>(a, s);
+        case CFG_RING_64x32: return launch_ring<64, 32, 2, 2, EPI>(a, s);
+        case CFG_RING_64x64: return launch_ring<64, 64, 2, 2, EPI>(a, s);
+        case CFG_RING_32x32: return launch_ring<32, 32, 2, 2, EPI>(a, s);
+        case CFG_RING_32x64: return launch_ring<32, 64, 2, 2, EPI>(a, s);
         default: return launch_bf16_cfg<128, 128, 2, 2, EPI>(a, s);
     }
 }

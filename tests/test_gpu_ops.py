@@ -361,15 +361,16 @@ def test_attention_edge_cases():
     _attention_case(MINI_ATT, "bf16", [(16, 512), (1, 512), (1, 513)], 6)  # split boundaries
 
 
-N_GEMM_CFGS = 23  # register-staged 128x128, 256x256 (4 and 8 waves), 256x128, 128x256; DMA-fed: 4 with BK 32, 2 with BK 64, 2 spread, 256x192 + 192x256 spread, skinny 64x32 / 64x16 / 64x64 with deep K pipelines, 256x384 spread; register rings 64x32, 64x64, 32x32, 32x64
+N_GEMM_CFGS = 23  # register-staged 128x128, 256x256 (4 and 8 waves), 256x128, 128x256; DMA-fed: 4 with BK 32, 2 with BK 64, 2 spread, 256x192 + 192x256 spread, skinny 64x32 / 64x16 / 64x64 with deep K pipelines, 256x384 spread; register rings 64x32, 64x64, 32x32, 32x64 (128-deep K steps, or 64-deep when K % 128 != 0)
 
 
 @pytest.mark.parametrize("cfg", range(N_GEMM_CFGS))
 @pytest.mark.parametrize("epi", ["bias", "gelu", "resid", "swiglu"])
-@pytest.mark.parametrize("K", [512, 64, 192])
+@pytest.mark.parametrize("K", [512, 64, 192, 256, 384])
 def test_gemm_every_tile_config(cfg, epi, K, monkeypatch):
     """Each bf16 tile configuration (forced) on a ragged shape: M and N not multiples of the tile;
-    K = 64 and 192 leave fewer K tiles than LDS stages / a partial ring trip."""
+    K = 64 and 192 leave fewer K tiles than LDS stages / a partial ring trip (64-deep ring steps);
+    K = 256 and 384 leave two and three of the rings' four 128-deep steps in flight."""
     monkeypatch.setenv("SB_GEMM_CFG", str(cfg))
     M, N = 300, 640
     print_case("gemm cfg", cfg, epi, M, N, K)
@@ -426,11 +427,13 @@ def test_gemm_every_tile_config_few_rows(cfg, epi, M, monkeypatch):
 
 @pytest.mark.parametrize("epi", ["bias", "swiglu"])
 @pytest.mark.parametrize("M", [300, 33])
-def test_gemm_configs_bitwise_identical(epi, M, monkeypatch):
+@pytest.mark.parametrize("K", [512, 192])
+def test_gemm_configs_bitwise_identical(epi, M, K, monkeypatch):
     """Every tile configuration gives the same bits: each output sums K in 32-wide MFMA steps in
     ascending order whatever the tile, so the launcher's choice (which depends on M, i.e. on the
-    batch) never changes a result."""
-    N, K = 640, 512
+    batch) never changes a result.  K = 192 takes the register rings' 64-deep steps, K = 512 their
+    128-deep ones."""
+    N = 640
     A = normal(7, "A", (M, K), dtype="bf16")
     W = normal(7, "W", (2 * N if epi == "swiglu" else N, K), std=0.05, dtype="bf16")
     b = normal(7, "b", (N,), std=0.5, dtype="bf16")
