@@ -263,14 +263,17 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_bf16_kernel(GemmA
 // latency (copy to LDS, barrier, operand reads, MFMA chain) besides its bytes, so
 // deeper steps move more bytes per step: 128-deep steps with 4 in flight take the
 // 8B-shaped FFN2 at 64 rows from 46 to 37 us against 64-deep steps with 8 in
-// flight (same bytes in flight).  Same operand layout, MFMA and K order (32-wide
-// MFMA steps, ascending) as gemm_bf16_kernel, so results are bitwise those of
-// every other configuration.
-template <int BM, int BN, int WAVES_M, int WAVES_N, int PF, int EPI, int BK>
-__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_bf16_ring_kernel(GemmArgs a) {
+// flight (same bytes in flight).  With LW = 2 the workgroup has twice the waves
+// its MFMAs need: all of them load and copy, the first half computes, so the CU
+// keeps more loads outstanding (64 x 64 tiles at 330 rows: QKV 55 -> 44 us).
+// Same operand layout, MFMA and K order (32-wide MFMA steps, ascending) as
+// gemm_bf16_kernel, so results are bitwise those of every other configuration.
+template <int BM, int BN, int WAVES_M, int WAVES_N, int PF, int EPI, int BK, int LW>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N * LW) void gemm_bf16_ring_kernel(GemmArgs a) {
     static_assert(PF % 2 == 0, "ring slot parity selects the LDS buffer");
     static_assert(BK % 64 == 0, "K depth of a step");
-    constexpr int THREADS = 64 * WAVES_M * WAVES_N;
+    constexpr int THREADS = 64 * WAVES_M * WAVES_N * LW;
+    constexpr int NCW = WAVES_M * WAVES_N;           // waves that compute; all LW x NCW waves load
     constexpr int LDSK = BK + 8;                     // rows padded by 16 bytes: conflict-free 16-byte reads
     constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
     constexpr int MI = WM / 16, NI = WN / 16;
@@ -281,7 +284,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_bf16_ring_kernel(
     __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * LDSK];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+    const int wm = (wave % NCW) / WAVES_N, wn = (wave % NCW) % WAVES_N;
     const int tiles_m = (a.M + BM - 1) / BM;
     const int out_cols = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
     const int tiles_n = (a.N + out_cols - 1) / out_cols;
@@ -377,10 +380,11 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_bf16_ring_kernel(
             stash(s, s & 1);
             __syncthreads();
             load(s, kt0 + s + PF);
-            if (kt0 + s < nk) compute(s & 1);
+            if (kt0 + s < nk && wave < NCW) compute(s & 1);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
+    if (wave >= NCW) return;                         // a loading-only wave
 
     const int n_lane = (EPI == EPI_SWIGLU ? tn * (BN / 2) + wn * (WN / 2) : tn * BN + wn * WN) + (lane >> 4) * 4;
     tile_epilogue<MI, NI, EPI>(a, acc, m0 + wm * WM + lrow, n_lane);
@@ -679,20 +683,20 @@ int launch_dma(const GemmArgs& a, hipStream_t s) {
     }
 }
 
-// Register rings take 128-deep K steps, 4 in flight; a K that is not a multiple of 128 takes 64-deep steps,
-// 8 in flight (the same MFMA sequence either way).
-template <int BM, int BN, int WMW, int WNW, int EPI>
+// Register rings take 128-deep K steps (PF in flight, LW x the computing waves loading); a K that is not a
+// multiple of 128 takes 64-deep steps, 8 in flight, every wave computing (the same MFMA sequence either way).
+template <int BM, int BN, int WMW, int WNW, int LW, int PF, int EPI>
 int launch_ring(const GemmArgs& a, hipStream_t s) {
     if constexpr (EPI == EPI_SWIGLU && (BN / WNW / 2) % 16 != 0) {
-        return launch_ring<BM, 2 * BN, WMW, WNW, EPI>(a, s);      // gate/up need 16-wide halves per wave
+        return launch_ring<BM, 2 * BN, WMW, WNW, LW, PF, EPI>(a, s);      // gate/up need 16-wide halves per wave
     } else {
         const int out_cols = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
         const long long tiles = (long long)((a.M + BM - 1) / BM) * ((a.N + out_cols - 1) / out_cols);
         if (a.K % 128 == 0)
-            hipLaunchKernelGGL((gemm_bf16_ring_kernel<BM, BN, WMW, WNW, 4, EPI, 128>), dim3((unsigned)tiles),
-                               dim3(64 * WMW * WNW), 0, s, a);
+            hipLaunchKernelGGL((gemm_bf16_ring_kernel<BM, BN, WMW, WNW, PF, EPI, 128, LW>), dim3((unsigned)tiles),
+                               dim3(64 * WMW * WNW * LW), 0, s, a);
         else
-            hipLaunchKernelGGL((gemm_bf16_ring_kernel<BM, BN, WMW, WNW, 8, EPI, 64>), dim3((unsigned)tiles),
+            hipLaunchKernelGGL((gemm_bf16_ring_kernel<BM, BN, WMW, WNW, 8, EPI, 64, 1>), dim3((unsigned)tiles),
                                dim3(64 * WMW * WNW), 0, s, a);
         return check_launch("gemm_bf16_ring");
     }
@@ -707,7 +711,9 @@ int launch_ring(const GemmArgs& a, hipStream_t s) {
 // cu_rate (the CU's ceiling with several) are measured on MI355X, in GB/s: 128 x
 // 128 register-staged 42 / 55; 64 x 32 and 64 x 64 DMA-fed with 8 and 6 stages 40
 // and 44, 256 x 256 DMA-fed 40 (one per CU: their rings fill LDS); the
-// register-ring tiles (128-deep steps) 50 / 60.  Up to 256 rows the big tile competes here too (an
+// register-ring tiles (128-deep steps) 50 / 60 at 32 x 32, 53 / 70 at 64 x 32 and
+// 32 x 64 and 55 / 72 at 64 x 64 (those two with loading-only waves beside the
+// computing ones).  Up to 256 rows the big tile competes here too (an
 // LM head over 64 rows streams its 1 GB of weights faster from 64 x 64 rings).  A
 // 64-deep K tile of a BM x BN workgroup is (BM + BN) x 128 bytes.  SwiGLU needs
 // 16-wide gate and up halves per wave, which the 32-column tiles do not have.
@@ -719,15 +725,15 @@ int pick_small(const GemmArgs& a, int epi) {
                            {CFG_DMA_256x256_8W_K64_S2, 256, 256, 40.0, 40.0},
                            {CFG_DMA_64x32_4W_K64_S8, 64, 32, 40.0, 40.0},
                            {CFG_DMA_64x64_4W_K64_S6, 64, 64, 44.0, 44.0},
-                           {CFG_RING_64x32, 64, 32, 50.0, 60.0},
-                           {CFG_RING_64x64, 64, 64, 50.0, 60.0},
+                           {CFG_RING_64x32, 64, 32, 53.0, 70.0},
+                           {CFG_RING_64x64, 64, 64, 55.0, 72.0},
                            {CFG_RING_32x32, 32, 32, 50.0, 60.0},
-                           {CFG_RING_32x64, 32, 64, 50.0, 60.0}};
+                           {CFG_RING_32x64, 32, 64, 53.0, 70.0}};
     const int cus = num_cus();
     const double nk = (double)a.K / 64.0;
     const double wbytes = (double)(epi == EPI_SWIGLU ? 2 * a.N : a.N) * a.K * 2.0;
     int best = CFG_128x128_4W;
-    double best_t = 0.0;
+    double best_t = 0.0, best_cu = 0.0;
     for (int c = 0; c < 8; ++c) {
         const Cand& k = cands[c];
         if (epi == EPI_SWIGLU && k.bn == 32) continue;
@@ -736,8 +742,10 @@ int pick_small(const GemmArgs& a, int epi) {
         const double busiest = (double)((tiles + cus - 1) / cus);
         const double bytes = busiest * nk * (k.bm + k.bn) * 128.0;
         const double rate = std::min(k.cu_gbs, k.wg_gbs * busiest) * 1e3;        // bytes per us
-        const double t = std::max(bytes / rate, wbytes / 6e6);
-        if (c == 0 || t < best_t) { best = k.cfg; best_t = t; }
+        const double t_cu = bytes / rate;
+        const double t = std::max(t_cu, wbytes / 6e6);
+        // ties (both at the weight bound) go to the lighter per-CU load
+        if (c == 0 || t < best_t || (t == best_t && t_cu < best_cu)) { best = k.cfg; best_t = t; best_cu = t_cu; }
     }
     return best;
 }
@@ -805,10 +813,10 @@ int launch_bf16(const GemmArgs& a, hipStream_t s) {
         case CFG_DMA_64x16_2W_K64_S6: return launch_dma<64, 16, 2, 1, 64, 6, 2, 0, EPI>(a, s);
         case CFG_DMA_64x64_4W_K64_S6: return launch_dma<64, 64, 2, 2, 64, 6, 2, 0, EPI>(a, s);
         case CFG_DMA_256x384_8W_K64_S2_SPREAD: return launch_dma<256, 384, 2, 4, 64, 2, 2, 1, EPI>(a, s);
-        case CFG_RING_64x32: return launch_ring<64, 32, 2, 2, EPI>(a, s);
-        case CFG_RING_64x64: return launch_ring<64, 64, 2, 2, EPI>(a, s);
-        case CFG_RING_32x32: return launch_ring<32, 32, 2, 2, EPI>(a, s);
-        case CFG_RING_32x64: return launch_ring<32, 64, 2, 2, EPI>(a, s);
+        case CFG_RING_64x32: return launch_ring<64, 32, 2, 2, 2, 4, EPI>(a, s);
+        case CFG_RING_64x64: return launch_ring<64, 64, 2, 2, 2, 2, EPI>(a, s);
+        case CFG_RING_32x32: return launch_ring<32, 32, 2, 2, 1, 4, EPI>(a, s);
+        case CFG_RING_32x64: return launch_ring<32, 64, 2, 2, 2, 4, EPI>(a, s);
         default: return launch_bf16_cfg<128, 128, 2, 2, EPI>(a, s);
     }
 }
