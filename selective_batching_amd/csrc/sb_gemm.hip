@@ -658,6 +658,7 @@ enum {
     CFG_DMA_64x32_4W_K64_S8, CFG_DMA_64x16_2W_K64_S6, CFG_DMA_64x64_4W_K64_S6,                // skinny: deep K pipelines
     CFG_DMA_256x384_8W_K64_S2_SPREAD,                                                         // all of LDS
     CFG_RING_64x32, CFG_RING_64x64, CFG_RING_32x32, CFG_RING_32x64,                          // register rings
+    CFG_RING_96x64, CFG_RING_96x96, CFG_RING_128x128,                                        // register rings, mid M
     CFG_COUNT
 };
 
@@ -711,9 +712,11 @@ int launch_ring(const GemmArgs& a, hipStream_t s) {
 // cu_rate (the CU's ceiling with several) are measured on MI355X, in GB/s: 128 x
 // 128 register-staged 42 / 55; 64 x 32 and 64 x 64 DMA-fed with 8 and 6 stages 40
 // and 44, 256 x 256 DMA-fed 40 (one per CU: their rings fill LDS); the
-// register-ring tiles (128-deep steps) 50 / 60 at 32 x 32, 53 / 70 at 64 x 32 and
-// 32 x 64 and 55 / 72 at 64 x 64 (those two with loading-only waves beside the
-// computing ones).  Up to 256 rows the big tile competes here too (an
+// register-ring tiles (128-deep steps) 50 / 60 at 32 x 32 and 53 / 70 for the
+// larger ones (with loading-only waves beside the computing ones).  The 96- and
+// 128-row rings serve the few-hundred-row GEMMs of an iteration in which a prompt
+// joins the decodes (8B shapes at 330 rows: QKV 48 -> 32 us on 96 x 96 tiles,
+// FFN2 114 -> 82 us on 96 x 64).  Up to 256 rows the big tile competes here too (an
 // LM head over 64 rows streams its 1 GB of weights faster from 64 x 64 rings).  A
 // 64-deep K tile of a BM x BN workgroup is (BM + BN) x 128 bytes.  SwiGLU needs
 // 16-wide gate and up halves per wave, which the 32-column tiles do not have.
@@ -721,20 +724,24 @@ int launch_ring(const GemmArgs& a, hipStream_t s) {
 // tiles, one per CU, 1.84 MB each: ~37 us instead of 53 us with 64 x 32 tiles.
 int pick_small(const GemmArgs& a, int epi) {
     struct Cand { int cfg, bm, bn; double wg_gbs, cu_gbs; };
-    const Cand cands[8] = {{CFG_128x128_4W, 128, 128, 42.0, 55.0},
-                           {CFG_DMA_256x256_8W_K64_S2, 256, 256, 40.0, 40.0},
-                           {CFG_DMA_64x32_4W_K64_S8, 64, 32, 40.0, 40.0},
-                           {CFG_DMA_64x64_4W_K64_S6, 64, 64, 44.0, 44.0},
-                           {CFG_RING_64x32, 64, 32, 53.0, 70.0},
-                           {CFG_RING_64x64, 64, 64, 55.0, 72.0},
-                           {CFG_RING_32x32, 32, 32, 50.0, 60.0},
-                           {CFG_RING_32x64, 32, 64, 53.0, 70.0}};
+    constexpr int NC = 11;
+    const Cand cands[NC] = {{CFG_128x128_4W, 128, 128, 42.0, 55.0},
+                            {CFG_DMA_256x256_8W_K64_S2, 256, 256, 40.0, 40.0},
+                            {CFG_DMA_64x32_4W_K64_S8, 64, 32, 40.0, 40.0},
+                            {CFG_DMA_64x64_4W_K64_S6, 64, 64, 44.0, 44.0},
+                            {CFG_RING_64x32, 64, 32, 53.0, 70.0},
+                            {CFG_RING_64x64, 64, 64, 53.0, 70.0},
+                            {CFG_RING_32x32, 32, 32, 50.0, 60.0},
+                            {CFG_RING_32x64, 32, 64, 53.0, 70.0},
+                            {CFG_RING_96x64, 96, 64, 53.0, 70.0},
+                            {CFG_RING_96x96, 96, 96, 53.0, 70.0},
+                            {CFG_RING_128x128, 128, 128, 53.0, 70.0}};
     const int cus = num_cus();
     const double nk = (double)a.K / 64.0;
     const double wbytes = (double)(epi == EPI_SWIGLU ? 2 * a.N : a.N) * a.K * 2.0;
     int best = CFG_128x128_4W;
     double best_t = 0.0, best_cu = 0.0;
-    for (int c = 0; c < 8; ++c) {
+    for (int c = 0; c < NC; ++c) {
         const Cand& k = cands[c];
         if (epi == EPI_SWIGLU && k.bn == 32) continue;
         const int out_cols = (epi == EPI_SWIGLU) ? k.bn / 2 : k.bn;
@@ -817,6 +824,9 @@ int launch_bf16(const GemmArgs& a, hipStream_t s) {
         case CFG_RING_64x64: return launch_ring<64, 64, 2, 2, 2, 2, EPI>(a, s);
         case CFG_RING_32x32: return launch_ring<32, 32, 2, 2, 1, 4, EPI>(a, s);
         case CFG_RING_32x64: return launch_ring<32, 64, 2, 2, 2, 4, EPI>(a, s);
+        case CFG_RING_96x64: return launch_ring<96, 64, 2, 2, 2, 2, EPI>(a, s);
+        case CFG_RING_96x96: return launch_ring<96, 96, 2, 2, 2, 2, EPI>(a, s);
+        case CFG_RING_128x128: return launch_ring<128, 128, 2, 2, 2, 2, EPI>(a, s);
         default: return launch_bf16_cfg<128, 128, 2, 2, EPI>(a, s);
     }
 }
