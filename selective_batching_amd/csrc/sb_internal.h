@@ -39,7 +39,7 @@ constexpr int kRowBlocksBf16 = 2;                          // most 16-row blocks
 // staged K/V tile then serves more rows); fewer tiles keep one block per wave (more, shorter items).
 constexpr int kRowBlocksMinTiles = 1024;
 constexpr int kUnitKeys = 512;            // keys per independently reduced unit
-constexpr int kTargetRuns = 1024;         // runs per launch the builder aims at (balance vs. run length)
+constexpr int kTargetRuns = 512;          // runs per launch the builder aims at (balance vs. run length)
 // An item also carries its request's first row, cached-token count and slot base (the
 // request-level metadata a workgroup would otherwise fetch through two more dependent
 // loads before its first q/K/V load); a group carries the request's first row.
