@@ -263,9 +263,11 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_bf16_kernel(GemmA
 // latency (copy to LDS, barrier, operand reads, MFMA chain) besides its bytes, so
 // deeper steps move more bytes per step: 128-deep steps with 4 in flight take the
 // 8B-shaped FFN2 at 64 rows from 46 to 37 us against 64-deep steps with 8 in
-// flight (same bytes in flight).  With LW = 2 the workgroup has twice the waves
-// its MFMAs need: all of them load and copy, the first half computes, so the CU
-// keeps more loads outstanding (64 x 64 tiles at 330 rows: QKV 55 -> 44 us).
+// flight (same bytes in flight).  With LW = 2 or 4 the workgroup has that many
+// times the waves its MFMAs need: all of them load and copy, the first NCW
+// compute, so the CU keeps more loads outstanding (64 x 64 tiles at 330 rows:
+// QKV 55 -> 44 us; 32 x 32 tiles with 256-deep steps and LW = 4 at 64 rows:
+// attention-out 12.0 -> 10.0 us).
 // Same operand layout, MFMA and K order (32-wide MFMA steps, ascending) as
 // gemm_bf16_kernel, so results are bitwise those of every other configuration.
 template <int BM, int BN, int WAVES_M, int WAVES_N, int PF, int EPI, int BK, int LW>
@@ -684,21 +686,28 @@ int launch_dma(const GemmArgs& a, hipStream_t s) {
     }
 }
 
-// Register rings take 128-deep K steps (PF in flight, LW x the computing waves loading); a K that is not a
-// multiple of 128 takes 64-deep steps, 8 in flight, every wave computing (the same MFMA sequence either way).
-template <int BM, int BN, int WMW, int WNW, int LW, int PF, int EPI>
+// Register rings: BIG tiles (96 rows or more) take 128-deep K steps, two in flight, twice the computing waves
+// loading; the small ones 256-deep steps, two in flight, four times the computing waves loading (128-deep,
+// four in flight, twice the waves, when K is not a multiple of 256).  A K that is not a multiple of 128 takes
+// 64-deep steps, 8 in flight, every wave computing.  The MFMA sequence is the same on every path.
+template <int BM, int BN, int WMW, int WNW, bool BIG, int EPI>
 int launch_ring(const GemmArgs& a, hipStream_t s) {
     if constexpr (EPI == EPI_SWIGLU && (BN / WNW / 2) % 16 != 0) {
-        return launch_ring<BM, 2 * BN, WMW, WNW, LW, PF, EPI>(a, s);      // gate/up need 16-wide halves per wave
+        return launch_ring<BM, 2 * BN, WMW, WNW, BIG, EPI>(a, s);      // gate/up need 16-wide halves per wave
     } else {
         const int out_cols = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
-        const long long tiles = (long long)((a.M + BM - 1) / BM) * ((a.N + out_cols - 1) / out_cols);
+        const dim3 grid((unsigned)((long long)((a.M + BM - 1) / BM) * ((a.N + out_cols - 1) / out_cols)));
+        constexpr int W = 64 * WMW * WNW;
+        if constexpr (!BIG) {
+            if (a.K % 256 == 0) {
+                hipLaunchKernelGGL((gemm_bf16_ring_kernel<BM, BN, WMW, WNW, 2, EPI, 256, 4>), grid, dim3(4 * W), 0, s, a);
+                return check_launch("gemm_bf16_ring");
+            }
+        }
         if (a.K % 128 == 0)
-            hipLaunchKernelGGL((gemm_bf16_ring_kernel<BM, BN, WMW, WNW, PF, EPI, 128, LW>), dim3((unsigned)tiles),
-                               dim3(64 * WMW * WNW * LW), 0, s, a);
+            hipLaunchKernelGGL((gemm_bf16_ring_kernel<BM, BN, WMW, WNW, BIG ? 2 : 4, EPI, 128, 2>), grid, dim3(2 * W), 0, s, a);
         else
-            hipLaunchKernelGGL((gemm_bf16_ring_kernel<BM, BN, WMW, WNW, 8, EPI, 64, 1>), dim3((unsigned)tiles),
-                               dim3(64 * WMW * WNW), 0, s, a);
+            hipLaunchKernelGGL((gemm_bf16_ring_kernel<BM, BN, WMW, WNW, 8, EPI, 64, 1>), grid, dim3(W), 0, s, a);
         return check_launch("gemm_bf16_ring");
     }
 }
@@ -820,13 +829,13 @@ int launch_bf16(const GemmArgs& a, hipStream_t s) {
         case CFG_DMA_64x16_2W_K64_S6: return launch_dma<64, 16, 2, 1, 64, 6, 2, 0, EPI>(a, s);
         case CFG_DMA_64x64_4W_K64_S6: return launch_dma<64, 64, 2, 2, 64, 6, 2, 0, EPI>(a, s);
         case CFG_DMA_256x384_8W_K64_S2_SPREAD: return launch_dma<256, 384, 2, 4, 64, 2, 2, 1, EPI>(a, s);
-        case CFG_RING_64x32: return launch_ring<64, 32, 2, 2, 2, 4, EPI>(a, s);
-        case CFG_RING_64x64: return launch_ring<64, 64, 2, 2, 2, 2, EPI>(a, s);
-        case CFG_RING_32x32: return launch_ring<32, 32, 2, 2, 1, 4, EPI>(a, s);
-        case CFG_RING_32x64: return launch_ring<32, 64, 2, 2, 2, 4, EPI>(a, s);
-        case CFG_RING_96x64: return launch_ring<96, 64, 2, 2, 2, 2, EPI>(a, s);
-        case CFG_RING_96x96: return launch_ring<96, 96, 2, 2, 2, 2, EPI>(a, s);
-        case CFG_RING_128x128: return launch_ring<128, 128, 2, 2, 2, 2, EPI>(a, s);
+        case CFG_RING_64x32: return launch_ring<64, 32, 2, 2, false, EPI>(a, s);
+        case CFG_RING_64x64: return launch_ring<64, 64, 2, 2, false, EPI>(a, s);
+        case CFG_RING_32x32: return launch_ring<32, 32, 2, 2, false, EPI>(a, s);
+        case CFG_RING_32x64: return launch_ring<32, 64, 2, 2, false, EPI>(a, s);
+        case CFG_RING_96x64: return launch_ring<96, 64, 2, 2, true, EPI>(a, s);
+        case CFG_RING_96x96: return launch_ring<96, 96, 2, 2, true, EPI>(a, s);
+        case CFG_RING_128x128: return launch_ring<128, 128, 2, 2, true, EPI>(a, s);
         default: return launch_bf16_cfg<128, 128, 2, 2, EPI>(a, s);
     }
 }
