@@ -682,11 +682,22 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
             if (t == ntiles - 1 && kb + (t + 1) * KT > ke) {
                 // the last tile holds keys at or past ke: zero their V entries (a probability of 0 times
                 // stale memory could be NaN); K rows there are copies of key ke - 1, masked in the scores
+                // blocks of 8 keys [D][8]: the blocks past the one holding key ke - 1 as whole 16-byte rows,
+                // that block's entries past ke - 1 with one masked rewrite of each of its D rows
                 const int nvalid = ke - (kb + t * KT);
                 uint16_t* lvw = (uint16_t*)smem + (t % ROWS_NS) * ROWS_STAGE + KT * D;
-                for (int idx = tid; idx < (KT - nvalid) * D; idx += 256) {
-                    const int kk = nvalid + idx / D, d = idx % D;
-                    lvw[(kk >> 3) * 8 * D + d * 8 + (kk & 7)] = 0;
+                const int vb0 = nvalid >> 3, e0 = nvalid & 7;
+                const int zb = e0 ? vb0 + 1 : vb0;              // first block with no valid key
+                for (int r = tid; r < (KT / 8 - zb) * D; r += 256) *(u32x4*)(lvw + (zb * D + r) * 8) = u32x4{0u, 0u, 0u, 0u};
+                if (e0) {
+                    for (int d = tid; d < D; d += 256) {
+                        u32x4* row = (u32x4*)(lvw + (vb0 * D + d) * 8);
+                        u32x4 v = *row;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            v[e] &= (2 * e < e0 ? 0xffffu : 0u) | (2 * e + 1 < e0 ? 0xffff0000u : 0u);
+                        *row = v;
+                    }
                 }
                 __syncthreads();
             }
