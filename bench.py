@@ -768,8 +768,8 @@ def main():
     f1 = kern["gemm_ffn1"]
     f1_flops = work["gemm_per_layer"]["ffn1"]
     f1_tflops = f1_flops / (f1["avg_ms"] * 1e-3) / 1e12
-    kern_name = ("gemm_bf16_dma_kernel<256,256,2,4,64,2,2,true,SWIGLU> (FFN1 gate/up GEMM + SiLU*up epilogue, "
-                 "256x256x64 tiles, copies spread over the MFMAs)")
+    kern_name = ("gemm_bf16_dma_kernel<224,384,2,4,64,2,2,true,SWIGLU> (FFN1 gate/up GEMM + SiLU*up epilogue, "
+                 "224x384x64 tiles: 1275 tiles, 5 full rounds at T = 3741; copies spread over the MFMAs)")
     roofline = {"kernel": kern_name, "bound": "mfma",
                 "achieved": round(f1_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(f1_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": ffn1_traffic(),

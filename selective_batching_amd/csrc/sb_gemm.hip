@@ -412,11 +412,16 @@ struct DmaCfg {
     static constexpr int CH = BK / 8;                            // 16-byte chunks per row
     static constexpr int RPI = 64 / CH;                          // rows per copy instruction
     static constexpr int STAGE_ELEMS = (BM + BN) * BK;           // A rows then B rows
-    static constexpr int A_INSTR = BM / RPI / NWAVES;            // copy instructions per wave per stage
-    static constexpr int B_INSTR = BN / RPI / NWAVES;
-    static constexpr int PER = A_INSTR + B_INSTR;
+    static constexpr int NA = BM / RPI, NCOPY = (BM + BN) / RPI; // copy instructions per stage, A's first
+    // EVEN: each wave issues A_INSTR copies of A and B_INSTR of W per stage (contiguous row blocks);
+    // otherwise copy c of a stage is issued by wave c % NWAVES, so a wave issues PER or PER - 1
+    static constexpr bool EVEN = NA % NWAVES == 0 && (NCOPY - NA) % NWAVES == 0;
+    static constexpr int A_INSTR = NA / NWAVES, B_INSTR = (NCOPY - NA) / NWAVES;
+    static constexpr int PER = EVEN ? A_INSTR + B_INSTR : (NCOPY + NWAVES - 1) / NWAVES;
     static_assert(BK == 32 || BK == 64, "BK");
-    static_assert(A_INSTR * RPI * NWAVES == BM && B_INSTR * RPI * NWAVES == BN, "rows must split evenly over waves");
+    static_assert(NA * RPI == BM && NCOPY * RPI == BM + BN, "whole copy instructions per operand");
+    // the two-stage ring waits for every copy before each step, so waves may issue different counts
+    static_assert(EVEN || STAGES == 2, "uneven copy split needs two stages");
     static_assert(STAGES >= 2 && (STAGES - 2) * PER <= 63, "vmcnt range");
     static_assert(STAGES * STAGE_ELEMS * 2 <= 160 * 1024, "LDS");
 };
@@ -429,6 +434,7 @@ __global__ __launch_bounds__(64 * WAVES_M_ * WAVES_N_, MINW) void gemm_bf16_dma_
     constexpr int BM = C::BM, BN = C::BN, BK = C::BK, WAVES_N = C::WAVES_N, STAGES = C::STAGES;
     constexpr int WM = C::WM, WN = C::WN, MI = C::MI, NI = C::NI, CH = C::CH, RPI = C::RPI;
     constexpr int STAGE_ELEMS = C::STAGE_ELEMS, A_INSTR = C::A_INSTR, B_INSTR = C::B_INSTR, PER = C::PER;
+    constexpr int NA = C::NA, NCOPY = C::NCOPY, NWAVES = C::NWAVES;
     __shared__ __attribute__((aligned(1024))) uint16_t smem[STAGES * STAGE_ELEMS];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -449,19 +455,15 @@ __global__ __launch_bounds__(64 * WAVES_M_ * WAVES_N_, MINW) void gemm_bf16_dma_
 
     const uint16_t* A = (const uint16_t*)a.A;
     const uint16_t* W = (const uint16_t*)a.W;
-    // element offsets (32-bit: every operand here is < 2^31 elements) of this lane's source chunks:
-    // lane -> row lane / CH of the instruction's rows, LDS slot lane % CH, source chunk slot ^ sw(row)
-    int srcA[A_INSTR];
-    int srcB[B_INSTR];
-#pragma unroll
-    for (int j = 0; j < A_INSTR; ++j) {
-        const int row = (wave * A_INSTR + j) * RPI + lane / CH;
+    // Copy instruction c of a stage (c < NCOPY) fills stage bytes [1024 c, 1024 (c + 1)): row block c
+    // (rows RPI c ..) of A for c < NA, else row block c - NA of W.  Element offsets (32-bit: every
+    // operand here is < 2^31 elements) of this lane's source chunk for a tile row: lane -> row lane / CH
+    // of the instruction's rows, LDS slot lane % CH, source chunk slot ^ sw(row).
+    auto a_src = [&](int row) {
         const int chunk = (lane % CH) ^ ((row >> 1) % CH);
-        srcA[j] = min(m0 + row, a.M - 1) * (int)a.lda + chunk * 8;
-    }
-#pragma unroll
-    for (int j = 0; j < B_INSTR; ++j) {
-        const int row = (wave * B_INSTR + j) * RPI + lane / CH;
+        return min(m0 + row, a.M - 1) * (int)a.lda + chunk * 8;
+    };
+    auto b_src = [&](int row) {
         const int chunk = (lane % CH) ^ ((row >> 1) % CH);
         int gr;
         if (EPI == EPI_SWIGLU) {
@@ -471,16 +473,39 @@ __global__ __launch_bounds__(64 * WAVES_M_ * WAVES_N_, MINW) void gemm_bf16_dma_
         } else {
             gr = min(tn * BN + row, a.N - 1);
         }
-        srcB[j] = gr * (int)a.ldw + chunk * 8;
+        return gr * (int)a.ldw + chunk * 8;
+    };
+    int src[PER];
+    uint32_t dstA = 0, dstB = 0;
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    if constexpr (C::EVEN) {
+        // the wave's copies are A blocks wave * A_INSTR .. and W blocks wave * B_INSTR ..
+#pragma unroll
+        for (int j = 0; j < A_INSTR; ++j) src[j] = a_src((wave * A_INSTR + j) * RPI + lane / CH);
+#pragma unroll
+        for (int j = 0; j < B_INSTR; ++j) src[A_INSTR + j] = b_src((wave * B_INSTR + j) * RPI + lane / CH);
+        // LDS byte address of this wave's first A and B copy in stage 0 (wave-uniform, so scalar)
+        dstA = __builtin_amdgcn_readfirstlane(lds_addr(smem) + wave * A_INSTR * 1024);
+        dstB = __builtin_amdgcn_readfirstlane(lds_addr(smem) + BM * BK * 2 + wave * B_INSTR * 1024);
+    } else {
+        // the wave's copy d is the stage's copy wave + NWAVES d
+#pragma unroll
+        for (int d = 0; d < PER; ++d) {
+            const int c = wv + NWAVES * d;
+            src[d] = c < NA ? a_src(c * RPI + lane / CH) : b_src((c - NA) * RPI + lane / CH);
+        }
+        dstA = __builtin_amdgcn_readfirstlane(lds_addr(smem));
     }
-    // LDS byte address of this wave's first A and B copy in stage 0 (wave-uniform, so scalar)
-    const uint32_t dstA = __builtin_amdgcn_readfirstlane(lds_addr(smem) + wave * A_INSTR * 1024);
-    const uint32_t dstB = __builtin_amdgcn_readfirstlane(lds_addr(smem) + BM * BK * 2 + wave * B_INSTR * 1024);
-    // copy instruction d (A copies first, then B) of the tile at k0 into `stage`
+    // copy instruction d of this wave (EVEN: A copies first, then B) of the tile at k0 into `stage`
     auto piece = [&](int stage, int k0, int d) {
         const uint32_t so = (uint32_t)(stage * STAGE_ELEMS * 2);
-        if (d < A_INSTR) dma16(A + (srcA[d] + k0), dstA + so + d * 1024);
-        else dma16(W + (srcB[d - A_INSTR] + k0), dstB + so + (d - A_INSTR) * 1024);
+        if constexpr (C::EVEN) {
+            if (d < A_INSTR) dma16(A + (src[d] + k0), dstA + so + d * 1024);
+            else dma16(W + (src[d] + k0), dstB + so + (d - A_INSTR) * 1024);
+        } else {
+            const int c = wv + NWAVES * d;           // wave-uniform
+            if (c < NCOPY) dma16((c < NA ? A : W) + (src[d] + k0), dstA + so + c * 1024);
+        }
     };
     auto issue = [&](int stage, int k0) {
 #pragma unroll
@@ -661,6 +686,7 @@ enum {
     CFG_DMA_256x384_8W_K64_S2_SPREAD,                                                         // all of LDS
     CFG_RING_64x32, CFG_RING_64x64, CFG_RING_32x32, CFG_RING_32x64,                          // register rings
     CFG_RING_96x64, CFG_RING_96x96, CFG_RING_128x128,                                        // register rings, mid M
+    CFG_DMA_224x384_8W_K64_S2_SPREAD,                                                         // 76 copies per stage
     CFG_COUNT
 };
 
@@ -767,18 +793,19 @@ int pick_small(const GemmArgs& a, int epi) {
 }
 
 // Pick the tile.  Small GEMMs: pick_small.  Otherwise DMA-fed tiles of 64-deep
-// K: among 256x256, 256x192, 192x256 and 256x384 the one with the least
-// estimated time, rounds x tile area x feed factor, where rounds = ceil(tiles /
-// CUs) (one such workgroup per CU: a partial last round costs a whole one) and
-// the feed factor is the measured time per unit of tile area relative to
-// 256x256 on MI355X (1.083 for the 192-wide tiles, which move more bytes per
-// flop; 0.956 for 256x384, which moves fewer).  E.g. 3741 x 6144 (QKV) takes
-// 256x384 (240 tiles, one round) over 256x192 (480 tiles, two rounds); the FFN1
-// gate/up GEMM (28672 W rows) stays on 256x256 (7 rounds of 1680 tiles against
-// 5 rounds of 1125 larger ones, the last 39% full).  Copies are spread over the
-// MFMAs unless there is only one row of tiles (measured faster in one burst).
-// Every configuration sums each output's K in the same order with the same
-// MFMA, so the choice never changes a result bit.
+// K: among 256x256, 256x192, 192x256, 256x384 and 224x384 the one with the
+// least estimated time, rounds x tile area x feed factor, where rounds =
+// ceil(tiles / CUs) (one such workgroup per CU: a partial last round costs a
+// whole one) and the feed factor is the measured time per unit of tile area
+// relative to 256x256 on MI355X (1.083 for the 192-wide tiles, which move more
+// bytes per flop; 0.956 for 256x384, which moves fewer; 1.02 for 224x384,
+// whose 76 copies per stage split unevenly over the 8 waves).  E.g. 3741 x
+// 6144 (QKV) takes 256x384 (240 tiles, one round) over 256x192 (480 tiles, two
+// rounds); the FFN1 gate/up GEMM (28672 W rows) takes 224x384: 1275 tiles fill
+// exactly 5 rounds, against 7 rounds of 1680 256x256 tiles (the last 56% full;
+// measured 675 against 706 us).  Copies are spread over the MFMAs.  Every
+// configuration sums each output's K in the same order with the same MFMA, so
+// the choice never changes a result bit.
 int pick_cfg(const GemmArgs& a, int epi) {
     const char* e = getenv("SB_GEMM_CFG");             // tuning / test override: a CFG_* index
     if (e && *e) {
@@ -789,17 +816,19 @@ int pick_cfg(const GemmArgs& a, int epi) {
     const long long big = (long long)((a.M + 255) / 256) * ((ncols + 255) / 256);
     if (big < 128 || a.M <= 256) return pick_small(a, epi);
     struct Cand { int cfg, bm, bn; double feed; };
-    const Cand cands[4] = {{CFG_DMA_256x256_8W_K64_S2_SPREAD, 256, 256, 1.0},
-                           {CFG_DMA_256x192_8W_K64_S2_SPREAD, 256, 192, 1.083},
-                           {CFG_DMA_192x256_8W_K64_S2_SPREAD, 192, 256, 1.083},
-                           {CFG_DMA_256x384_8W_K64_S2_SPREAD, 256, 384, 0.956}};
+    constexpr int NC = 5;
+    const Cand cands[NC] = {{CFG_DMA_256x256_8W_K64_S2_SPREAD, 256, 256, 1.0},
+                            {CFG_DMA_256x192_8W_K64_S2_SPREAD, 256, 192, 1.083},
+                            {CFG_DMA_192x256_8W_K64_S2_SPREAD, 192, 256, 1.083},
+                            {CFG_DMA_256x384_8W_K64_S2_SPREAD, 256, 384, 0.956},
+                            {CFG_DMA_224x384_8W_K64_S2_SPREAD, 224, 384, 1.02}};
     const int cus = num_cus();
     int best = cands[0].cfg;
     double best_cost = 0.0;
-    for (int c = 0; c < 4; ++c) {
+    for (int c = 0; c < NC; ++c) {
         const Cand& k = cands[c];
         if (epi == EPI_SWIGLU && k.bn == 192) continue;           // gate/up need 16-wide halves per wave
-        if (epi == EPI_GELU && k.bn == 384) continue;             // erf's registers do not fit beside 192 accumulators
+        if (epi == EPI_GELU && k.bn == 384) continue;             // erf's registers do not fit beside 168+ accumulators
         const long long tiles = (long long)((a.M + k.bm - 1) / k.bm) * ((ncols + k.bn - 1) / k.bn);
         const long long rounds = (tiles + cus - 1) / cus;
         const double cost = (double)rounds * k.bm * k.bn * k.feed;
@@ -836,6 +865,7 @@ int launch_bf16(const GemmArgs& a, hipStream_t s) {
         case CFG_RING_96x64: return launch_ring<96, 64, 2, 2, true, EPI>(a, s);
         case CFG_RING_96x96: return launch_ring<96, 96, 2, 2, true, EPI>(a, s);
         case CFG_RING_128x128: return launch_ring<128, 128, 2, 2, true, EPI>(a, s);
+        case CFG_DMA_224x384_8W_K64_S2_SPREAD: return launch_dma<224, 384, 2, 4, 64, 2, 2, 1, EPI>(a, s);
         default: return launch_bf16_cfg<128, 128, 2, 2, EPI>(a, s);
     }
 }
