@@ -129,13 +129,10 @@ __device__ __forceinline__ void store4(typename Store<DT>::T* p, const float (&v
 // in ascending order; the 64 lane sums meet in an xor butterfly.
 //   norm_kernel<.., WPR = 1>: one wave per row (four rows per workgroup), the
 //     order above directly (hidden <= 256 PER).
-//   norm_kernel<.., WPR = 4>: one row per workgroup, for few rows (more CUs
-//     streaming, a quarter of the dependent loads per lane) or wide rows; the
-//     256 threads leave their piece sums in LDS and one wave adds them in the
-//     order above.
-//   norm_stream_kernel: many rows; each wave walks rows gw, gw + W, ... with
-//     the next row's loads in flight while it reduces and stores the current
-//     one, the gain and shift staged once per workgroup in LDS.
+//   norm_kernel<.., WPR = 4>: one row per workgroup (hidden > 1024): a quarter
+//     of the dependent loads per lane and several small workgroups per CU, so
+//     many rows' loads are in flight at once; the 256 threads leave their piece
+//     sums in LDS and one wave adds them in the order above.
 // 16-byte loads along the row.
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
@@ -237,60 +234,6 @@ __global__ __launch_bounds__(256) void norm_kernel(const float* x, const int* ro
     for (int q = 0; q < PER; ++q) {
         const int i = lane + LANES * q;
         if (i < n4) norm_piece_out<DT>(o + 4 * i, v[q], mean, rstd, gr[q], b ? &br[q] : nullptr);
-    }
-}
-
-template <int DT, int PER>
-__global__ __launch_bounds__(256) void norm_stream_kernel(const float* x, const int* row_map, const void* gam,
-                                                          const void* bet, void* out, int rows, int H, int kind,
-                                                          float eps) {
-    using T = typename Store<DT>::T;
-    using R = typename Raw4<DT>::T;
-    __shared__ R gs[64 * PER], bs[64 * PER];
-    const int lane = threadIdx.x & 63;
-    const int n4 = H / 4;
-    const T* g = (const T*)gam;
-    const T* b = (const T*)bet;
-    for (int i = threadIdx.x; i < n4; i += blockDim.x) {
-        gs[i] = *(const R*)(g + 4 * i);
-        if (b) bs[i] = *(const R*)(b + 4 * i);
-    }
-    __syncthreads();
-    const int W = gridDim.x * (blockDim.x >> 6);
-    int r = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-    if (r >= rows) return;
-    // a row's pieces lane, lane + 64, ...; past the row's end the last piece again (never used), so
-    // every load is issued unconditionally and the next row's stay in flight during this row's work
-    auto load_row = [&](float4 (&v)[PER], int rr) {
-        const long long src = row_map ? row_map[rr] : rr;
-        const float4* xr = (const float4*)(x + src * H);
-#pragma unroll
-        for (int q = 0; q < PER; ++q) v[q] = xr[min(lane + 64 * q, n4 - 1)];
-    };
-    float4 cur[PER], nxt[PER];
-    load_row(cur, r);
-    for (; r < rows; r += W) {
-        load_row(nxt, min(r + W, rows - 1));
-        float s = 0.f;
-        if (kind == 0) {
-#pragma unroll
-            for (int q = 0; q < PER; ++q)
-                if (lane + 64 * q < n4) s += piece_sum(cur[q]);
-        }
-        const float mean = kind == 0 ? wave_sum(s) / H : 0.f;
-        float s2 = 0.f;
-#pragma unroll
-        for (int q = 0; q < PER; ++q)
-            if (lane + 64 * q < n4) s2 += piece_sq(cur[q], mean);
-        const float rstd = 1.0f / sqrtf(wave_sum(s2) / H + eps);
-        T* o = (T*)out + (long long)r * H;
-#pragma unroll
-        for (int q = 0; q < PER; ++q) {
-            const int i = lane + 64 * q;
-            if (i < n4) norm_piece_out<DT>(o + 4 * i, cur[q], mean, rstd, gs[i], b ? &bs[i] : nullptr);
-        }
-#pragma unroll
-        for (int q = 0; q < PER; ++q) cur[q] = nxt[q];
     }
 }
 
@@ -539,11 +482,6 @@ __global__ __launch_bounds__(kArgmaxThreads) void argmax_kernel(const float* log
 
 }  // namespace
 
-// below this many rows a workgroup takes one row (see norm_kernel); from it on, the streaming
-// kernel with kNormStreamBlocksPerCU workgroups of four waves per CU
-constexpr int kNormRowsPerBlockMin = 1024;
-constexpr int kNormStreamBlocksPerCU = 2;
-
 int launch_norm(int dtype, int kind, int rows, int H, const float* x, const int* row_map, const void* g,
                 const void* b, float eps, void* out, hipStream_t s) {
     if (rows <= 0) return SB_OK;
@@ -553,17 +491,16 @@ int launch_norm(int dtype, int kind, int rows, int H, const float* x, const int*
     auto go = [&](auto kern, int blocks) {
         hipLaunchKernelGGL(kern, dim3(blocks), block, 0, s, x, row_map, g, b, out, rows, H, kind, eps);
     };
+    // one row per workgroup above hidden 1024, at every row count: at 3741 x 4096 17 us against 20 us for
+    // waves that each walk ~2 rows with the next row's loads in flight
     const int per4 = (rows + 3) / 4;
-    const int stream_blocks = std::min(per4, kNormStreamBlocksPerCU * num_cus());
     if (dtype == SB_BF16) {
         if (H <= 1024) go(norm_kernel<SB_BF16, 4, 1>, per4);
-        else if (H <= 4096 && rows < kNormRowsPerBlockMin) go(norm_kernel<SB_BF16, 4, 4>, rows);
-        else if (H <= 4096) go(norm_stream_kernel<SB_BF16, 16>, stream_blocks);
+        else if (H <= 4096) go(norm_kernel<SB_BF16, 4, 4>, rows);
         else go(norm_kernel<SB_BF16, 12, 4>, rows);
     } else {
         if (H <= 1024) go(norm_kernel<SB_F32, 4, 1>, per4);
-        else if (H <= 4096 && rows < kNormRowsPerBlockMin) go(norm_kernel<SB_F32, 4, 4>, rows);
-        else if (H <= 4096) go(norm_stream_kernel<SB_F32, 16>, stream_blocks);
+        else if (H <= 4096) go(norm_kernel<SB_F32, 4, 4>, rows);
         else go(norm_kernel<SB_F32, 12, 4>, rows);
     }
     return check_launch("norm");
