@@ -73,30 +73,6 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
     return t;
 }
 
-// x[t] = E[id_t] (+ P[pos_t]) in fp32.  A negative id -(1 + j) refers to the
-// token the previous iteration generated in its batch row j (prev[j], still on
-// the device); ids are clamped into the tables so no value can read outside them.
-template <int DT>
-__global__ __launch_bounds__(256) void embed_kernel(const int* ids, const int* pos, const void* tok, const void* pe,
-                                                    const int* prev, int prev_n, int vocab, float* x, int H) {
-    using T = typename Store<DT>::T;
-    const int t = blockIdx.x;
-    int id = ids[t];
-    if (id < 0) {
-        const int j = -1 - id;
-        id = (prev && j < prev_n) ? prev[j] : 0;
-    }
-    id = min(max(id, 0), vocab - 1);
-    const T* e = (const T*)tok + (long long)id * H;
-    const T* p = pe ? (const T*)pe + (long long)pos[t] * H : nullptr;
-    float* xo = x + (long long)t * H;
-    for (int i = threadIdx.x; i < H; i += blockDim.x) {
-        float v = Store<DT>::ld(e + i);
-        if (p) v += Store<DT>::ld(p + i);
-        xo[i] = v;
-    }
-}
-
 // Four consecutive elements of a dtype row as one 8-byte access (bf16) or one 16-byte access
 // (fp32); the pointer is aligned to the access.
 template <int DT>
@@ -119,6 +95,57 @@ __device__ __forceinline__ void store4(typename Store<DT>::T* p, const float (&v
         *(float4*)p = make_float4(v[0], v[1], v[2], v[3]);
     }
 }
+
+// x[t] = E[id_t] (+ P[pos_t]) in fp32.  A negative id -(1 + j) refers to the
+// token the previous iteration generated in its batch row j (prev[j], still on
+// the device); ids are clamped into the tables so no value can read outside them.
+template <int DT>
+__global__ __launch_bounds__(256) void embed_kernel(const int* ids, const int* pos, const void* tok, const void* pe,
+                                                    const int* prev, int prev_n, int vocab, float* x, int H, int vec) {
+    using T = typename Store<DT>::T;
+    const int t = blockIdx.x;
+    int id = ids[t];
+    if (id < 0) {
+        const int j = -1 - id;
+        id = (prev && j < prev_n) ? prev[j] : 0;
+    }
+    id = min(max(id, 0), vocab - 1);
+    const T* e = (const T*)tok + (long long)id * H;
+    const T* p = pe ? (const T*)pe + (long long)pos[t] * H : nullptr;
+    float* xo = x + (long long)t * H;
+    if (vec) {
+        // four elements per access (8-byte bf16 / 16-byte fp32 loads, 16-byte stores), every load of the row
+        // issued before the first store
+        constexpr int NV = 4;                         // hidden <= 4096: at most 4 pieces per thread
+        const int n4 = H / 4;
+        float v[NV][4];
+#pragma unroll
+        for (int q = 0; q < NV; ++q) {
+            const int i = threadIdx.x + q * blockDim.x;
+            if (i < n4) {
+                load4<DT>(e + 4 * i, v[q]);
+                if (p) {
+                    float w[4];
+                    load4<DT>(p + 4 * i, w);
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) v[q][c] += w[c];
+                }
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < NV; ++q) {
+            const int i = threadIdx.x + q * blockDim.x;
+            if (i < n4) *(float4*)(xo + 4 * i) = make_float4(v[q][0], v[q][1], v[q][2], v[q][3]);
+        }
+        return;
+    }
+    for (int i = threadIdx.x; i < H; i += blockDim.x) {
+        float v = Store<DT>::ld(e + i);
+        if (p) v += Store<DT>::ld(p + i);
+        xo[i] = v;
+    }
+}
+
 
 // LayerNorm (kind 0) or RMSNorm (kind 1) of fp32 rows into dtype rows; fp32
 // statistics, two passes over registers (mean, then centred second moment).
@@ -440,15 +467,28 @@ __global__ __launch_bounds__(kArgmaxThreads) void argmax_kernel(const float* log
     const float* x = logits + (long long)r * V;
     float bv = -INFINITY;
     int bi = V;
-    if ((V & 3) == 0) {
+    if ((V & 3) == 0 && ((uintptr_t)logits & 15) == 0) {
+        // 16-byte pieces k = threadIdx.x, + 1024, ... in ascending order, eight loads in flight per thread
         const float4* x4 = (const float4*)x;
-#pragma unroll 4
-        for (int k = threadIdx.x; k < V / 4; k += kArgmaxThreads) {
-            const float4 v = x4[k];
-            argmax_take(v.x, 4 * k, bv, bi, V);
-            argmax_take(v.y, 4 * k + 1, bv, bi, V);
-            argmax_take(v.z, 4 * k + 2, bv, bi, V);
-            argmax_take(v.w, 4 * k + 3, bv, bi, V);
+        const int n4 = V / 4;
+        constexpr int NB = 8;
+        for (int k0 = threadIdx.x; k0 < n4; k0 += NB * kArgmaxThreads) {
+            float4 v[NB];
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                const int k = k0 + b * kArgmaxThreads;
+                if (k < n4) v[b] = x4[k];
+            }
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                const int k = k0 + b * kArgmaxThreads;
+                if (k < n4) {
+                    argmax_take(v[b].x, 4 * k, bv, bi, V);
+                    argmax_take(v[b].y, 4 * k + 1, bv, bi, V);
+                    argmax_take(v[b].z, 4 * k + 2, bv, bi, V);
+                    argmax_take(v[b].w, 4 * k + 3, bv, bi, V);
+                }
+            }
         }
     } else {
         for (int i = threadIdx.x; i < V; i += kArgmaxThreads) argmax_take(x[i], i, bv, bi, V);
@@ -593,12 +633,15 @@ extern "C" int sb_embed_chained(const sb_model_dims* dims, const sb_model_weight
     if (dims->arch == SB_ARCH_GPT && !pe) return fail(SB_ERR_INVALID, "sb_embed: GPT needs pos_emb");
     hipStream_t s = (hipStream_t)stream;
     TimedScope ts(SB_K_EMBED, s);
+    // whole 4-element pieces, 16-byte aligned output rows and tables: the vector path (hidden <= 4096)
+    const int vec = dims->hidden % 4 == 0 && dims->hidden <= 4 * 4 * 256 &&
+                    (((uintptr_t)x | (uintptr_t)w->tok_emb | (uintptr_t)pe) % 16) == 0;
     if (dims->dtype == SB_BF16)
         hipLaunchKernelGGL(embed_kernel<SB_BF16>, dim3(rg->n_tokens), dim3(256), 0, s, rg->tok_ids, rg->tok_pos,
-                           w->tok_emb, pe, prev_ids, prev_n, dims->vocab, x, dims->hidden);
+                           w->tok_emb, pe, prev_ids, prev_n, dims->vocab, x, dims->hidden, vec);
     else
         hipLaunchKernelGGL(embed_kernel<SB_F32>, dim3(rg->n_tokens), dim3(256), 0, s, rg->tok_ids, rg->tok_pos,
-                           w->tok_emb, pe, prev_ids, prev_n, dims->vocab, x, dims->hidden);
+                           w->tok_emb, pe, prev_ids, prev_n, dims->vocab, x, dims->hidden, vec);
     return check_launch("embed");
 }
 
