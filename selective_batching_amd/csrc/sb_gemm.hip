@@ -6,11 +6,13 @@
 // arbitrary (ragged), so rows beyond T are masked; N and K come from the model.
 //
 // bf16: v_mfma_f32_16x16x32_bf16 tiles.  Large GEMMs: 256 x 256 (or 256 x 192,
-// 192 x 256, 256 x 384) workgroup tiles of 8 waves, two waves per SIMD, two LDS
-// stages of 64-deep K filled straight from global memory (global_load_lds,
-// XOR-swizzled rows: no bank conflicts on the operand reads), XCD-aware grouped
-// tile order.  Small GEMMs (decode-heavy batches): 128 x 128 register-staged
-// tiles or 64-row tiles with deep K rings, by a cost model.
+// 192 x 256, 256 x 384, 224 x 384) workgroup tiles of 8 waves, two waves per
+// SIMD, two LDS stages of 64-deep K filled straight from global memory
+// (global_load_lds, XOR-swizzled rows: no bank conflicts on the operand reads),
+// XCD-aware grouped tile order, the shape picked per GEMM from the rounds of
+// tiles over the CUs.  Small GEMMs (decode-heavy batches): register-ring tiles
+// of 32 to 128 rows (K steps of loads in flight in registers, loading-only
+// waves beside the computing ones), by a per-CU bytes cost model.
 // fp32: 16x16x4 fp32 MFMA tiles with a fixed, ascending K order.
 // Epilogues fuse bias, exact GeLU, SwiGLU (SiLU(gate) * up) or the residual
 // add into the fp32 stream x.
@@ -750,8 +752,8 @@ int launch_ring(const GemmArgs& a, hipStream_t s) {
 // cu_rate (the CU's ceiling with several) are measured on MI355X, in GB/s: 128 x
 // 128 register-staged 42 / 55; 64 x 32 and 64 x 64 DMA-fed with 8 and 6 stages 40
 // and 44, 256 x 256 DMA-fed 40 (one per CU: their rings fill LDS); the
-// register-ring tiles (128-deep steps) 50 / 60 at 32 x 32 and 53 / 70 for the
-// larger ones (with loading-only waves beside the computing ones).  The 96- and
+// register-ring tiles (128- or 256-deep steps) 50 / 60 at 32 x 32 and 53 / 70
+// for the larger ones (with loading-only waves beside the computing ones).  The 96- and
 // 128-row rings serve the few-hundred-row GEMMs of an iteration in which a prompt
 // joins the decodes (8B shapes at 330 rows: QKV 48 -> 32 us on 96 x 96 tiles,
 // FFN2 114 -> 82 us on 96 x 64).  Up to 256 rows the big tile competes here too (an
