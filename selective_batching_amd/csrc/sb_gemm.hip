@@ -692,6 +692,7 @@ enum {
     CFG_RING_64x32, CFG_RING_64x64, CFG_RING_32x32, CFG_RING_32x64,                          // register rings
     CFG_RING_96x64, CFG_RING_96x96, CFG_RING_128x128,                                        // register rings, mid M
     CFG_DMA_224x384_8W_K64_S2_SPREAD,                                                         // 76 copies per stage
+    CFG_RING_64x128,                                                                          // register ring, wide
     CFG_COUNT
 };
 
@@ -762,9 +763,15 @@ int launch_ring(const GemmArgs& a, hipStream_t s) {
 // 16-wide gate and up halves per wave, which the 32-column tiles do not have.
 // E.g. the 8B-shaped FFN2 (N 4096, K 14336) at M 64 takes the 32 x 32 ring: 256
 // tiles, one per CU, 1.84 MB each: ~37 us instead of 53 us with 64 x 32 tiles.
+// The 64 x 128 ring (128-deep steps) comes before the 96- and 128-row rings, so it
+// takes the estimates it ties with them (measured 5-10% faster there: QKV at 193
+// to 320 rows, attention-out and FFN2 at 385 to 512), and it wins where both it
+// and 64 x 64 sit at the weight bound but it moves fewer bytes per CU: the LM head
+// over 64 rows (196 -> 182 us) and the SwiGLU FFN1 at 33 to 64 rows (one 1.5 MB
+// tile per CU for 224 of them, against two 1 MB tiles on 192: 50.3 -> 49.3 us).
 int pick_small(const GemmArgs& a, int epi) {
     struct Cand { int cfg, bm, bn; double wg_gbs, cu_gbs; };
-    constexpr int NC = 11;
+    constexpr int NC = 12;
     const Cand cands[NC] = {{CFG_128x128_4W, 128, 128, 42.0, 55.0},
                             {CFG_DMA_256x256_8W_K64_S2, 256, 256, 40.0, 40.0},
                             {CFG_DMA_64x32_4W_K64_S8, 64, 32, 40.0, 40.0},
@@ -773,6 +780,7 @@ int pick_small(const GemmArgs& a, int epi) {
                             {CFG_RING_64x64, 64, 64, 53.0, 70.0},
                             {CFG_RING_32x32, 32, 32, 50.0, 60.0},
                             {CFG_RING_32x64, 32, 64, 53.0, 70.0},
+                            {CFG_RING_64x128, 64, 128, 53.0, 70.0},
                             {CFG_RING_96x64, 96, 64, 53.0, 70.0},
                             {CFG_RING_96x96, 96, 96, 53.0, 70.0},
                             {CFG_RING_128x128, 128, 128, 53.0, 70.0}};
@@ -871,6 +879,7 @@ int launch_bf16(const GemmArgs& a, hipStream_t s) {
         case CFG_RING_96x96: return launch_ring<96, 96, 2, 2, true, EPI>(a, s);
         case CFG_RING_128x128: return launch_ring<128, 128, 2, 2, true, EPI>(a, s);
         case CFG_DMA_224x384_8W_K64_S2_SPREAD: return launch_dma<224, 384, 2, 4, 64, 2, 2, 1, EPI>(a, s);
+        case CFG_RING_64x128: return launch_ring<64, 128, 2, 2, true, EPI>(a, s);
         default: return launch_bf16_cfg<128, 128, 2, 2, EPI>(a, s);
     }
 }

@@ -361,7 +361,7 @@ def test_attention_edge_cases():
     _attention_case(MINI_ATT, "bf16", [(16, 512), (1, 512), (1, 513)], 6)  # split boundaries
 
 
-N_GEMM_CFGS = 27  # register-staged 128x128, 256x256 (4 and 8 waves), 256x128, 128x256; DMA-fed: 4 with BK 32, 2 with BK 64, 2 spread, 256x192 + 192x256 spread, skinny 64x32 / 64x16 / 64x64 with deep K pipelines, 256x384 spread; register rings 64x32, 64x64, 32x32, 32x64, 96x64, 96x96, 128x128 (128-deep K steps, or 64-deep when K % 128 != 0); DMA-fed 224x384 spread (76 copies per stage, split unevenly over 8 waves)
+N_GEMM_CFGS = 28  # register-staged 128x128, 256x256 (4 and 8 waves), 256x128, 128x256; DMA-fed: 4 with BK 32, 2 with BK 64, 2 spread, 256x192 + 192x256 spread, skinny 64x32 / 64x16 / 64x64 with deep K pipelines, 256x384 spread; register rings 64x32, 64x64, 32x32, 32x64, 96x64, 96x96, 128x128 (128-deep K steps, or 64-deep when K % 128 != 0); DMA-fed 224x384 spread (76 copies per stage, split unevenly over 8 waves); register ring 64x128
 
 
 @pytest.mark.parametrize("cfg", range(N_GEMM_CFGS))
