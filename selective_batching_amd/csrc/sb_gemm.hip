@@ -754,7 +754,10 @@ int launch_ring(const GemmArgs& a, hipStream_t s) {
 // 128 register-staged 42 / 55; 64 x 32 and 64 x 64 DMA-fed with 8 and 6 stages 40
 // and 44, 256 x 256 DMA-fed 40 (one per CU: their rings fill LDS); the
 // register-ring tiles (128- or 256-deep steps) 50 / 60 at 32 x 32 and 53 / 70
-// for the larger ones (with loading-only waves beside the computing ones).  The 96- and
+// for the larger ones (with loading-only waves beside the computing ones), 53 /
+// 65 for 96 x 64 and 128 x 128 (fitted to the measured best tile of the 8B shapes
+// at 8 to 2000 rows: QKV at 385-480 rows, attention-out and FFN2 at 513-768 and
+// SwiGLU at 65-96 then take 128 x 128 rings, 3-16% faster).  The 96- and
 // 128-row rings serve the few-hundred-row GEMMs of an iteration in which a prompt
 // joins the decodes (8B shapes at 330 rows: QKV 48 -> 32 us on 96 x 96 tiles,
 // FFN2 114 -> 82 us on 96 x 64).  Up to 256 rows the big tile competes here too (an
@@ -781,9 +784,9 @@ int pick_small(const GemmArgs& a, int epi) {
                             {CFG_RING_32x32, 32, 32, 50.0, 60.0},
                             {CFG_RING_32x64, 32, 64, 53.0, 70.0},
                             {CFG_RING_64x128, 64, 128, 53.0, 70.0},
-                            {CFG_RING_96x64, 96, 64, 53.0, 70.0},
+                            {CFG_RING_96x64, 96, 64, 53.0, 65.0},
                             {CFG_RING_96x96, 96, 96, 53.0, 70.0},
-                            {CFG_RING_128x128, 128, 128, 53.0, 70.0}};
+                            {CFG_RING_128x128, 128, 128, 53.0, 65.0}};
     const int cus = num_cus();
     const double nk = (double)a.K / 64.0;
     const double wbytes = (double)(epi == EPI_SWIGLU ? 2 * a.N : a.N) * a.K * 2.0;
