@@ -452,6 +452,46 @@ def test_gemm_configs_bitwise_identical(epi, M, K, monkeypatch):
         assert torch.equal(outs[cfg], outs[0]), f"cfg {cfg} differs from cfg 0"
 
 
+# indices of register-ring tiles in the launcher's configuration list
+CFG_RING_32x32, CFG_RING_96x64, CFG_RING_128x128, CFG_RING_64x128 = 21, 23, 25, 27
+
+
+@pytest.mark.parametrize("cfg", [CFG_RING_64x128, CFG_RING_128x128, CFG_RING_96x64])
+@pytest.mark.parametrize("M", [64, 200])
+@pytest.mark.parametrize("K", [4096, 14336])
+@pytest.mark.parametrize("epi", ["swiglu", "resid"])
+def test_gemm_ring_tiles_at_model_k(cfg, M, K, epi, monkeypatch):
+    """The register-ring tiles the small-problem picker takes at decode and mid sizes, at the 8B-shaped model's
+    own K (4096: QKV, attention-out, FFN1, LM head; 14336: FFN2), i.e. over 32 or 112 of their 128-deep K steps:
+    element-wise against the oracle, and bitwise equal to the 32 x 32 ring with its 256-deep steps (one MFMA
+    chain per output over ascending K in both)."""
+    N = 512
+    print_case("gemm ring at model K", cfg, M, K, epi)
+    A = normal(cfg + M, "A", (M, K), dtype="bf16")
+    W = normal(cfg + M, "W", (2 * N if epi == "swiglu" else N, K), std=0.02, dtype="bf16")
+    x0 = normal(cfg + M, "x0", (M, N)).astype(np.float64)
+    dA, dW = dev(A, "bf16"), dev(W, "bf16")
+    code = sb.SB_EPI_SWIGLU if epi == "swiglu" else sb.SB_EPI_RESID
+
+    def run(c):
+        monkeypatch.setenv("SB_GEMM_CFG", str(c))
+        out = torch.from_numpy(x0.astype(np.float32)).cuda() if epi == "resid" else \
+            torch.zeros((M, N), dtype=torch.bfloat16, device="cuda")
+        sb.sb_op_gemm(sb.SB_BF16, code, M, N, K, dA.data_ptr(), K, dW.data_ptr(), K, None, out.data_ptr(), N, 0,
+                      N if epi == "swiglu" else 0, stream_handle())
+        _sync()
+        return out
+
+    got, ref = run(cfg), run(CFG_RING_32x32)
+    view = torch.int32 if epi == "resid" else torch.int16
+    assert torch.equal(got.view(view).cpu(), ref.view(view).cpu()), f"cfg {cfg} differs from the 32 x 32 ring"
+    if epi == "resid":
+        assert_close_rms(host(got), x0 + OM.linear(A, W), TOL["fp32"], f"cfg {cfg} resid M {M} K {K}")
+    else:
+        assert_close_elem(host(got), OM.silu(OM.linear(A, W[:N])) * OM.linear(A, W[N:]), "bf16",
+                          f"cfg {cfg} swiglu M {M} K {K}")
+
+
 def test_attention_unit_merge_is_batch_invariant():
     """A request's attention output does not depend on the batch around it.  Alone, its 512-key units are
     spread over several workgroups and merged by the combine step; among 400 long requests one workgroup
